@@ -1,0 +1,447 @@
+/*
+ * moe_oracle.c -- plain, slow CPU oracle of the local MoE forward chain.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or
+ * call this file; only the tests, the smoke check and the CPU-baseline leg
+ * of the benchmark use it.  It shares no code, header or table with the HIP
+ * library: it has its own number formats, its own rounding and its own loops.
+ *
+ * What it follows (citations name the page and its section):
+ *   - ruDNN User Guide (ruDNN 0.1.5 on docs.rs), section 3 "MoE workflow":
+ *     the chain is logits -> softmax/top-k -> compact dispatch -> SwiGLU
+ *     experts -> weighted combine.
+ *   - same guide, section 4 "Routing contract": FP32 softmax over all E
+ *     experts before top-k, ties to the lower expert id, optional
+ *     renormalisation of the selected weights, then a cast to the logits
+ *     dtype; rows holding NaN, +inf or only -inf keep NaN weights.
+ *   - same guide, section 5 "Expert weights and dispatch": x is [T,H], gate
+ *     and up are [E,I,H], down is [E,H,I]; dispatch drops no token; a saved
+ *     mapping restores token order.
+ *   - tiny-llm deep dive 5 (ops.rs), "softmax" block: max-shifted softmax;
+ *     "SiLU" block: silu(z) = z / (1 + exp(-z)) and the SwiGLU FFN
+ *     W_down(SiLU(W_gate x) * W_up x); "RMSNorm" block: why sums are kept
+ *     in double; "matvec" block: rows are independent, so rows may be
+ *     split over threads without locks.
+ *
+ * Precision: routing runs in binary32 exactly as the contract fixes it
+ * (each exp is computed in double and rounded once, the sum is taken
+ * sequentially in ascending expert id, p = q / S by IEEE division).  The
+ * experts and the combine accumulate in binary64 and round once to the
+ * storage dtype.  Build with -ffp-contract=off and without -ffast-math.
+ *
+ * Parity status: every function here is pinned by the CPU tests in
+ * tests/test_oracle.py (closed forms, brute force, library routines,
+ * invariants, the printed gather example).  Agreement with the oracle on
+ * the large workloads beyond those invariants is, by nature, unpinned.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* dtype codes of this file (its own numbering, matched by oracle/__init__.py) */
+enum { O_F32 = 0, O_F16 = 1, O_BF16 = 2 };
+
+#define O_INVALID_ROW 0xFFFFFFFFu
+
+/* ------------------------------------------------------------------ */
+/* Number formats, written from the IEEE 754 definitions.              */
+/* ------------------------------------------------------------------ */
+
+/* Round x to a binary format with p significand bits (hidden bit
+ * included), minimum normal exponent emin and maximum exponent emax,
+ * rounding to nearest, ties to even.  Subnormals keep the fixed quantum
+ * 2^(emin-p+1); values past the largest finite number become +-inf. */
+static double round_to_format(double x, int p, int emin, int emax)
+{
+    if (isnan(x) || isinf(x) || x == 0.0) return x;
+    int e2;
+    frexp(fabs(x), &e2);          /* |x| = m * 2^e2, m in [0.5, 1) */
+    int lead = e2 - 1;            /* exponent of the leading bit */
+    if (lead < emin) lead = emin; /* subnormal range: fixed quantum */
+    double quantum = ldexp(1.0, lead - (p - 1));
+    double r = nearbyint(x / quantum) * quantum; /* default mode: ties to even */
+    double maxfin = ldexp(2.0 - ldexp(1.0, 1 - p), emax);
+    if (fabs(r) > maxfin) return copysign(INFINITY, x);
+    return r;
+}
+
+double oracle_round_f32(double x) { return round_to_format(x, 24, -126, 127); }
+double oracle_round_f16(double x) { return round_to_format(x, 11, -14, 15); }
+double oracle_round_bf16(double x) { return round_to_format(x, 8, -126, 127); }
+
+static double f16_bits_to_double(uint16_t b)
+{
+    int sign = b >> 15, ex = (b >> 10) & 31, man = b & 1023;
+    double v;
+    if (ex == 31) v = man ? NAN : INFINITY;
+    else if (ex == 0) v = ldexp((double)man, -24);
+    else v = ldexp((double)(1024 + man), ex - 25);
+    return sign ? -v : v;
+}
+
+static uint16_t double_to_f16_bits(double x) /* x already representable */
+{
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    if (isnan(x)) return sign | 0x7E00;
+    double a = fabs(x);
+    if (isinf(a)) return sign | 0x7C00;
+    if (a == 0.0) return sign;
+    if (a < ldexp(1.0, -14)) return sign | (uint16_t)ldexp(a, 24); /* subnormal */
+    int e2;
+    frexp(a, &e2);
+    int lead = e2 - 1;
+    uint16_t man = (uint16_t)(ldexp(a, -lead) * 1024.0 - 1024.0);
+    return sign | (uint16_t)((lead + 15) << 10) | man;
+}
+
+static double bf16_bits_to_double(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+static uint16_t double_to_bf16_bits(double x) /* x already representable */
+{
+    if (isnan(x)) return (uint16_t)((signbit(x) ? 0x8000 : 0) | 0x7FC0);
+    float f = (float)x; /* exact: every bf16 value is a binary32 value */
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    return (uint16_t)(u >> 16);
+}
+
+/* element i of a buffer of dtype dt, widened to double (exact) */
+static double load_elem(const void* base, int dt, int64_t i)
+{
+    switch (dt) {
+    case O_F32: return (double)((const float*)base)[i];
+    case O_F16: return f16_bits_to_double(((const uint16_t*)base)[i]);
+    default:    return bf16_bits_to_double(((const uint16_t*)base)[i]);
+    }
+}
+
+/* store v into element i of a buffer of dtype dt, rounding once (RNE) */
+static void store_elem(void* base, int dt, int64_t i, double v)
+{
+    switch (dt) {
+    case O_F32: ((float*)base)[i] = (float)oracle_round_f32(v); break;
+    case O_F16: ((uint16_t*)base)[i] = double_to_f16_bits(oracle_round_f16(v)); break;
+    default:    ((uint16_t*)base)[i] = double_to_bf16_bits(oracle_round_bf16(v)); break;
+    }
+}
+
+static int elem_bytes(int dt) { return dt == O_F32 ? 4 : 2; }
+
+/* Exposed so the tests can pin the formats against numpy / torch. */
+void oracle_widen(const void* src, int dt, int64_t n, double* dst)
+{
+    for (int64_t i = 0; i < n; ++i) dst[i] = load_elem(src, dt, i);
+}
+
+void oracle_narrow(const double* src, int dt, int64_t n, void* dst)
+{
+    for (int64_t i = 0; i < n; ++i) store_elem(dst, dt, i, src[i]);
+}
+
+/* ------------------------------------------------------------------ */
+/* A tiny row-parallel loop (rows are independent, as in the matvec     */
+/* block of the tiny-llm ops.rs walk-through).                          */
+/* ------------------------------------------------------------------ */
+
+typedef void (*row_fn)(void* ctx, int64_t row);
+
+typedef struct {
+    row_fn fn;
+    void* ctx;
+    int64_t begin, end;
+} slice_t;
+
+static void* run_slice(void* arg)
+{
+    slice_t* s = (slice_t*)arg;
+    for (int64_t r = s->begin; r < s->end; ++r) s->fn(s->ctx, r);
+    return NULL;
+}
+
+static void parallel_rows(int64_t n, int nthreads, row_fn fn, void* ctx)
+{
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    if ((int64_t)nthreads > n) nthreads = (int)(n > 0 ? n : 1);
+    if (nthreads == 1) {
+        for (int64_t r = 0; r < n; ++r) fn(ctx, r);
+        return;
+    }
+    pthread_t th[256];
+    slice_t sl[256];
+    for (int t = 0; t < nthreads; ++t) {
+        sl[t].fn = fn;
+        sl[t].ctx = ctx;
+        sl[t].begin = n * t / nthreads;
+        sl[t].end = n * (t + 1) / nthreads;
+        pthread_create(&th[t], NULL, run_slice, &sl[t]);
+    }
+    for (int t = 0; t < nthreads; ++t) pthread_join(th[t], NULL);
+}
+
+/* ------------------------------------------------------------------ */
+/* Routing (ruDNN User Guide, section 4 "Routing contract").            */
+/* ------------------------------------------------------------------ */
+
+/* FP32 softmax of one row, max-shifted as in the tiny-llm softmax block.
+ * A NaN never wins "v > m"; a NaN, a +inf (inf - inf) or an all -inf row
+ * (-inf - -inf) therefore gives NaN in d, so S and every p become NaN:
+ * the plain arithmetic itself yields the NaN rows the contract keeps. */
+static void softmax_row_f32(const void* logits, int dt, int64_t row, int64_t E, float* p)
+{
+    float m = -INFINITY;
+    for (int64_t e = 0; e < E; ++e) {
+        float v = (float)load_elem(logits, dt, row * E + e);
+        if (v > m) m = v;
+    }
+    float S = 0.0f;
+    for (int64_t e = 0; e < E; ++e) {
+        float d = (float)load_elem(logits, dt, row * E + e) - m;
+        float q = (float)exp((double)d); /* exp rounded once to binary32 */
+        p[e] = q;
+        S += q; /* sequential, ascending expert id */
+    }
+    for (int64_t e = 0; e < E; ++e) p[e] = p[e] / S;
+}
+
+void oracle_softmax(const void* logits, int dt, int64_t T, int64_t E, float* probs)
+{
+    for (int64_t t = 0; t < T; ++t) softmax_row_f32(logits, dt, t, E, probs + t * E);
+}
+
+typedef struct {
+    const void* logits;
+    int dt;
+    int64_t E;
+    int k, renorm;
+    uint32_t* idx;
+    void* w;
+    float* w_f32;
+} route_ctx;
+
+static void route_one(void* vctx, int64_t t)
+{
+    route_ctx* c = (route_ctx*)vctx;
+    int64_t E = c->E;
+    int k = c->k;
+    float* p = (float*)malloc(sizeof(float) * (size_t)E);
+    unsigned char* taken = (unsigned char*)calloc((size_t)E, 1);
+    float* sel = (float*)malloc(sizeof(float) * (size_t)k);
+    softmax_row_f32(c->logits, c->dt, t, E, p);
+    /* top-k: k rounds, each takes the largest p not yet taken; only a
+     * strictly larger p displaces the current pick, so among equal p the
+     * lower expert id wins (ties favour lower ids).  In a NaN row no p is
+     * larger than another, so the picks are experts 0, 1, ..., k-1. */
+    for (int j = 0; j < k; ++j) {
+        int64_t best = -1;
+        for (int64_t e = 0; e < E; ++e) {
+            if (taken[e]) continue;
+            if (best < 0 || p[e] > p[best]) best = e;
+        }
+        taken[best] = 1;
+        c->idx[t * k + j] = (uint32_t)best;
+        sel[j] = p[best];
+    }
+    if (c->renorm) {
+        float R = 0.0f;
+        for (int j = 0; j < k; ++j) R += sel[j]; /* FP32, slot order */
+        for (int j = 0; j < k; ++j) sel[j] = sel[j] / R;
+    }
+    for (int j = 0; j < k; ++j) {
+        if (c->w_f32) c->w_f32[t * k + j] = sel[j];
+        store_elem(c->w, c->dt, t * k + j, (double)sel[j]); /* cast to logits dtype */
+    }
+    free(sel);
+    free(taken);
+    free(p);
+}
+
+/* logits [T,E] (dt), top_k in 1..E.  Writes idx [T,k] (U32), w [T,k] in the
+ * logits dtype and, if w_f32 is non-NULL, the FP32 weights before the cast.
+ * Returns 0, or -1 on a bad argument. */
+int oracle_route(const void* logits, int dt, int64_t T, int64_t E, int k, int renorm,
+                 uint32_t* idx, void* w, float* w_f32, int nthreads)
+{
+    if (T < 0 || E < 1 || k < 1 || k > E) return -1;
+    route_ctx c = {logits, dt, E, k, renorm, idx, w, w_f32};
+    parallel_rows(T, nthreads, route_one, &c);
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Dispatch (ruDNN User Guide, section 5): drop-free, grouped by expert. */
+/* ------------------------------------------------------------------ */
+
+/* Canonical order inside an expert: slots by (token, slot) ascending.
+ * The contract leaves the order inside an expert open; this is one valid
+ * order.  A slot whose expert id is >= E is not copied and its row_of_slot
+ * is 0xFFFFFFFF.  offsets is [E+1]: rows of expert e are
+ * [offsets[e], offsets[e+1]). */
+int oracle_dispatch(const uint32_t* idx, int64_t T, int k, int64_t E,
+                    const void* x, int64_t H, int dt,
+                    uint32_t* offsets, uint32_t* row_of_slot, uint32_t* token_of_row,
+                    void* dispatched)
+{
+    if (T < 0 || E < 1 || k < 1 || H < 0) return -1;
+    int64_t N = T * (int64_t)k;
+    uint32_t* cursor = (uint32_t*)calloc((size_t)E + 1, sizeof(uint32_t));
+    for (int64_t s = 0; s < N; ++s)
+        if (idx[s] < (uint64_t)E) cursor[idx[s]] += 1; /* counts */
+    uint32_t run = 0;
+    for (int64_t e = 0; e < E; ++e) { /* exclusive prefix sum, ascending e */
+        uint32_t n = cursor[e];
+        offsets[e] = run;
+        cursor[e] = run;
+        run += n;
+    }
+    offsets[E] = run;
+    size_t rowb = (size_t)H * (size_t)elem_bytes(dt);
+    for (int64_t t = 0; t < T; ++t) {
+        for (int j = 0; j < k; ++j) {
+            int64_t s = t * k + j;
+            uint32_t e = idx[s];
+            if (e >= (uint64_t)E) {
+                row_of_slot[s] = O_INVALID_ROW;
+                continue;
+            }
+            uint32_t r = cursor[e]++;
+            row_of_slot[s] = r;
+            token_of_row[r] = (uint32_t)t;
+            memcpy((char*)dispatched + (size_t)r * rowb, (const char*)x + (size_t)t * rowb, rowb);
+        }
+    }
+    free(cursor);
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* SwiGLU experts (ruDNN User Guide, section 5; tiny-llm ops.rs, SiLU). */
+/* ------------------------------------------------------------------ */
+
+double oracle_silu(double z) { return z / (1.0 + exp(-z)); }
+
+typedef struct {
+    const void* const* gate; /* E pointers, each [I,H] of dtype dt */
+    const void* const* up;   /* E pointers, each [I,H] */
+    const void* const* down; /* E pointers, each [H,I] */
+    int dt;
+    const void* rows; /* [N,H] dispatched rows */
+    const uint32_t* offsets;
+    int64_t E, H, I;
+    void* out;   /* [N,H] */
+    void* h_out; /* optional [N,I]: the stored activation */
+    int* bad;
+} experts_ctx;
+
+static int64_t expert_of_row(const uint32_t* offsets, int64_t E, int64_t r)
+{
+    for (int64_t e = 0; e < E; ++e)
+        if ((uint64_t)r < offsets[e + 1]) return e;
+    return -1;
+}
+
+static void expert_row(void* vctx, int64_t r)
+{
+    experts_ctx* c = (experts_ctx*)vctx;
+    int64_t e = expert_of_row(c->offsets, c->E, r);
+    int64_t H = c->H, I = c->I;
+    if (e < 0 || !c->gate[e] || !c->up[e] || !c->down[e]) {
+        *c->bad = 1;
+        return;
+    }
+    double* x = (double*)malloc(sizeof(double) * (size_t)H);
+    double* h = (double*)malloc(sizeof(double) * (size_t)I);
+    for (int64_t c2 = 0; c2 < H; ++c2) x[c2] = load_elem(c->rows, c->dt, r * H + c2);
+    for (int64_t i = 0; i < I; ++i) {
+        double g = 0.0, u = 0.0;
+        for (int64_t c2 = 0; c2 < H; ++c2) {
+            g += x[c2] * load_elem(c->gate[e], c->dt, i * H + c2);
+            u += x[c2] * load_elem(c->up[e], c->dt, i * H + c2);
+        }
+        double a = oracle_silu(g) * u;
+        /* h is stored in the weight dtype before the down projection */
+        switch (c->dt) {
+        case O_F32: h[i] = oracle_round_f32(a); break;
+        case O_F16: h[i] = oracle_round_f16(a); break;
+        default:    h[i] = oracle_round_bf16(a); break;
+        }
+        if (c->h_out) store_elem(c->h_out, c->dt, r * I + i, h[i]);
+    }
+    for (int64_t c2 = 0; c2 < H; ++c2) {
+        double y = 0.0;
+        for (int64_t i = 0; i < I; ++i) y += h[i] * load_elem(c->down[e], c->dt, c2 * I + i);
+        store_elem(c->out, c->dt, r * H + c2, y);
+    }
+    free(h);
+    free(x);
+}
+
+/* rows [N,H] grouped by offsets [E+1]; per-expert weight pointers (NULL for
+ * an expert that owns no row is fine).  out [N,H]; h_out [N,I] or NULL.
+ * Returns 0, or -1 if a row's expert has no weights. */
+int oracle_experts(const void* const* gate, const void* const* up, const void* const* down, int dt,
+                   const void* rows, const uint32_t* offsets, int64_t E, int64_t H, int64_t I,
+                   void* out, void* h_out, int nthreads)
+{
+    if (E < 1 || H < 1 || I < 1) return -1;
+    int bad = 0;
+    experts_ctx c = {gate, up, down, dt, rows, offsets, E, H, I, out, h_out, &bad};
+    parallel_rows((int64_t)offsets[E], nthreads, expert_row, &c);
+    return bad ? -1 : 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Combine (ruDNN User Guide, sections 5 and 6): restore token order    */
+/* through the saved mapping and merge with the routing weights.        */
+/* ------------------------------------------------------------------ */
+
+typedef struct {
+    const void* Y;
+    int dt;
+    const uint32_t* row_of_slot;
+    const void* w;
+    int wdt;
+    int k;
+    int64_t H;
+    void* out;
+} combine_ctx;
+
+static void combine_one(void* vctx, int64_t t)
+{
+    combine_ctx* c = (combine_ctx*)vctx;
+    int k = c->k;
+    int64_t H = c->H;
+    int invalid = 0;
+    for (int j = 0; j < k; ++j)
+        if (c->row_of_slot[t * k + j] == O_INVALID_ROW) invalid = 1;
+    for (int64_t col = 0; col < H; ++col) {
+        double acc = 0.0;
+        if (invalid) {
+            acc = NAN;
+        } else {
+            for (int j = 0; j < k; ++j) { /* fixed slot order */
+                double wj = load_elem(c->w, c->wdt, t * k + j); /* stored, cast weight */
+                double y = load_elem(c->Y, c->dt, (int64_t)c->row_of_slot[t * k + j] * H + col);
+                acc += wj * y;
+            }
+        }
+        store_elem(c->out, c->dt, t * H + col, acc);
+    }
+}
+
+int oracle_combine(const void* Y, int dt, const uint32_t* row_of_slot, const void* w, int wdt,
+                   int64_t T, int k, int64_t H, void* out, int nthreads)
+{
+    if (T < 0 || k < 1 || H < 0) return -1;
+    combine_ctx c = {Y, dt, row_of_slot, w, wdt, k, H, out};
+    parallel_rows(T, nthreads, combine_one, &c);
+    return 0;
+}
