@@ -1,0 +1,210 @@
+/*
+ * moe.h -- C ABI of libmoe.so, the gfx950 (MI355X) local MoE forward chain.
+ *
+ * The chain and its contract come from the ruDNN User Guide (ruDNN 0.1.5 on
+ * docs.rs, and the same text in the 0.1.13 Chinese README and the RUDA
+ * Japanese guide):
+ *   section 3 "MoE workflow":       logits -> softmax/top-k -> compact
+ *                                    dispatch -> SwiGLU experts -> weighted
+ *                                    combine, run locally on one device;
+ *   section 4 "Routing contract":    [T,E] F32/F16/BF16 logits, 1 <= top_k <= E,
+ *                                    FP32 softmax over all experts before top-k,
+ *                                    ties to the lower expert id, optional
+ *                                    renormalisation, weights cast to the logits
+ *                                    dtype, NaN kept for NaN/+inf/all -inf rows,
+ *                                    [T,top_k] U32 indices;
+ *   section 5 "Expert weights and dispatch": x [T,H], gate/up [E,I,H],
+ *                                    down [E,H,I], one float dtype and device,
+ *                                    no capacity drop, unspecified order inside
+ *                                    an expert, a saved mapping restores order;
+ *   section 6 "Call MoE":            the fused forward and the split
+ *                                    route / dispatch / forward_dispatched /
+ *                                    combine stages; shape, dtype and device
+ *                                    mismatches are reported as errors.
+ *
+ * Conventions shared by every call:
+ *   - Tensors are dense row-major device buffers (hipMalloc'd memory of the
+ *     device the stream belongs to).  The caller owns every buffer; the
+ *     library never allocates or frees device memory and keeps no pointer
+ *     after a call returns.  Expert weights are only read, so one set can
+ *     serve any number of batches.
+ *   - `stream` is a hipStream_t (NULL: the null stream of the current
+ *     device).  Every call only enqueues kernels and returns; it never waits
+ *     for the device and never reads device memory on the host.
+ *   - Arguments are checked before anything is enqueued; on any error
+ *     nothing is written.  Check order: null pointers / negative extents,
+ *     dtypes, shapes, top_k, limits of this implementation, workspace size,
+ *     device residency, then the launches.
+ *   - A tensor with zero elements may have data == NULL.  T = 0 is a valid
+ *     no-op.
+ *   - Results are bitwise reproducible run to run, although the row order
+ *     inside an expert (which follows device atomics) is not.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_dtype {
+    MOE_F32 = 0,
+    MOE_F16 = 1,
+    MOE_BF16 = 2,
+    MOE_U32 = 3
+} moe_dtype;
+
+typedef enum moe_status {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARGUMENT = 1, /* null pointer, negative extent, bad ndim */
+    MOE_ERR_DTYPE = 2,            /* a dtype the contract does not allow */
+    MOE_ERR_SHAPE = 3,            /* extents that disagree with each other */
+    MOE_ERR_TOP_K = 4,            /* top_k < 1 or top_k > E */
+    MOE_ERR_DEVICE = 5,           /* a buffer not on the stream's device */
+    MOE_ERR_WORKSPACE = 6,        /* workspace missing or too small */
+    MOE_ERR_LAUNCH = 7,           /* a HIP error; never hidden */
+    MOE_ERR_UNSUPPORTED = 8       /* outside this implementation's limits */
+} moe_status;
+
+/* A dense row-major tensor: ndim in 1..3 extents in dims[0..ndim-1]. */
+typedef struct moe_tensor {
+    void* data;
+    int32_t dtype; /* moe_dtype */
+    int32_t ndim;
+    int64_t dims[3];
+} moe_tensor;
+
+/* Routing contract options: 1 <= top_k <= E; renormalize is 0 or 1. */
+typedef struct moe_routing_options {
+    int32_t top_k;
+    int32_t renormalize;
+} moe_routing_options;
+
+/* Limits of this implementation (beyond them: MOE_ERR_UNSUPPORTED). */
+#define MOE_MAX_EXPERTS 4096   /* E */
+#define MOE_DIM_MULTIPLE 8     /* H and I of the expert products */
+
+/*
+ * moe_route -- routing contract (section 4).
+ *   logits  [T,E]  F32 | F16 | BF16, read only.
+ *   indices [T,k]  U32, written: per token the k experts with the largest
+ *                  FP32 softmax probability, largest first, ties to the
+ *                  lower id.  A row holding a NaN or +inf, or only -inf,
+ *                  gets indices 0..k-1.
+ *   weights [T,k]  logits dtype, written: the selected probabilities,
+ *                  divided by their FP32 sum when renormalize is set, then
+ *                  rounded to nearest even; NaN for the rows above.
+ */
+moe_status moe_route(const moe_tensor* logits, moe_routing_options options,
+                     moe_tensor* indices, moe_tensor* weights, void* stream);
+
+/* Workspace bytes moe_dispatch needs for T tokens, E experts, top_k. */
+size_t moe_dispatch_workspace_bytes(int64_t T, int64_t E, int32_t top_k);
+
+/*
+ * moe_dispatch -- compact, drop-free dispatch (section 5).
+ *   input          [T,H]   F32 | F16 | BF16, read only.
+ *   indices        [T,k]   U32 expert ids, read only.  An id >= E is not
+ *                          checked on the host (that would need a sync): its
+ *                          slot is not copied, its row_of_slot is 0xFFFFFFFF,
+ *                          and moe_combine turns that token's row into NaN.
+ *   num_experts    E, 1..MOE_MAX_EXPERTS.
+ *   dispatched     [T*k,H] input dtype, written: rows grouped by expert in
+ *                          ascending expert id; each row is a bit copy of its
+ *                          token.  Rows past expert_offsets[E] are untouched.
+ *   expert_offsets [E+1]   U32, written: rows of expert e are
+ *                          [expert_offsets[e], expert_offsets[e+1]).
+ *   row_of_slot    [T*k]   U32, written: dispatched row of slot t*k+j.
+ *   token_of_row   [T*k]   U32, written: token of each dispatched row.
+ *   workspace      >= moe_dispatch_workspace_bytes(T,E,k) device bytes.
+ * The order of rows inside an expert follows device atomics and is not
+ * fixed from run to run.
+ */
+moe_status moe_dispatch(const moe_tensor* input, const moe_tensor* indices, int64_t num_experts,
+                        moe_tensor* dispatched, moe_tensor* expert_offsets,
+                        moe_tensor* row_of_slot, moe_tensor* token_of_row,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes moe_experts_forward needs for N dispatched rows. */
+size_t moe_experts_workspace_bytes(int64_t N, int64_t H, int64_t I, int64_t E, int32_t dtype);
+
+/*
+ * moe_experts_forward -- SwiGLU experts on dispatched rows (section 5):
+ * for every row r of expert e, y_r = down_e (silu(gate_e x_r) * up_e x_r),
+ * silu(z) = z / (1 + exp(-z)), FP32 accumulation, the activation stored in
+ * the weight dtype between the two products.
+ *   gate, up       [E,I,H]  F32 | F16 | BF16 (one dtype), read only.
+ *   down           [E,H,I]  same dtype, read only.
+ *   dispatched     [N,H]    same dtype, read only.
+ *   expert_offsets [E+1]    U32 (as written by moe_dispatch), read only;
+ *                           offsets past N or out of order are clamped, so
+ *                           no access leaves the buffers.
+ *   expert_out     [N,H]    same dtype, written for rows < expert_offsets[E].
+ *   workspace      >= moe_experts_workspace_bytes(N,H,I,E,dtype) bytes.
+ * H and I must be multiples of MOE_DIM_MULTIPLE.
+ */
+moe_status moe_experts_forward(const moe_tensor* gate, const moe_tensor* up, const moe_tensor* down,
+                               const moe_tensor* dispatched, const moe_tensor* expert_offsets,
+                               moe_tensor* expert_out, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/*
+ * moe_experts_gate_up / moe_experts_down -- the two halves of
+ * moe_experts_forward, for callers that want the activation or time the
+ * products separately.  Together they compute exactly what
+ * moe_experts_forward computes (the same kernels, bit for bit).
+ *   moe_experts_gate_up: h [N,I] (weight dtype) written for rows <
+ *     expert_offsets[E]: h_r = silu(gate_e x_r) * up_e x_r, FP32 accumulation,
+ *     rounded once to the weight dtype.
+ *   moe_experts_down: expert_out [N,H] written for rows < expert_offsets[E]:
+ *     y_r = down_e h_r, FP32 accumulation.
+ *   Other arguments as for moe_experts_forward; the workspace of
+ *   moe_experts_workspace_bytes is enough for either.
+ */
+moe_status moe_experts_gate_up(const moe_tensor* gate, const moe_tensor* up, const moe_tensor* dispatched,
+                               const moe_tensor* expert_offsets, moe_tensor* h, void* workspace,
+                               size_t workspace_bytes, void* stream);
+moe_status moe_experts_down(const moe_tensor* down, const moe_tensor* h, const moe_tensor* expert_offsets,
+                            moe_tensor* expert_out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * moe_combine -- weighted combine in token order (sections 5 and 6):
+ * out[t] = sum over j < k, in order, of weights[t,j] * expert_out[row_of_slot[t*k+j]],
+ * accumulated in FP32 and rounded once to the input dtype.
+ *   expert_out  [N,H]  F32 | F16 | BF16, read only.
+ *   row_of_slot [T*k]  U32, read only; a row >= N (e.g. 0xFFFFFFFF) makes
+ *                      the token's output row NaN.
+ *   weights     [T,k]  F32 | F16 | BF16, read only.
+ *   output      [T,H]  expert_out dtype, written.
+ */
+moe_status moe_combine(const moe_tensor* expert_out, const moe_tensor* row_of_slot,
+                       const moe_tensor* weights, moe_tensor* output, void* stream);
+
+/* Workspace bytes moe_forward needs. */
+size_t moe_forward_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int32_t top_k,
+                                   int32_t dtype);
+
+/*
+ * moe_forward -- the whole local chain (section 6, SwiGluExperts::forward):
+ * route, dispatch, experts and combine on one stream.
+ *   gate, up [E,I,H]; down [E,H,I]; input [T,H]: one float dtype.
+ *   logits [T,E]: F32 | F16 | BF16, independent of the input dtype.
+ *   output [T,H]: input dtype, written.
+ *   workspace >= moe_forward_workspace_bytes(T,H,I,E,k,dtype) bytes.
+ */
+moe_status moe_forward(const moe_tensor* gate, const moe_tensor* up, const moe_tensor* down,
+                       const moe_tensor* input, const moe_tensor* logits,
+                       moe_routing_options options, moe_tensor* output,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static text of a status code. */
+const char* moe_status_string(moe_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

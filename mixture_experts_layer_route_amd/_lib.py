@@ -1,0 +1,116 @@
+"""ctypes view of libmoe.so (include/moe.h).  Argument marshalling only.
+
+There is no fallback: if the library is missing or does not export the
+declared symbols, loading raises, and nothing is computed anywhere else.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe.so")
+
+MOE_F32, MOE_F16, MOE_BF16, MOE_U32 = 0, 1, 2, 3
+STATUS = {
+    0: "MOE_OK",
+    1: "MOE_ERR_INVALID_ARGUMENT",
+    2: "MOE_ERR_DTYPE",
+    3: "MOE_ERR_SHAPE",
+    4: "MOE_ERR_TOP_K",
+    5: "MOE_ERR_DEVICE",
+    6: "MOE_ERR_WORKSPACE",
+    7: "MOE_ERR_LAUNCH",
+    8: "MOE_ERR_UNSUPPORTED",
+}
+MAX_EXPERTS = 4096
+DIM_MULTIPLE = 8
+
+# every function include/moe.h declares
+EXPORTS = (
+    "moe_route",
+    "moe_dispatch_workspace_bytes",
+    "moe_dispatch",
+    "moe_experts_workspace_bytes",
+    "moe_experts_forward",
+    "moe_experts_gate_up",
+    "moe_experts_down",
+    "moe_combine",
+    "moe_forward_workspace_bytes",
+    "moe_forward",
+    "moe_status_string",
+)
+
+
+class MoeTensor(ctypes.Structure):
+    _fields_ = [
+        ("data", ctypes.c_void_p),
+        ("dtype", ctypes.c_int32),
+        ("ndim", ctypes.c_int32),
+        ("dims", ctypes.c_int64 * 3),
+    ]
+
+
+class MoeRoutingOptions(ctypes.Structure):
+    _fields_ = [("top_k", ctypes.c_int32), ("renormalize", ctypes.c_int32)]
+
+
+class MoeError(RuntimeError):
+    """A non-OK moe_status from the library (shape, dtype, device, ...)."""
+
+    def __init__(self, status: int, where: str):
+        self.status = int(status)
+        self.name = STATUS.get(self.status, f"status {status}")
+        super().__init__(f"{where}: {self.name}")
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m mixture_experts_layer_route_amd.build` "
+            "(there is no fallback implementation)")
+    L = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER(MoeTensor)
+    vp, sz, i64, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int64, ctypes.c_int32
+    L.moe_route.argtypes = [P, MoeRoutingOptions, P, P, vp]
+    L.moe_dispatch_workspace_bytes.argtypes = [i64, i64, i32]
+    L.moe_dispatch_workspace_bytes.restype = sz
+    L.moe_dispatch.argtypes = [P, P, i64, P, P, P, P, vp, sz, vp]
+    L.moe_experts_workspace_bytes.argtypes = [i64, i64, i64, i64, i32]
+    L.moe_experts_workspace_bytes.restype = sz
+    L.moe_experts_forward.argtypes = [P, P, P, P, P, P, vp, sz, vp]
+    L.moe_experts_gate_up.argtypes = [P, P, P, P, P, vp, sz, vp]
+    L.moe_experts_down.argtypes = [P, P, P, P, vp, sz, vp]
+    L.moe_combine.argtypes = [P, P, P, P, vp]
+    L.moe_forward_workspace_bytes.argtypes = [i64, i64, i64, i64, i32, i32]
+    L.moe_forward_workspace_bytes.restype = sz
+    L.moe_forward.argtypes = [P, P, P, P, P, MoeRoutingOptions, P, vp, sz, vp]
+    L.moe_status_string.argtypes = [i32]
+    L.moe_status_string.restype = ctypes.c_char_p
+    for f in ("moe_route", "moe_dispatch", "moe_experts_forward", "moe_experts_gate_up", "moe_experts_down",
+              "moe_combine", "moe_forward"):
+        getattr(L, f).restype = i32
+    _lib = L
+    return L
+
+
+def check(status: int, where: str) -> None:
+    if status != 0:
+        raise MoeError(status, where)
+
+
+def raw_tensor(ptr: int | None, dtype: int, dims) -> MoeTensor:
+    """A moe_tensor from a raw pointer and extents (used by tests of the ABI)."""
+    t = MoeTensor()
+    t.data = ptr
+    t.dtype = dtype
+    t.ndim = len(dims)
+    for i, d in enumerate(dims):
+        t.dims[i] = int(d)
+    return t

@@ -1,0 +1,249 @@
+"""Python face of libmoe.so, shaped like the ruDNN MoE API.
+
+The objects mirror the ruDNN User Guide (ruDNN 0.1.5 on docs.rs), section 6
+"Call MoE": ``route(logits, options)`` gives a ``RoutingPlan`` with
+``expert_indices()``, ``weights()`` and ``dispatch(input)``; dispatching gives
+``DispatchedTokens`` whose ``combine(expert_output)`` restores token order;
+``SwiGluExperts(gate, up, down)`` holds the weights and runs ``forward`` (the
+whole chain from precomputed logits) or ``forward_dispatched``.  Errors come
+back as ``MoeError`` (the guide's section 3 error convention).
+
+This module only allocates torch tensors and passes pointers and extents
+to the C ABI: every step of the chain runs in the HIP kernels.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib
+from ._lib import MoeError, MoeRoutingOptions, MoeTensor
+
+_DTYPES = {
+    torch.float32: _lib.MOE_F32,
+    torch.float16: _lib.MOE_F16,
+    torch.bfloat16: _lib.MOE_BF16,
+    torch.uint32: _lib.MOE_U32,
+}
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    try:
+        return _DTYPES[t.dtype]
+    except KeyError:
+        raise MoeError(2, f"unsupported tensor dtype {t.dtype}") from None
+
+
+def _desc(t: torch.Tensor) -> MoeTensor:
+    if not t.is_contiguous():
+        raise MoeError(1, "tensors must be contiguous (dense row-major)")
+    if t.dim() < 1 or t.dim() > 3:
+        raise MoeError(1, f"tensors must have 1 to 3 dims, got {t.dim()}")
+    d = MoeTensor()
+    d.data = t.data_ptr() if t.numel() else None
+    d.dtype = _dtype_code(t)
+    d.ndim = t.dim()
+    for i, s in enumerate(t.shape):
+        d.dims[i] = int(s)
+    return d
+
+
+def _stream(device: torch.device) -> ctypes.c_void_p:
+    # a tensor that is not on a GPU still gets the current stream; the
+    # library's device check then refuses its pointer with MOE_ERR_DEVICE
+    if device.type != "cuda":
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ref(d: MoeTensor):
+    return ctypes.byref(d)
+
+
+@dataclass(frozen=True)
+class RoutingOptions:
+    """top_k with 1 <= top_k <= E; renormalize the selected weights or not."""
+    top_k: int
+    renormalize: bool = True
+
+    def _c(self) -> MoeRoutingOptions:
+        return MoeRoutingOptions(int(self.top_k), int(bool(self.renormalize)))
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+class RoutingPlan:
+    """Selected experts [T,k] (U32) and weights [T,k] (logits dtype)."""
+
+    def __init__(self, indices: torch.Tensor, weights: torch.Tensor, num_experts: int):
+        self._indices = indices
+        self._weights = weights
+        self.num_experts = int(num_experts)
+
+    def expert_indices(self) -> torch.Tensor:
+        return self._indices
+
+    def weights(self) -> torch.Tensor:
+        return self._weights
+
+    @property
+    def top_k(self) -> int:
+        return int(self._indices.shape[1])
+
+    def dispatch(self, input: torch.Tensor) -> "DispatchedTokens":
+        return dispatch(input, self._indices, self.num_experts, self._weights)
+
+
+def route(logits: torch.Tensor, options: RoutingOptions) -> RoutingPlan:
+    """FP32 softmax + top-k routing of [T,E] logits (moe_route)."""
+    L = _lib.load()
+    T, E = logits.shape
+    k = int(options.top_k)
+    idx = torch.empty((T, max(k, 0)), dtype=torch.uint32, device=logits.device)
+    w = torch.empty((T, max(k, 0)), dtype=logits.dtype, device=logits.device)
+    dl, di, dw = _desc(logits), _desc(idx), _desc(w)
+    _lib.check(L.moe_route(_ref(dl), options._c(), _ref(di), _ref(dw), _stream(logits.device)), "moe_route")
+    return RoutingPlan(idx, w, E)
+
+
+class DispatchedTokens:
+    """Rows grouped by expert plus the saved mapping back to tokens."""
+
+    def __init__(self, rows, expert_offsets, row_of_slot, token_of_row, weights, num_tokens, top_k):
+        self.rows = rows                      # [T*k, H]
+        self.expert_offsets = expert_offsets  # [E+1] U32
+        self.row_of_slot = row_of_slot        # [T*k] U32
+        self.token_of_row = token_of_row      # [T*k] U32
+        self.routing_weights = weights        # [T,k] or None
+        self.num_tokens = int(num_tokens)
+        self.top_k = int(top_k)
+
+    def combine(self, expert_output: torch.Tensor, weights: torch.Tensor | None = None) -> torch.Tensor:
+        w = self.routing_weights if weights is None else weights
+        if w is None:
+            raise MoeError(1, "combine needs routing weights")
+        return combine(expert_output, self.row_of_slot, w)
+
+
+def dispatch(input: torch.Tensor, indices: torch.Tensor, num_experts: int,
+             weights: torch.Tensor | None = None) -> DispatchedTokens:
+    """Compact, drop-free dispatch of [T,H] tokens by expert (moe_dispatch)."""
+    L = _lib.load()
+    T, H = input.shape
+    k = int(indices.shape[1])
+    dev = input.device
+    rows = torch.empty((T * k, H), dtype=input.dtype, device=dev)
+    offsets = torch.empty((num_experts + 1,), dtype=torch.uint32, device=dev)
+    ros = torch.empty((T * k,), dtype=torch.uint32, device=dev)
+    tor = torch.empty((T * k,), dtype=torch.uint32, device=dev)
+    ws = _workspace(L.moe_dispatch_workspace_bytes(T, num_experts, k), dev)
+    d = [_desc(x) for x in (input, indices, rows, offsets, ros, tor)]
+    st = L.moe_dispatch(_ref(d[0]), _ref(d[1]), int(num_experts), _ref(d[2]), _ref(d[3]), _ref(d[4]),
+                        _ref(d[5]), ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(dev))
+    _lib.check(st, "moe_dispatch")
+    return DispatchedTokens(rows, offsets, ros, tor, weights, T, k)
+
+
+def combine(expert_output: torch.Tensor, row_of_slot: torch.Tensor, weights: torch.Tensor) -> torch.Tensor:
+    """Weighted combine back into token order (moe_combine)."""
+    L = _lib.load()
+    T = weights.shape[0]
+    out = torch.empty((T, expert_output.shape[1]), dtype=expert_output.dtype, device=expert_output.device)
+    d = [_desc(x) for x in (expert_output, row_of_slot, weights, out)]
+    _lib.check(L.moe_combine(_ref(d[0]), _ref(d[1]), _ref(d[2]), _ref(d[3]), _stream(out.device)),
+               "moe_combine")
+    return out
+
+
+class SwiGluExperts:
+    """Bias-free SwiGLU expert weights: gate, up [E,I,H]; down [E,H,I]."""
+
+    def __init__(self, gate: torch.Tensor, up: torch.Tensor, down: torch.Tensor):
+        if gate.dim() != 3 or up.shape != gate.shape or down.dim() != 3:
+            raise MoeError(3, "gate/up must be [E,I,H] and down [E,H,I]")
+        E, I, H = gate.shape
+        if tuple(down.shape) != (E, H, I):
+            raise MoeError(3, "down must be [E,H,I]")
+        if up.dtype != gate.dtype or down.dtype != gate.dtype:
+            raise MoeError(2, "gate, up and down must share one float dtype")
+        if up.device != gate.device or down.device != gate.device:
+            raise MoeError(5, "gate, up and down must share one device")
+        self.gate, self.up, self.down = gate, up, down
+        self.num_experts, self.intermediate, self.hidden = E, I, H
+        self._dw = [_desc(w) for w in (gate, up, down)]
+
+    def forward(self, input: torch.Tensor, logits: torch.Tensor, options: RoutingOptions,
+                workspace: torch.Tensor | None = None) -> torch.Tensor:
+        """The whole local chain from precomputed logits (moe_forward)."""
+        L = _lib.load()
+        T, H = input.shape
+        out = torch.empty((T, H), dtype=input.dtype, device=input.device)
+        need = L.moe_forward_workspace_bytes(T, self.hidden, self.intermediate, self.num_experts,
+                                             int(options.top_k), _dtype_code(input))
+        if workspace is None or workspace.numel() < need:
+            workspace = _workspace(need, input.device)
+        dx, dl, do = _desc(input), _desc(logits), _desc(out)
+        g, u, d = self._dw
+        st = L.moe_forward(_ref(g), _ref(u), _ref(d), _ref(dx), _ref(dl), options._c(), _ref(do),
+                           ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), _stream(input.device))
+        _lib.check(st, "moe_forward")
+        return out
+
+    def forward_workspace_bytes(self, T: int, top_k: int, dtype: torch.dtype) -> int:
+        return int(_lib.load().moe_forward_workspace_bytes(T, self.hidden, self.intermediate,
+                                                          self.num_experts, int(top_k), _DTYPES[dtype]))
+
+    def forward_dispatched(self, dispatched: DispatchedTokens | torch.Tensor,
+                           expert_offsets: torch.Tensor | None = None) -> torch.Tensor:
+        """SwiGLU experts on rows grouped by expert (moe_experts_forward)."""
+        L = _lib.load()
+        if isinstance(dispatched, DispatchedTokens):
+            rows, offsets = dispatched.rows, dispatched.expert_offsets
+        else:
+            rows, offsets = dispatched, expert_offsets
+        N = rows.shape[0]
+        out = torch.empty((N, self.hidden), dtype=rows.dtype, device=rows.device)
+        ws = _workspace(L.moe_experts_workspace_bytes(N, self.hidden, self.intermediate, self.num_experts,
+                                                      _dtype_code(rows)), rows.device)
+        dr, do_, dy = _desc(rows), _desc(offsets), _desc(out)
+        g, u, d = self._dw
+        st = L.moe_experts_forward(_ref(g), _ref(u), _ref(d), _ref(dr), _ref(do_), _ref(dy),
+                                   ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(rows.device))
+        _lib.check(st, "moe_experts_forward")
+        return out
+
+    def gate_up(self, rows: torch.Tensor, expert_offsets: torch.Tensor,
+                workspace: torch.Tensor | None = None) -> torch.Tensor:
+        """First half of the experts: h = silu(gate_e x) * up_e x (moe_experts_gate_up)."""
+        L = _lib.load()
+        N = rows.shape[0]
+        h = torch.empty((N, self.intermediate), dtype=rows.dtype, device=rows.device)
+        ws = workspace if workspace is not None else _workspace(
+            L.moe_experts_workspace_bytes(N, self.hidden, self.intermediate, self.num_experts, _dtype_code(rows)),
+            rows.device)
+        dr, do_, dh = _desc(rows), _desc(expert_offsets), _desc(h)
+        g, u, _ = self._dw
+        st = L.moe_experts_gate_up(_ref(g), _ref(u), _ref(dr), _ref(do_), _ref(dh),
+                                   ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(rows.device))
+        _lib.check(st, "moe_experts_gate_up")
+        return h
+
+    def down_proj(self, h: torch.Tensor, expert_offsets: torch.Tensor,
+                  workspace: torch.Tensor | None = None) -> torch.Tensor:
+        """Second half of the experts: y = down_e h (moe_experts_down)."""
+        L = _lib.load()
+        N = h.shape[0]
+        out = torch.empty((N, self.hidden), dtype=h.dtype, device=h.device)
+        ws = workspace if workspace is not None else _workspace(
+            L.moe_experts_workspace_bytes(N, self.hidden, self.intermediate, self.num_experts, _dtype_code(h)),
+            h.device)
+        dh, do_, dy = _desc(h), _desc(expert_offsets), _desc(out)
+        _, _, d = self._dw
+        st = L.moe_experts_down(_ref(d), _ref(dh), _ref(do_), _ref(dy), ctypes.c_void_p(ws.data_ptr()),
+                                ws.numel(), _stream(h.device))
+        _lib.check(st, "moe_experts_down")
+        return out

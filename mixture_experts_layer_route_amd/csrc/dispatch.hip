@@ -1,0 +1,169 @@
+// dispatch.hip -- compact, drop-free dispatch of tokens by expert.
+//
+// Follows the ruDNN User Guide, section 5 "Expert weights and dispatch":
+// every selected (token, slot) pair gets its own row (no capacity drop),
+// rows are grouped by expert, the order inside an expert comes from atomics
+// and is not fixed, and a saved mapping (row_of_slot / token_of_row) lets the
+// combine restore token order.
+//
+// Three kernels:
+//   hist    -- per-workgroup LDS histogram; the LDS atomic returns each slot's
+//              rank inside its workgroup, and one global atomic per
+//              (workgroup, expert) reserves that workgroup's base, so
+//              rank_in_expert = base + local rank.
+//   scan    -- one workgroup: exclusive prefix sum of the counts, ascending
+//              expert id, into offsets[E+1].
+//   gather  -- one wavefront per token: the token's row is read once with
+//              16-byte loads and written to each of its k dispatched rows.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kHistThreads = 256;
+constexpr int kHistSlotsPerThread = 8;
+
+__global__ void fill_u32_kernel(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = v;
+}
+
+__global__ __launch_bounds__(kHistThreads) void hist_kernel(const uint32_t* __restrict__ idx, int64_t N,
+                                                            int E, uint32_t* __restrict__ counts,
+                                                            uint32_t* __restrict__ rank) {
+    extern __shared__ uint32_t h[];  // [E]
+    for (int e = threadIdx.x; e < E; e += blockDim.x) h[e] = 0;
+    __syncthreads();
+    const int64_t base = (int64_t)blockIdx.x * kHistThreads * kHistSlotsPerThread;
+    uint32_t ex[kHistSlotsPerThread], loc[kHistSlotsPerThread];
+#pragma unroll
+    for (int i = 0; i < kHistSlotsPerThread; ++i) {
+        const int64_t s = base + (int64_t)i * kHistThreads + threadIdx.x;
+        ex[i] = (s < N) ? idx[s] : kInvalidRow;
+        loc[i] = 0;
+        if (ex[i] < (uint32_t)E) loc[i] = atomicAdd(&h[ex[i]], 1u);
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+        const uint32_t c = h[e];
+        if (c) h[e] = atomicAdd(&counts[e], c);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kHistSlotsPerThread; ++i) {
+        const int64_t s = base + (int64_t)i * kHistThreads + threadIdx.x;
+        if (s < N) rank[s] = (ex[i] < (uint32_t)E) ? h[ex[i]] + loc[i] : kInvalidRow;
+    }
+}
+
+// exclusive scan of the block's values; 1024 threads (16 waves)
+__device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* total) {
+    __shared__ uint32_t wsum[16];
+    const int lane = lane_id(), wid = threadIdx.x / kWave;
+    const uint32_t inc = wave_inclusive_scan(v);
+    if (lane == kWave - 1) wsum[wid] = inc;
+    __syncthreads();
+    if (wid == 0) {
+        const int nw = blockDim.x / kWave;
+        uint32_t s = (lane < nw) ? wsum[lane] : 0u;
+        s = wave_inclusive_scan(s);
+        if (lane < nw) wsum[lane] = s;
+    }
+    __syncthreads();
+    const uint32_t prefix = wid ? wsum[wid - 1] : 0u;
+    *total = wsum[blockDim.x / kWave - 1];
+    __syncthreads();
+    return prefix + inc - v;
+}
+
+__global__ __launch_bounds__(1024) void scan_kernel(const uint32_t* __restrict__ counts, int E,
+                                                    uint32_t* __restrict__ offsets) {
+    const int per = (E + blockDim.x - 1) / blockDim.x;  // contiguous experts per thread
+    const int e0 = threadIdx.x * per;
+    uint32_t local = 0;
+    for (int i = 0; i < per; ++i)
+        if (e0 + i < E) local += counts[e0 + i];
+    uint32_t total;
+    uint32_t run = block_exclusive_scan(local, &total);
+    for (int i = 0; i < per; ++i) {
+        if (e0 + i < E) {
+            offsets[e0 + i] = run;
+            run += counts[e0 + i];
+        }
+    }
+    if (threadIdx.x == 0) offsets[E] = total;
+}
+
+// V: copy unit (uint4 = 16 bytes when rows allow it, else 4 or 2 bytes)
+template <typename V>
+__global__ __launch_bounds__(256) void gather_kernel(const V* __restrict__ x, int64_t T, int64_t row_units,
+                                                     int k, int E, const uint32_t* __restrict__ idx,
+                                                     const uint32_t* __restrict__ rank,
+                                                     const uint32_t* __restrict__ offsets,
+                                                     V* __restrict__ dispatched,
+                                                     uint32_t* __restrict__ row_of_slot,
+                                                     uint32_t* __restrict__ token_of_row) {
+    const int lane = lane_id();
+    const int64_t t = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
+    if (t >= T) return;
+    for (int j0 = 0; j0 < k; j0 += kWave) {
+        const int j = j0 + lane;
+        uint32_t row = kInvalidRow;
+        if (j < k) {
+            const uint32_t e = idx[t * k + j];
+            if (e < (uint32_t)E) {
+                row = offsets[e] + rank[t * k + j];
+                token_of_row[row] = (uint32_t)t;
+            }
+            row_of_slot[t * k + j] = row;
+        }
+        const int nj = min(kWave, k - j0);
+        const V* src = x + t * row_units;
+        // the loop bound is wave-uniform so every lane takes part in the shuffles
+        for (int64_t u0 = 0; u0 < row_units; u0 += kWave) {
+            const int64_t u = u0 + lane;
+            const bool ok = u < row_units;
+            V val{};
+            if (ok) val = src[u];
+            for (int jj = 0; jj < nj; ++jj) {
+                const uint32_t r = __shfl(row, jj, kWave);
+                if (ok && r != kInvalidRow) dispatched[(int64_t)r * row_units + u] = val;
+            }
+        }
+    }
+}
+
+template <typename V>
+hipError_t launch_gather(const DispatchArgs& a, hipStream_t s) {
+    const int wpb = 4;
+    const dim3 grid((unsigned)((a.T + wpb - 1) / wpb)), block(wpb * kWave);
+    gather_kernel<V><<<grid, block, 0, s>>>((const V*)a.x, a.T, a.row_bytes / (int64_t)sizeof(V), a.k,
+                                            a.E, a.idx, a.rank, a.offsets, (V*)a.dispatched,
+                                            a.row_of_slot, a.token_of_row);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
+    hipError_t err;
+    fill_u32_kernel<<<(a.E + 255) / 256, 256, 0, s>>>(a.counts, a.E, 0u);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    const int64_t N = a.T * (int64_t)a.k;
+    if (N > 0) {
+        const int64_t per_block = (int64_t)kHistThreads * kHistSlotsPerThread;
+        hist_kernel<<<(unsigned)((N + per_block - 1) / per_block), kHistThreads, a.E * sizeof(uint32_t), s>>>(
+            a.idx, N, a.E, a.counts, a.rank);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+    scan_kernel<<<1, 1024, 0, s>>>(a.counts, a.E, a.offsets);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if (a.T == 0) return hipSuccess;
+    const uintptr_t al = (uintptr_t)a.x | (uintptr_t)a.dispatched;
+    if (a.row_bytes % 16 == 0 && al % 16 == 0) return launch_gather<uint4>(a, s);
+    if (a.row_bytes % 4 == 0 && al % 4 == 0) return launch_gather<uint32_t>(a, s);
+    return launch_gather<uint16_t>(a, s);
+}
+
+}  // namespace moe

@@ -1,0 +1,152 @@
+// moe_internal.h -- device helpers and kernel launchers shared by the HIP
+// sources of libmoe.so (not installed, not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+constexpr uint32_t kInvalidRow = 0xFFFFFFFFu;
+constexpr int kWave = 64;
+
+// ------------------------------------------------------------------ formats
+// 16-bit floats travel as raw uint16_t; conversions are written out so their
+// rounding (to nearest, ties to even) and NaN handling are explicit.
+struct f32_t { using storage = float; };
+struct f16_t { using storage = uint16_t; };
+struct bf16_t { using storage = uint16_t; };
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x0040u);  // quiet NaN
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float f16_to_f32(uint16_t b) {
+    _Float16 h = __builtin_bit_cast(_Float16, b);
+    return (float)h;
+}
+
+__device__ __forceinline__ uint16_t f32_to_f16(float f) {
+    _Float16 h = (_Float16)f;  // v_cvt_f16_f32: nearest even, NaN stays NaN
+    return __builtin_bit_cast(uint16_t, h);
+}
+
+template <typename DT> struct fmt;
+template <> struct fmt<f32_t> {
+    static __device__ __forceinline__ float load(float v) { return v; }
+    static __device__ __forceinline__ float store(float v) { return v; }
+};
+template <> struct fmt<f16_t> {
+    static __device__ __forceinline__ float load(uint16_t v) { return f16_to_f32(v); }
+    static __device__ __forceinline__ uint16_t store(float v) { return f32_to_f16(v); }
+};
+template <> struct fmt<bf16_t> {
+    static __device__ __forceinline__ float load(uint16_t v) { return bf16_to_f32(v); }
+    static __device__ __forceinline__ uint16_t store(float v) { return f32_to_bf16(v); }
+};
+
+// ------------------------------------------------------------------ wave helpers
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+    return v;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        uint32_t lo = __shfl_xor((uint32_t)v, m, kWave);
+        uint32_t hi = __shfl_xor((uint32_t)(v >> 32), m, kWave);
+        uint64_t o = ((uint64_t)hi << 32) | lo;
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+// inclusive scan over the 64 lanes of a wave
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        uint32_t y = __shfl_up(v, d, kWave);
+        if (lane >= d) v += y;
+    }
+    return v;
+}
+
+// ------------------------------------------------------------------ launchers
+// Each returns hipSuccess or the launch error.  Shapes are checked by the
+// caller (moe_api.hip) before these run.
+struct RouteArgs {
+    const void* logits;
+    int ldtype;  // moe_dtype of logits and weights
+    int64_t T;
+    int E, k, renorm;
+    uint32_t* idx;
+    void* w;
+};
+hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+
+struct DispatchArgs {
+    const void* x;
+    int64_t T;
+    int64_t row_bytes;  // H * element size
+    int k, E;
+    const uint32_t* idx;
+    uint32_t* counts;   // [E] scratch
+    uint32_t* rank;     // [T*k] scratch
+    uint32_t* offsets;  // [E+1]
+    void* dispatched;
+    uint32_t* row_of_slot;
+    uint32_t* token_of_row;
+};
+hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s);
+
+struct ExpertsArgs {
+    int dtype;
+    const void* gate;
+    const void* up;
+    const void* down;
+    const void* x;  // [N,H] dispatched rows
+    const uint32_t* offsets;
+    void* y;        // [N,H]
+    void* h;        // [N,I] workspace
+    void* tiles;    // tile list workspace
+    int64_t N, H, I;
+    int E;
+};
+size_t experts_tile_bytes(int64_t N, int64_t E);
+// which products to run: both (the whole experts stage) or one half
+enum ExpertsPart { kBoth = 0, kGateUp = 1, kDown = 2 };
+hipError_t launch_experts(const ExpertsArgs& a, hipStream_t s, ExpertsPart part = kBoth);
+
+struct CombineArgs {
+    const void* y;
+    int dtype;
+    int64_t N;  // rows of y
+    const uint32_t* row_of_slot;
+    const void* w;
+    int wdtype;
+    int64_t T;
+    int k;
+    int64_t H;
+    void* out;
+};
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+
+}  // namespace moe

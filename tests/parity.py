@@ -1,0 +1,116 @@
+"""Comparison rules between the HIP path and the CPU oracle.
+
+Agreement is defined as follows (the rules of the build's parity contract):
+  * indices match bit-exactly, except where the oracle's FP32 probabilities
+    of the two experts in question differ by less than 1e-6 (a near tie, where
+    ulp-level differences in exp and summation order may flip the order);
+    exact ties -- bit-identical logits -- are not exempt;
+  * NaN rows: identical NaN masks, indices 0..k-1;
+  * dispatch: the per-expert set of token ids (the order inside an expert
+    follows atomics and is not fixed), every row a bit copy of its token;
+  * values: |got - ref| <= tol * (1 + |ref|), tol = 1e-4 for F32 and 2e-2
+    for F16/BF16, NaN positions identical.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import moe_synth as S
+import oracle
+
+TOL = {"f32": 1e-4, "f16": 2e-2, "bf16": 2e-2}
+NEAR_TIE = 1e-6
+
+
+def host_bits(t: torch.Tensor) -> np.ndarray:
+    return S.to_bits(t)
+
+
+def values(a, dt: str) -> np.ndarray:
+    """float64 values of a torch tensor or of oracle bits."""
+    if isinstance(a, torch.Tensor):
+        return a.detach().cpu().double().numpy()
+    return oracle.widen(np.ascontiguousarray(a), dt)
+
+
+def assert_close(got, ref, dt: str, what: str, rows_mask=None):
+    g, r = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    assert g.shape == r.shape, (what, g.shape, r.shape)
+    if rows_mask is not None:
+        g, r = g[rows_mask], r[rows_mask]
+    gn, rn = np.isnan(g), np.isnan(r)
+    assert np.array_equal(gn, rn), f"{what}: NaN positions differ ({int((gn != rn).sum())} elements)"
+    ok = ~rn
+    err = np.abs(g[ok] - r[ok])
+    lim = TOL[dt] * (1.0 + np.abs(r[ok]))
+    if err.size:
+        worst = int(np.argmax(err - lim))
+        assert np.all(err <= lim), (f"{what}: max excess {float((err - lim)[worst]):.3g} "
+                                    f"(got {g[ok][worst]!r}, ref {r[ok][worst]!r}, tol {TOL[dt]})")
+
+
+def compare_routing(gpu_idx: np.ndarray, gpu_w: np.ndarray, logits_bits: np.ndarray, ldt: str,
+                    top_k: int, renorm: bool, nthreads: int | None = None):
+    """Checks GPU routing against the oracle; returns (oracle result, near-tie token mask)."""
+    o_idx, o_w, _ = oracle.route(logits_bits, ldt, top_k, renorm, nthreads)
+    p = oracle.softmax(logits_bits, ldt).astype(np.float64)
+    lg = oracle.widen(logits_bits, ldt)
+    T, E = p.shape
+    k = top_k
+    gi = gpu_idx.astype(np.int64)
+    oi = o_idx.astype(np.int64)
+    assert gi.shape == (T, k)
+    nan_rows = np.isnan(p).any(axis=1)
+    # the all-or-none property of the oracle's NaN rows
+    assert np.array_equal(nan_rows, np.isnan(p).all(axis=1))
+    gw, ow = values(gpu_w, ldt), oracle.widen(o_w, ldt)
+    # NaN rows
+    if nan_rows.any():
+        assert (gi[nan_rows] == np.arange(k)[None, :]).all(), "NaN rows must select experts 0..k-1"
+        assert np.isnan(gw[nan_rows]).all(), "NaN rows must keep NaN weights"
+    fin = ~nan_rows
+    assert not np.isnan(gw[fin]).any(), "finite rows must have finite weights"
+    assert ((gi >= 0) & (gi < E)).all()
+    srt = np.sort(gi, axis=1)
+    assert (np.diff(srt, axis=1) > 0).all(), "indices of a token must be distinct"
+    mism = (gi != oi) & fin[:, None]
+    near = np.zeros(T, bool)
+    if mism.any():
+        t_ids, j_ids = np.nonzero(mism)
+        pa = p[t_ids, oi[t_ids, j_ids]]
+        pb = p[t_ids, gi[t_ids, j_ids]]
+        la = lg[t_ids, oi[t_ids, j_ids]]
+        lb = lg[t_ids, gi[t_ids, j_ids]]
+        gap = np.abs(pa - pb)
+        bad = (gap >= NEAR_TIE) | (la == lb)
+        assert not bad.any(), (
+            f"index mismatch outside the near-tie rule at token {t_ids[bad][0]} slot {j_ids[bad][0]}: "
+            f"oracle {oi[t_ids[bad][0]]} gpu {gi[t_ids[bad][0]]} gap {gap[bad][0]:.3g}")
+        near[t_ids] = True
+    assert_close(gw, ow, ldt, "routing weights")
+    return (o_idx, o_w), near
+
+
+def compare_dispatch(gpu: dict, o_offsets, o_ros, o_tor, o_rows, x_bits: np.ndarray, idx: np.ndarray, E: int):
+    """gpu: dict of host numpy arrays rows/offsets/row_of_slot/token_of_row."""
+    T, k = idx.shape
+    offs = gpu["offsets"].astype(np.int64)
+    assert np.array_equal(offs, o_offsets.astype(np.int64)), "expert offsets differ"
+    n = int(offs[E])
+    ros = gpu["row_of_slot"].astype(np.int64)
+    tor = gpu["token_of_row"][:n].astype(np.int64)
+    flat = idx.reshape(-1).astype(np.int64)
+    valid = flat < E
+    assert np.array_equal(ros[~valid], np.full((~valid).sum(), 0xFFFFFFFF)), "invalid slots must be unmapped"
+    assert np.array_equal(np.sort(ros[valid]), np.arange(n)), "every row must belong to exactly one slot"
+    slot_tok = np.nonzero(valid)[0] // k
+    assert np.array_equal(tor[ros[valid]], slot_tok), "token_of_row must invert row_of_slot"
+    exp_of_row = np.searchsorted(offs, np.arange(n), side="right") - 1
+    assert np.array_equal(exp_of_row[ros[valid]], flat[valid]), "a slot's row must lie in its expert's range"
+    otor = o_tor.astype(np.int64)
+    for e in range(E):
+        a, b = offs[e], offs[e + 1]
+        assert np.array_equal(np.sort(tor[a:b]), np.sort(otor[a:b])), f"token set of expert {e} differs"
+    rows = gpu["rows"][:n]
+    assert np.array_equal(rows, x_bits[tor]), "dispatched rows must be bit copies of their tokens"

@@ -1,0 +1,197 @@
+"""Host-side tests of the C ABI: the library loads, exports what include/moe.h
+declares, sizes workspaces, and rejects bad arguments before touching a device.
+
+Every call here fails validation (or the device check) on the host, so no
+kernel is launched; these run without a GPU.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mixture_experts_layer_route_amd as moe
+from mixture_experts_layer_route_amd import _lib
+from mixture_experts_layer_route_amd._lib import MoeRoutingOptions, raw_tensor
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+F32, F16, BF16, U32 = _lib.MOE_F32, _lib.MOE_F16, _lib.MOE_BF16, _lib.MOE_U32
+OK, INVALID, DTYPE, SHAPE, TOPK, DEVICE, WORKSPACE, LAUNCH, UNSUPPORTED = range(9)
+FAKE = 0x10000  # never dereferenced: validation rejects the call first
+
+
+@pytest.fixture(scope="module")
+def L():
+    return _lib.load()
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\*\s]+?\b(moe_\w+)\s*\(", src, re.M)))
+
+
+def test_library_exports_every_declared_function(L):
+    declared = header_functions()
+    assert set(declared) == set(_lib.EXPORTS), declared
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_status_strings(L):
+    for code, name in _lib.STATUS.items():
+        assert L.moe_status_string(code).decode().startswith(name)
+
+
+def test_header_limits_match_binding():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    assert f"#define MOE_MAX_EXPERTS {_lib.MAX_EXPERTS}" in src
+    assert f"#define MOE_DIM_MULTIPLE {_lib.DIM_MULTIPLE}" in src
+
+
+def test_workspace_sizes(L):
+    assert L.moe_dispatch_workspace_bytes(100, 8, 2) >= 100 * 2 * 4 + 8 * 4
+    assert L.moe_dispatch_workspace_bytes(-1, 8, 2) == 0
+    assert L.moe_experts_workspace_bytes(256, 128, 64, 8, BF16) >= 256 * 64 * 2
+    assert L.moe_experts_workspace_bytes(256, 128, 64, 8, U32) == 0
+    small = L.moe_forward_workspace_bytes(64, 128, 256, 8, 2, F32)
+    big = L.moe_forward_workspace_bytes(8192, 2048, 1408, 64, 6, BF16)
+    assert 0 < small < big
+    # dispatched rows, expert outputs and the activation must all fit
+    N = 8192 * 6
+    assert big >= N * 2048 * 2 * 2 + N * 1408 * 2
+    assert L.moe_forward_workspace_bytes(64, 128, 256, 8, 0, F32) == 0
+
+
+def _route(L, logits, k, idx, w, renorm=1):
+    return L.moe_route(ctypes.byref(logits), MoeRoutingOptions(k, renorm), ctypes.byref(idx),
+                       ctypes.byref(w), None)
+
+
+def test_route_validation(L):
+    T, E, k = 16, 8, 2
+    lg = raw_tensor(FAKE, F32, (T, E))
+    idx = raw_tensor(FAKE, U32, (T, k))
+    w = raw_tensor(FAKE, F32, (T, k))
+    assert _route(L, raw_tensor(None, F32, (T, E)), k, idx, w) == INVALID
+    assert _route(L, raw_tensor(FAKE, F32, (T, E, 1)), k, idx, w) == INVALID
+    assert _route(L, raw_tensor(FAKE, F32, (-1, E)), k, idx, w) == INVALID
+    assert _route(L, raw_tensor(FAKE, U32, (T, E)), k, idx, w) == DTYPE       # quantised/int logits
+    assert _route(L, lg, k, raw_tensor(FAKE, F32, (T, k)), w) == DTYPE        # indices must be U32
+    assert _route(L, lg, k, idx, raw_tensor(FAKE, BF16, (T, k))) == DTYPE     # weights in logits dtype
+    assert _route(L, lg, 0, raw_tensor(FAKE, U32, (T, 0)), raw_tensor(FAKE, F32, (T, 0))) == TOPK
+    assert _route(L, lg, E + 1, raw_tensor(FAKE, U32, (T, E + 1)), raw_tensor(FAKE, F32, (T, E + 1))) == TOPK
+    assert _route(L, lg, k, raw_tensor(FAKE, U32, (T + 1, k)), w) == SHAPE
+    assert _route(L, lg, k, idx, raw_tensor(FAKE, F32, (T, k + 1))) == SHAPE
+    assert _route(L, lg, k, idx, w, renorm=2) == INVALID
+    big = raw_tensor(FAKE, F32, (T, _lib.MAX_EXPERTS + 1))
+    assert _route(L, big, k, idx, w) == UNSUPPORTED
+    # T = 0 is a valid no-op
+    assert _route(L, raw_tensor(None, F32, (0, E)), k, raw_tensor(None, U32, (0, k)),
+                  raw_tensor(None, F32, (0, k))) == OK
+
+
+def test_route_device_check_without_device(L):
+    """A well-formed call whose buffers are not device memory of the stream's
+    device is refused with MOE_ERR_DEVICE, never launched."""
+    T, E, k = 16, 8, 2
+    st = _route(L, raw_tensor(FAKE, F32, (T, E)), k, raw_tensor(FAKE, U32, (T, k)), raw_tensor(FAKE, F32, (T, k)))
+    assert st == DEVICE
+
+
+def _dispatch(L, x, idx, E, rows, off, ros, tor, ws=FAKE, wsb=1 << 30):
+    return L.moe_dispatch(ctypes.byref(x), ctypes.byref(idx), E, ctypes.byref(rows), ctypes.byref(off),
+                          ctypes.byref(ros), ctypes.byref(tor), ctypes.c_void_p(ws), wsb, None)
+
+
+def test_dispatch_validation(L):
+    T, H, E, k = 10, 16, 4, 2
+    x = raw_tensor(FAKE, BF16, (T, H))
+    idx = raw_tensor(FAKE, U32, (T, k))
+    rows = raw_tensor(FAKE, BF16, (T * k, H))
+    off = raw_tensor(FAKE, U32, (E + 1,))
+    ros = raw_tensor(FAKE, U32, (T * k,))
+    tor = raw_tensor(FAKE, U32, (T * k,))
+    assert _dispatch(L, x, idx, E, raw_tensor(FAKE, F16, (T * k, H)), off, ros, tor) == DTYPE
+    assert _dispatch(L, x, raw_tensor(FAKE, F32, (T, k)), E, rows, off, ros, tor) == DTYPE
+    assert _dispatch(L, x, idx, E, raw_tensor(FAKE, BF16, (T * k, H + 1)), off, ros, tor) == SHAPE
+    assert _dispatch(L, x, idx, E, rows, raw_tensor(FAKE, U32, (E,)), ros, tor) == SHAPE
+    assert _dispatch(L, x, idx, E, rows, off, raw_tensor(FAKE, U32, (T,)), tor) == SHAPE
+    assert _dispatch(L, x, raw_tensor(FAKE, U32, (T, 5)), E, raw_tensor(FAKE, BF16, (T * 5, H)), off,
+                     raw_tensor(FAKE, U32, (T * 5,)), raw_tensor(FAKE, U32, (T * 5,))) == TOPK
+    assert _dispatch(L, x, idx, E, rows, off, ros, tor, ws=0) == WORKSPACE
+    assert _dispatch(L, x, idx, E, rows, off, ros, tor, wsb=8) == WORKSPACE
+    assert _dispatch(L, x, idx, -1, rows, off, ros, tor) == INVALID
+
+
+def _experts(L, g, u, d, rows, off, out, ws=FAKE, wsb=1 << 30):
+    return L.moe_experts_forward(ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), ctypes.byref(rows),
+                                 ctypes.byref(off), ctypes.byref(out), ctypes.c_void_p(ws), wsb, None)
+
+
+def test_experts_validation(L):
+    E, I, H, N = 4, 32, 16, 20
+    g = raw_tensor(FAKE, BF16, (E, I, H))
+    u = raw_tensor(FAKE, BF16, (E, I, H))
+    d = raw_tensor(FAKE, BF16, (E, H, I))
+    rows = raw_tensor(FAKE, BF16, (N, H))
+    off = raw_tensor(FAKE, U32, (E + 1,))
+    out = raw_tensor(FAKE, BF16, (N, H))
+    assert _experts(L, g, raw_tensor(FAKE, F16, (E, I, H)), d, rows, off, out) == DTYPE   # one weight dtype
+    assert _experts(L, g, u, d, raw_tensor(FAKE, F32, (N, H)), off, out) == DTYPE         # input = weight dtype
+    assert _experts(L, g, u, raw_tensor(FAKE, BF16, (E, I, H)), rows, off, out) == SHAPE  # down is [E,H,I]
+    assert _experts(L, g, raw_tensor(FAKE, BF16, (E + 1, I, H)), d, rows, off, out) == SHAPE
+    assert _experts(L, g, u, d, raw_tensor(FAKE, BF16, (N, H + 8)), off, out) == SHAPE
+    assert _experts(L, g, u, d, rows, raw_tensor(FAKE, U32, (E + 2,)), out) == SHAPE
+    assert _experts(L, g, u, d, rows, off, raw_tensor(FAKE, BF16, (N + 1, H))) == SHAPE
+    odd = (E, 12, H)
+    assert _experts(L, raw_tensor(FAKE, BF16, odd), raw_tensor(FAKE, BF16, odd),
+                    raw_tensor(FAKE, BF16, (E, H, 12)), rows, off, out) == UNSUPPORTED
+    assert _experts(L, g, u, d, raw_tensor(FAKE + 2, BF16, (N, H)), off, out) == UNSUPPORTED  # unaligned
+    assert _experts(L, g, u, d, rows, off, out, wsb=16) == WORKSPACE
+
+
+def test_combine_validation(L):
+    T, k, H, N = 8, 2, 16, 16
+    y = raw_tensor(FAKE, F32, (N, H))
+    ros = raw_tensor(FAKE, U32, (T * k,))
+    w = raw_tensor(FAKE, F32, (T, k))
+    out = raw_tensor(FAKE, F32, (T, H))
+    c = lambda *a: L.moe_combine(*[ctypes.byref(t) for t in a], None)
+    assert c(y, ros, w, raw_tensor(FAKE, BF16, (T, H))) == DTYPE
+    assert c(y, raw_tensor(FAKE, F32, (T * k,)), w, out) == DTYPE
+    assert c(y, raw_tensor(FAKE, U32, (T * k + 1,)), w, out) == SHAPE
+    assert c(y, ros, w, raw_tensor(FAKE, F32, (T, H + 1))) == SHAPE
+    assert c(y, ros, w, out) == DEVICE
+
+
+def test_forward_validation(L):
+    E, I, H, T, k = 8, 64, 32, 16, 2
+    g = raw_tensor(FAKE, BF16, (E, I, H))
+    u = raw_tensor(FAKE, BF16, (E, I, H))
+    d = raw_tensor(FAKE, BF16, (E, H, I))
+    x = raw_tensor(FAKE, BF16, (T, H))
+    lg = raw_tensor(FAKE, F32, (T, E))   # logits dtype is independent of the input dtype
+    out = raw_tensor(FAKE, BF16, (T, H))
+    ws = L.moe_forward_workspace_bytes(T, H, I, E, k, BF16)
+
+    def f(x=x, lg=lg, out=out, k=k, renorm=1, wsb=ws, g=g):
+        return L.moe_forward(ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), ctypes.byref(x),
+                             ctypes.byref(lg), MoeRoutingOptions(k, renorm), ctypes.byref(out),
+                             ctypes.c_void_p(FAKE), wsb, None)
+
+    assert f(lg=raw_tensor(FAKE, U32, (T, E))) == DTYPE
+    assert f(x=raw_tensor(FAKE, F16, (T, H))) == DTYPE
+    assert f(lg=raw_tensor(FAKE, F32, (T, E + 1))) == SHAPE
+    assert f(lg=raw_tensor(FAKE, F32, (T + 1, E))) == SHAPE
+    assert f(x=raw_tensor(FAKE, BF16, (T, H + 8))) == SHAPE
+    assert f(k=0) == TOPK and f(k=E + 1) == TOPK
+    assert f(wsb=ws - 1) == WORKSPACE
+    assert f(g=raw_tensor(FAKE, F32, (E, I, H))) == DTYPE
+    assert f() == DEVICE  # well-formed: only the device check is left
+
+
+def test_python_layer_rejects_non_contiguous():
+    import torch
+    x = torch.zeros(4, 6)[:, ::2]
+    with pytest.raises(moe.MoeError):
+        moe.api._desc(x)

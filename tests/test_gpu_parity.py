@@ -1,0 +1,329 @@
+"""HIP path vs the CPU oracle, through the C ABI, on a gfx950 GPU.
+
+Small cases run every stage against the oracle element by element; they span
+several GEMM tiles and a ragged tail.  The full-size workloads run the fused
+forward exactly as the benchmark launches it and compare routing and
+dispatch in full and the output on sampled tokens.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_layer_route_amd as moe
+import moe_synth as S
+import oracle
+from parity import TOL, assert_close, compare_dispatch, compare_routing, host_bits, values
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+NTHREADS = min(16, oracle.default_threads())
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    moe.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def upload(cfg, x, lg, weights):
+    return (x.to(DEV), lg.to(DEV), [w.to(DEV) for w in weights])
+
+
+def small_cases():
+    return [
+        S.CONFIGS["tiny_f32"],
+        S.small_config("ragged_bf16", T=301, H=200, I=136, E=5, top_k=2, dtype="bf16", seed=11),
+        S.small_config("ragged_f16", T=77, H=264, I=72, E=3, top_k=3, dtype="f16", logits_dtype="f32", seed=12),
+        S.small_config("many_experts_bf16", T=96, H=64, I=96, E=40, top_k=4, dtype="bf16", seed=13),
+        S.small_config("wide_rows_bf16", T=700, H=128, I=128, E=4, top_k=2, dtype="bf16", seed=14),
+        S.small_config("one_expert_f32", T=50, H=64, I=64, E=1, top_k=1, dtype="f32", seed=15),
+        S.small_config("k_equals_e_f32", T=40, H=32, I=48, E=6, top_k=6, renormalize=False, seed=16),
+    ]
+
+
+# ------------------------------------------------------------------ routing
+@pytest.mark.parametrize("cfg", [
+    S.CONFIGS["tiny_f32"],
+    S.CONFIGS["edge_f32"],
+    S.small_config("edge_norenorm", T=1024, H=8, I=8, E=16, top_k=4, renormalize=False, edge_rows=True,
+                   seed=1001),
+    S.small_config("route_bf16", T=513, H=8, I=8, E=64, top_k=6, dtype="bf16", seed=21),
+    S.small_config("route_f16", T=300, H=8, I=8, E=128, top_k=8, dtype="f16", seed=22),
+    S.small_config("route_bigE", T=64, H=8, I=8, E=1000, top_k=10, dtype="f32", seed=23),
+    S.small_config("route_maxE", T=8, H=8, I=8, E=4096, top_k=70, dtype="bf16", seed=24),
+    S.small_config("route_k_eq_e", T=100, H=8, I=8, E=7, top_k=7, dtype="f32", seed=25),
+    S.small_config("route_ties_bf16", T=400, H=8, I=8, E=256, top_k=8, dtype="bf16", edge_rows=True, seed=26),
+], ids=lambda c: c.name)
+def test_route_parity(cfg):
+    log(f"route parity {cfg.name}")
+    _, lg = S.make_tokens(cfg)
+    plan = moe.route(lg.to(DEV), moe.RoutingOptions(cfg.top_k, cfg.renormalize))
+    torch.cuda.synchronize()
+    gi = host_bits(plan.expert_indices())
+    compare_routing(gi, plan.weights().cpu(), host_bits(lg), cfg.logits_dtype, cfg.top_k, cfg.renormalize,
+                    NTHREADS)
+
+
+def test_route_exact_ties_pick_lower_id():
+    lg = torch.tensor([[0.5, 2.0, 2.0, 2.0, -1.0, 2.0]] * 3, dtype=torch.float32)
+    plan = moe.route(lg.to(DEV), moe.RoutingOptions(3, True))
+    assert host_bits(plan.expert_indices()).tolist() == [[1, 2, 3]] * 3
+
+
+def test_route_nan_rows_keep_nan():
+    E, k = 6, 3
+    rows = []
+    for pos in range(E):
+        r = [0.0] * E; r[pos] = float("nan"); rows.append(r)
+        r = [0.0] * E; r[pos] = float("inf"); rows.append(r)
+    rows.append([float("-inf")] * E)
+    for dt in ("f32", "bf16", "f16"):
+        lg = torch.tensor(rows).to(S.TORCH_DT[dt])
+        plan = moe.route(lg.to(DEV), moe.RoutingOptions(k, True))
+        assert (host_bits(plan.expert_indices()) == np.arange(k)[None, :]).all()
+        assert torch.isnan(plan.weights().float().cpu()).all()
+
+
+# ------------------------------------------------------------------ dispatch
+@pytest.mark.parametrize("cfg", small_cases() + [S.CONFIGS["edge_f32"]], ids=lambda c: c.name)
+def test_dispatch_parity(cfg):
+    log(f"dispatch parity {cfg.name}")
+    x, lg = S.make_tokens(cfg)
+    idx, _, _ = oracle.route(host_bits(lg), cfg.logits_dtype, cfg.top_k, cfg.renormalize, NTHREADS)
+    xb = host_bits(x)
+    o = oracle.dispatch(idx, cfg.E, xb, cfg.dtype)
+    gidx = torch.from_numpy(idx.view(np.int32)).view(torch.uint32).to(DEV)
+    d = moe.dispatch(x.to(DEV), gidx, cfg.E)
+    torch.cuda.synchronize()
+    gpu = {"rows": host_bits(d.rows), "offsets": host_bits(d.expert_offsets),
+           "row_of_slot": host_bits(d.row_of_slot), "token_of_row": host_bits(d.token_of_row)}
+    compare_dispatch(gpu, *o, xb, idx, cfg.E)
+
+
+def test_dispatch_all_tokens_to_one_expert():
+    cfg = S.small_config("hot", T=3000, H=64, I=64, E=32, top_k=2, dtype="bf16", seed=31)
+    x, _ = S.make_tokens(cfg)
+    idx = np.zeros((cfg.T, 2), np.uint32)
+    idx[:, 1] = 7
+    xb = host_bits(x)
+    o = oracle.dispatch(idx, cfg.E, xb, "bf16")
+    d = moe.dispatch(x.to(DEV), torch.from_numpy(idx.view(np.int32)).view(torch.uint32).to(DEV), cfg.E)
+    torch.cuda.synchronize()
+    gpu = {"rows": host_bits(d.rows), "offsets": host_bits(d.expert_offsets),
+           "row_of_slot": host_bits(d.row_of_slot), "token_of_row": host_bits(d.token_of_row)}
+    compare_dispatch(gpu, *o, xb, idx, cfg.E)
+
+
+def test_invalid_indices_give_nan_rows_without_oob():
+    """An expert id >= E is skipped by dispatch and turns the token's output row
+    NaN at combine (the training section's convention for bad indices)."""
+    T, H, E, k = 33, 64, 4, 2
+    x = torch.randn(T, H).to(torch.bfloat16)
+    idx = np.tile(np.array([[0, 1]], np.uint32), (T, 1))
+    idx[3, 1] = 4
+    idx[10, 0] = 0xFFFFFFFF
+    d = moe.dispatch(x.to(DEV), torch.from_numpy(idx.view(np.int32)).view(torch.uint32).to(DEV), E,
+                     weights=torch.full((T, k), 0.5, dtype=torch.bfloat16, device=DEV))
+    out = d.combine(d.rows).float().cpu()
+    torch.cuda.synchronize()
+    assert int(host_bits(d.expert_offsets)[E]) == T * k - 2
+    ros = host_bits(d.row_of_slot)
+    assert ros[3 * k + 1] == 0xFFFFFFFF and ros[10 * k] == 0xFFFFFFFF
+    nan_rows = torch.isnan(out).all(dim=1)
+    assert nan_rows[3] and nan_rows[10] and int(nan_rows.sum()) == 2
+
+
+# ------------------------------------------------------------------ experts
+@pytest.mark.parametrize("cfg", small_cases() + [S.CONFIGS["edge_f32"]], ids=lambda c: c.name)
+def test_experts_parity(cfg):
+    log(f"experts parity {cfg.name}")
+    x, lg = S.make_tokens(cfg)
+    W = S.make_weights(cfg)
+    Wb = [host_bits(w) for w in W]
+    idx, _, _ = oracle.route(host_bits(lg), cfg.logits_dtype, cfg.top_k, cfg.renormalize, NTHREADS)
+    offsets, ros, tor, rows = oracle.dispatch(idx, cfg.E, host_bits(x), cfg.dtype)
+    Y, h = oracle.experts(*Wb, cfg.dtype, rows, offsets, cfg.E, cfg.H, cfg.I, with_h=True, nthreads=NTHREADS)
+    ex = moe.SwiGluExperts(*[w.to(DEV) for w in W])
+    g_rows = S.from_bits(rows, cfg.dtype, DEV)
+    g_off = torch.from_numpy(offsets.view(np.int32)).view(torch.uint32).to(DEV)
+    gy = ex.forward_dispatched(g_rows, g_off)
+    torch.cuda.synchronize()
+    assert_close(values(gy, cfg.dtype), oracle.widen(Y, cfg.dtype), cfg.dtype, f"expert outputs {cfg.name}")
+
+
+# ------------------------------------------------------------------ combine
+@pytest.mark.parametrize("cfg", small_cases(), ids=lambda c: c.name)
+def test_combine_parity(cfg):
+    log(f"combine parity {cfg.name}")
+    x, lg = S.make_tokens(cfg)
+    W = [host_bits(w) for w in S.make_weights(cfg)]
+    res = oracle.forward(host_bits(x), host_bits(lg), *W, cfg.dtype, cfg.logits_dtype, cfg.top_k,
+                         cfg.renormalize, NTHREADS)
+    gy = S.from_bits(res["Y"], cfg.dtype, DEV)
+    gros = torch.from_numpy(res["row_of_slot"].view(np.int32)).view(torch.uint32).to(DEV)
+    gw = S.from_bits(res["weights"], cfg.logits_dtype, DEV)
+    out = moe.combine(gy, gros, gw)
+    torch.cuda.synchronize()
+    assert_close(values(out, cfg.dtype), oracle.widen(res["output"], cfg.dtype), cfg.dtype, "combine")
+
+
+# ------------------------------------------------------------------ whole chain
+def run_forward_case(cfg, repeat_check=True):
+    x, lg = S.make_tokens(cfg)
+    W = S.make_weights(cfg)
+    res = oracle.forward(host_bits(x), host_bits(lg), *[host_bits(w) for w in W], cfg.dtype, cfg.logits_dtype,
+                         cfg.top_k, cfg.renormalize, NTHREADS)
+    ex = moe.SwiGluExperts(*[w.to(DEV) for w in W])
+    opts = moe.RoutingOptions(cfg.top_k, cfg.renormalize)
+    gx, glg = x.to(DEV), lg.to(DEV)
+    out = ex.forward(gx, glg, opts)
+    plan = moe.route(glg, opts)
+    torch.cuda.synchronize()
+    _, near = compare_routing(host_bits(plan.expert_indices()), plan.weights().cpu(), host_bits(lg),
+                              cfg.logits_dtype, cfg.top_k, cfg.renormalize, NTHREADS)
+    assert near.mean() < 0.01, f"too many near-tie tokens: {near.sum()}"
+    assert_close(values(out, cfg.dtype), oracle.widen(res["output"], cfg.dtype), cfg.dtype,
+                 f"forward {cfg.name}", rows_mask=~near)
+    if repeat_check:
+        out2 = ex.forward(gx, glg, opts)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.uint8) if out.dtype != torch.float32 else out.view(torch.int32),
+                           out2.view(torch.uint8) if out.dtype != torch.float32 else out2.view(torch.int32)), \
+            "forward must be bitwise reproducible"
+    return out
+
+
+@pytest.mark.parametrize("cfg", small_cases() + [
+    S.CONFIGS["edge_f32"],
+    S.small_config("edge_norenorm", T=1024, H=256, I=512, E=16, top_k=4, renormalize=False, edge_rows=True,
+                   seed=1001),
+], ids=lambda c: c.name)
+def test_forward_parity(cfg):
+    log(f"forward parity {cfg.name}")
+    run_forward_case(cfg)
+
+
+def test_split_stages_equal_fused_forward():
+    cfg = S.small_config("split", T=257, H=128, I=192, E=9, top_k=3, dtype="bf16", seed=41)
+    x, lg = S.make_tokens(cfg)
+    W = [w.to(DEV) for w in S.make_weights(cfg)]
+    ex = moe.SwiGluExperts(*W)
+    opts = moe.RoutingOptions(cfg.top_k, True)
+    gx, glg = x.to(DEV), lg.to(DEV)
+    fused = ex.forward(gx, glg, opts)
+    plan = moe.route(glg, opts)
+    disp = plan.dispatch(gx)
+    y = ex.forward_dispatched(disp)
+    split = disp.combine(y)
+    torch.cuda.synchronize()
+    assert torch.equal(fused.view(torch.int16), split.view(torch.int16))
+
+
+def test_forward_empty_batch():
+    cfg = S.small_config("empty", T=0, H=64, I=64, E=4, top_k=2, dtype="bf16")
+    W = [w.to(DEV) for w in S.make_weights(cfg)]
+    ex = moe.SwiGluExperts(*W)
+    out = ex.forward(torch.empty(0, 64, dtype=torch.bfloat16, device=DEV),
+                     torch.empty(0, 4, dtype=torch.bfloat16, device=DEV), moe.RoutingOptions(2, True))
+    torch.cuda.synchronize()
+    assert out.shape == (0, 64)
+
+
+def test_forward_single_token():
+    run_forward_case(S.small_config("single", T=1, H=64, I=128, E=8, top_k=2, dtype="bf16", seed=42))
+
+
+def test_errors_surface_as_moeerror():
+    W = [w.to(DEV) for w in S.make_weights(S.small_config("err", T=4, H=64, I=64, E=4, top_k=2, dtype="bf16"))]
+    ex = moe.SwiGluExperts(*W)
+    x = torch.zeros(4, 64, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(moe.MoeError) as e:
+        ex.forward(x, torch.zeros(4, 5, dtype=torch.bfloat16, device=DEV), moe.RoutingOptions(2, True))
+    assert e.value.name == "MOE_ERR_SHAPE"
+    with pytest.raises(moe.MoeError) as e:
+        ex.forward(x, torch.zeros(4, 4, dtype=torch.bfloat16, device=DEV), moe.RoutingOptions(5, True))
+    assert e.value.name == "MOE_ERR_TOP_K"
+    with pytest.raises(moe.MoeError) as e:
+        ex.forward(x.cpu(), torch.zeros(4, 4, dtype=torch.bfloat16, device=DEV), moe.RoutingOptions(2, True))
+    assert e.value.name == "MOE_ERR_DEVICE"
+
+
+# ------------------------------------------------------------------ full-size workloads, sampled
+@pytest.mark.parametrize("name,n_sample", [("prefill_bf16", 24), ("decode_bf16", 32), ("skewed_bf16", 12)])
+def test_full_size_sampled(name, n_sample):
+    cfg = S.CONFIGS[name]
+    log(f"full-size {name}: generating inputs on the GPU")
+    x, lg = S.make_tokens(cfg, device=DEV)
+    W = S.make_weights(cfg, device=DEV)
+    ex = moe.SwiGluExperts(*W)
+    opts = moe.RoutingOptions(cfg.top_k, cfg.renormalize)
+    out = ex.forward(x, lg, opts)
+    plan = moe.route(lg, opts)
+    torch.cuda.synchronize()
+    log(f"full-size {name}: routing parity over all {cfg.T} tokens")
+    lgb = host_bits(lg)
+    (o_idx, _), near = compare_routing(host_bits(plan.expert_indices()), plan.weights().cpu(), lgb,
+                                       cfg.logits_dtype, cfg.top_k, cfg.renormalize, NTHREADS)
+    assert near.mean() < 0.01
+    log(f"full-size {name}: dispatch invariants over all rows")
+    xb = host_bits(x)
+    d = plan.dispatch(x)
+    torch.cuda.synchronize()
+    gidx = host_bits(plan.expert_indices())
+    o = oracle.dispatch(gidx, cfg.E, xb, cfg.dtype)
+    gpu = {"rows": host_bits(d.rows), "offsets": host_bits(d.expert_offsets),
+           "row_of_slot": host_bits(d.row_of_slot), "token_of_row": host_bits(d.token_of_row)}
+    compare_dispatch(gpu, *o, xb, gidx, cfg.E)
+    del d, gpu, o
+    rng = np.random.default_rng(cfg.seed)
+    cand = np.nonzero(~near)[0]
+    sample = np.sort(rng.choice(cand, size=min(n_sample, len(cand)), replace=False))
+    experts = sorted(set(o_idx[sample].reshape(-1).tolist()))
+    log(f"full-size {name}: oracle on {len(sample)} sampled tokens, {len(experts)} experts")
+    g = {e: host_bits(W[0][e]) for e in experts}
+    u = {e: host_bits(W[1][e]) for e in experts}
+    dn = {e: host_bits(W[2][e]) for e in experts}
+    res = oracle.forward(xb[sample], lgb[sample], g, u, dn, cfg.dtype, cfg.logits_dtype, cfg.top_k,
+                         cfg.renormalize, NTHREADS)
+    assert_close(values(out, cfg.dtype)[sample], oracle.widen(res["output"], cfg.dtype), cfg.dtype,
+                 f"forward {name} (sampled tokens)")
+    # properties at every token: finite output, bitwise reproducible
+    assert torch.isfinite(out.float()).all()
+    out2 = ex.forward(x, lg, opts)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+
+
+@pytest.mark.parametrize("cfg", [
+    S.small_config("halves_bf16", T=300, H=128, I=192, E=6, top_k=2, dtype="bf16", seed=51),
+    S.small_config("halves_small_f16", T=20, H=64, I=96, E=16, top_k=4, dtype="f16", seed=52),
+], ids=lambda c: c.name)
+def test_gate_up_and_down_halves_equal_experts_forward(cfg):
+    """moe_experts_gate_up followed by moe_experts_down runs the same kernels
+    as moe_experts_forward: the results are bitwise equal, and h matches the
+    oracle's stored activation."""
+    x, lg = S.make_tokens(cfg)
+    W = S.make_weights(cfg)
+    Wb = [host_bits(w) for w in W]
+    idx, _, _ = oracle.route(host_bits(lg), cfg.logits_dtype, cfg.top_k, cfg.renormalize, NTHREADS)
+    offsets, _, _, rows = oracle.dispatch(idx, cfg.E, host_bits(x), cfg.dtype)
+    _, h_ref = oracle.experts(*Wb, cfg.dtype, rows, offsets, cfg.E, cfg.H, cfg.I, with_h=True, nthreads=NTHREADS)
+    ex = moe.SwiGluExperts(*[w.to(DEV) for w in W])
+    g_rows = S.from_bits(rows, cfg.dtype, DEV)
+    g_off = torch.from_numpy(offsets.view(np.int32)).view(torch.uint32).to(DEV)
+    whole = ex.forward_dispatched(g_rows, g_off)
+    h = ex.gate_up(g_rows, g_off)
+    y = ex.down_proj(h, g_off)
+    torch.cuda.synchronize()
+    assert torch.equal(whole.view(torch.int16), y.view(torch.int16))
+    assert_close(values(h, cfg.dtype), oracle.widen(h_ref, cfg.dtype), cfg.dtype, "activation h")
