@@ -1,0 +1,279 @@
+#!/usr/bin/env python3
+"""Benchmark of the local MoE forward chain (route -> dispatch -> SwiGLU
+experts -> combine) on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload prefill_bf16]
+
+A step is one fused moe_forward over the whole batch (all stages), with the
+inputs and weights already resident in HBM.  Prints one JSON line:
+  value        whole-job tokens/s of the timed fused forwards;
+  roofline     the dominant kernel (the gate/up grouped GEMM), its
+               algorithmic FLOPs (or bytes, at decode) per launch over its
+               average launch time, measured with HIP events recorded on the
+               stream it runs on, against the MI355X dense peak;
+  stages_ms    per-stage times of the split calls (same kernels);
+  cpu_baseline the CPU oracle timed on a bounded sample of the same workload;
+  secondary    the decode and skewed workloads, same measurement.
+The pages publish no throughput for this chain, so vs_baseline is null.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE forward tokens/s + TFLOP/s (% bf16 MFMA peak) / HBM GB/s at decode"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+GEMM_SRC = os.path.join(ROOT, "mixture_experts_layer_route_amd", "csrc", "experts.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="prefill_bf16",
+                    choices=["prefill_bf16", "decode_bf16", "skewed_bf16"])
+    ap.add_argument("--secondary", default="decode_bf16,skewed_bf16",
+                    help="comma-separated extra workloads to measure ('' for none)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--only-forward", action="store_true",
+                    help="time only the fused forward (for profiler runs)")
+    return ap.parse_args()
+
+
+def kernel_hash() -> str:
+    with open(GEMM_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_for(workload: str):
+    """HBM bytes per launch of the dominant kernel from the committed PMC
+    counter summary, or None when absent or taken on an older kernel."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != kernel_hash():
+        return None
+    w = t.get("workloads", {}).get(workload)
+    return None if w is None else w.get("bytes_per_launch")
+
+
+def measure(name: str, steps: int, warmup: int, only_forward: bool = False) -> dict:
+    import torch
+
+    import mixture_experts_layer_route_amd as moe
+    import moe_synth as S
+
+    cfg = S.CONFIGS[name]
+    dev = "cuda:0"
+    x, lg = S.make_tokens(cfg, device=dev)
+    W = S.make_weights(cfg, device=dev)
+    ex = moe.SwiGluExperts(*W)
+    opts = moe.RoutingOptions(cfg.top_k, cfg.renormalize)
+    ws = torch.empty(ex.forward_workspace_bytes(cfg.T, cfg.top_k, x.dtype), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(x)
+    for _ in range(warmup):
+        ex.forward(x, lg, opts, ws, out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        ex.forward(x, lg, opts, ws, out)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / steps
+    res = {"workload": name, "cfg": cfg, "ms_per_step": ms_step, "event_ms_per_step": e0.elapsed_time(e1) / steps,
+           "tokens_per_s": cfg.T * steps / wall}
+    res["tflops"] = cfg.flops() / (ms_step * 1e-3) / 1e12
+    if only_forward:
+        return res
+
+    # stage times: the split calls run the same kernels; events sit on the
+    # stream every call is launched on (torch's current stream)
+    names = ["route", "dispatch", "experts_gate_up", "experts_down", "combine"]
+    acc = {n: 0.0 for n in names}
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    ews = torch.empty(moe.load().moe_experts_workspace_bytes(cfg.N, cfg.H, cfg.I, cfg.E, 2 if cfg.dtype == "bf16"
+                                                              else (1 if cfg.dtype == "f16" else 0)),
+                      dtype=torch.uint8, device=dev)
+    plan = None
+    for it in range(warmup + steps):
+        evs[0].record()
+        plan = moe.route(lg, opts)
+        evs[1].record()
+        disp = plan.dispatch(x)
+        evs[2].record()
+        h = ex.gate_up(disp.rows, disp.expert_offsets, ews)
+        evs[3].record()
+        y = ex.down_proj(h, disp.expert_offsets, ews)
+        evs[4].record()
+        disp.combine(y)
+        evs[5].record()
+        torch.cuda.synchronize()
+        if it >= warmup:
+            for i, n in enumerate(names):
+                acc[n] += evs[i].elapsed_time(evs[i + 1])
+    res["stages_ms"] = {n: acc[n] / steps for n in names}
+    idx = plan.expert_indices().view(torch.int32).long()
+    res["active_experts"] = int(torch.unique(idx).numel())
+    return res
+
+
+def roofline(res: dict) -> dict:
+    cfg = res["cfg"]
+    t = res["stages_ms"]["experts_gate_up"] * 1e-3
+    es = 2 if cfg.dtype in ("bf16", "f16") else 4
+    if res["workload"] == "decode_bf16":
+        # weight streaming: each active expert's gate and up rows are read
+        # once; plus the dispatched rows read and the activation written
+        nbytes = res["active_experts"] * 2 * cfg.I * cfg.H * es + cfg.N * cfg.H * es + cfg.N * cfg.I * es
+        ach = nbytes / t / 1e9
+        r = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+             "frac": round(ach / PEAK_HBM_GBS, 4)}
+    else:
+        flops = 4.0 * cfg.N * cfg.H * cfg.I  # gate and up products
+        ach = flops / t / 1e12
+        r = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+             "frac": round(ach / PEAK_BF16_TFLOPS, 4)}
+    r["kernel"] = "grouped_gemm_kernel (gate/up, fused SiLU*mul)"
+    r["avg_launch_ms"] = round(res["stages_ms"]["experts_gate_up"], 4)
+    r["traffic"] = traffic_for(res["workload"])
+    return r
+
+
+def hbm_bytes_forward(res: dict) -> float:
+    """Algorithmic HBM bytes of one forward: active experts' weights once,
+    tokens/logits/output once, dispatched rows and expert outputs written and
+    read once, the activation written and read once."""
+    cfg = res["cfg"]
+    es = 2 if cfg.dtype in ("bf16", "f16") else 4
+    w = res["active_experts"] * 3 * cfg.H * cfg.I * es
+    io = cfg.T * cfg.H * es * 2 + cfg.T * cfg.E * es + cfg.N * (4 + es)
+    inter = 2 * (2 * cfg.N * cfg.H * es) + 2 * cfg.N * cfg.I * es
+    return w + io + inter
+
+
+def cpu_baseline(name: str, target_s: float) -> dict:
+    import torch
+
+    import moe_synth as S
+    import oracle
+
+    cfg = S.CONFIGS[name]
+    threads = min(16, oracle.default_threads())
+    x, lg = S.make_tokens(cfg, device="cuda:0")
+    W = S.make_weights(cfg, device="cuda:0")
+    xb, lgb = S.to_bits(x), S.to_bits(lg)
+    cache = {}
+
+    def run(n):
+        idx, _, _ = oracle.route(lgb[:n], cfg.logits_dtype, cfg.top_k, cfg.renormalize, threads)
+        need = sorted(set(idx.reshape(-1).tolist()))
+        for e in need:
+            if e not in cache:
+                cache[e] = tuple(S.to_bits(w[e]) for w in W)
+        g = {e: cache[e][0] for e in need}
+        u = {e: cache[e][1] for e in need}
+        d = {e: cache[e][2] for e in need}
+        t0 = time.perf_counter()
+        oracle.forward(xb[:n], lgb[:n], g, u, d, cfg.dtype, cfg.logits_dtype, cfg.top_k, cfg.renormalize, threads)
+        return time.perf_counter() - t0
+
+    probe = 16
+    dt = run(probe)
+    n = int(max(probe, min(cfg.T, probe * target_s / max(dt, 1e-3))))
+    dt = run(n)
+    del W
+    torch.cuda.empty_cache()
+    return {"value": round(n / dt, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n} of {cfg.T} tokens of {name}, whole forward (route, dispatch, experts, "
+                      f"combine), {dt:.1f} s"}
+
+
+def summary(res: dict) -> dict:
+    cfg = res["cfg"]
+    d = {"workload": res["workload"], "tokens_per_s": round(res["tokens_per_s"], 1),
+         "ms_per_step": round(res["ms_per_step"], 4), "tflops": round(res["tflops"], 2),
+         "pct_bf16_peak": round(100 * res["tflops"] / PEAK_BF16_TFLOPS, 2)}
+    if "stages_ms" in res:
+        d["stages_ms"] = {k: round(v, 4) for k, v in res["stages_ms"].items()}
+        d["active_experts"] = res["active_experts"]
+        d["hbm_gbs_forward"] = round(hbm_bytes_forward(res) / (res["ms_per_step"] * 1e-3) / 1e9, 1)
+        d["roofline"] = roofline(res)
+    d["config"] = {"T": cfg.T, "H": cfg.H, "I": cfg.I, "E": cfg.E, "top_k": cfg.top_k,
+                   "renormalize": cfg.renormalize, "dtype": cfg.dtype}
+    return d
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the MoE chain here runs on a single device "
+              "(no multi-GPU path is built); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import mixture_experts_layer_route_amd as moe
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    moe.load()
+    res = measure(args.workload, args.steps, args.warmup, args.only_forward)
+    head = summary(res)
+    cfg = res["cfg"]
+    line = {
+        "metric": METRIC,
+        "value": round(res["tokens_per_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded; weights ~N(0,1/sqrt(fan_in)), no checkpoint)",
+        "config": {"workload": f"{args.workload}: {cfg.description}", "T": cfg.T, "H": cfg.H, "I": cfg.I,
+                   "E": cfg.E, "top_k": cfg.top_k, "renormalize": cfg.renormalize, "parallelism": "single GPU"},
+        "tflops": head["tflops"],
+        "pct_bf16_peak": head["pct_bf16_peak"],
+    }
+    if "roofline" in head:
+        line["roofline"] = head["roofline"]
+        line["stages_ms"] = head["stages_ms"]
+        line["hbm_gbs_forward"] = head["hbm_gbs_forward"]
+        line["active_experts"] = head["active_experts"]
+    if not args.only_forward:
+        sec = [s for s in args.secondary.split(",") if s and s != args.workload]
+        line["secondary"] = {}
+        for s in sec:
+            torch.cuda.empty_cache()
+            r = measure(s, args.steps, args.warmup)
+            line["secondary"][s] = summary(r)
+            del r
+        torch.cuda.empty_cache()
+        if not args.no_cpu_baseline:
+            line["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

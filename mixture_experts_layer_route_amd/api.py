@@ -177,11 +177,12 @@ class SwiGluExperts:
         self._dw = [_desc(w) for w in (gate, up, down)]
 
     def forward(self, input: torch.Tensor, logits: torch.Tensor, options: RoutingOptions,
-                workspace: torch.Tensor | None = None) -> torch.Tensor:
+                workspace: torch.Tensor | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
         """The whole local chain from precomputed logits (moe_forward)."""
         L = _lib.load()
         T, H = input.shape
-        out = torch.empty((T, H), dtype=input.dtype, device=input.device)
+        if out is None:
+            out = torch.empty((T, H), dtype=input.dtype, device=input.device)
         need = L.moe_forward_workspace_bytes(T, self.hidden, self.intermediate, self.num_experts,
                                              int(options.top_k), _dtype_code(input))
         if workspace is None or workspace.numel() < need:
