@@ -25,6 +25,8 @@
 // by 16 bytes, so the 16 rows a ds_read_b128 touches fall in distinct banks),
 // double buffered: the global loads of slice k+1 are in flight while the
 // matrix cores work on slice k.  FP32 accumulation throughout.
+#include <type_traits>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -113,9 +115,35 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const uint32_t* __res
 }
 
 // ------------------------------------------------------------------ grouped GEMM
+// SiLU(g) * u in FP32: exp on the hardware exp2 unit and a hardware
+// reciprocal; the product is then rounded to the weight dtype, whose
+// precision (bf16/f16), or the f32 tolerance, dwarfs their few-ulp error.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+    return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
+
+template <typename DT> struct store4;
+template <> struct store4<f32_t> {
+    static __device__ __forceinline__ void run(float* p, const float* v) {
+        *(float4*)p = make_float4(v[0], v[1], v[2], v[3]);
+    }
+};
+template <typename DT> struct store4 {
+    static __device__ __forceinline__ void run(uint16_t* p, const float* v) {
+        uint2 w;
+        w.x = (uint32_t)fmt<DT>::store(v[0]) | ((uint32_t)fmt<DT>::store(v[1]) << 16);
+        w.y = (uint32_t)fmt<DT>::store(v[2]) | ((uint32_t)fmt<DT>::store(v[3]) << 16);
+        *(uint2*)p = w;
+    }
+};
+
+// MFMA operand roles: the weight rows are the A operand (16 rows of the
+// output's columns) and the token rows the B operand, so the 16x16 result
+// fragment leaves lane l holding token (l % 16) and four consecutive output
+// columns 4 (l / 16) + 0..3 -- one 8-byte (bf16/f16) or 16-byte (f32) store.
 template <typename DT, bool GATEUP, int BM, int BNB, int WGM, int WGN>
 __global__ __launch_bounds__(WGM* WGN* kWave) void grouped_gemm_kernel(
-    const typename DT::storage* __restrict__ A,   // [rows, K]
+    const typename DT::storage* __restrict__ A,   // [rows, K] token rows
     const typename DT::storage* __restrict__ B0,  // [E, NOUT, K]  (gate or down)
     const typename DT::storage* __restrict__ B1,  // [E, NOUT, K]  (up; GATEUP only)
     typename DT::storage* __restrict__ C,         // [rows, NOUT]
@@ -130,9 +158,9 @@ __global__ __launch_bounds__(WGM* WGN* kWave) void grouped_gemm_kernel(
     constexpr int A_CH = (A_CHUNKS + NT - 1) / NT;
     constexpr int B_CH = (B_CHUNKS + NT - 1) / NT;
     constexpr int BN_OUT = GATEUP ? BNB / 2 : BNB;
-    constexpr int WTM = BM / WGM;             // rows per wave
-    constexpr int MF = WTM / 16;              // 16-row fragments per wave
-    constexpr int NF = BNB / WGN / 16;        // 16-col B fragments per wave
+    constexpr int WTM = BM / WGM;             // token rows per wave
+    constexpr int MF = WTM / 16;              // 16-row token fragments per wave
+    constexpr int NF = BNB / WGN / 16;        // 16-row weight fragments per wave
     constexpr int WCN = BN_OUT / WGN;         // output columns per wave
     constexpr int STAGE = (BM + BNB) * LDS_STRIDE;
     static_assert(NT % CPR == 0, "chunk column must be fixed per thread");
@@ -185,17 +213,25 @@ __global__ __launch_bounds__(WGM* WGN* kWave) void grouped_gemm_kernel(
     }
 
     uint4 ra[A_CH], rb[B_CH];
+    // loads never branch: a chunk past K reads a valid address and is zeroed
     auto gload = [&](int kt) {
         const int kb = kt * ROWB;
         const bool kin = kb + my_ch * 16 < kbytes;
+        const int off = kin ? kb : 0;
 #pragma unroll
-        for (int i = 0; i < A_CH; ++i)
-            ra[i] = (kin && (A_CHUNKS % NT == 0 || tid + i * NT < A_CHUNKS))
-                        ? *(const uint4*)(a_src[i] + kb) : make_uint4(0, 0, 0, 0);
+        for (int i = 0; i < A_CH; ++i) {
+            if (A_CHUNKS % NT == 0 || tid + i * NT < A_CHUNKS) {
+                uint4 v = *(const uint4*)(a_src[i] + off);
+                ra[i] = kin ? v : make_uint4(0, 0, 0, 0);
+            }
+        }
 #pragma unroll
-        for (int i = 0; i < B_CH; ++i)
-            rb[i] = (kin && (B_CHUNKS % NT == 0 || tid + i * NT < B_CHUNKS))
-                        ? *(const uint4*)(b_src[i] + kb) : make_uint4(0, 0, 0, 0);
+        for (int i = 0; i < B_CH; ++i) {
+            if (B_CHUNKS % NT == 0 || tid + i * NT < B_CHUNKS) {
+                uint4 v = *(const uint4*)(b_src[i] + off);
+                rb[i] = kin ? v : make_uint4(0, 0, 0, 0);
+            }
+        }
     };
     auto lstore = [&](int st) {
         unsigned char* base = smem + st * STAGE;
@@ -246,34 +282,265 @@ __global__ __launch_bounds__(WGM* WGN* kWave) void grouped_gemm_kernel(
 #pragma unroll
             for (int i = 0; i < MF; ++i)
 #pragma unroll
-                for (int f = 0; f < NF; ++f) acc[i][f] = mma<DT>::run(av[i], bv[f], acc[i][f]);
+                for (int f = 0; f < NF; ++f) acc[i][f] = mma<DT>::run(bv[f], av[i], acc[i][f]);
         }
         if (kt + 1 < nk) lstore(st ^ 1);
         __syncthreads();
     }
 
-    // epilogue: lane holds rows 4*(lane/16)+rr, column lane%16 of each fragment
+    // epilogue: lane holds token (lane % 16) of each token fragment and
+    // output columns 4 (lane / 16) + 0..3 of each weight fragment
 #pragma unroll
     for (int i = 0; i < MF; ++i) {
+        const int grow = r0 + wm * WTM + i * 16 + (lane & 15);
+        if (grow >= r1) continue;
+        S* crow = C + (int64_t)grow * NOUT;
+        if (GATEUP) {
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            const int grow = r0 + wm * WTM + i * 16 + (lane >> 4) * 4 + rr;
-            if (grow >= r1) continue;
-            S* crow = C + (int64_t)grow * NOUT;
+            for (int f = 0; f < NF / 2; ++f) {
+                const int col = n0 + wn * WCN + f * 16 + (lane >> 4) * 4;
+                if (col < NOUT) {
+                    float v[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) v[r] = silu_mul(acc[i][f][r], acc[i][f + NF / 2][r]);
+                    store4<DT>::run(crow + col, v);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int f = 0; f < NF; ++f) {
+                const int col = n0 + wn * WCN + f * 16 + (lane >> 4) * 4;
+                if (col < NOUT) {
+                    float v[4] = {acc[i][f][0], acc[i][f][1], acc[i][f][2], acc[i][f][3]};
+                    store4<DT>::run(crow + col, v);
+                }
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------ pipelined grouped GEMM (16-bit)
+// The large-tile kernel for bf16/f16: a 256-token x 256-weight-row workgroup
+// tile, a ring of 4 LDS stages of 32 K-elements each, filled by direct
+// global->LDS loads (global_load_lds_dwordx4: each wave instruction writes
+// 1 KB of LDS, lane l at +16 l), issued three stages ahead.  Every LDS row is
+// 64 bytes; the 16-byte chunk c of row r sits at chunk c ^ ((r >> 1) & 3), so
+// the 16 rows a fragment read touches spread over all banks.  While the
+// matrix cores work on step k, the wave reads the fragments of step k+1 into
+// a second register set; one barrier per step publishes the next stage.
+// Requires K % 32 == 0 (no tail handling: loads never leave the rows).
+#ifndef MOE_P_STAGES
+#define MOE_P_STAGES 4
+#endif
+constexpr int kPipeBM = 256, kPipeBN = 256, kPipeBK = 32, kPipeStages = MOE_P_STAGES;
+constexpr int kPipeAhead = kPipeStages - 1;  // K steps of DMA in flight ahead of the reads
+
+// The stage ring is driven by hand: the DMA loads, the vmcnt waits and the
+// barriers below are the whole ordering protocol of the pipeline, so they
+// are written as volatile asm that the compiler neither reorders memory
+// around nor pads with waits of its own (it would otherwise drain every DMA
+// before each fragment read, since it cannot tell the stages apart).
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+// 16 bytes per lane from global address g into LDS at m0 + 16 * lane.
+// m0 is written here and nowhere else in these kernels.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g),
+                 "s"(__builtin_amdgcn_readfirstlane(lds_base))
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+__device__ __forceinline__ void barrier_lds() { asm volatile("s_barrier" ::: "memory"); }
+
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// 32x32x16 matrix op: lane l supplies 8 K-values of row (l % 32) of each
+// operand, K group (l / 32); lane l receives column (l % 32) and rows
+// 8 (r / 4) + 4 (l / 32) + (r % 4) of the result in register r.
+template <typename DT> struct mma32;
+template <> struct mma32<bf16_t> {
+    static __device__ __forceinline__ f32x16_t run(uint4 a, uint4 b, f32x16_t c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                       __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+    }
+};
+template <> struct mma32<f16_t> {
+    static __device__ __forceinline__ f32x16_t run(uint4 a, uint4 b, f32x16_t c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                      __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+    }
+};
+
+template <int N> __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+// lgkmcnt(0) through the builtin, so the compiler's own LDS-read tracking
+// knows the fragment registers are complete
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+template <typename DT, bool GATEUP, int WGM, int WGN>
+__global__ __launch_bounds__(WGM* WGN* kWave, 1) void grouped_gemm_pipe_kernel(
+    const typename DT::storage* __restrict__ A, const typename DT::storage* __restrict__ B0,
+    const typename DT::storage* __restrict__ B1, typename DT::storage* __restrict__ C,
+    const int4* __restrict__ tiles, const uint32_t* __restrict__ tile_count, int K, int NOUT, int n_tiles,
+    int nblocks) {
+    using S = typename DT::storage;
+    constexpr int NW = WGM * WGN;
+    constexpr int ROWB = kPipeBK * 2;                      // 64 bytes per row per stage
+    constexpr int STAGE = (kPipeBM + kPipeBN) * ROWB;      // 32 KB
+    constexpr int LPW = (kPipeBM + kPipeBN) * ROWB / 1024 / NW;  // 1 KB loads per wave per stage
+    constexpr int BN_OUT = GATEUP ? kPipeBN / 2 : kPipeBN;
+    constexpr int WTM = kPipeBM / WGM, WTN = kPipeBN / WGN;
+    constexpr int MB = WTM / 32, NB = WTN / 32;            // 32x32 blocks per wave
+    constexpr int WCN = BN_OUT / WGN;
+    static_assert(!GATEUP || NB % 2 == 0, "gate and up blocks pair up");
+
+    constexpr int NSTAGE = kPipeStages;
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[NSTAGE * STAGE];
+
+    const int bid = blockIdx.x;
+    const int q = nblocks / 8, rem = nblocks % 8;
+    const int xcd = bid % 8, loc = bid / 8;
+    const int pid = (xcd < rem ? xcd * (q + 1) : rem * (q + 1) + (xcd - rem) * q) + loc;
+    const int m_idx = pid / n_tiles, n_idx = pid % n_tiles;
+    if (m_idx >= (int)*tile_count) return;
+    const int4 tl = tiles[m_idx];
+    const int e = tl.x, r0 = tl.y, r1 = tl.z;
+    const int n0 = n_idx * BN_OUT;
+    const int lane = lane_id(), wid = threadIdx.x / kWave;
+    const int wm = wid / WGN, wn = wid % WGN;
+
+    // global sources of this lane's LDS-DMA chunks (one per load instruction)
+    const char* src[LPW];
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) {
+        const int row = (wid * LPW + j) * 16 + (lane >> 2);  // stage row 0..511
+        const int lc = (lane & 3) ^ ((row >> 1) & 3);        // logical chunk for this physical slot
+        const S* p;
+        if (row < kPipeBM) {
+            p = A + (int64_t)min(r0 + row, r1 - 1) * K;
+        } else {
+            const int w = row - kPipeBM;
+            if (GATEUP)
+                p = (w < BN_OUT ? B0 : B1) + ((int64_t)e * NOUT + min(n0 + (w % BN_OUT), NOUT - 1)) * K;
+            else
+                p = B0 + ((int64_t)e * NOUT + min(n0 + w, NOUT - 1)) * K;
+        }
+        src[j] = (const char*)p + lc * 16;
+    }
+    const int nk = K / kPipeBK;
+    const uint32_t smem_base = lds_offset(smem) + wid * LPW * 1024;
+    // fragment rows; the swizzle term depends only on the lane for every block
+    const int frow = lane & 31;
+    const int sw0 = (((lane >> 5) + 0) ^ ((frow >> 1) & 3)) * 16;  // K half 0 of a stage
+    const int sw1 = (((lane >> 5) + 2) ^ ((frow >> 1) & 3)) * 16;  // K half 1
+    const int fa0 = (wm * WTM + frow) * ROWB;
+    int fb[NB];
+#pragma unroll
+    for (int f = 0; f < NB; ++f) {
+        int brow;
+        if (GATEUP)
+            brow = (f < NB / 2) ? wn * WCN + f * 32 : BN_OUT + wn * WCN + (f - NB / 2) * 32;
+        else
+            brow = wn * WTN + f * 32;
+        fb[f] = (kPipeBM + brow + frow) * ROWB;
+    }
+
+    f32x16_t acc[MB][NB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int f = 0; f < NB; ++f)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][f][r] = 0.0f;
+
+    uint4 av[2][MB], bv[2][NB];
+    auto read_frags = [&](int kt, int half, int set) {
+        const unsigned char* base = smem + (kt % NSTAGE) * STAGE + (half ? sw1 : sw0);
+#pragma unroll
+        for (int i = 0; i < MB; ++i) av[set][i] = *(const uint4*)(base + fa0 + i * 32 * ROWB);
+#pragma unroll
+        for (int f = 0; f < NB; ++f) bv[set][f] = *(const uint4*)(base + fb[f]);
+    };
+    {
+        // DMA of one 1 KB piece j of K step kt; steps past the end re-load the
+        // last step into a stage nobody reads again, so every count is static
+        auto issue_part = [&](int kt, int j) {
+            const int ks = min(kt, nk - 1);
+            lds_dma16(src[j] + ks * ROWB, smem_base + (kt % NSTAGE) * STAGE + j * 1024);
+        };
+        // MFMAs of one K half with the DMA pieces [j0, j0 + LPW/2) of step dkt
+        // spread between them, so the address unit drains between issues
+        auto compute_dma = [&](int set, int dkt, int j0) {
+            constexpr int NM = MB * NB, ND = LPW / 2, EVERY = NM / (ND > 0 ? ND : 1);
+            int m = 0;
+#pragma unroll
+            for (int i = 0; i < MB; ++i)
+#pragma unroll
+                for (int f = 0; f < NB; ++f) {
+                    acc[i][f] = mma32<DT>::run(bv[set][f], av[set][i], acc[i][f]);
+                    if (m % EVERY == EVERY - 1 && m / EVERY < ND) issue_part(dkt, j0 + m / EVERY);
+                    ++m;
+                }
+        };
+        static_assert(LPW % 2 == 0 && (MB * NB) % (LPW / 2) == 0, "DMA pieces spread evenly");
+#pragma unroll
+        for (int p = 0; p < kPipeAhead; ++p)
+#pragma unroll
+            for (int j = 0; j < LPW; ++j) issue_part(p, j);
+        wait_vm<(kPipeAhead - 1) * LPW>();  // stage 0 landed
+        barrier_lds();
+        read_frags(0, 0, 0);
+        for (int kt = 0; kt < nk; ++kt) {
+            // read the second K half of step kt, multiply the first half while
+            // starting the DMA of step kt+3, publish stage kt+1, read its first
+            // half, multiply the second half of step kt with the rest of the DMA
+            read_frags(kt, 1, 1);
+            compute_dma(0, kt + kPipeAhead, 0);
+            // stage kt+1 landed; step kt+2 and half of kt+3 may be in flight.
+            // This wave's reads of stage kt complete before the barrier, so the
+            // stage can be refilled once every wave has passed it.
+            wait_vm<(kPipeAhead - 2) * LPW + LPW / 2>();
+            wait_lgkm0();
+            barrier_lds();
+            read_frags(kt + 1, 0, 0);
+            compute_dma(1, kt + kPipeAhead, LPW / 2);
+        }
+        wait_vm<0>();
+    }
+
+    // epilogue: lane holds token (lane % 32) of each token block and output
+    // columns 8 (r / 4) + 4 (lane / 32) + (r % 4) of each weight block
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+        const int grow = r0 + wm * WTM + i * 32 + frow;
+        if (grow >= r1) continue;
+        S* crow = C + (int64_t)grow * NOUT;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int cb = g * 8 + (lane >> 5) * 4;
             if (GATEUP) {
 #pragma unroll
-                for (int f = 0; f < NF / 2; ++f) {
-                    const int col = n0 + wn * WCN + f * 16 + (lane & 15);
+                for (int f = 0; f < NB / 2; ++f) {
+                    const int col = n0 + wn * WCN + f * 32 + cb;
                     if (col < NOUT) {
-                        const float g = acc[i][f][rr], u = acc[i][f + NF / 2][rr];
-                        crow[col] = fmt<DT>::store(g / (1.0f + expf(-g)) * u);
+                        float v[4];
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            v[r] = silu_mul(acc[i][f][g * 4 + r], acc[i][f + NB / 2][g * 4 + r]);
+                        store4<DT>::run(crow + col, v);
                     }
                 }
             } else {
 #pragma unroll
-                for (int f = 0; f < NF; ++f) {
-                    const int col = n0 + wn * WCN + f * 16 + (lane & 15);
-                    if (col < NOUT) crow[col] = fmt<DT>::store(acc[i][f][rr]);
+                for (int f = 0; f < NB; ++f) {
+                    const int col = n0 + wn * WTN + f * 32 + cb;
+                    if (col < NOUT) {
+                        float v[4] = {acc[i][f][g * 4], acc[i][f][g * 4 + 1], acc[i][f][g * 4 + 2],
+                                      acc[i][f][g * 4 + 3]};
+                        store4<DT>::run(crow + col, v);
+                    }
                 }
             }
         }
@@ -304,15 +571,46 @@ hipError_t launch_gemm(const void* A, const void* B0, const void* B1, void* C, c
     return hipGetLastError();
 }
 
-// Two tile shapes: a 128-row tile for experts that own many rows, and a
+template <typename DT, bool GATEUP, int WGM, int WGN>
+hipError_t launch_pipe(const void* A, const void* B0, const void* B1, void* C, const int4* tiles,
+                       const uint32_t* count, int64_t mt, int K, int NOUT, hipStream_t s) {
+    using S = typename DT::storage;
+    constexpr int BN_OUT = GATEUP ? kPipeBN / 2 : kPipeBN;
+    const int n_tiles = (NOUT + BN_OUT - 1) / BN_OUT;
+    const int64_t nb = mt * n_tiles;
+    if (nb == 0) return hipSuccess;
+    if (nb > 0x7fffffff) return hipErrorInvalidValue;
+    grouped_gemm_pipe_kernel<DT, GATEUP, WGM, WGN><<<(unsigned)nb, WGM * WGN * kWave, 0, s>>>(
+        (const S*)A, (const S*)B0, (const S*)B1, (S*)C, tiles, count, K, NOUT, n_tiles, (int)nb);
+    return hipGetLastError();
+}
+
+#ifndef MOE_P_WM
+#define MOE_P_WM 2   // waves along token rows of the pipelined tile
+#define MOE_P_WN 4   // waves along weight rows
+#endif
+
+// Two tile shapes: a large tile for experts that own many rows, and a
 // 16-row tile for decode-sized batches, where each expert owns a handful of
 // rows and the products are a stream of weight rows.
+#ifndef MOE_L_BM
+#define MOE_L_BM 128   // rows of the large tile
+#define MOE_L_BN 128   // weight rows of the large tile
+#define MOE_L_WM 2     // waves along rows
+#define MOE_L_WN 2     // waves along weight rows
+#endif
+#ifndef MOE_S_BN
+#define MOE_S_BN 256   // weight rows of the 16-row tile
+#define MOE_S_WN 4
+#endif
 constexpr int kSmallBM = 16;
 
 template <typename DT>
 hipError_t launch_typed(const ExpertsArgs& a, hipStream_t s, ExpertsPart part) {
     const bool small = a.N < 64 * (int64_t)a.E;
-    const int BM = small ? kSmallBM : 128;
+    // the pipelined kernel: 16-bit types, both K extents whole stages
+    const bool pipe = !small && sizeof(typename DT::storage) == 2 && a.H % kPipeBK == 0 && a.I % kPipeBK == 0;
+    const int BM = small ? kSmallBM : (pipe ? kPipeBM : MOE_L_BM);
     int4* tiles = (int4*)((char*)a.tiles + 256);
     uint32_t* count = (uint32_t*)a.tiles;
     const int64_t mt = max_mtiles(a.N, a.E, BM);
@@ -320,14 +618,25 @@ hipError_t launch_typed(const ExpertsArgs& a, hipStream_t s, ExpertsPart part) {
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int H = (int)a.H, I = (int)a.I;
+    if (pipe) {
+        if constexpr (sizeof(typename DT::storage) == 2) {
+            if (part != kDown) {
+                err = launch_pipe<DT, true, MOE_P_WM, MOE_P_WN>(a.x, a.gate, a.up, a.h, tiles, count, mt, H, I, s);
+                if (err != hipSuccess) return err;
+            }
+            if (part != kGateUp)
+                err = launch_pipe<DT, false, MOE_P_WM, MOE_P_WN>(a.h, a.down, nullptr, a.y, tiles, count, mt, I, H, s);
+        }
+        return err;
+    }
     if (part != kDown) {
-        err = small ? launch_gemm<DT, true, 16, 256, 1, 4>(a.x, a.gate, a.up, a.h, tiles, count, mt, H, I, s)
-                    : launch_gemm<DT, true, 128, 128, 2, 2>(a.x, a.gate, a.up, a.h, tiles, count, mt, H, I, s);
+        err = small ? launch_gemm<DT, true, 16, MOE_S_BN, 1, MOE_S_WN>(a.x, a.gate, a.up, a.h, tiles, count, mt, H, I, s)
+                    : launch_gemm<DT, true, MOE_L_BM, MOE_L_BN, MOE_L_WM, MOE_L_WN>(a.x, a.gate, a.up, a.h, tiles, count, mt, H, I, s);
         if (err != hipSuccess) return err;
     }
     if (part != kGateUp) {
-        err = small ? launch_gemm<DT, false, 16, 256, 1, 4>(a.h, a.down, nullptr, a.y, tiles, count, mt, I, H, s)
-                    : launch_gemm<DT, false, 128, 128, 2, 2>(a.h, a.down, nullptr, a.y, tiles, count, mt, I, H, s);
+        err = small ? launch_gemm<DT, false, 16, MOE_S_BN, 1, MOE_S_WN>(a.h, a.down, nullptr, a.y, tiles, count, mt, I, H, s)
+                    : launch_gemm<DT, false, MOE_L_BM, MOE_L_BN, MOE_L_WM, MOE_L_WN>(a.h, a.down, nullptr, a.y, tiles, count, mt, I, H, s);
     }
     return err;
 }

@@ -48,6 +48,11 @@ def small_cases():
         S.small_config("wide_rows_bf16", T=700, H=128, I=128, E=4, top_k=2, dtype="bf16", seed=14),
         S.small_config("one_expert_f32", T=50, H=64, I=64, E=1, top_k=1, dtype="f32", seed=15),
         S.small_config("k_equals_e_f32", T=40, H=32, I=48, E=6, top_k=6, renormalize=False, seed=16),
+        # large-tile pipelined kernel (16-bit, H and I multiples of 32): ragged
+        # token tiles, one and two K stages, f16
+        S.small_config("pipe_f16", T=500, H=96, I=160, E=3, top_k=2, dtype="f16", seed=17),
+        S.small_config("pipe_short_k_bf16", T=600, H=64, I=32, E=4, top_k=2, dtype="bf16", seed=18),
+        S.small_config("pipe_many_tiles_bf16", T=1100, H=256, I=320, E=5, top_k=3, dtype="bf16", seed=19),
     ]
 
 
