@@ -49,6 +49,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--only-forward", action="store_true",
                     help="time only the fused forward (for profiler runs)")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="after measuring, copy this many MiB device-to-device once: a kernel of known "
+                         "traffic for scaling HBM byte counters (FETCH_SIZE / WRITE_SIZE)")
     return ap.parse_args()
 
 
@@ -272,6 +275,15 @@ def main():
         torch.cuda.empty_cache()
         if not args.no_cpu_baseline:
             line["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_seconds)
+    if args.calibrate_copy_mib > 0:
+        n = args.calibrate_copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        line["calibration_copy_bytes"] = n
+        del src, dst
     print(json.dumps(line), flush=True)
 
 

@@ -8,59 +8,69 @@
 // row is out of range (an expert id >= E at dispatch) makes the whole output
 // row NaN, with no out-of-bounds access.
 //
-// One wavefront per token; each lane owns VEC consecutive columns, so every
-// row of Y is read with wide coalesced loads.
+// Each thread owns VEC consecutive columns of one token, so every row of Y is
+// read with wide coalesced loads.
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
 
+// grid (tokens, column chunks): thread -> VEC consecutive columns of one
+// token.  The token's k rows and weights are wave-uniform; the k loads are
+// issued in batches of 8 before their multiply-adds, so the loads of one
+// thread overlap instead of forming a chain of round trips.
 template <typename DT, typename WT, int VEC>
 __global__ __launch_bounds__(256) void combine_kernel(const typename DT::storage* __restrict__ Y, int64_t N,
                                                       const uint32_t* __restrict__ row_of_slot,
                                                       const typename WT::storage* __restrict__ w,
-                                                      int64_t T, int k, int64_t H,
+                                                      int k, int64_t H,
                                                       typename DT::storage* __restrict__ out) {
     using S = typename DT::storage;
-    const int lane = lane_id();
-    const int64_t t = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
-    if (t >= T) return;
-    bool bad = false;
-    for (int j = lane; j < k; j += kWave) bad |= (int64_t)row_of_slot[t * k + j] >= N;
-    const bool nan_row = __any(bad);
-    S* o = out + t * H;
-    for (int64_t c0 = (int64_t)lane * VEC; c0 < H; c0 += (int64_t)kWave * VEC) {
-        float acc[VEC];
+    const int64_t t = blockIdx.x;
+    const int64_t c0 = ((int64_t)blockIdx.y * blockDim.x + threadIdx.x) * VEC;
+    if (c0 >= H) return;
+    const uint32_t* rs = row_of_slot + t * k;
+    const typename WT::storage* ws = w + t * k;
+    bool nan_row = false;
+    for (int j = 0; j < k; ++j) nan_row |= (int64_t)rs[j] >= N;
+    float acc[VEC];
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) acc[v] = 0.0f;
-        if (!nan_row) {
-            for (int j = 0; j < k; ++j) {
-                const uint32_t r = row_of_slot[t * k + j];  // wave-uniform, cached
-                const float wj = fmt<WT>::load(w[t * k + j]);
-                const S* yr = Y + (int64_t)r * H + c0;
-                S vals[VEC];
-                if constexpr (VEC * sizeof(S) == 16) {
-                    *(uint4*)vals = *(const uint4*)yr;
-                } else {
+    for (int v = 0; v < VEC; ++v) acc[v] = nan_row ? __uint_as_float(0x7fc00000u) : 0.0f;
+    if (!nan_row) {
+        constexpr int B = 8;
+        for (int j0 = 0; j0 < k; j0 += B) {
+            S vals[B][VEC];
 #pragma unroll
-                    for (int v = 0; v < VEC; ++v) vals[v] = yr[v];
+            for (int b = 0; b < B; ++b) {
+                if (j0 + b < k) {
+                    const S* yr = Y + (int64_t)rs[j0 + b] * H + c0;
+                    if constexpr (VEC * sizeof(S) == 16) {
+                        *(uint4*)vals[b] = *(const uint4*)yr;
+                    } else {
+#pragma unroll
+                        for (int v = 0; v < VEC; ++v) vals[b][v] = yr[v];
+                    }
                 }
-#pragma unroll
-                for (int v = 0; v < VEC; ++v) acc[v] = fmaf(wj, fmt<DT>::load(vals[v]), acc[v]);
             }
-        } else {
 #pragma unroll
-            for (int v = 0; v < VEC; ++v) acc[v] = __uint_as_float(0x7fc00000u);
+            for (int b = 0; b < B; ++b) {
+                if (j0 + b < k) {  // slots in fixed order j = 0..k-1
+                    const float wj = fmt<WT>::load(ws[j0 + b]);
+#pragma unroll
+                    for (int v = 0; v < VEC; ++v) acc[v] = fmaf(wj, fmt<DT>::load(vals[b][v]), acc[v]);
+                }
+            }
         }
-        S res[VEC];
+    }
+    S res[VEC];
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) res[v] = fmt<DT>::store(acc[v]);
-        if constexpr (VEC * sizeof(S) == 16) {
-            *(uint4*)(o + c0) = *(const uint4*)res;
-        } else {
+    for (int v = 0; v < VEC; ++v) res[v] = fmt<DT>::store(acc[v]);
+    S* o = out + t * H + c0;
+    if constexpr (VEC * sizeof(S) == 16) {
+        *(uint4*)o = *(const uint4*)res;
+    } else {
 #pragma unroll
-            for (int v = 0; v < VEC; ++v) o[c0 + v] = res[v];
-        }
+        for (int v = 0; v < VEC; ++v) o[v] = res[v];
     }
 }
 
@@ -68,16 +78,21 @@ template <typename DT, typename WT>
 hipError_t launch_typed(const CombineArgs& a, hipStream_t s) {
     using S = typename DT::storage;
     using W = typename WT::storage;
-    const int wpb = 4;
-    const dim3 grid((unsigned)((a.T + wpb - 1) / wpb)), block(wpb * kWave);
     constexpr int V16 = 16 / sizeof(S);
     const uintptr_t al = (uintptr_t)a.y | (uintptr_t)a.out;
-    if (a.H % V16 == 0 && al % 16 == 0)
+    const bool wide = a.H % V16 == 0 && al % 16 == 0;
+    const int64_t chunks = ((wide ? a.H / V16 : a.H) + 255) / 256;
+    if (a.T > 0x7fffffff || chunks > 65535) return hipErrorInvalidValue;
+    const dim3 block(256);
+    if (wide) {
+        const dim3 grid((unsigned)a.T, (unsigned)chunks);
         combine_kernel<DT, WT, V16><<<grid, block, 0, s>>>((const S*)a.y, a.N, a.row_of_slot, (const W*)a.w,
-                                                           a.T, a.k, a.H, (S*)a.out);
-    else
+                                                           a.k, a.H, (S*)a.out);
+    } else {
+        const dim3 grid((unsigned)a.T, (unsigned)chunks);
         combine_kernel<DT, WT, 1><<<grid, block, 0, s>>>((const S*)a.y, a.N, a.row_of_slot, (const W*)a.w,
-                                                         a.T, a.k, a.H, (S*)a.out);
+                                                         a.k, a.H, (S*)a.out);
+    }
     return hipGetLastError();
 }
 

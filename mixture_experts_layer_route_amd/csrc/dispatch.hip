@@ -13,8 +13,8 @@
 //              rank_in_expert = base + local rank.
 //   scan    -- one workgroup: exclusive prefix sum of the counts, ascending
 //              expert id, into offsets[E+1].
-//   gather  -- one wavefront per token: the token's row is read once with
-//              16-byte loads and written to each of its k dispatched rows.
+//   gather  -- one thread per (token, 16-byte unit): the unit is read once
+//              and written to each of the token's k dispatched rows.
 #include "moe_internal.h"
 
 namespace moe {
@@ -95,52 +95,49 @@ __global__ __launch_bounds__(1024) void scan_kernel(const uint32_t* __restrict__
     if (threadIdx.x == 0) offsets[E] = total;
 }
 
-// V: copy unit (uint4 = 16 bytes when rows allow it, else 4 or 2 bytes)
+// V: copy unit (uint4 = 16 bytes when rows allow it, else 4 or 2 bytes).
+// grid (tokens, unit chunks): each thread reads one unit of its token once
+// and writes it to the token's k dispatched rows; the first chunk's threads
+// also record the mapping.
 template <typename V>
-__global__ __launch_bounds__(256) void gather_kernel(const V* __restrict__ x, int64_t T, int64_t row_units,
-                                                     int k, int E, const uint32_t* __restrict__ idx,
+__global__ __launch_bounds__(256) void gather_kernel(const V* __restrict__ x, int64_t row_units, int k, int E,
+                                                     const uint32_t* __restrict__ idx,
                                                      const uint32_t* __restrict__ rank,
                                                      const uint32_t* __restrict__ offsets,
                                                      V* __restrict__ dispatched,
                                                      uint32_t* __restrict__ row_of_slot,
                                                      uint32_t* __restrict__ token_of_row) {
-    const int lane = lane_id();
-    const int64_t t = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
-    if (t >= T) return;
-    for (int j0 = 0; j0 < k; j0 += kWave) {
-        const int j = j0 + lane;
-        uint32_t row = kInvalidRow;
-        if (j < k) {
-            const uint32_t e = idx[t * k + j];
+    const int64_t t = blockIdx.x;
+    const uint32_t* it = idx + t * k;
+    const uint32_t* rt = rank + t * k;
+    if (blockIdx.y == 0) {
+        for (int j = threadIdx.x; j < k; j += blockDim.x) {
+            const uint32_t e = it[j];
+            uint32_t row = kInvalidRow;
             if (e < (uint32_t)E) {
-                row = offsets[e] + rank[t * k + j];
+                row = offsets[e] + rt[j];
                 token_of_row[row] = (uint32_t)t;
             }
             row_of_slot[t * k + j] = row;
         }
-        const int nj = min(kWave, k - j0);
-        const V* src = x + t * row_units;
-        // the loop bound is wave-uniform so every lane takes part in the shuffles
-        for (int64_t u0 = 0; u0 < row_units; u0 += kWave) {
-            const int64_t u = u0 + lane;
-            const bool ok = u < row_units;
-            V val{};
-            if (ok) val = src[u];
-            for (int jj = 0; jj < nj; ++jj) {
-                const uint32_t r = __shfl(row, jj, kWave);
-                if (ok && r != kInvalidRow) dispatched[(int64_t)r * row_units + u] = val;
-            }
-        }
+    }
+    const int64_t u = (int64_t)blockIdx.y * blockDim.x + threadIdx.x;
+    if (u >= row_units) return;
+    const V val = x[t * row_units + u];
+    for (int j = 0; j < k; ++j) {
+        const uint32_t e = it[j];  // wave-uniform
+        if (e < (uint32_t)E) dispatched[(int64_t)(offsets[e] + rt[j]) * row_units + u] = val;
     }
 }
 
 template <typename V>
 hipError_t launch_gather(const DispatchArgs& a, hipStream_t s) {
-    const int wpb = 4;
-    const dim3 grid((unsigned)((a.T + wpb - 1) / wpb)), block(wpb * kWave);
-    gather_kernel<V><<<grid, block, 0, s>>>((const V*)a.x, a.T, a.row_bytes / (int64_t)sizeof(V), a.k,
-                                            a.E, a.idx, a.rank, a.offsets, (V*)a.dispatched,
-                                            a.row_of_slot, a.token_of_row);
+    const int64_t units = a.row_bytes / (int64_t)sizeof(V);
+    const int64_t chunks = (units + 255) / 256;
+    if (a.T > 0x7fffffff || chunks > 65535) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)a.T, (unsigned)(chunks > 0 ? chunks : 1)), block(256);
+    gather_kernel<V><<<grid, block, 0, s>>>((const V*)a.x, units, a.k, a.E, a.idx, a.rank, a.offsets,
+                                            (V*)a.dispatched, a.row_of_slot, a.token_of_row);
     return hipGetLastError();
 }
 

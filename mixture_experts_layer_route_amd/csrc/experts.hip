@@ -114,6 +114,26 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const uint32_t* __res
     if (threadIdx.x == 0) *count = min(total, max_tiles);
 }
 
+// ------------------------------------------------------------------ tile order
+// Workgroup b -> (token tile, weight tile).  The hardware hands workgroup b to
+// XCD b % 8, so ids are first remapped to give each XCD a contiguous run of
+// logical tiles; the run is then walked in groups of kGroupM token tiles,
+// weight tile by weight tile, so the ~32 workgroups an XCD runs at once share
+// a few token tiles and a few weight tiles in that XCD's L2.
+constexpr int kGroupM = 8;
+__device__ __forceinline__ void tile_of_block(int bid, int nblocks, int n_tiles, int m_tiles, int* m_idx,
+                                              int* n_idx) {
+    const int q = nblocks / 8, rem = nblocks % 8;
+    const int xcd = bid % 8, loc = bid / 8;
+    const int pid = (xcd < rem ? xcd * (q + 1) : rem * (q + 1) + (xcd - rem) * q) + loc;
+    const int group = pid / (kGroupM * n_tiles);
+    const int first_m = group * kGroupM;
+    const int gm = min(kGroupM, m_tiles - first_m);  // the last group may be short
+    const int in_group = pid - group * kGroupM * n_tiles;
+    *m_idx = first_m + in_group % gm;
+    *n_idx = in_group / gm;
+}
+
 // ------------------------------------------------------------------ grouped GEMM
 // SiLU(g) * u in FP32: exp on the hardware exp2 unit and a hardware
 // reciprocal; the product is then rounded to the weight dtype, whose
@@ -169,13 +189,8 @@ __global__ __launch_bounds__(WGM* WGN* kWave) void grouped_gemm_kernel(
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE];
 
-    // XCD-aware remap: hardware hands workgroup b to XCD b % 8; give each XCD
-    // a contiguous range of logical tiles.
-    const int bid = blockIdx.x;
-    const int q = nblocks / 8, rem = nblocks % 8;
-    const int xcd = bid % 8, loc = bid / 8;
-    const int pid = (xcd < rem ? xcd * (q + 1) : rem * (q + 1) + (xcd - rem) * q) + loc;
-    const int m_idx = pid / n_tiles, n_idx = pid % n_tiles;
+    int m_idx, n_idx;
+    tile_of_block(blockIdx.x, nblocks, n_tiles, nblocks / n_tiles, &m_idx, &n_idx);
     if (m_idx >= (int)*tile_count) return;
     const int4 tl = tiles[m_idx];
     const int e = tl.x, r0 = tl.y, r1 = tl.z;
@@ -332,7 +347,10 @@ __global__ __launch_bounds__(WGM* WGN* kWave) void grouped_gemm_kernel(
 #ifndef MOE_P_STAGES
 #define MOE_P_STAGES 4
 #endif
-constexpr int kPipeBM = 256, kPipeBN = 256, kPipeBK = 32, kPipeStages = MOE_P_STAGES;
+#ifndef MOE_P_BN
+#define MOE_P_BN 256
+#endif
+constexpr int kPipeBM = 256, kPipeBN = MOE_P_BN, kPipeBK = 32, kPipeStages = MOE_P_STAGES;
 constexpr int kPipeAhead = kPipeStages - 1;  // K steps of DMA in flight ahead of the reads
 
 // The stage ring is driven by hand: the DMA loads, the vmcnt waits and the
@@ -379,8 +397,11 @@ template <int N> __device__ __forceinline__ void wait_vm() { asm volatile("s_wai
 // knows the fragment registers are complete
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
+#ifndef MOE_P_MINB
+#define MOE_P_MINB 1   // workgroups per CU the register budget must allow
+#endif
 template <typename DT, bool GATEUP, int WGM, int WGN>
-__global__ __launch_bounds__(WGM* WGN* kWave, 1) void grouped_gemm_pipe_kernel(
+__global__ __launch_bounds__(WGM* WGN* kWave, MOE_P_MINB) void grouped_gemm_pipe_kernel(
     const typename DT::storage* __restrict__ A, const typename DT::storage* __restrict__ B0,
     const typename DT::storage* __restrict__ B1, typename DT::storage* __restrict__ C,
     const int4* __restrict__ tiles, const uint32_t* __restrict__ tile_count, int K, int NOUT, int n_tiles,
@@ -399,11 +420,8 @@ __global__ __launch_bounds__(WGM* WGN* kWave, 1) void grouped_gemm_pipe_kernel(
     constexpr int NSTAGE = kPipeStages;
     __shared__ __attribute__((aligned(1024))) unsigned char smem[NSTAGE * STAGE];
 
-    const int bid = blockIdx.x;
-    const int q = nblocks / 8, rem = nblocks % 8;
-    const int xcd = bid % 8, loc = bid / 8;
-    const int pid = (xcd < rem ? xcd * (q + 1) : rem * (q + 1) + (xcd - rem) * q) + loc;
-    const int m_idx = pid / n_tiles, n_idx = pid % n_tiles;
+    int m_idx, n_idx;
+    tile_of_block(blockIdx.x, nblocks, n_tiles, nblocks / n_tiles, &m_idx, &n_idx);
     if (m_idx >= (int)*tile_count) return;
     const int4 tl = tiles[m_idx];
     const int e = tl.x, r0 = tl.y, r1 = tl.z;
@@ -473,18 +491,19 @@ __global__ __launch_bounds__(WGM* WGN* kWave, 1) void grouped_gemm_pipe_kernel(
         // MFMAs of one K half with the DMA pieces [j0, j0 + LPW/2) of step dkt
         // spread between them, so the address unit drains between issues
         auto compute_dma = [&](int set, int dkt, int j0) {
-            constexpr int NM = MB * NB, ND = LPW / 2, EVERY = NM / (ND > 0 ? ND : 1);
+            constexpr int NM = MB * NB, ND = LPW / 2;
             int m = 0;
 #pragma unroll
             for (int i = 0; i < MB; ++i)
 #pragma unroll
                 for (int f = 0; f < NB; ++f) {
                     acc[i][f] = mma32<DT>::run(bv[set][f], av[set][i], acc[i][f]);
-                    if (m % EVERY == EVERY - 1 && m / EVERY < ND) issue_part(dkt, j0 + m / EVERY);
+                    // piece number (m * ND) / NM is issued after the MFMA where it first appears
+                    if (((m + 1) * ND) / NM != (m * ND) / NM) issue_part(dkt, j0 + (m * ND) / NM);
                     ++m;
                 }
         };
-        static_assert(LPW % 2 == 0 && (MB * NB) % (LPW / 2) == 0, "DMA pieces spread evenly");
+        static_assert(LPW % 2 == 0 && LPW / 2 <= MB * NB, "DMA pieces spread over the MFMAs");
 #pragma unroll
         for (int p = 0; p < kPipeAhead; ++p)
 #pragma unroll
