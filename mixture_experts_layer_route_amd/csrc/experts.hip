@@ -115,15 +115,21 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const uint32_t* __res
 }
 
 // ------------------------------------------------------------------ tile order
-// Workgroup b -> (token tile, weight tile).  The hardware hands workgroup b to
-// XCD b % 8, so ids are first remapped to give each XCD a contiguous run of
-// logical tiles; the run is then walked in groups of kGroupM token tiles,
+// Workgroup b -> (token tile, weight tile).  The grid is sized for the most
+// token tiles the routing could produce; only the first m_tiles (the count the
+// tile-list kernel wrote) exist.  The hardware hands workgroup b to XCD b % 8,
+// so the live workgroups are the first m_tiles * n_tiles ids, which every XCD
+// shares evenly; their ids are remapped to give each XCD a contiguous run of
+// logical tiles, and the run is walked in groups of kGroupM token tiles,
 // weight tile by weight tile, so the ~32 workgroups an XCD runs at once share
-// a few token tiles and a few weight tiles in that XCD's L2.
+// a few token tiles and a few weight tiles in that XCD's L2.  Returns false
+// for a workgroup with no tile.
 constexpr int kGroupM = 8;
-__device__ __forceinline__ void tile_of_block(int bid, int nblocks, int n_tiles, int m_tiles, int* m_idx,
+__device__ __forceinline__ bool tile_of_block(int bid, int nblocks, int n_tiles, int m_tiles, int* m_idx,
                                               int* n_idx) {
-    const int q = nblocks / 8, rem = nblocks % 8;
+    const int live = min(nblocks, m_tiles * n_tiles);
+    if (bid >= live) return false;
+    const int q = live / 8, rem = live % 8;
     const int xcd = bid % 8, loc = bid / 8;
     const int pid = (xcd < rem ? xcd * (q + 1) : rem * (q + 1) + (xcd - rem) * q) + loc;
     const int group = pid / (kGroupM * n_tiles);
@@ -132,6 +138,7 @@ __device__ __forceinline__ void tile_of_block(int bid, int nblocks, int n_tiles,
     const int in_group = pid - group * kGroupM * n_tiles;
     *m_idx = first_m + in_group % gm;
     *n_idx = in_group / gm;
+    return true;
 }
 
 // ------------------------------------------------------------------ grouped GEMM
@@ -190,8 +197,7 @@ __global__ __launch_bounds__(WGM* WGN* kWave) void grouped_gemm_kernel(
     __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE];
 
     int m_idx, n_idx;
-    tile_of_block(blockIdx.x, nblocks, n_tiles, nblocks / n_tiles, &m_idx, &n_idx);
-    if (m_idx >= (int)*tile_count) return;
+    if (!tile_of_block(blockIdx.x, nblocks, n_tiles, (int)*tile_count, &m_idx, &n_idx)) return;
     const int4 tl = tiles[m_idx];
     const int e = tl.x, r0 = tl.y, r1 = tl.z;
     const int n0 = n_idx * BN_OUT;
@@ -421,8 +427,7 @@ __global__ __launch_bounds__(WGM* WGN* kWave, MOE_P_MINB) void grouped_gemm_pipe
     __shared__ __attribute__((aligned(1024))) unsigned char smem[NSTAGE * STAGE];
 
     int m_idx, n_idx;
-    tile_of_block(blockIdx.x, nblocks, n_tiles, nblocks / n_tiles, &m_idx, &n_idx);
-    if (m_idx >= (int)*tile_count) return;
+    if (!tile_of_block(blockIdx.x, nblocks, n_tiles, (int)*tile_count, &m_idx, &n_idx)) return;
     const int4 tl = tiles[m_idx];
     const int e = tl.x, r0 = tl.y, r1 = tl.z;
     const int n0 = n_idx * BN_OUT;
