@@ -124,7 +124,10 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const uint32_t* __res
 // weight tile by weight tile, so the ~32 workgroups an XCD runs at once share
 // a few token tiles and a few weight tiles in that XCD's L2.  Returns false
 // for a workgroup with no tile.
-constexpr int kGroupM = 8;
+#ifndef MOE_GROUP_M
+#define MOE_GROUP_M 8
+#endif
+constexpr int kGroupM = MOE_GROUP_M;
 __device__ __forceinline__ bool tile_of_block(int bid, int nblocks, int n_tiles, int m_tiles, int* m_idx,
                                               int* n_idx) {
     const int live = min(nblocks, m_tiles * n_tiles);
@@ -378,6 +381,11 @@ __device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds_base) {
 }
 #pragma clang diagnostic pop
 __device__ __forceinline__ void barrier_lds() { asm volatile("s_barrier" ::: "memory"); }
+// Keeps the instruction scheduler from moving anything across this point.
+// Placed after the fragment reads of a K half, so they are issued a whole
+// K half of MFMAs before their first use instead of being sunk next to it
+// (the scheduler otherwise trades that latency slack for fewer registers).
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
@@ -470,6 +478,10 @@ __global__ __launch_bounds__(WGM* WGN* kWave, MOE_P_MINB) void grouped_gemm_pipe
         fb[f] = (kPipeBM + brow + frow) * ROWB;
     }
 
+    // Token blocks of 32 rows that lie wholly past the tile's last row are
+    // skipped (wave-uniform): the last tile of an expert is often nearly
+    // empty, and its MFMAs would otherwise cost as much as a full tile.
+    const int rows_live = __builtin_amdgcn_readfirstlane(r1 - r0) - __builtin_amdgcn_readfirstlane(wm) * WTM;
     f32x16_t acc[MB][NB];
 #pragma unroll
     for (int i = 0; i < MB; ++i)
@@ -493,22 +505,42 @@ __global__ __launch_bounds__(WGM* WGN* kWave, MOE_P_MINB) void grouped_gemm_pipe
             const int ks = min(kt, nk - 1);
             lds_dma16(src[j] + ks * ROWB, smem_base + (kt % NSTAGE) * STAGE + j * 1024);
         };
-        // MFMAs of one K half with the DMA pieces [j0, j0 + LPW/2) of step dkt
-        // spread between them, so the address unit drains between issues
-        auto compute_dma = [&](int set, int dkt, int j0) {
-            constexpr int NM = MB * NB, ND = LPW / 2;
-            int m = 0;
-#pragma unroll
-            for (int i = 0; i < MB; ++i)
-#pragma unroll
-                for (int f = 0; f < NB; ++f) {
-                    acc[i][f] = mma32<DT>::run(bv[set][f], av[set][i], acc[i][f]);
-                    // piece number (m * ND) / NM is issued after the MFMA where it first appears
-                    if (((m + 1) * ND) / NM != (m * ND) / NM) issue_part(dkt, j0 + (m * ND) / NM);
-                    ++m;
-                }
-        };
         static_assert(LPW % 2 == 0 && LPW / 2 <= MB * NB, "DMA pieces spread over the MFMAs");
+        // One fragment read (r < MB: token block r, else weight block r - MB).
+        auto read_one = [&](int kt, int half, int set, int r) {
+            const unsigned char* base = smem + (kt % NSTAGE) * STAGE + (half ? sw1 : sw0);
+            if (r < MB)
+                av[set][r] = *(const uint4*)(base + fa0 + r * 32 * ROWB);
+            else
+                bv[set][r - MB] = *(const uint4*)(base + fb[r - MB]);
+        };
+        // The MFMAs of one K half (operands in `set`), with the fragment reads
+        // of the next K half (rkt, rhalf) into the other set spread over the
+        // first half of the MFMAs and the DMA pieces [j0, j0 + LPW/2) of step
+        // dkt over the second half.  Issue is in order, so a burst of reads or
+        // DMAs would hold the MFMAs behind a full queue; one or two per MFMA
+        // keep the matrix pipe fed while the reads still land a quarter stage
+        // before their use.  The fences pin this order against the scheduler.
+        // `full` (a std::bool_constant) says every token block of the wave
+        // holds live rows, so the common case carries no per-MFMA branch.
+        auto compute_mix = [&](auto full, int set, int rkt, int rhalf, int dkt, int j0) {
+            constexpr int NM = MB * NB, NR = MB + NB, ND = LPW / 2, H1 = NM / 2, H2 = NM - NM / 2;
+#pragma unroll
+            for (int m = 0; m < NM; ++m) {
+                const int i = m / NB, f = m % NB;
+                if (decltype(full)::value || i * 32 < rows_live)
+                    acc[i][f] = mma32<DT>::run(bv[set][f], av[set][i], acc[i][f]);
+                if (m < H1) {
+#pragma unroll
+                    for (int r = (m * NR) / H1; r < ((m + 1) * NR) / H1; ++r) read_one(rkt, rhalf, set ^ 1, r);
+                } else {
+                    const int q = m - H1;
+#pragma unroll
+                    for (int d = (q * ND) / H2; d < ((q + 1) * ND) / H2; ++d) issue_part(dkt, j0 + d);
+                }
+                sched_fence();
+            }
+        };
 #pragma unroll
         for (int p = 0; p < kPipeAhead; ++p)
 #pragma unroll
@@ -516,21 +548,31 @@ __global__ __launch_bounds__(WGM* WGN* kWave, MOE_P_MINB) void grouped_gemm_pipe
         wait_vm<(kPipeAhead - 1) * LPW>();  // stage 0 landed
         barrier_lds();
         read_frags(0, 0, 0);
-        for (int kt = 0; kt < nk; ++kt) {
-            // read the second K half of step kt, multiply the first half while
-            // starting the DMA of step kt+3, publish stage kt+1, read its first
-            // half, multiply the second half of step kt with the rest of the DMA
-            read_frags(kt, 1, 1);
-            compute_dma(0, kt + kPipeAhead, 0);
-            // stage kt+1 landed; step kt+2 and half of kt+3 may be in flight.
-            // This wave's reads of stage kt complete before the barrier, so the
-            // stage can be refilled once every wave has passed it.
-            wait_vm<(kPipeAhead - 2) * LPW + LPW / 2>();
-            wait_lgkm0();
-            barrier_lds();
-            read_frags(kt + 1, 0, 0);
-            compute_dma(1, kt + kPipeAhead, LPW / 2);
-        }
+        // Per K step: multiply the first K half while reading the second half
+        // and starting half of the DMA of step kt+3; publish stage kt+1; then
+        // multiply the second half while reading the first half of step kt+1
+        // and starting the rest of the DMA.
+        auto main_loop = [&](auto full) {
+            for (int kt = 0; kt < nk; ++kt) {
+                // the first half's fragments were read a whole K half ago; an
+                // explicit wait here lets the compiler see the counter at zero,
+                // so the half's MFMAs do not wait on the reads issued next
+                wait_lgkm0();
+                compute_mix(full, 0, kt, 1, kt + kPipeAhead, 0);
+                // stage kt+1 landed; step kt+2 and half of kt+3 may be in
+                // flight.  This wave's reads of stage kt complete before the
+                // barrier, so the stage can be refilled once every wave has
+                // passed it.
+                wait_vm<(kPipeAhead - 2) * LPW + LPW / 2>();
+                wait_lgkm0();
+                barrier_lds();
+                compute_mix(full, 1, kt + 1, 0, kt + kPipeAhead, LPW / 2);
+            }
+        };
+        if (rows_live >= MB * 32)
+            main_loop(std::true_type{});
+        else
+            main_loop(std::false_type{});
         wait_vm<0>();
     }
 
