@@ -63,6 +63,13 @@ template <> struct mma<f32_t> {
     }
 };
 
+#ifndef MOE_GROUP_M
+#define MOE_GROUP_M 8
+#endif
+constexpr int kGroupM = MOE_GROUP_M;
+static_assert(kGroupM >= 1 && kGroupM < 64, "group size is packed in 6 bits");
+constexpr int64_t kMaxTiles = int64_t(1) << 26;  // tile index packed in 26 bits
+
 // ------------------------------------------------------------------ tile list
 // offsets are clamped to [0, N] and to be non-decreasing per expert, so even
 // a corrupt offsets array cannot send a tile outside the row buffers; at most
@@ -107,8 +114,24 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const uint32_t* __res
         if (e < E) {
             const uint32_t b = min(offsets[e], N);
             const uint32_t en = max(min(offsets[e + 1], N), b);
-            for (uint32_t r = b; r < en; r += BM, ++t)
-                if (t < max_tiles) tiles[t] = make_int4(e, (int)r, (int)min(r + BM, en), 0);
+            // the expert's M-tiles are split into ceil(n / kGroupM) groups of
+            // near-equal size; each tile records its group (first tile, size)
+            const uint32_t n = (en - b + BM - 1) / BM;
+            const uint32_t ng = (n + kGroupM - 1) / kGroupM;
+            const uint32_t sz = ng ? n / ng : 0, big = ng ? n % ng : 0;  // `big` groups of sz+1
+            for (uint32_t j = 0; j < n; ++j, ++t) {
+                uint32_t first, gm;
+                if (j < big * (sz + 1)) {
+                    first = j / (sz + 1) * (sz + 1);
+                    gm = sz + 1;
+                } else {
+                    first = big * (sz + 1) + (j - big * (sz + 1)) / sz * sz;
+                    gm = sz;
+                }
+                const uint32_t r = b + j * BM;
+                if (t < max_tiles)
+                    tiles[t] = make_int4(e, (int)r, (int)min(r + BM, en), (int)((t - j + first) | (gm << 26)));
+            }
         }
     }
     if (threadIdx.x == 0) *count = min(total, max_tiles);
@@ -120,25 +143,24 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const uint32_t* __res
 // tile-list kernel wrote) exist.  The hardware hands workgroup b to XCD b % 8,
 // so the live workgroups are the first m_tiles * n_tiles ids, which every XCD
 // shares evenly; their ids are remapped to give each XCD a contiguous run of
-// logical tiles, and the run is walked in groups of kGroupM token tiles,
-// weight tile by weight tile, so the ~32 workgroups an XCD runs at once share
-// a few token tiles and a few weight tiles in that XCD's L2.  Returns false
+// logical tiles.  The run is walked group by group -- a group is a few token
+// tiles of ONE expert (at most kGroupM), taken token tile first, then weight
+// tile -- so the ~32 workgroups an XCD runs at once share that expert's weight
+// tiles and the group's token tiles in the XCD's L2.  A group of g token tiles
+// starting at tile f owns logical ids [f * n_tiles, (f + g) * n_tiles), so id
+// p belongs to the group recorded with token tile p / n_tiles.  Returns false
 // for a workgroup with no tile.
-#ifndef MOE_GROUP_M
-#define MOE_GROUP_M 8
-#endif
-constexpr int kGroupM = MOE_GROUP_M;
-__device__ __forceinline__ bool tile_of_block(int bid, int nblocks, int n_tiles, int m_tiles, int* m_idx,
-                                              int* n_idx) {
+__device__ __forceinline__ bool tile_of_block(int bid, int nblocks, int n_tiles, int m_tiles,
+                                              const int4* __restrict__ tiles, int* m_idx, int* n_idx) {
     const int live = min(nblocks, m_tiles * n_tiles);
     if (bid >= live) return false;
     const int q = live / 8, rem = live % 8;
     const int xcd = bid % 8, loc = bid / 8;
     const int pid = (xcd < rem ? xcd * (q + 1) : rem * (q + 1) + (xcd - rem) * q) + loc;
-    const int group = pid / (kGroupM * n_tiles);
-    const int first_m = group * kGroupM;
-    const int gm = min(kGroupM, m_tiles - first_m);  // the last group may be short
-    const int in_group = pid - group * kGroupM * n_tiles;
+    const uint32_t g = (uint32_t)tiles[pid / n_tiles].w;
+    const int first_m = (int)(g & 0x3ffffffu);  // 26 bits of first tile, 6 of group size
+    const int gm = max(1, min((int)(g >> 26), m_tiles - first_m));
+    const int in_group = pid - first_m * n_tiles;
     *m_idx = first_m + in_group % gm;
     *n_idx = in_group / gm;
     return true;
@@ -200,7 +222,7 @@ __global__ __launch_bounds__(WGM* WGN* kWave) void grouped_gemm_kernel(
     __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE];
 
     int m_idx, n_idx;
-    if (!tile_of_block(blockIdx.x, nblocks, n_tiles, (int)*tile_count, &m_idx, &n_idx)) return;
+    if (!tile_of_block(blockIdx.x, nblocks, n_tiles, (int)*tile_count, tiles, &m_idx, &n_idx)) return;
     const int4 tl = tiles[m_idx];
     const int e = tl.x, r0 = tl.y, r1 = tl.z;
     const int n0 = n_idx * BN_OUT;
@@ -435,7 +457,7 @@ __global__ __launch_bounds__(WGM* WGN* kWave, MOE_P_MINB) void grouped_gemm_pipe
     __shared__ __attribute__((aligned(1024))) unsigned char smem[NSTAGE * STAGE];
 
     int m_idx, n_idx;
-    if (!tile_of_block(blockIdx.x, nblocks, n_tiles, (int)*tile_count, &m_idx, &n_idx)) return;
+    if (!tile_of_block(blockIdx.x, nblocks, n_tiles, (int)*tile_count, tiles, &m_idx, &n_idx)) return;
     const int4 tl = tiles[m_idx];
     const int e = tl.x, r0 = tl.y, r1 = tl.z;
     const int n0 = n_idx * BN_OUT;
@@ -523,8 +545,10 @@ __global__ __launch_bounds__(WGM* WGN* kWave, MOE_P_MINB) void grouped_gemm_pipe
         // before their use.  The fences pin this order against the scheduler.
         // `full` (a std::bool_constant) says every token block of the wave
         // holds live rows, so the common case carries no per-MFMA branch.
-        auto compute_mix = [&](auto full, int set, int rkt, int rhalf, int dkt, int j0) {
-            constexpr int NM = MB * NB, NR = MB + NB, ND = LPW / 2, H1 = NM / 2, H2 = NM - NM / 2;
+        // `nd` (a std::integral_constant) is the number of DMA pieces, issued
+        // by calling dma(d) for d = 0 .. nd-1.
+        auto compute_mix = [&](auto full, auto nd, int set, int rkt, int rhalf, auto&& dma) {
+            constexpr int NM = MB * NB, NR = MB + NB, ND = decltype(nd)::value, H1 = NM / 2, H2 = NM - NM / 2;
 #pragma unroll
             for (int m = 0; m < NM; ++m) {
                 const int i = m / NB, f = m % NB;
@@ -536,11 +560,12 @@ __global__ __launch_bounds__(WGM* WGN* kWave, MOE_P_MINB) void grouped_gemm_pipe
                 } else {
                     const int q = m - H1;
 #pragma unroll
-                    for (int d = (q * ND) / H2; d < ((q + 1) * ND) / H2; ++d) issue_part(dkt, j0 + d);
+                    for (int d = (q * ND) / H2; d < ((q + 1) * ND) / H2; ++d) dma(d);
                 }
                 sched_fence();
             }
         };
+        using half_dma = std::integral_constant<int, LPW / 2>;
 #pragma unroll
         for (int p = 0; p < kPipeAhead; ++p)
 #pragma unroll
@@ -558,7 +583,7 @@ __global__ __launch_bounds__(WGM* WGN* kWave, MOE_P_MINB) void grouped_gemm_pipe
                 // explicit wait here lets the compiler see the counter at zero,
                 // so the half's MFMAs do not wait on the reads issued next
                 wait_lgkm0();
-                compute_mix(full, 0, kt, 1, kt + kPipeAhead, 0);
+                compute_mix(full, half_dma{}, 0, kt, 1, [&](int d) { issue_part(kt + kPipeAhead, d); });
                 // stage kt+1 landed; step kt+2 and half of kt+3 may be in
                 // flight.  This wave's reads of stage kt complete before the
                 // barrier, so the stage can be refilled once every wave has
@@ -566,7 +591,7 @@ __global__ __launch_bounds__(WGM* WGN* kWave, MOE_P_MINB) void grouped_gemm_pipe
                 wait_vm<(kPipeAhead - 2) * LPW + LPW / 2>();
                 wait_lgkm0();
                 barrier_lds();
-                compute_mix(full, 1, kt + 1, 0, kt + kPipeAhead, LPW / 2);
+                compute_mix(full, half_dma{}, 1, kt + 1, 0, [&](int d) { issue_part(kt + kPipeAhead, LPW / 2 + d); });
             }
         };
         if (rows_live >= MB * 32)
@@ -680,6 +705,7 @@ hipError_t launch_typed(const ExpertsArgs& a, hipStream_t s, ExpertsPart part) {
     int4* tiles = (int4*)((char*)a.tiles + 256);
     uint32_t* count = (uint32_t*)a.tiles;
     const int64_t mt = max_mtiles(a.N, a.E, BM);
+    if (mt >= kMaxTiles) return hipErrorInvalidValue;
     build_tiles_kernel<<<1, 1024, 0, s>>>(a.offsets, a.E, (uint32_t)a.N, BM, (uint32_t)mt, tiles, count);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
