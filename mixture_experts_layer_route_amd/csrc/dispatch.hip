@@ -132,7 +132,7 @@ __global__ __launch_bounds__(256) void gather_kernel(const V* __restrict__ x, in
 
 template <typename V>
 hipError_t launch_gather(const DispatchArgs& a, hipStream_t s) {
-    const int64_t units = a.row_bytes / (int64_t)sizeof(V);
+    const int64_t units = a.dispatched ? a.row_bytes / (int64_t)sizeof(V) : 0;
     const int64_t chunks = (units + 255) / 256;
     if (a.T > 0x7fffffff || chunks > 65535) return hipErrorInvalidValue;
     const dim3 grid((unsigned)a.T, (unsigned)(chunks > 0 ? chunks : 1)), block(256);

@@ -167,6 +167,12 @@ __device__ __forceinline__ bool tile_of_block(int bid, int nblocks, int n_tiles,
 }
 
 // ------------------------------------------------------------------ grouped GEMM
+// Source row of product row r: r itself, or (fused gather) the token row
+// a_rows[r], clamped into the token buffer.
+__device__ __forceinline__ int64_t src_row(const uint32_t* __restrict__ a_rows, int a_nrows, int r) {
+    return a_rows ? (int64_t)min(a_rows[r], (uint32_t)(a_nrows - 1)) : (int64_t)r;
+}
+
 // SiLU(g) * u in FP32: exp on the hardware exp2 unit and a hardware
 // reciprocal; the product is then rounded to the weight dtype, whose
 // precision (bf16/f16), or the f32 tolerance, dwarfs their few-ulp error.
@@ -199,7 +205,8 @@ __global__ __launch_bounds__(WGM* WGN* kWave) void grouped_gemm_kernel(
     const typename DT::storage* __restrict__ B0,  // [E, NOUT, K]  (gate or down)
     const typename DT::storage* __restrict__ B1,  // [E, NOUT, K]  (up; GATEUP only)
     typename DT::storage* __restrict__ C,         // [rows, NOUT]
-    const int4* __restrict__ tiles, const uint32_t* __restrict__ tile_count, int K, int NOUT,
+    const uint32_t* __restrict__ a_rows, int a_nrows, const int4* __restrict__ tiles,
+    const uint32_t* __restrict__ tile_count, int K, int NOUT,
     int n_tiles, int nblocks) {
     using S = typename DT::storage;
     constexpr int NT = WGM * WGN * kWave;
@@ -237,7 +244,7 @@ __global__ __launch_bounds__(WGM* WGN* kWave) void grouped_gemm_kernel(
         const int c = tid + i * NT;
         const int row = min(c / CPR, BM - 1);
         const int grow = min(r0 + row, r1 - 1);
-        a_src[i] = (const char*)(A + (int64_t)grow * K) + my_ch * 16;
+        a_src[i] = (const char*)(A + src_row(a_rows, a_nrows, grow) * K) + my_ch * 16;
         a_lds[i] = row * LDS_STRIDE + my_ch * 16;
     }
     const char* b_src[B_CH];
@@ -440,7 +447,8 @@ template <typename DT, bool GATEUP, int WGM, int WGN>
 __global__ __launch_bounds__(WGM* WGN* kWave, MOE_P_MINB) void grouped_gemm_pipe_kernel(
     const typename DT::storage* __restrict__ A, const typename DT::storage* __restrict__ B0,
     const typename DT::storage* __restrict__ B1, typename DT::storage* __restrict__ C,
-    const int4* __restrict__ tiles, const uint32_t* __restrict__ tile_count, int K, int NOUT, int n_tiles,
+    const uint32_t* __restrict__ a_rows, int a_nrows, const int4* __restrict__ tiles,
+    const uint32_t* __restrict__ tile_count, int K, int NOUT, int n_tiles,
     int nblocks) {
     using S = typename DT::storage;
     constexpr int NW = WGM * WGN;
@@ -472,7 +480,7 @@ __global__ __launch_bounds__(WGM* WGN* kWave, MOE_P_MINB) void grouped_gemm_pipe
         const int lc = (lane & 3) ^ ((row >> 1) & 3);        // logical chunk for this physical slot
         const S* p;
         if (row < kPipeBM) {
-            p = A + (int64_t)min(r0 + row, r1 - 1) * K;
+            p = A + src_row(a_rows, a_nrows, min(r0 + row, r1 - 1)) * K;
         } else {
             const int w = row - kPipeBM;
             if (GATEUP)
@@ -649,8 +657,9 @@ int64_t max_mtiles(int64_t N, int64_t E, int BM) {
 }
 
 template <typename DT, bool GATEUP, int BM, int BNB, int WGM, int WGN>
-hipError_t launch_gemm(const void* A, const void* B0, const void* B1, void* C, const int4* tiles,
-                       const uint32_t* count, int64_t mt, int K, int NOUT, hipStream_t s) {
+hipError_t launch_gemm(const void* A, const uint32_t* a_rows, int64_t a_nrows, const void* B0, const void* B1,
+                       void* C, const int4* tiles, const uint32_t* count, int64_t mt, int K, int NOUT,
+                       hipStream_t s) {
     using S = typename DT::storage;
     constexpr int BN_OUT = GATEUP ? BNB / 2 : BNB;
     const int n_tiles = (NOUT + BN_OUT - 1) / BN_OUT;
@@ -658,13 +667,15 @@ hipError_t launch_gemm(const void* A, const void* B0, const void* B1, void* C, c
     if (nb == 0) return hipSuccess;
     if (nb > 0x7fffffff) return hipErrorInvalidValue;
     grouped_gemm_kernel<DT, GATEUP, BM, BNB, WGM, WGN><<<(unsigned)nb, WGM * WGN * kWave, 0, s>>>(
-        (const S*)A, (const S*)B0, (const S*)B1, (S*)C, tiles, count, K, NOUT, n_tiles, (int)nb);
+        (const S*)A, (const S*)B0, (const S*)B1, (S*)C, a_rows, (int)a_nrows, tiles, count, K, NOUT, n_tiles,
+        (int)nb);
     return hipGetLastError();
 }
 
 template <typename DT, bool GATEUP, int WGM, int WGN>
-hipError_t launch_pipe(const void* A, const void* B0, const void* B1, void* C, const int4* tiles,
-                       const uint32_t* count, int64_t mt, int K, int NOUT, hipStream_t s) {
+hipError_t launch_pipe(const void* A, const uint32_t* a_rows, int64_t a_nrows, const void* B0, const void* B1,
+                       void* C, const int4* tiles, const uint32_t* count, int64_t mt, int K, int NOUT,
+                       hipStream_t s) {
     using S = typename DT::storage;
     constexpr int BN_OUT = GATEUP ? kPipeBN / 2 : kPipeBN;
     const int n_tiles = (NOUT + BN_OUT - 1) / BN_OUT;
@@ -672,7 +683,8 @@ hipError_t launch_pipe(const void* A, const void* B0, const void* B1, void* C, c
     if (nb == 0) return hipSuccess;
     if (nb > 0x7fffffff) return hipErrorInvalidValue;
     grouped_gemm_pipe_kernel<DT, GATEUP, WGM, WGN><<<(unsigned)nb, WGM * WGN * kWave, 0, s>>>(
-        (const S*)A, (const S*)B0, (const S*)B1, (S*)C, tiles, count, K, NOUT, n_tiles, (int)nb);
+        (const S*)A, (const S*)B0, (const S*)B1, (S*)C, a_rows, (int)a_nrows, tiles, count, K, NOUT, n_tiles,
+        (int)nb);
     return hipGetLastError();
 }
 
@@ -713,22 +725,22 @@ hipError_t launch_typed(const ExpertsArgs& a, hipStream_t s, ExpertsPart part) {
     if (pipe) {
         if constexpr (sizeof(typename DT::storage) == 2) {
             if (part != kDown) {
-                err = launch_pipe<DT, true, MOE_P_WM, MOE_P_WN>(a.x, a.gate, a.up, a.h, tiles, count, mt, H, I, s);
+                err = launch_pipe<DT, true, MOE_P_WM, MOE_P_WN>(a.x, a.x_rows, a.x_nrows, a.gate, a.up, a.h, tiles, count, mt, H, I, s);
                 if (err != hipSuccess) return err;
             }
             if (part != kGateUp)
-                err = launch_pipe<DT, false, MOE_P_WM, MOE_P_WN>(a.h, a.down, nullptr, a.y, tiles, count, mt, I, H, s);
+                err = launch_pipe<DT, false, MOE_P_WM, MOE_P_WN>(a.h, nullptr, 0, a.down, nullptr, a.y, tiles, count, mt, I, H, s);
         }
         return err;
     }
     if (part != kDown) {
-        err = small ? launch_gemm<DT, true, 16, MOE_S_BN, 1, MOE_S_WN>(a.x, a.gate, a.up, a.h, tiles, count, mt, H, I, s)
-                    : launch_gemm<DT, true, MOE_L_BM, MOE_L_BN, MOE_L_WM, MOE_L_WN>(a.x, a.gate, a.up, a.h, tiles, count, mt, H, I, s);
+        err = small ? launch_gemm<DT, true, 16, MOE_S_BN, 1, MOE_S_WN>(a.x, a.x_rows, a.x_nrows, a.gate, a.up, a.h, tiles, count, mt, H, I, s)
+                    : launch_gemm<DT, true, MOE_L_BM, MOE_L_BN, MOE_L_WM, MOE_L_WN>(a.x, a.x_rows, a.x_nrows, a.gate, a.up, a.h, tiles, count, mt, H, I, s);
         if (err != hipSuccess) return err;
     }
     if (part != kGateUp) {
-        err = small ? launch_gemm<DT, false, 16, MOE_S_BN, 1, MOE_S_WN>(a.h, a.down, nullptr, a.y, tiles, count, mt, I, H, s)
-                    : launch_gemm<DT, false, MOE_L_BM, MOE_L_BN, MOE_L_WM, MOE_L_WN>(a.h, a.down, nullptr, a.y, tiles, count, mt, I, H, s);
+        err = small ? launch_gemm<DT, false, 16, MOE_S_BN, 1, MOE_S_WN>(a.h, nullptr, 0, a.down, nullptr, a.y, tiles, count, mt, I, H, s)
+                    : launch_gemm<DT, false, MOE_L_BM, MOE_L_BN, MOE_L_WM, MOE_L_WN>(a.h, nullptr, 0, a.down, nullptr, a.y, tiles, count, mt, I, H, s);
     }
     return err;
 }

@@ -106,7 +106,7 @@ ExpertsWs experts_ws(int64_t N, int64_t I, int64_t E, int dtype) {
 }
 
 struct ForwardWs {
-    size_t idx, w, offsets, ros, tor, disp, y, dws, ews, total;
+    size_t idx, w, offsets, ros, tor, y, dws, ews, total;
 };
 ForwardWs forward_ws(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int dtype) {
     ForwardWs f;
@@ -118,7 +118,6 @@ ForwardWs forward_ws(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int 
     f.offsets = o; o += align_up((size_t)(E + 1) * 4);
     f.ros = o;     o += align_up((size_t)N * 4);
     f.tor = o;     o += align_up((size_t)N * 4);
-    f.disp = o;    o += align_up((size_t)N * H * es);
     f.y = o;       o += align_up((size_t)N * H * es);
     f.dws = o;     o += dispatch_ws(T, E, k).total;
     f.ews = o;     o += experts_ws(N, I, E, dtype).total;
@@ -263,9 +262,11 @@ moe_status enqueue_dispatch(const void* x, int dtype, int64_t T, int64_t H, cons
     return launch_status(launch_dispatch(a, s));
 }
 
+// x_rows: null when x holds the N dispatched rows; else token_of_row, and x
+// holds the x_nrows token rows the products read through it.
 moe_status enqueue_experts(int dtype, int64_t E, int64_t H, int64_t I, const void* gate, const void* up,
-                           const void* down, const void* x, int64_t N, const uint32_t* offsets, void* y,
-                           void* h, void* ws, hipStream_t s, ExpertsPart part) {
+                           const void* down, const void* x, const uint32_t* x_rows, int64_t x_nrows, int64_t N,
+                           const uint32_t* offsets, void* y, void* h, void* ws, hipStream_t s, ExpertsPart part) {
     const ExpertsWs l = experts_ws(N, I, E, dtype);
     ExpertsArgs a;
     a.dtype = dtype;
@@ -273,6 +274,8 @@ moe_status enqueue_experts(int dtype, int64_t E, int64_t H, int64_t I, const voi
     a.up = up;
     a.down = down;
     a.x = x;
+    a.x_rows = x_rows;
+    a.x_nrows = x_nrows;
     a.offsets = offsets;
     a.y = y;
     a.h = h ? h : (char*)ws + l.h;
@@ -365,7 +368,7 @@ moe_status moe_experts_forward(const moe_tensor* gate, const moe_tensor* up, con
     MOE_TRY(check_devices(s, {gate->data, up->data, down->data, dispatched->data, expert_offsets->data,
                               expert_out->data, workspace}));
     return enqueue_experts(gate->dtype, E, gate->dims[2], I, gate->data, up->data, down->data, dispatched->data,
-                           N, (const uint32_t*)expert_offsets->data, expert_out->data, nullptr, workspace, s,
+                           nullptr, 0, N, (const uint32_t*)expert_offsets->data, expert_out->data, nullptr, workspace, s,
                            kBoth);
 }
 
@@ -391,7 +394,7 @@ moe_status moe_experts_gate_up(const moe_tensor* gate, const moe_tensor* up, con
     if (N == 0) return MOE_OK;
     hipStream_t s = (hipStream_t)stream;
     MOE_TRY(check_devices(s, {gate->data, up->data, dispatched->data, expert_offsets->data, h->data, workspace}));
-    return enqueue_experts(gate->dtype, E, H, I, gate->data, up->data, nullptr, dispatched->data, N,
+    return enqueue_experts(gate->dtype, E, H, I, gate->data, up->data, nullptr, dispatched->data, nullptr, 0, N,
                            (const uint32_t*)expert_offsets->data, nullptr, h->data, workspace, s, kGateUp);
 }
 
@@ -413,7 +416,7 @@ moe_status moe_experts_down(const moe_tensor* down, const moe_tensor* h, const m
     if (N == 0) return MOE_OK;
     hipStream_t s = (hipStream_t)stream;
     MOE_TRY(check_devices(s, {down->data, h->data, expert_offsets->data, expert_out->data, workspace}));
-    return enqueue_experts(down->dtype, E, H, I, nullptr, nullptr, down->data, nullptr, N,
+    return enqueue_experts(down->dtype, E, H, I, nullptr, nullptr, down->data, nullptr, nullptr, 0, N,
                            (const uint32_t*)expert_offsets->data, expert_out->data, h->data, workspace, s,
                            kDown);
 }
@@ -466,13 +469,14 @@ moe_status moe_forward(const moe_tensor* gate, const moe_tensor* up, const moe_t
     uint32_t* offsets = (uint32_t*)(ws + l.offsets);
     uint32_t* ros = (uint32_t*)(ws + l.ros);
     uint32_t* tor = (uint32_t*)(ws + l.tor);
-    void* disp = ws + l.disp;
     void* y = ws + l.y;
     MOE_TRY(enqueue_route(logits, options, idx, w, s));
-    MOE_TRY(enqueue_dispatch(input->data, input->dtype, T, H, idx, (int)k, E, disp, offsets, ros, tor,
+    MOE_TRY(enqueue_dispatch(input->data, input->dtype, T, H, idx, (int)k, E, nullptr, offsets, ros, tor,
                              ws + l.dws, s));
-    MOE_TRY(enqueue_experts(gate->dtype, E, H, I, gate->data, up->data, down->data, disp, N, offsets, y, nullptr,
-                            ws + l.ews, s, kBoth));
+    // the gate/up products read the token rows through token_of_row, so the
+    // dispatch writes only the mapping and no dispatched copy of the rows
+    MOE_TRY(enqueue_experts(gate->dtype, E, H, I, gate->data, up->data, down->data, input->data, tor, T, N,
+                            offsets, y, nullptr, ws + l.ews, s, kBoth));
     return enqueue_combine(y, input->dtype, N, ros, w, logits->dtype, T, (int)k, H, output->data, s);
 }
 

@@ -111,7 +111,7 @@ struct DispatchArgs {
     uint32_t* counts;   // [E] scratch
     uint32_t* rank;     // [T*k] scratch
     uint32_t* offsets;  // [E+1]
-    void* dispatched;
+    void* dispatched;   // null: write the mapping only, copy no rows
     uint32_t* row_of_slot;
     uint32_t* token_of_row;
 };
@@ -122,7 +122,9 @@ struct ExpertsArgs {
     const void* gate;
     const void* up;
     const void* down;
-    const void* x;  // [N,H] dispatched rows
+    const void* x;  // [N,H] dispatched rows, or [x_nrows,H] rows picked by x_rows
+    const uint32_t* x_rows;  // null, or token_of_row [N]: row r of the products is x[x_rows[r]]
+    int64_t x_nrows;
     const uint32_t* offsets;
     void* y;        // [N,H]
     void* h;        // [N,I] workspace

@@ -218,8 +218,17 @@ def test_forward_parity(cfg):
     run_forward_case(cfg)
 
 
-def test_split_stages_equal_fused_forward():
-    cfg = S.small_config("split", T=257, H=128, I=192, E=9, top_k=3, dtype="bf16", seed=41)
+@pytest.mark.parametrize("cfg", [
+    # pipelined large-tile kernel, 16-row small-tile kernel, f32 kernel: the
+    # fused forward reads token rows through token_of_row, the split path
+    # reads the dispatched copy; both must give the same bits
+    S.small_config("split", T=257, H=128, I=192, E=9, top_k=3, dtype="bf16", seed=41),
+    S.small_config("split_small", T=20, H=96, I=64, E=16, top_k=2, dtype="f16", seed=43),
+    S.small_config("split_f32", T=130, H=40, I=24, E=4, top_k=2, dtype="f32", seed=44),
+    S.small_config("split_edge", T=300, H=64, I=96, E=16, top_k=4, dtype="bf16", edge_rows=True, seed=45),
+], ids=lambda c: c.name)
+def test_split_stages_equal_fused_forward(cfg):
+    log(f"split == fused {cfg.name}")
     x, lg = S.make_tokens(cfg)
     W = [w.to(DEV) for w in S.make_weights(cfg)]
     ex = moe.SwiGluExperts(*W)
@@ -231,7 +240,8 @@ def test_split_stages_equal_fused_forward():
     y = ex.forward_dispatched(disp)
     split = disp.combine(y)
     torch.cuda.synchronize()
-    assert torch.equal(fused.view(torch.int16), split.view(torch.int16))
+    bits = torch.int32 if fused.dtype == torch.float32 else torch.int16
+    assert torch.equal(fused.view(bits), split.view(bits))
 
 
 def test_forward_empty_batch():
