@@ -106,31 +106,36 @@ def measure(name: str, steps: int, warmup: int, only_forward: bool = False) -> d
     if only_forward:
         return res
 
-    # stage times: the split calls run the same kernels; events sit on the
-    # stream every call is launched on (torch's current stream)
+    # stage times: the split calls run the kernels of the fused forward
+    # (mapping-only dispatch, gate/up reading the tokens in place), back to
+    # back like the forward steps, with events on the stream every call is
+    # launched on (torch's current stream) and one synchronisation at the end
     names = ["route", "dispatch", "experts_gate_up", "experts_down", "combine"]
     acc = {n: 0.0 for n in names}
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
     ews = torch.empty(moe.load().moe_experts_workspace_bytes(cfg.N, cfg.H, cfg.I, cfg.E, 2 if cfg.dtype == "bf16"
                                                               else (1 if cfg.dtype == "f16" else 0)),
                       dtype=torch.uint8, device=dev)
     plan = None
+    marks = []
     for it in range(warmup + steps):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
         evs[0].record()
         plan = moe.route(lg, opts)
         evs[1].record()
-        disp = plan.dispatch(x)
+        disp = plan.dispatch(x, copy_rows=False)
         evs[2].record()
-        h = ex.gate_up(disp.rows, disp.expert_offsets, ews)
+        h = ex.gate_up_gathered(x, disp.token_of_row, disp.expert_offsets, ews)
         evs[3].record()
         y = ex.down_proj(h, disp.expert_offsets, ews)
         evs[4].record()
         disp.combine(y)
         evs[5].record()
-        torch.cuda.synchronize()
         if it >= warmup:
-            for i, n in enumerate(names):
-                acc[n] += evs[i].elapsed_time(evs[i + 1])
+            marks.append(evs)
+    torch.cuda.synchronize()
+    for evs in marks:
+        for i, n in enumerate(names):
+            acc[n] += evs[i].elapsed_time(evs[i + 1])
     res["stages_ms"] = {n: acc[n] / steps for n in names}
     idx = plan.expert_indices().view(torch.int32).long()
     res["active_experts"] = int(torch.unique(idx).numel())
@@ -143,8 +148,9 @@ def roofline(res: dict) -> dict:
     es = 2 if cfg.dtype in ("bf16", "f16") else 4
     if res["workload"] == "decode_bf16":
         # weight streaming: each active expert's gate and up rows are read
-        # once; plus the dispatched rows read and the activation written
-        nbytes = res["active_experts"] * 2 * cfg.I * cfg.H * es + cfg.N * cfg.H * es + cfg.N * cfg.I * es
+        # once; plus the token rows read (in place, once per token) and the
+        # activation written
+        nbytes = res["active_experts"] * 2 * cfg.I * cfg.H * es + cfg.T * cfg.H * es + cfg.N * cfg.I * es
         ach = nbytes / t / 1e9
         r = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
              "frac": round(ach / PEAK_HBM_GBS, 4)}
@@ -161,13 +167,14 @@ def roofline(res: dict) -> dict:
 
 def hbm_bytes_forward(res: dict) -> float:
     """Algorithmic HBM bytes of one forward: active experts' weights once,
-    tokens/logits/output once, dispatched rows and expert outputs written and
-    read once, the activation written and read once."""
+    tokens/logits/output once, the routing and mapping arrays once, the
+    expert outputs written and read once, the activation written and read
+    once (the token rows are read in place, no dispatched copy)."""
     cfg = res["cfg"]
     es = 2 if cfg.dtype in ("bf16", "f16") else 4
     w = res["active_experts"] * 3 * cfg.H * cfg.I * es
     io = cfg.T * cfg.H * es * 2 + cfg.T * cfg.E * es + cfg.N * (4 + es)
-    inter = 2 * (2 * cfg.N * cfg.H * es) + 2 * cfg.N * cfg.I * es
+    inter = 2 * cfg.N * cfg.H * es + 2 * cfg.N * cfg.I * es
     return w + io + inter
 
 

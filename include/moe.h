@@ -115,6 +115,10 @@ size_t moe_dispatch_workspace_bytes(int64_t T, int64_t E, int32_t top_k);
  *   dispatched     [T*k,H] input dtype, written: rows grouped by expert in
  *                          ascending expert id; each row is a bit copy of its
  *                          token.  Rows past expert_offsets[E] are untouched.
+ *                          May be NULL: then no row is copied and only the
+ *                          three mapping outputs are written (for
+ *                          moe_experts_gate_up_gathered, which reads the
+ *                          tokens in place).
  *   expert_offsets [E+1]   U32, written: rows of expert e are
  *                          [expert_offsets[e], expert_offsets[e+1]).
  *   row_of_slot    [T*k]   U32, written: dispatched row of slot t*k+j.
@@ -169,6 +173,23 @@ moe_status moe_experts_gate_up(const moe_tensor* gate, const moe_tensor* up, con
                                size_t workspace_bytes, void* stream);
 moe_status moe_experts_down(const moe_tensor* down, const moe_tensor* h, const moe_tensor* expert_offsets,
                             moe_tensor* expert_out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * moe_experts_gate_up_gathered -- moe_experts_gate_up with the dispatch
+ * gather folded in (section 5: the saved token<->row mapping): product row r
+ * reads token row input[token_of_row[r]] in place instead of a dispatched
+ * copy.  Bit for bit the result of moe_experts_gate_up on the rows that
+ * moe_dispatch would copy; moe_forward runs its products this way.
+ *   input        [T,H]  weight dtype, read only.
+ *   token_of_row [N]    U32 as written by moe_dispatch, read only; an entry
+ *                       >= T is clamped to T-1, so no access leaves input.
+ *   h            [N,I]  written for rows < expert_offsets[E].
+ *   Other arguments as for moe_experts_gate_up (workspace of
+ *   moe_experts_workspace_bytes(N, ...)).
+ */
+moe_status moe_experts_gate_up_gathered(const moe_tensor* gate, const moe_tensor* up, const moe_tensor* input,
+                                        const moe_tensor* token_of_row, const moe_tensor* expert_offsets,
+                                        moe_tensor* h, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * moe_combine -- weighted combine in token order (sections 5 and 6):

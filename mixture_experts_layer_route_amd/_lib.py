@@ -34,6 +34,7 @@ EXPORTS = (
     "moe_experts_workspace_bytes",
     "moe_experts_forward",
     "moe_experts_gate_up",
+    "moe_experts_gate_up_gathered",
     "moe_experts_down",
     "moe_combine",
     "moe_forward_workspace_bytes",
@@ -86,6 +87,7 @@ def load() -> ctypes.CDLL:
     L.moe_experts_workspace_bytes.restype = sz
     L.moe_experts_forward.argtypes = [P, P, P, P, P, P, vp, sz, vp]
     L.moe_experts_gate_up.argtypes = [P, P, P, P, P, vp, sz, vp]
+    L.moe_experts_gate_up_gathered.argtypes = [P, P, P, P, P, P, vp, sz, vp]
     L.moe_experts_down.argtypes = [P, P, P, P, vp, sz, vp]
     L.moe_combine.argtypes = [P, P, P, P, vp]
     L.moe_forward_workspace_bytes.argtypes = [i64, i64, i64, i64, i32, i32]
@@ -93,8 +95,8 @@ def load() -> ctypes.CDLL:
     L.moe_forward.argtypes = [P, P, P, P, P, MoeRoutingOptions, P, vp, sz, vp]
     L.moe_status_string.argtypes = [i32]
     L.moe_status_string.restype = ctypes.c_char_p
-    for f in ("moe_route", "moe_dispatch", "moe_experts_forward", "moe_experts_gate_up", "moe_experts_down",
-              "moe_combine", "moe_forward"):
+    for f in ("moe_route", "moe_dispatch", "moe_experts_forward", "moe_experts_gate_up",
+              "moe_experts_gate_up_gathered", "moe_experts_down", "moe_combine", "moe_forward"):
         getattr(L, f).restype = i32
     _lib = L
     return L

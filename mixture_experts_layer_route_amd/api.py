@@ -94,8 +94,8 @@ class RoutingPlan:
     def top_k(self) -> int:
         return int(self._indices.shape[1])
 
-    def dispatch(self, input: torch.Tensor) -> "DispatchedTokens":
-        return dispatch(input, self._indices, self.num_experts, self._weights)
+    def dispatch(self, input: torch.Tensor, copy_rows: bool = True) -> "DispatchedTokens":
+        return dispatch(input, self._indices, self.num_experts, self._weights, copy_rows)
 
 
 def route(logits: torch.Tensor, options: RoutingOptions) -> RoutingPlan:
@@ -114,7 +114,7 @@ class DispatchedTokens:
     """Rows grouped by expert plus the saved mapping back to tokens."""
 
     def __init__(self, rows, expert_offsets, row_of_slot, token_of_row, weights, num_tokens, top_k):
-        self.rows = rows                      # [T*k, H]
+        self.rows = rows                      # [T*k, H], or None when no rows were copied
         self.expert_offsets = expert_offsets  # [E+1] U32
         self.row_of_slot = row_of_slot        # [T*k] U32
         self.token_of_row = token_of_row      # [T*k] U32
@@ -130,20 +130,24 @@ class DispatchedTokens:
 
 
 def dispatch(input: torch.Tensor, indices: torch.Tensor, num_experts: int,
-             weights: torch.Tensor | None = None) -> DispatchedTokens:
-    """Compact, drop-free dispatch of [T,H] tokens by expert (moe_dispatch)."""
+             weights: torch.Tensor | None = None, copy_rows: bool = True) -> DispatchedTokens:
+    """Compact, drop-free dispatch of [T,H] tokens by expert (moe_dispatch).
+
+    With copy_rows=False only the offsets and the mapping are written (for
+    SwiGluExperts.gate_up_gathered, which reads the tokens in place)."""
     L = _lib.load()
     T, H = input.shape
     k = int(indices.shape[1])
     dev = input.device
-    rows = torch.empty((T * k, H), dtype=input.dtype, device=dev)
+    rows = torch.empty((T * k, H), dtype=input.dtype, device=dev) if copy_rows else None
     offsets = torch.empty((num_experts + 1,), dtype=torch.uint32, device=dev)
     ros = torch.empty((T * k,), dtype=torch.uint32, device=dev)
     tor = torch.empty((T * k,), dtype=torch.uint32, device=dev)
     ws = _workspace(L.moe_dispatch_workspace_bytes(T, num_experts, k), dev)
-    d = [_desc(x) for x in (input, indices, rows, offsets, ros, tor)]
-    st = L.moe_dispatch(_ref(d[0]), _ref(d[1]), int(num_experts), _ref(d[2]), _ref(d[3]), _ref(d[4]),
-                        _ref(d[5]), ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(dev))
+    d = [_desc(x) if x is not None else None for x in (input, indices, rows, offsets, ros, tor)]
+    st = L.moe_dispatch(_ref(d[0]), _ref(d[1]), int(num_experts), _ref(d[2]) if d[2] is not None else None,
+                        _ref(d[3]), _ref(d[4]), _ref(d[5]), ctypes.c_void_p(ws.data_ptr()), ws.numel(),
+                        _stream(dev))
     _lib.check(st, "moe_dispatch")
     return DispatchedTokens(rows, offsets, ros, tor, weights, T, k)
 
@@ -231,6 +235,22 @@ class SwiGluExperts:
         st = L.moe_experts_gate_up(_ref(g), _ref(u), _ref(dr), _ref(do_), _ref(dh),
                                    ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(rows.device))
         _lib.check(st, "moe_experts_gate_up")
+        return h
+
+    def gate_up_gathered(self, input: torch.Tensor, token_of_row: torch.Tensor, expert_offsets: torch.Tensor,
+                         workspace: torch.Tensor | None = None) -> torch.Tensor:
+        """gate_up reading token rows in place through token_of_row (moe_experts_gate_up_gathered)."""
+        L = _lib.load()
+        N = token_of_row.shape[0]
+        h = torch.empty((N, self.intermediate), dtype=input.dtype, device=input.device)
+        ws = workspace if workspace is not None else _workspace(
+            L.moe_experts_workspace_bytes(N, self.hidden, self.intermediate, self.num_experts, _dtype_code(input)),
+            input.device)
+        dx, dt, do_, dh = _desc(input), _desc(token_of_row), _desc(expert_offsets), _desc(h)
+        g, u, _ = self._dw
+        st = L.moe_experts_gate_up_gathered(_ref(g), _ref(u), _ref(dx), _ref(dt), _ref(do_), _ref(dh),
+                                            ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(input.device))
+        _lib.check(st, "moe_experts_gate_up_gathered")
         return h
 
     def down_proj(self, h: torch.Tensor, expert_offsets: torch.Tensor,

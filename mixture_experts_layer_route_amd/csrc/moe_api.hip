@@ -150,7 +150,7 @@ moe_status check_dispatch(const moe_tensor* input, const moe_tensor* indices, in
                           const moe_tensor* ros, const moe_tensor* tor) {
     MOE_TRY(check_tensor(input, 2));
     MOE_TRY(check_tensor(indices, 2));
-    MOE_TRY(check_tensor(dispatched, 2));
+    if (dispatched) MOE_TRY(check_tensor(dispatched, 2));
     MOE_TRY(check_tensor(offsets, 1));
     MOE_TRY(check_tensor(ros, 1));
     MOE_TRY(check_tensor(tor, 1));
@@ -159,12 +159,12 @@ moe_status check_dispatch(const moe_tensor* input, const moe_tensor* indices, in
     if (indices->dtype != MOE_U32 || offsets->dtype != MOE_U32 || ros->dtype != MOE_U32 ||
         tor->dtype != MOE_U32)
         return MOE_ERR_DTYPE;
-    if (dispatched->dtype != input->dtype) return MOE_ERR_DTYPE;
+    if (dispatched && dispatched->dtype != input->dtype) return MOE_ERR_DTYPE;
     const int64_t T = input->dims[0], H = input->dims[1], k = indices->dims[1];
     if (E < 1) return MOE_ERR_SHAPE;
     if (k < 1 || k > E) return MOE_ERR_TOP_K;
     if (indices->dims[0] != T) return MOE_ERR_SHAPE;
-    if (dispatched->dims[0] != T * k || dispatched->dims[1] != H) return MOE_ERR_SHAPE;
+    if (dispatched && (dispatched->dims[0] != T * k || dispatched->dims[1] != H)) return MOE_ERR_SHAPE;
     if (offsets->dims[0] != E + 1) return MOE_ERR_SHAPE;
     if (ros->dims[0] != T * k || tor->dims[0] != T * k) return MOE_ERR_SHAPE;
     if (E > MOE_MAX_EXPERTS) return MOE_ERR_UNSUPPORTED;
@@ -343,10 +343,11 @@ moe_status moe_dispatch(const moe_tensor* input, const moe_tensor* indices, int6
     const int64_t T = input->dims[0], H = input->dims[1], k = indices->dims[1];
     if (!workspace || workspace_bytes < dispatch_ws(T, num_experts, k).total) return MOE_ERR_WORKSPACE;
     hipStream_t s = (hipStream_t)stream;
-    MOE_TRY(check_devices(s, {input->data, indices->data, dispatched->data, expert_offsets->data,
+    void* disp = dispatched ? dispatched->data : nullptr;
+    MOE_TRY(check_devices(s, {input->data, indices->data, disp ? disp : input->data, expert_offsets->data,
                               row_of_slot->data, token_of_row->data, workspace}));
     return enqueue_dispatch(input->data, input->dtype, T, H, (const uint32_t*)indices->data, (int)k,
-                            num_experts, dispatched->data, (uint32_t*)expert_offsets->data,
+                            num_experts, disp, (uint32_t*)expert_offsets->data,
                             (uint32_t*)row_of_slot->data, (uint32_t*)token_of_row->data, workspace, s);
 }
 
@@ -396,6 +397,37 @@ moe_status moe_experts_gate_up(const moe_tensor* gate, const moe_tensor* up, con
     MOE_TRY(check_devices(s, {gate->data, up->data, dispatched->data, expert_offsets->data, h->data, workspace}));
     return enqueue_experts(gate->dtype, E, H, I, gate->data, up->data, nullptr, dispatched->data, nullptr, 0, N,
                            (const uint32_t*)expert_offsets->data, nullptr, h->data, workspace, s, kGateUp);
+}
+
+moe_status moe_experts_gate_up_gathered(const moe_tensor* gate, const moe_tensor* up, const moe_tensor* input,
+                                       const moe_tensor* token_of_row, const moe_tensor* expert_offsets,
+                                       moe_tensor* h, void* workspace, size_t workspace_bytes, void* stream) {
+    MOE_TRY(check_tensor(gate, 3));
+    MOE_TRY(check_tensor(up, 3));
+    MOE_TRY(check_tensor(input, 2));
+    MOE_TRY(check_tensor(token_of_row, 1));
+    MOE_TRY(check_tensor(expert_offsets, 1));
+    MOE_TRY(check_tensor(h, 2));
+    if (!is_float(gate->dtype)) return MOE_ERR_DTYPE;
+    if (up->dtype != gate->dtype || input->dtype != gate->dtype || h->dtype != gate->dtype)
+        return MOE_ERR_DTYPE;
+    if (token_of_row->dtype != MOE_U32 || expert_offsets->dtype != MOE_U32) return MOE_ERR_DTYPE;
+    const int64_t E = gate->dims[0], I = gate->dims[1], H = gate->dims[2];
+    const int64_t T = input->dims[0], N = token_of_row->dims[0];
+    if (up->dims[0] != E || up->dims[1] != I || up->dims[2] != H) return MOE_ERR_SHAPE;
+    if (E < 1 || H < 1 || I < 1) return MOE_ERR_SHAPE;
+    if (input->dims[1] != H || expert_offsets->dims[0] != E + 1) return MOE_ERR_SHAPE;
+    if (h->dims[0] != N || h->dims[1] != I) return MOE_ERR_SHAPE;
+    if (N > 0 && T < 1) return MOE_ERR_SHAPE;
+    MOE_TRY(check_gemm_limits(E, H, I, N, {gate->data, up->data, input->data, h->data}));
+    if (!workspace || workspace_bytes < align_up(experts_tile_bytes(N, E))) return MOE_ERR_WORKSPACE;
+    if (N == 0) return MOE_OK;
+    hipStream_t s = (hipStream_t)stream;
+    MOE_TRY(check_devices(s, {gate->data, up->data, input->data, token_of_row->data, expert_offsets->data,
+                              h->data, workspace}));
+    return enqueue_experts(gate->dtype, E, H, I, gate->data, up->data, nullptr, input->data,
+                           (const uint32_t*)token_of_row->data, T, N, (const uint32_t*)expert_offsets->data,
+                           nullptr, h->data, workspace, s, kGateUp);
 }
 
 moe_status moe_experts_down(const moe_tensor* down, const moe_tensor* h, const moe_tensor* expert_offsets,

@@ -166,6 +166,48 @@ def test_experts_parity(cfg):
     assert_close(values(gy, cfg.dtype), oracle.widen(Y, cfg.dtype), cfg.dtype, f"expert outputs {cfg.name}")
 
 
+@pytest.mark.parametrize("cfg", [
+    S.small_config("gather_pipe_bf16", T=700, H=128, I=96, E=5, top_k=2, dtype="bf16", seed=51),
+    S.small_config("gather_small_f16", T=24, H=64, I=64, E=32, top_k=3, dtype="f16", seed=52),
+    S.small_config("gather_f32", T=90, H=48, I=40, E=3, top_k=2, dtype="f32", seed=53),
+    S.small_config("gather_edge_bf16", T=1024, H=64, I=64, E=16, top_k=4, dtype="bf16", edge_rows=True, seed=54),
+], ids=lambda c: c.name)
+def test_mapping_only_dispatch_and_gathered_gate_up(cfg):
+    """moe_dispatch with no dispatched buffer writes the same offsets and a
+    valid mapping; gate/up reading the tokens in place through token_of_row
+    gives the bits of gate/up on the copied rows, and matches the oracle."""
+    log(f"gathered gate/up {cfg.name}")
+    x, lg = S.make_tokens(cfg)
+    W = S.make_weights(cfg)
+    idx, _, _ = oracle.route(host_bits(lg), cfg.logits_dtype, cfg.top_k, cfg.renormalize, NTHREADS)
+    xb = host_bits(x)
+    o = oracle.dispatch(idx, cfg.E, xb, cfg.dtype)
+    gx = x.to(DEV)
+    gidx = torch.from_numpy(idx.view(np.int32)).view(torch.uint32).to(DEV)
+    m = moe.dispatch(gx, gidx, cfg.E, copy_rows=False)
+    torch.cuda.synchronize()
+    assert m.rows is None
+    tor = host_bits(m.token_of_row)
+    gpu = {"rows": xb[np.minimum(tor, cfg.T - 1)], "offsets": host_bits(m.expert_offsets),
+           "row_of_slot": host_bits(m.row_of_slot), "token_of_row": tor}
+    compare_dispatch(gpu, *o, xb, idx, cfg.E)
+    ex = moe.SwiGluExperts(*[w.to(DEV) for w in W])
+    d = moe.dispatch(gx, gidx, cfg.E)
+    h_copy = ex.gate_up(d.rows, d.expert_offsets)
+    h_in_place = ex.gate_up_gathered(gx, d.token_of_row, d.expert_offsets)
+    torch.cuda.synchronize()
+    n = int(host_bits(d.expert_offsets)[cfg.E])
+    bits = torch.int32 if h_copy.dtype == torch.float32 else torch.int16
+    assert torch.equal(h_copy[:n].view(bits), h_in_place[:n].view(bits))
+    # the oracle's activation for the same per-expert rows (row order inside
+    # an expert is the device's; map each row to its token)
+    Wb = [host_bits(w) for w in W]
+    _, h_ref = oracle.experts(*Wb, cfg.dtype, xb[host_bits(d.token_of_row)[:n]], host_bits(d.expert_offsets),
+                              cfg.E, cfg.H, cfg.I, with_h=True, nthreads=NTHREADS)
+    assert_close(values(h_in_place[:n], cfg.dtype), oracle.widen(h_ref[:n], cfg.dtype), cfg.dtype,
+                 f"gathered activation {cfg.name}")
+
+
 # ------------------------------------------------------------------ combine
 @pytest.mark.parametrize("cfg", small_cases(), ids=lambda c: c.name)
 def test_combine_parity(cfg):
