@@ -125,6 +125,51 @@ def test_dispatch_validation(L):
     assert _dispatch(L, x, idx, -1, rows, off, ros, tor) == INVALID
 
 
+def test_dispatch_mapping_only_validation(L):
+    """A NULL dispatched tensor asks for the mapping only; the other
+    arguments are still checked, and a well-formed call reaches the device
+    check."""
+    T, H, E, k = 10, 16, 4, 2
+    x = raw_tensor(FAKE, BF16, (T, H))
+    idx = raw_tensor(FAKE, U32, (T, k))
+    off = raw_tensor(FAKE, U32, (E + 1,))
+    ros = raw_tensor(FAKE, U32, (T * k,))
+    tor = raw_tensor(FAKE, U32, (T * k,))
+
+    def d(idx=idx, off=off, ros=ros):
+        return L.moe_dispatch(ctypes.byref(x), ctypes.byref(idx), E, None, ctypes.byref(off), ctypes.byref(ros),
+                              ctypes.byref(tor), ctypes.c_void_p(FAKE), 1 << 30, None)
+
+    assert d(idx=raw_tensor(FAKE, F32, (T, k))) == DTYPE
+    assert d(off=raw_tensor(FAKE, U32, (E,))) == SHAPE
+    assert d(ros=raw_tensor(FAKE, U32, (T,))) == SHAPE
+    assert d() == DEVICE
+
+
+def test_gate_up_gathered_validation(L):
+    E, I, H, T, N = 4, 32, 16, 10, 20
+    g = raw_tensor(FAKE, BF16, (E, I, H))
+    u = raw_tensor(FAKE, BF16, (E, I, H))
+    x = raw_tensor(FAKE, BF16, (T, H))
+    tor = raw_tensor(FAKE, U32, (N,))
+    off = raw_tensor(FAKE, U32, (E + 1,))
+    h = raw_tensor(FAKE, BF16, (N, I))
+
+    def f(u=u, x=x, tor=tor, off=off, h=h, wsb=1 << 30):
+        return L.moe_experts_gate_up_gathered(ctypes.byref(g), ctypes.byref(u), ctypes.byref(x), ctypes.byref(tor),
+                                              ctypes.byref(off), ctypes.byref(h), ctypes.c_void_p(FAKE), wsb, None)
+
+    assert f(x=raw_tensor(FAKE, F16, (T, H))) == DTYPE
+    assert f(tor=raw_tensor(FAKE, F32, (N,))) == DTYPE
+    assert f(x=raw_tensor(FAKE, BF16, (T, H + 8))) == SHAPE
+    assert f(h=raw_tensor(FAKE, BF16, (N + 1, I))) == SHAPE     # h has a row per token_of_row entry
+    assert f(off=raw_tensor(FAKE, U32, (E,))) == SHAPE
+    assert f(x=raw_tensor(FAKE, BF16, (0, H))) == SHAPE         # rows to gather but no tokens
+    assert f(x=raw_tensor(FAKE + 2, BF16, (T, H))) == UNSUPPORTED
+    assert f(wsb=16) == WORKSPACE
+    assert f() == DEVICE
+
+
 def _experts(L, g, u, d, rows, off, out, ws=FAKE, wsb=1 << 30):
     return L.moe_experts_forward(ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), ctypes.byref(rows),
                                  ctypes.byref(off), ctypes.byref(out), ctypes.c_void_p(ws), wsb, None)
