@@ -14,17 +14,25 @@
 //             the weight dtype.
 //   down:     y[r, c] = sum_i h[r,i] down[e,c,i]
 //
+// Row source: row r of the products is either row r of a dispatched copy, or
+// (fused gather) token row x[token_of_row[r]] read in place, so the forward
+// needs no dispatched copy of the tokens.
+//
 // Work list: a one-workgroup kernel turns expert_offsets into a list of
 // (expert, row_begin, row_end) M-tiles in ascending expert order, on the
 // device, so no host sync is needed.  The GEMM grid is sized for the most
-// M-tiles any routing could produce; surplus workgroups exit at once.
-// Workgroup ids are remapped so each of the 8 XCDs works on a contiguous run
-// of tiles (tiles of one expert share A rows and weight rows in that XCD's L2).
+// M-tiles any routing could produce; only the live ones get workgroup ids,
+// spread over the 8 XCDs, each XCD walking groups of one expert's tiles.
 //
-// Pipeline: 128-byte K slices of A and B are staged in LDS (row stride padded
-// by 16 bytes, so the 16 rows a ds_read_b128 touches fall in distinct banks),
-// double buffered: the global loads of slice k+1 are in flight while the
-// matrix cores work on slice k.  FP32 accumulation throughout.
+// Two kernels:
+//   grouped_gemm_pipe_kernel (bf16/f16, K a multiple of 32): 256x256 tiles on
+//     8 waves of 32x32x16 MFMAs; 32-element K stages filled by direct
+//     global->LDS loads in a 4-stage ring, issued three stages ahead and
+//     interleaved with the MFMAs and the next fragment reads.
+//   grouped_gemm_kernel (f32, other K, and the 16-row tile for decode-sized
+//     batches): 128-byte K slices staged through registers into padded LDS,
+//     double buffered, 16x16 MFMAs.
+// FP32 accumulation throughout.
 #include <type_traits>
 
 #include "moe_internal.h"
