@@ -393,6 +393,9 @@ __global__ __launch_bounds__(WGM* WGN* kWave) void grouped_gemm_kernel(
 #ifndef MOE_P_STAGES
 #define MOE_P_STAGES 4
 #endif
+#ifndef MOE_P_BK64
+#define MOE_P_BK64 1
+#endif
 #ifndef MOE_P_BN
 #define MOE_P_BN 256
 #endif
@@ -447,6 +450,50 @@ template <int N> __device__ __forceinline__ void wait_vm() { asm volatile("s_wai
 // lgkmcnt(0) through the builtin, so the compiler's own LDS-read tracking
 // knows the fragment registers are complete
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// Epilogue of the 32x32-block kernels: lane holds token (lane % 32) of each
+// token block and output columns 8 (r / 4) + 4 (lane / 32) + (r % 4) of each
+// weight block; gate/up pairs go through SiLU*mul, rows past r1 and columns
+// past NOUT are not written.
+template <typename DT, bool GATEUP, int MB, int NB, int WTM, int WTN, int WCN>
+__device__ __forceinline__ void store_tile32(const f32x16_t (&acc)[MB][NB], typename DT::storage* __restrict__ C,
+                                             int r0, int r1, int n0, int wm, int wn, int NOUT, int lane) {
+    using S = typename DT::storage;
+    const int frow = lane & 31;
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+        const int grow = r0 + wm * WTM + i * 32 + frow;
+        if (grow >= r1) continue;
+        S* crow = C + (int64_t)grow * NOUT;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int cb = g * 8 + (lane >> 5) * 4;
+            if (GATEUP) {
+#pragma unroll
+                for (int f = 0; f < NB / 2; ++f) {
+                    const int col = n0 + wn * WCN + f * 32 + cb;
+                    if (col < NOUT) {
+                        float v[4];
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            v[r] = silu_mul(acc[i][f][g * 4 + r], acc[i][f + NB / 2][g * 4 + r]);
+                        store4<DT>::run(crow + col, v);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int f = 0; f < NB; ++f) {
+                    const int col = n0 + wn * WTN + f * 32 + cb;
+                    if (col < NOUT) {
+                        float v[4] = {acc[i][f][g * 4], acc[i][f][g * 4 + 1], acc[i][f][g * 4 + 2],
+                                      acc[i][f][g * 4 + 3]};
+                        store4<DT>::run(crow + col, v);
+                    }
+                }
+            }
+        }
+    }
+}
 
 #ifndef MOE_P_MINB
 #define MOE_P_MINB 1   // workgroups per CU the register budget must allow
@@ -617,41 +664,164 @@ __global__ __launch_bounds__(WGM* WGN* kWave, MOE_P_MINB) void grouped_gemm_pipe
         wait_vm<0>();
     }
 
-    // epilogue: lane holds token (lane % 32) of each token block and output
-    // columns 8 (r / 4) + 4 (lane / 32) + (r % 4) of each weight block
+    store_tile32<DT, GATEUP, MB, NB, WTM, WTN, WCN>(acc, C, r0, r1, n0, wm, wn, NOUT, lane);
+}
+
+// ------------------------------------------------------------------ pipelined grouped GEMM, 64-wide K stages
+// The same 256x256 tile and 8 waves of 128x64 as above, with 64-element K
+// stages: every LDS row holds 128 bytes (one whole cache line of each operand
+// row per stage, chunk c of row r at c ^ (r & 7)), so each DMA instruction
+// moves 8 rows x 128 bytes, and one barrier covers 64 K instead of 32.  Two
+// stages of 64 KB fill the ring.  A stage runs as four 16-K sub-steps; the
+// fragments of the next sub-step are read during the current one.  The
+// barrier sits between sub-steps 2 and 3 of step kt: by then every wave has
+// read all of stage kt and landed its DMA of stage kt+1, so sub-step 3 can
+// read the first fragments of kt+1 and start the DMA of kt+2 into the slot
+// stage kt leaves -- a whole step ahead of its use.  Requires K % 64 == 0.
+template <typename DT, bool GATEUP>
+__global__ __launch_bounds__(512, 1) void grouped_gemm_pipe64_kernel(
+    const typename DT::storage* __restrict__ A, const typename DT::storage* __restrict__ B0,
+    const typename DT::storage* __restrict__ B1, typename DT::storage* __restrict__ C,
+    const uint32_t* __restrict__ a_rows, int a_nrows, const int4* __restrict__ tiles,
+    const uint32_t* __restrict__ tile_count, int K, int NOUT, int n_tiles, int nblocks) {
+    using S = typename DT::storage;
+    constexpr int WGM = 2, WGN = 4, NW = WGM * WGN;
+    constexpr int ROWB = 128;                                   // bytes per row per stage
+    constexpr int STAGE = (kPipeBM + kPipeBN) * ROWB;           // 64 KB
+    constexpr int LPW = STAGE / 1024 / NW;                      // 8 pieces of 8 rows per wave
+    constexpr int BN_OUT = GATEUP ? kPipeBN / 2 : kPipeBN;
+    constexpr int WTM = kPipeBM / WGM, WTN = kPipeBN / WGN;
+    constexpr int MB = WTM / 32, NB = WTN / 32;
+    constexpr int WCN = BN_OUT / WGN;
+    constexpr int NM = MB * NB, NR = MB + NB;                   // MFMAs and fragment reads per sub-step
+    static_assert(!GATEUP || NB % 2 == 0, "gate and up blocks pair up");
+    static_assert(LPW <= NM, "one DMA piece per MFMA of a sub-step at most");
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE];
+
+    int m_idx, n_idx;
+    if (!tile_of_block(blockIdx.x, nblocks, n_tiles, (int)*tile_count, tiles, &m_idx, &n_idx)) return;
+    const int4 tl = tiles[m_idx];
+    const int e = tl.x, r0 = tl.y, r1 = tl.z;
+    const int n0 = n_idx * BN_OUT;
+    const int lane = lane_id(), wid = threadIdx.x / kWave;
+    const int wm = wid / WGN, wn = wid % WGN;
+
+    // DMA piece j of this wave: stage rows (wid * LPW + j) * 8 + lane / 8, the
+    // lane's 16-byte physical slot (lane & 7) holding logical chunk slot ^ (row & 7)
+    const char* src[LPW];
 #pragma unroll
-    for (int i = 0; i < MB; ++i) {
-        const int grow = r0 + wm * WTM + i * 32 + frow;
-        if (grow >= r1) continue;
-        S* crow = C + (int64_t)grow * NOUT;
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int cb = g * 8 + (lane >> 5) * 4;
-            if (GATEUP) {
-#pragma unroll
-                for (int f = 0; f < NB / 2; ++f) {
-                    const int col = n0 + wn * WCN + f * 32 + cb;
-                    if (col < NOUT) {
-                        float v[4];
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            v[r] = silu_mul(acc[i][f][g * 4 + r], acc[i][f + NB / 2][g * 4 + r]);
-                        store4<DT>::run(crow + col, v);
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int f = 0; f < NB; ++f) {
-                    const int col = n0 + wn * WTN + f * 32 + cb;
-                    if (col < NOUT) {
-                        float v[4] = {acc[i][f][g * 4], acc[i][f][g * 4 + 1], acc[i][f][g * 4 + 2],
-                                      acc[i][f][g * 4 + 3]};
-                        store4<DT>::run(crow + col, v);
-                    }
-                }
-            }
+    for (int j = 0; j < LPW; ++j) {
+        const int row = (wid * LPW + j) * 8 + (lane >> 3);
+        const int lc = (lane & 7) ^ (row & 7);
+        const S* p;
+        if (row < kPipeBM) {
+            p = A + src_row(a_rows, a_nrows, min(r0 + row, r1 - 1)) * K;
+        } else {
+            const int w = row - kPipeBM;
+            if (GATEUP)
+                p = (w < BN_OUT ? B0 : B1) + ((int64_t)e * NOUT + min(n0 + (w % BN_OUT), NOUT - 1)) * K;
+            else
+                p = B0 + ((int64_t)e * NOUT + min(n0 + w, NOUT - 1)) * K;
         }
+        src[j] = (const char*)p + lc * 16;
     }
+    const int nk = K / 64;
+    const uint32_t smem_base = lds_offset(smem) + wid * LPW * 1024;
+    // fragment rows are 32-aligned blocks plus (lane & 31), so row & 7 == lane & 7
+    const int frow = lane & 31, kg = lane >> 5;
+    const int fa0 = (wm * WTM + frow) * ROWB;
+    int fb[NB];
+#pragma unroll
+    for (int f = 0; f < NB; ++f) {
+        int brow;
+        if (GATEUP)
+            brow = (f < NB / 2) ? wn * WCN + f * 32 : BN_OUT + wn * WCN + (f - NB / 2) * 32;
+        else
+            brow = wn * WTN + f * 32;
+        fb[f] = (kPipeBM + brow + frow) * ROWB;
+    }
+    int csw[4];  // byte offset of sub-step q's chunk in this lane's rows
+#pragma unroll
+    for (int q = 0; q < 4; ++q) csw[q] = ((2 * q + kg) ^ (frow & 7)) * 16;
+
+    const int rows_live = __builtin_amdgcn_readfirstlane(r1 - r0) - __builtin_amdgcn_readfirstlane(wm) * WTM;
+    f32x16_t acc[MB][NB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int f = 0; f < NB; ++f)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][f][r] = 0.0f;
+
+    uint4 av[2][MB], bv[2][NB];
+    auto read_one = [&](int kt, int q, int set, int r) {
+        const unsigned char* base = smem + (kt & 1) * STAGE + csw[q];
+        if (r < MB)
+            av[set][r] = *(const uint4*)(base + fa0 + r * 32 * ROWB);
+        else
+            bv[set][r - MB] = *(const uint4*)(base + fb[r - MB]);
+    };
+    // steps past the end re-load the last step into a slot nobody reads again
+    auto issue_part = [&](int kt, int j) {
+        const int ks = min(kt, nk - 1);
+        lds_dma16(src[j] + ks * ROWB, smem_base + (kt & 1) * STAGE + j * 1024);
+    };
+    // the MFMAs of sub-step (set), the reads of the next sub-step (rkt, rq)
+    // into the other set over the first half of them, and `nd` DMA pieces of
+    // step dkt over the second half
+    auto substep = [&](auto full, auto nd, int set, int rkt, int rq, int dkt) {
+        constexpr int ND = decltype(nd)::value, H1 = NM / 2, H2 = NM - NM / 2;
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+            const int i = m / NB, f = m % NB;
+            if (decltype(full)::value || i * 32 < rows_live)
+                acc[i][f] = mma32<DT>::run(bv[set][f], av[set][i], acc[i][f]);
+            if (m < H1) {
+#pragma unroll
+                for (int r = (m * NR) / H1; r < ((m + 1) * NR) / H1; ++r) read_one(rkt, rq, set ^ 1, r);
+            } else {
+                const int q = m - H1;
+#pragma unroll
+                for (int d = (q * ND) / H2; d < ((q + 1) * ND) / H2; ++d) issue_part(dkt, d);
+            }
+            sched_fence();
+        }
+    };
+    using no_dma = std::integral_constant<int, 0>;
+    using all_dma = std::integral_constant<int, LPW>;
+    {
+#pragma unroll
+        for (int j = 0; j < LPW; ++j) issue_part(0, j);
+#pragma unroll
+        for (int j = 0; j < LPW; ++j) issue_part(1, j);
+        wait_vm<LPW>();  // step 0 landed
+        barrier_lds();
+#pragma unroll
+        for (int r = 0; r < NR; ++r) read_one(0, 0, 0, r);
+        auto main_loop = [&](auto full) {
+            for (int kt = 0; kt < nk; ++kt) {
+                wait_lgkm0();
+                substep(full, no_dma{}, 0, kt, 1, 0);
+                wait_lgkm0();
+                substep(full, no_dma{}, 1, kt, 2, 0);
+                wait_lgkm0();
+                substep(full, no_dma{}, 0, kt, 3, 0);
+                // step kt+1 landed (this wave's DMA of it was its last); the
+                // reads of step kt complete before the barrier, so its slot
+                // can be refilled once every wave has passed it
+                wait_vm<0>();
+                wait_lgkm0();
+                barrier_lds();
+                substep(full, all_dma{}, 1, kt + 1, 0, kt + 2);
+            }
+        };
+        if (rows_live >= MB * 32)
+            main_loop(std::true_type{});
+        else
+            main_loop(std::false_type{});
+        wait_vm<0>();
+    }
+    store_tile32<DT, GATEUP, MB, NB, WTM, WTN, WCN>(acc, C, r0, r1, n0, wm, wn, NOUT, lane);
 }
 
 struct GemmShape {
@@ -696,6 +866,22 @@ hipError_t launch_pipe(const void* A, const uint32_t* a_rows, int64_t a_nrows, c
     return hipGetLastError();
 }
 
+template <typename DT, bool GATEUP>
+hipError_t launch_pipe64(const void* A, const uint32_t* a_rows, int64_t a_nrows, const void* B0, const void* B1,
+                         void* C, const int4* tiles, const uint32_t* count, int64_t mt, int K, int NOUT,
+                         hipStream_t s) {
+    using S = typename DT::storage;
+    constexpr int BN_OUT = GATEUP ? kPipeBN / 2 : kPipeBN;
+    const int n_tiles = (NOUT + BN_OUT - 1) / BN_OUT;
+    const int64_t nb = mt * n_tiles;
+    if (nb == 0) return hipSuccess;
+    if (nb > 0x7fffffff) return hipErrorInvalidValue;
+    grouped_gemm_pipe64_kernel<DT, GATEUP><<<(unsigned)nb, 512, 0, s>>>(
+        (const S*)A, (const S*)B0, (const S*)B1, (S*)C, a_rows, (int)a_nrows, tiles, count, K, NOUT, n_tiles,
+        (int)nb);
+    return hipGetLastError();
+}
+
 #ifndef MOE_P_WM
 #define MOE_P_WM 2   // waves along token rows of the pipelined tile
 #define MOE_P_WN 4   // waves along weight rows
@@ -730,6 +916,17 @@ hipError_t launch_typed(const ExpertsArgs& a, hipStream_t s, ExpertsPart part) {
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int H = (int)a.H, I = (int)a.I;
+    if (pipe && MOE_P_BK64 && a.H % 64 == 0 && a.I % 64 == 0) {
+        if constexpr (sizeof(typename DT::storage) == 2) {
+            if (part != kDown) {
+                err = launch_pipe64<DT, true>(a.x, a.x_rows, a.x_nrows, a.gate, a.up, a.h, tiles, count, mt, H, I, s);
+                if (err != hipSuccess) return err;
+            }
+            if (part != kGateUp)
+                err = launch_pipe64<DT, false>(a.h, nullptr, 0, a.down, nullptr, a.y, tiles, count, mt, I, H, s);
+        }
+        return err;
+    }
     if (pipe) {
         if constexpr (sizeof(typename DT::storage) == 2) {
             if (part != kDown) {

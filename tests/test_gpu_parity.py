@@ -53,6 +53,10 @@ def small_cases():
         S.small_config("pipe_f16", T=500, H=96, I=160, E=3, top_k=2, dtype="f16", seed=17),
         S.small_config("pipe_short_k_bf16", T=600, H=64, I=32, E=4, top_k=2, dtype="bf16", seed=18),
         S.small_config("pipe_many_tiles_bf16", T=1100, H=256, I=320, E=5, top_k=3, dtype="bf16", seed=19),
+        # 64-wide K stages (H and I multiples of 64): a single K step each way,
+        # and several steps with ragged tiles in f16
+        S.small_config("pipe64_one_step_bf16", T=600, H=64, I=64, E=3, top_k=2, dtype="bf16", seed=20),
+        S.small_config("pipe64_f16", T=900, H=192, I=128, E=6, top_k=2, dtype="f16", seed=27),
     ]
 
 
