@@ -671,13 +671,17 @@ __global__ __launch_bounds__(WGM* WGN* kWave, MOE_P_MINB) void grouped_gemm_pipe
 // The same 256x256 tile and 8 waves of 128x64 as above, with 64-element K
 // stages: every LDS row holds 128 bytes (one whole cache line of each operand
 // row per stage, chunk c of row r at c ^ (r & 7)), so each DMA instruction
-// moves 8 rows x 128 bytes, and one barrier covers 64 K instead of 32.  Two
-// stages of 64 KB fill the ring.  A stage runs as four 16-K sub-steps; the
-// fragments of the next sub-step are read during the current one.  The
-// barrier sits between sub-steps 2 and 3 of step kt: by then every wave has
-// read all of stage kt and landed its DMA of stage kt+1, so sub-step 3 can
-// read the first fragments of kt+1 and start the DMA of kt+2 into the slot
-// stage kt leaves -- a whole step ahead of its use.  Requires K % 64 == 0.
+// moves 8 rows x 128 bytes, and one barrier covers 64 K instead of 32.
+// The token rows and the weight rows have rings of their own in the 160 KB
+// of LDS: 2 slots of 32 KB for the tokens, 3 for the weights, so the weight
+// tiles -- the operand L2 shares least -- are requested two steps ahead.
+// A step runs as four 16-K sub-steps; the fragments of the next sub-step are
+// read during the current one.  The barrier sits between sub-steps 2 and 3
+// of step kt: by then every wave has read all of step kt and landed its DMA
+// of step kt+1, so sub-step 3 reads the first fragments of kt+1 and starts
+// the DMA of the token rows of kt+2 and the weight rows of kt+3 into the
+// slots step kt leaves.  Requires K % 64 == 0.
+constexpr int kP64SlotsA = 2, kP64SlotsB = 3;
 template <typename DT, bool GATEUP>
 __global__ __launch_bounds__(512, 1) void grouped_gemm_pipe64_kernel(
     const typename DT::storage* __restrict__ A, const typename DT::storage* __restrict__ B0,
@@ -686,17 +690,20 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_pipe64_kernel(
     const uint32_t* __restrict__ tile_count, int K, int NOUT, int n_tiles, int nblocks) {
     using S = typename DT::storage;
     constexpr int WGM = 2, WGN = 4, NW = WGM * WGN;
-    constexpr int ROWB = 128;                                   // bytes per row per stage
-    constexpr int STAGE = (kPipeBM + kPipeBN) * ROWB;           // 64 KB
-    constexpr int LPW = STAGE / 1024 / NW;                      // 8 pieces of 8 rows per wave
+    constexpr int ROWB = 128;                                   // bytes per row per step
+    constexpr int SLOT = kPipeBM * ROWB;                        // 32 KB: one operand, one step
+    static_assert(kPipeBN == kPipeBM, "both operand tiles are 256 rows");
+    constexpr int NA = kP64SlotsA, NB_ = kP64SlotsB;
+    constexpr int LPO = SLOT / 1024 / NW;                       // 4 pieces of 8 rows per wave per operand
     constexpr int BN_OUT = GATEUP ? kPipeBN / 2 : kPipeBN;
     constexpr int WTM = kPipeBM / WGM, WTN = kPipeBN / WGN;
     constexpr int MB = WTM / 32, NB = WTN / 32;
     constexpr int WCN = BN_OUT / WGN;
     constexpr int NM = MB * NB, NR = MB + NB;                   // MFMAs and fragment reads per sub-step
     static_assert(!GATEUP || NB % 2 == 0, "gate and up blocks pair up");
-    static_assert(LPW <= NM, "one DMA piece per MFMA of a sub-step at most");
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE];
+    static_assert(2 * LPO <= NM, "at most one DMA piece per MFMA of a sub-step");
+    static_assert(NA == 2 && NB_ == 3, "the vmcnt waits below are counted for 2 token and 3 weight slots");
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[(NA + NB_) * SLOT];
 
     int m_idx, n_idx;
     if (!tile_of_block(blockIdx.x, nblocks, n_tiles, (int)*tile_count, tiles, &m_idx, &n_idx)) return;
@@ -706,27 +713,26 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_pipe64_kernel(
     const int lane = lane_id(), wid = threadIdx.x / kWave;
     const int wm = wid / WGN, wn = wid % WGN;
 
-    // DMA piece j of this wave: stage rows (wid * LPW + j) * 8 + lane / 8, the
-    // lane's 16-byte physical slot (lane & 7) holding logical chunk slot ^ (row & 7)
-    const char* src[LPW];
+    // DMA piece j of this wave, per operand: rows (wid * LPO + j) * 8 + lane / 8
+    // of the operand tile, the lane's 16-byte physical slot (lane & 7) holding
+    // logical chunk slot ^ (row & 7)
+    const char* srca[LPO];
+    const char* srcb[LPO];
 #pragma unroll
-    for (int j = 0; j < LPW; ++j) {
-        const int row = (wid * LPW + j) * 8 + (lane >> 3);
+    for (int j = 0; j < LPO; ++j) {
+        const int row = (wid * LPO + j) * 8 + (lane >> 3);
         const int lc = (lane & 7) ^ (row & 7);
+        srca[j] = (const char*)(A + src_row(a_rows, a_nrows, min(r0 + row, r1 - 1)) * K) + lc * 16;
         const S* p;
-        if (row < kPipeBM) {
-            p = A + src_row(a_rows, a_nrows, min(r0 + row, r1 - 1)) * K;
-        } else {
-            const int w = row - kPipeBM;
-            if (GATEUP)
-                p = (w < BN_OUT ? B0 : B1) + ((int64_t)e * NOUT + min(n0 + (w % BN_OUT), NOUT - 1)) * K;
-            else
-                p = B0 + ((int64_t)e * NOUT + min(n0 + w, NOUT - 1)) * K;
-        }
-        src[j] = (const char*)p + lc * 16;
+        if (GATEUP)
+            p = (row < BN_OUT ? B0 : B1) + ((int64_t)e * NOUT + min(n0 + (row % BN_OUT), NOUT - 1)) * K;
+        else
+            p = B0 + ((int64_t)e * NOUT + min(n0 + row, NOUT - 1)) * K;
+        srcb[j] = (const char*)p + lc * 16;
     }
     const int nk = K / 64;
-    const uint32_t smem_base = lds_offset(smem) + wid * LPW * 1024;
+    const uint32_t lds_a = lds_offset(smem) + wid * LPO * 1024;
+    const uint32_t lds_b = lds_a + NA * SLOT;
     // fragment rows are 32-aligned blocks plus (lane & 31), so row & 7 == lane & 7
     const int frow = lane & 31, kg = lane >> 5;
     const int fa0 = (wm * WTM + frow) * ROWB;
@@ -738,7 +744,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_pipe64_kernel(
             brow = (f < NB / 2) ? wn * WCN + f * 32 : BN_OUT + wn * WCN + (f - NB / 2) * 32;
         else
             brow = wn * WTN + f * 32;
-        fb[f] = (kPipeBM + brow + frow) * ROWB;
+        fb[f] = NA * SLOT + (brow + frow) * ROWB;
     }
     int csw[4];  // byte offset of sub-step q's chunk in this lane's rows
 #pragma unroll
@@ -755,21 +761,22 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_pipe64_kernel(
 
     uint4 av[2][MB], bv[2][NB];
     auto read_one = [&](int kt, int q, int set, int r) {
-        const unsigned char* base = smem + (kt & 1) * STAGE + csw[q];
         if (r < MB)
-            av[set][r] = *(const uint4*)(base + fa0 + r * 32 * ROWB);
+            av[set][r] = *(const uint4*)(smem + (kt % NA) * SLOT + csw[q] + fa0 + r * 32 * ROWB);
         else
-            bv[set][r - MB] = *(const uint4*)(base + fb[r - MB]);
+            bv[set][r - MB] = *(const uint4*)(smem + (kt % NB_) * SLOT + csw[q] + fb[r - MB]);
     };
     // steps past the end re-load the last step into a slot nobody reads again
-    auto issue_part = [&](int kt, int j) {
-        const int ks = min(kt, nk - 1);
-        lds_dma16(src[j] + ks * ROWB, smem_base + (kt & 1) * STAGE + j * 1024);
+    auto dma_a = [&](int kt, int j) {
+        lds_dma16(srca[j] + min(kt, nk - 1) * ROWB, lds_a + (kt % NA) * SLOT + j * 1024);
+    };
+    auto dma_b = [&](int kt, int j) {
+        lds_dma16(srcb[j] + min(kt, nk - 1) * ROWB, lds_b + (kt % NB_) * SLOT + j * 1024);
     };
     // the MFMAs of sub-step (set), the reads of the next sub-step (rkt, rq)
-    // into the other set over the first half of them, and `nd` DMA pieces of
-    // step dkt over the second half
-    auto substep = [&](auto full, auto nd, int set, int rkt, int rq, int dkt) {
+    // into the other set over the first half of them, and `nd` DMA pieces
+    // over the second half
+    auto substep = [&](auto full, auto nd, int set, int rkt, int rq, auto&& dma) {
         constexpr int ND = decltype(nd)::value, H1 = NM / 2, H2 = NM - NM / 2;
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
@@ -782,37 +789,50 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_pipe64_kernel(
             } else {
                 const int q = m - H1;
 #pragma unroll
-                for (int d = (q * ND) / H2; d < ((q + 1) * ND) / H2; ++d) issue_part(dkt, d);
+                for (int d = (q * ND) / H2; d < ((q + 1) * ND) / H2; ++d) dma(d);
             }
             sched_fence();
         }
     };
     using no_dma = std::integral_constant<int, 0>;
-    using all_dma = std::integral_constant<int, LPW>;
+    using step_dma = std::integral_constant<int, 2 * LPO>;
+    auto none = [](int) {};
     {
+        // issue order A0 B0 A1 B1 B2: step 0 has landed once the 3 * LPO
+        // pieces after B0 may still be in flight
 #pragma unroll
-        for (int j = 0; j < LPW; ++j) issue_part(0, j);
+        for (int j = 0; j < LPO; ++j) dma_a(0, j);
 #pragma unroll
-        for (int j = 0; j < LPW; ++j) issue_part(1, j);
-        wait_vm<LPW>();  // step 0 landed
+        for (int j = 0; j < LPO; ++j) dma_b(0, j);
+#pragma unroll
+        for (int j = 0; j < LPO; ++j) dma_a(1, j);
+#pragma unroll
+        for (int j = 0; j < LPO; ++j) dma_b(1, j);
+#pragma unroll
+        for (int j = 0; j < LPO; ++j) dma_b(2, j);
+        wait_vm<3 * LPO>();
         barrier_lds();
 #pragma unroll
         for (int r = 0; r < NR; ++r) read_one(0, 0, 0, r);
         auto main_loop = [&](auto full) {
             for (int kt = 0; kt < nk; ++kt) {
                 wait_lgkm0();
-                substep(full, no_dma{}, 0, kt, 1, 0);
+                substep(full, no_dma{}, 0, kt, 1, none);
                 wait_lgkm0();
-                substep(full, no_dma{}, 1, kt, 2, 0);
+                substep(full, no_dma{}, 1, kt, 2, none);
                 wait_lgkm0();
-                substep(full, no_dma{}, 0, kt, 3, 0);
-                // step kt+1 landed (this wave's DMA of it was its last); the
-                // reads of step kt complete before the barrier, so its slot
-                // can be refilled once every wave has passed it
-                wait_vm<0>();
+                substep(full, no_dma{}, 0, kt, 3, none);
+                // step kt+1 landed: its weight rows went out a step before its
+                // token rows, and only the weight rows of kt+2 (LPO pieces)
+                // were issued after them.  The reads of step kt complete
+                // before the barrier, so its slots can be refilled once every
+                // wave has passed it.
+                wait_vm<LPO>();
                 wait_lgkm0();
                 barrier_lds();
-                substep(full, all_dma{}, 1, kt + 1, 0, kt + 2);
+                // token rows of kt+2 first, then weight rows of kt+3
+                substep(full, step_dma{}, 1, kt + 1, 0,
+                        [&](int d) { if (d < LPO) dma_a(kt + 2, d); else dma_b(kt + 3, d - LPO); });
             }
         };
         if (rows_live >= MB * 32)
