@@ -396,6 +396,10 @@ __global__ __launch_bounds__(WGM* WGN* kWave) void grouped_gemm_kernel(
 #ifndef MOE_P_BK64
 #define MOE_P_BK64 1
 #endif
+#ifndef MOE_P64_WM
+#define MOE_P64_WM 2   // waves along token rows of the 64-K kernel's tile
+#define MOE_P64_WN 4   // waves along weight rows
+#endif
 #ifndef MOE_P_BN
 #define MOE_P_BN 256
 #endif
@@ -682,14 +686,14 @@ __global__ __launch_bounds__(WGM* WGN* kWave, MOE_P_MINB) void grouped_gemm_pipe
 // the DMA of the token rows of kt+2 and the weight rows of kt+3 into the
 // slots step kt leaves.  Requires K % 64 == 0.
 constexpr int kP64SlotsA = 2, kP64SlotsB = 3;
-template <typename DT, bool GATEUP>
-__global__ __launch_bounds__(512, 1) void grouped_gemm_pipe64_kernel(
+template <typename DT, bool GATEUP, int WGM, int WGN>
+__global__ __launch_bounds__(WGM* WGN* kWave, 1) void grouped_gemm_pipe64_kernel(
     const typename DT::storage* __restrict__ A, const typename DT::storage* __restrict__ B0,
     const typename DT::storage* __restrict__ B1, typename DT::storage* __restrict__ C,
     const uint32_t* __restrict__ a_rows, int a_nrows, const int4* __restrict__ tiles,
     const uint32_t* __restrict__ tile_count, int K, int NOUT, int n_tiles, int nblocks) {
     using S = typename DT::storage;
-    constexpr int WGM = 2, WGN = 4, NW = WGM * WGN;
+    constexpr int NW = WGM * WGN;
     constexpr int ROWB = 128;                                   // bytes per row per step
     constexpr int SLOT = kPipeBM * ROWB;                        // 32 KB: one operand, one step
     static_assert(kPipeBN == kPipeBM, "both operand tiles are 256 rows");
@@ -896,7 +900,7 @@ hipError_t launch_pipe64(const void* A, const uint32_t* a_rows, int64_t a_nrows,
     const int64_t nb = mt * n_tiles;
     if (nb == 0) return hipSuccess;
     if (nb > 0x7fffffff) return hipErrorInvalidValue;
-    grouped_gemm_pipe64_kernel<DT, GATEUP><<<(unsigned)nb, 512, 0, s>>>(
+    grouped_gemm_pipe64_kernel<DT, GATEUP, MOE_P64_WM, MOE_P64_WN><<<(unsigned)nb, MOE_P64_WM * MOE_P64_WN * kWave, 0, s>>>(
         (const S*)A, (const S*)B0, (const S*)B1, (S*)C, a_rows, (int)a_nrows, tiles, count, K, NOUT, n_tiles,
         (int)nb);
     return hipGetLastError();
