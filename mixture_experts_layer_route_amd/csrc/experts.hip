@@ -33,6 +33,7 @@
 //     batches): 128-byte K slices staged through registers into padded LDS,
 //     double buffered, 16x16 MFMAs.
 // FP32 accumulation throughout.
+#include <algorithm>
 #include <type_traits>
 
 #include "moe_internal.h"
@@ -396,6 +397,23 @@ __global__ __launch_bounds__(WGM* WGN* kWave) void grouped_gemm_kernel(
 #ifndef MOE_P_BK64
 #define MOE_P_BK64 1
 #endif
+#ifndef MOE_P64_PERSIST
+#define MOE_P64_PERSIST 0
+#endif
+// Workgroups that fit on the stream's device at one per CU, rounded down to a
+// multiple of 8 XCDs (256 on MI355X); cached per device.
+int persistent_slots(hipStream_t s) {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipStreamGetDevice(s, &dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (!cached[dev]) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8)
+            cus = 256;
+        cached[dev] = cus / 8 * 8;
+    }
+    return cached[dev];
+}
 #ifndef MOE_P64_WM
 #define MOE_P64_WM 2   // waves along token rows of the 64-K kernel's tile
 #define MOE_P64_WN 4   // waves along weight rows
@@ -709,32 +727,42 @@ __global__ __launch_bounds__(WGM* WGN* kWave, 1) void grouped_gemm_pipe64_kernel
     static_assert(NA == 2 && NB_ == 3, "the vmcnt waits below are counted for 2 token and 3 weight slots");
     __shared__ __attribute__((aligned(1024))) unsigned char smem[(NA + NB_) * SLOT];
 
-    int m_idx, n_idx;
-    if (!tile_of_block(blockIdx.x, nblocks, n_tiles, (int)*tile_count, tiles, &m_idx, &n_idx)) return;
-    const int4 tl = tiles[m_idx];
-    const int e = tl.x, r0 = tl.y, r1 = tl.z;
-    const int n0 = n_idx * BN_OUT;
     const int lane = lane_id(), wid = threadIdx.x / kWave;
     const int wm = wid / WGN, wn = wid % WGN;
+    const int live_m = (int)*tile_count;
+    const int nk = K / 64;
 
+    // The workgroup walks tiles t = blockIdx.x, + gridDim.x, ...; gridDim.x is
+    // a multiple of 8, so every tile of a workgroup stays on its XCD and the
+    // XCD still walks a contiguous run of logical tiles.
+    int t = blockIdx.x, m_idx, n_idx;
+    if (!tile_of_block(t, nblocks, n_tiles, live_m, tiles, &m_idx, &n_idx)) return;
+    int e, r0, r1, n0;
     // DMA piece j of this wave, per operand: rows (wid * LPO + j) * 8 + lane / 8
     // of the operand tile, the lane's 16-byte physical slot (lane & 7) holding
     // logical chunk slot ^ (row & 7)
     const char* srca[LPO];
     const char* srcb[LPO];
+    auto setup = [&](int mi, int ni) {
+        const int4 tl = tiles[mi];
+        e = tl.x;
+        r0 = tl.y;
+        r1 = tl.z;
+        n0 = ni * BN_OUT;
 #pragma unroll
-    for (int j = 0; j < LPO; ++j) {
-        const int row = (wid * LPO + j) * 8 + (lane >> 3);
-        const int lc = (lane & 7) ^ (row & 7);
-        srca[j] = (const char*)(A + src_row(a_rows, a_nrows, min(r0 + row, r1 - 1)) * K) + lc * 16;
-        const S* p;
-        if (GATEUP)
-            p = (row < BN_OUT ? B0 : B1) + ((int64_t)e * NOUT + min(n0 + (row % BN_OUT), NOUT - 1)) * K;
-        else
-            p = B0 + ((int64_t)e * NOUT + min(n0 + row, NOUT - 1)) * K;
-        srcb[j] = (const char*)p + lc * 16;
-    }
-    const int nk = K / 64;
+        for (int j = 0; j < LPO; ++j) {
+            const int row = (wid * LPO + j) * 8 + (lane >> 3);
+            const int lc = (lane & 7) ^ (row & 7);
+            srca[j] = (const char*)(A + src_row(a_rows, a_nrows, min(r0 + row, r1 - 1)) * K) + lc * 16;
+            const S* p;
+            if (GATEUP)
+                p = (row < BN_OUT ? B0 : B1) + ((int64_t)e * NOUT + min(n0 + (row % BN_OUT), NOUT - 1)) * K;
+            else
+                p = B0 + ((int64_t)e * NOUT + min(n0 + row, NOUT - 1)) * K;
+            srcb[j] = (const char*)p + lc * 16;
+        }
+    };
+    setup(m_idx, n_idx);
     const uint32_t lds_a = lds_offset(smem) + wid * LPO * 1024;
     const uint32_t lds_b = lds_a + NA * SLOT;
     // fragment rows are 32-aligned blocks plus (lane & 31), so row & 7 == lane & 7
@@ -754,15 +782,7 @@ __global__ __launch_bounds__(WGM* WGN* kWave, 1) void grouped_gemm_pipe64_kernel
 #pragma unroll
     for (int q = 0; q < 4; ++q) csw[q] = ((2 * q + kg) ^ (frow & 7)) * 16;
 
-    const int rows_live = __builtin_amdgcn_readfirstlane(r1 - r0) - __builtin_amdgcn_readfirstlane(wm) * WTM;
     f32x16_t acc[MB][NB];
-#pragma unroll
-    for (int i = 0; i < MB; ++i)
-#pragma unroll
-        for (int f = 0; f < NB; ++f)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][f][r] = 0.0f;
-
     uint4 av[2][MB], bv[2][NB];
     auto read_one = [&](int kt, int q, int set, int r) {
         if (r < MB)
@@ -777,9 +797,24 @@ __global__ __launch_bounds__(WGM* WGN* kWave, 1) void grouped_gemm_pipe64_kernel
     auto dma_b = [&](int kt, int j) {
         lds_dma16(srcb[j] + min(kt, nk - 1) * ROWB, lds_b + (kt % NB_) * SLOT + j * 1024);
     };
+    // issue order A0 B0 A1 B1 B2: step 0 has landed once the 3 * LPO pieces
+    // after B0 may still be in flight
+    auto prologue_dma = [&]() {
+#pragma unroll
+        for (int j = 0; j < LPO; ++j) dma_a(0, j);
+#pragma unroll
+        for (int j = 0; j < LPO; ++j) dma_b(0, j);
+#pragma unroll
+        for (int j = 0; j < LPO; ++j) dma_a(1, j);
+#pragma unroll
+        for (int j = 0; j < LPO; ++j) dma_b(1, j);
+#pragma unroll
+        for (int j = 0; j < LPO; ++j) dma_b(2, j);
+    };
     // the MFMAs of sub-step (set), the reads of the next sub-step (rkt, rq)
     // into the other set over the first half of them, and `nd` DMA pieces
     // over the second half
+    int rows_live = 0;
     auto substep = [&](auto full, auto nd, int set, int rkt, int rq, auto&& dma) {
         constexpr int ND = decltype(nd)::value, H1 = NM / 2, H2 = NM - NM / 2;
 #pragma unroll
@@ -801,51 +836,60 @@ __global__ __launch_bounds__(WGM* WGN* kWave, 1) void grouped_gemm_pipe64_kernel
     using no_dma = std::integral_constant<int, 0>;
     using step_dma = std::integral_constant<int, 2 * LPO>;
     auto none = [](int) {};
-    {
-        // issue order A0 B0 A1 B1 B2: step 0 has landed once the 3 * LPO
-        // pieces after B0 may still be in flight
+    auto main_loop = [&](auto full) {
+        for (int kt = 0; kt < nk; ++kt) {
+            wait_lgkm0();
+            substep(full, no_dma{}, 0, kt, 1, none);
+            wait_lgkm0();
+            substep(full, no_dma{}, 1, kt, 2, none);
+            wait_lgkm0();
+            substep(full, no_dma{}, 0, kt, 3, none);
+            // step kt+1 landed: its weight rows went out a step before its
+            // token rows, and only the weight rows of kt+2 (LPO pieces) were
+            // issued after them.  The reads of step kt complete before the
+            // barrier, so its slots can be refilled once every wave has
+            // passed it.
+            wait_vm<LPO>();
+            wait_lgkm0();
+            barrier_lds();
+            // token rows of kt+2 first, then weight rows of kt+3
+            substep(full, step_dma{}, 1, kt + 1, 0,
+                    [&](int d) { if (d < LPO) dma_a(kt + 2, d); else dma_b(kt + 3, d - LPO); });
+        }
+    };
+
+    prologue_dma();
+    while (true) {
+        rows_live = __builtin_amdgcn_readfirstlane(r1 - r0) - __builtin_amdgcn_readfirstlane(wm) * WTM;
 #pragma unroll
-        for (int j = 0; j < LPO; ++j) dma_a(0, j);
+        for (int i = 0; i < MB; ++i)
 #pragma unroll
-        for (int j = 0; j < LPO; ++j) dma_b(0, j);
+            for (int f = 0; f < NB; ++f)
 #pragma unroll
-        for (int j = 0; j < LPO; ++j) dma_a(1, j);
-#pragma unroll
-        for (int j = 0; j < LPO; ++j) dma_b(1, j);
-#pragma unroll
-        for (int j = 0; j < LPO; ++j) dma_b(2, j);
+                for (int r = 0; r < 16; ++r) acc[i][f][r] = 0.0f;
         wait_vm<3 * LPO>();
         barrier_lds();
 #pragma unroll
         for (int r = 0; r < NR; ++r) read_one(0, 0, 0, r);
-        auto main_loop = [&](auto full) {
-            for (int kt = 0; kt < nk; ++kt) {
-                wait_lgkm0();
-                substep(full, no_dma{}, 0, kt, 1, none);
-                wait_lgkm0();
-                substep(full, no_dma{}, 1, kt, 2, none);
-                wait_lgkm0();
-                substep(full, no_dma{}, 0, kt, 3, none);
-                // step kt+1 landed: its weight rows went out a step before its
-                // token rows, and only the weight rows of kt+2 (LPO pieces)
-                // were issued after them.  The reads of step kt complete
-                // before the barrier, so its slots can be refilled once every
-                // wave has passed it.
-                wait_vm<LPO>();
-                wait_lgkm0();
-                barrier_lds();
-                // token rows of kt+2 first, then weight rows of kt+3
-                substep(full, step_dma{}, 1, kt + 1, 0,
-                        [&](int d) { if (d < LPO) dma_a(kt + 2, d); else dma_b(kt + 3, d - LPO); });
-            }
-        };
         if (rows_live >= MB * 32)
             main_loop(std::true_type{});
         else
             main_loop(std::false_type{});
+        // every DMA of this tile landed and every wave finished its reads:
+        // the next tile's first steps can be loaded while this one is stored
         wait_vm<0>();
+        wait_lgkm0();
+        barrier_lds();
+        const int c_r0 = r0, c_r1 = r1, c_n0 = n0;
+        t += gridDim.x;
+        const bool more = tile_of_block(t, nblocks, n_tiles, live_m, tiles, &m_idx, &n_idx);
+        if (more) {
+            setup(m_idx, n_idx);
+            prologue_dma();
+        }
+        store_tile32<DT, GATEUP, MB, NB, WTM, WTN, WCN>(acc, C, c_r0, c_r1, c_n0, wm, wn, NOUT, lane);
+        if (!more) break;
     }
-    store_tile32<DT, GATEUP, MB, NB, WTM, WTN, WCN>(acc, C, r0, r1, n0, wm, wn, NOUT, lane);
 }
 
 struct GemmShape {
@@ -900,7 +944,10 @@ hipError_t launch_pipe64(const void* A, const uint32_t* a_rows, int64_t a_nrows,
     const int64_t nb = mt * n_tiles;
     if (nb == 0) return hipSuccess;
     if (nb > 0x7fffffff) return hipErrorInvalidValue;
-    grouped_gemm_pipe64_kernel<DT, GATEUP, MOE_P64_WM, MOE_P64_WN><<<(unsigned)nb, MOE_P64_WM * MOE_P64_WN * kWave, 0, s>>>(
+    // persistent: one workgroup per CU (the kernel takes the whole LDS), a
+    // multiple of 8 so each workgroup's tiles stay on one XCD
+    const int64_t grid = MOE_P64_PERSIST ? std::min<int64_t>(nb, (int64_t)persistent_slots(s)) : nb;
+    grouped_gemm_pipe64_kernel<DT, GATEUP, MOE_P64_WM, MOE_P64_WN><<<(unsigned)grid, MOE_P64_WM * MOE_P64_WN * kWave, 0, s>>>(
         (const S*)A, (const S*)B0, (const S*)B1, (S*)C, a_rows, (int)a_nrows, tiles, count, K, NOUT, n_tiles,
         (int)nb);
     return hipGetLastError();
