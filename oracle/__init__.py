@@ -65,6 +65,9 @@ def lib():
         L.oracle_softmax.argtypes = [vp, i32, i64, i64, vp]
         L.oracle_route.restype = i32
         L.oracle_route.argtypes = [vp, i32, i64, i64, i32, i32, vp, vp, vp, i32]
+        L.oracle_route_sigmoid_grouped.restype = i32
+        L.oracle_route_sigmoid_grouped.argtypes = [vp, i32, vp, i64, i64, i32, i32, i32, i32, i32,
+                                                   ctypes.c_float, vp, vp, vp, vp, i32]
         L.oracle_dispatch.restype = i32
         L.oracle_dispatch.argtypes = [vp, i64, i32, i64, vp, i64, i32, vp, vp, vp, vp]
         L.oracle_experts.restype = i32
@@ -145,6 +148,32 @@ def route(logits: np.ndarray, dt: str, top_k: int, renormalize: bool, nthreads: 
     if rc != 0:
         raise ValueError("oracle_route: bad arguments")
     return idx, w, w32
+
+
+def route_sigmoid_grouped(logits: np.ndarray, dt: str, bias: np.ndarray | None, top_k: int, groups: int,
+                          selected_groups: int, group_top_two: bool, renormalize: bool, scale: float,
+                          nthreads: int | None = None):
+    """Group-limited sigmoid routing (ruDNN user guide, section 10).
+
+    Returns (indices u32 [T,k], weights [T,k] in the logits dtype, FP32
+    weights before the cast, corrected scores sigmoid(l) + bias [T,E] FP32)."""
+    lg = _check(logits, dt, "logits")
+    T, E = lg.shape
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    if b is not None and b.shape != (E,):
+        raise ValueError("bias must be [E] float32")
+    idx = np.empty((T, top_k), dtype=np.uint32)
+    w = np.empty((T, top_k), dtype=storage_dtype(dt))
+    w32 = np.empty((T, top_k), dtype=np.float32)
+    corr = np.empty((T, E), dtype=np.float32)
+    rc = lib().oracle_route_sigmoid_grouped(_ptr(lg), DT[dt], _ptr(b) if b is not None else None, T, E,
+                                            int(top_k), int(groups), int(selected_groups),
+                                            int(bool(group_top_two)), int(bool(renormalize)), float(scale),
+                                            _ptr(idx), _ptr(w), _ptr(w32), _ptr(corr),
+                                            nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_route_sigmoid_grouped: options outside the section's limits")
+    return idx, w, w32, corr
 
 
 # ---------------------------------------------------------------- dispatch

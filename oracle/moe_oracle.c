@@ -277,6 +277,136 @@ int oracle_route(const void* logits, int dt, int64_t T, int64_t E, int k, int re
 }
 
 /* ------------------------------------------------------------------ */
+/* Group-limited sigmoid routing (ruDNN user guide, section 10).        */
+/* ------------------------------------------------------------------ */
+
+/* sigmoid in binary32: the exact 1/(1+exp(-x)) of the binary32 input,
+ * evaluated in double and rounded once. */
+static float sigmoid_f32(float x)
+{
+    return (float)(1.0 / (1.0 + exp(-(double)x)));
+}
+
+typedef struct {
+    const void* logits;
+    int dt;
+    const float* bias; /* [E] FP32 or NULL */
+    int64_t E;
+    int k, groups, selected, top_two, renorm;
+    float scale;
+    uint32_t* idx;
+    void* w;
+    float* w_f32;
+    float* corr; /* [T,E] corrected scores, or NULL */
+} sroute_ctx;
+
+static void sroute_one(void* vctx, int64_t t)
+{
+    sroute_ctx* c = (sroute_ctx*)vctx;
+    const int64_t E = c->E;
+    const int k = c->k, G = c->groups, m = c->selected;
+    const int64_t gsz = E / G;
+    float* s = (float*)malloc(sizeof(float) * (size_t)E);
+    float* cs = (float*)malloc(sizeof(float) * (size_t)E);
+    float* gscore = (float*)malloc(sizeof(float) * (size_t)G);
+    unsigned char* gtaken = (unsigned char*)calloc((size_t)G, 1);
+    unsigned char* taken = (unsigned char*)calloc((size_t)E, 1);
+    float* sel = (float*)malloc(sizeof(float) * (size_t)k);
+    int nan_row = 0;
+    /* 1. sigmoid scores, and the corrected scores that only steer selection */
+    for (int64_t e = 0; e < E; ++e) {
+        s[e] = sigmoid_f32((float)load_elem(c->logits, c->dt, t * E + e));
+        cs[e] = s[e] + (c->bias ? c->bias[e] : 0.0f);
+        if (cs[e] != cs[e]) nan_row = 1;
+        if (c->corr) c->corr[t * E + e] = cs[e];
+    }
+    if (nan_row) {
+        /* a NaN score leaves no order: experts 0..k-1 with NaN weights, as
+         * the routing contract does for softmax rows */
+        for (int j = 0; j < k; ++j) {
+            c->idx[t * k + j] = (uint32_t)j;
+            if (c->w_f32) c->w_f32[t * k + j] = NAN;
+            store_elem(c->w, c->dt, t * k + j, NAN);
+        }
+        goto done;
+    }
+    /* 2. group scores over contiguous blocks of E/G experts: the largest
+     *    corrected score, or the sum of the two largest */
+    for (int g = 0; g < G; ++g) {
+        float a = -INFINITY, b = -INFINITY;
+        for (int64_t e = g * gsz; e < (g + 1) * gsz; ++e) {
+            if (cs[e] > a) {
+                b = a;
+                a = cs[e];
+            } else if (cs[e] > b) {
+                b = cs[e];
+            }
+        }
+        gscore[g] = c->top_two ? a + b : a;
+    }
+    /* 3. the m best groups; a strictly larger score displaces the pick, so
+     *    equal scores favour the lower group id */
+    for (int r = 0; r < m; ++r) {
+        int best = -1;
+        for (int g = 0; g < G; ++g) {
+            if (gtaken[g]) continue;
+            if (best < 0 || gscore[g] > gscore[best]) best = g;
+        }
+        gtaken[best] = 1;
+    }
+    /* 4. top-k experts of the chosen groups by corrected score, in slot
+     *    order of decreasing score, equal scores favouring the lower id */
+    for (int j = 0; j < k; ++j) {
+        int64_t best = -1;
+        for (int64_t e = 0; e < E; ++e) {
+            if (taken[e] || !gtaken[e / gsz]) continue;
+            if (best < 0 || cs[e] > cs[best]) best = e;
+        }
+        taken[best] = 1;
+        c->idx[t * k + j] = (uint32_t)best;
+        sel[j] = s[best]; /* the weight uses the uncorrected score */
+    }
+    /* 5. optional renormalisation over the chosen scores (FP32, slot
+     *    order), then the scale, then the cast to the logits dtype */
+    if (c->renorm) {
+        float R = 0.0f;
+        for (int j = 0; j < k; ++j) R += sel[j];
+        for (int j = 0; j < k; ++j) sel[j] = sel[j] / R;
+    }
+    for (int j = 0; j < k; ++j) {
+        sel[j] = sel[j] * c->scale;
+        if (c->w_f32) c->w_f32[t * k + j] = sel[j];
+        store_elem(c->w, c->dt, t * k + j, (double)sel[j]);
+    }
+done:
+    free(sel);
+    free(taken);
+    free(gtaken);
+    free(gscore);
+    free(cs);
+    free(s);
+}
+
+/* logits [T,E] (dt); bias [E] FP32 or NULL; G groups of E/G experts, the
+ * best `selected` groups, then top_k experts inside them.  Writes idx [T,k]
+ * (U32), w [T,k] in the logits dtype, optionally the FP32 weights before the
+ * cast and the corrected scores [T,E].  Returns 0, or -1 when the options
+ * break the section's limits. */
+int oracle_route_sigmoid_grouped(const void* logits, int dt, const float* bias, int64_t T, int64_t E,
+                                 int k, int groups, int selected, int top_two, int renorm, float scale,
+                                 uint32_t* idx, void* w, float* w_f32, float* corr, int nthreads)
+{
+    if (T < 0 || E < 1 || E > 1024 || groups < 1 || groups > 128 || E % groups) return -1;
+    if (selected < 1 || selected > groups) return -1;
+    if (k < 1 || k > 64 || (int64_t)k > (int64_t)selected * (E / groups)) return -1;
+    if (top_two && E / groups < 2) return -1;
+    if (!(scale > 0.0f) || scale == INFINITY) return -1;
+    sroute_ctx c = {logits, dt, bias, E, k, groups, selected, top_two, renorm, scale, idx, w, w_f32, corr};
+    parallel_rows(T, nthreads, sroute_one, &c);
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
 /* Dispatch (ruDNN User Guide, section 5): drop-free, grouped by expert. */
 /* ------------------------------------------------------------------ */
 
