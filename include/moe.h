@@ -83,6 +83,19 @@ typedef struct moe_routing_options {
     int32_t renormalize;
 } moe_routing_options;
 
+/* Group-limited sigmoid routing options (section 10):
+ *   top_k 1..64; groups 1..128 dividing E; selected_groups 1..groups;
+ *   top_k <= selected_groups * (E / groups); group_top_two 0 or 1 (1 needs
+ *   E / groups >= 2); renormalize 0 or 1; scale finite and > 0. */
+typedef struct moe_group_routing_options {
+    int32_t top_k;
+    int32_t groups;
+    int32_t selected_groups;
+    int32_t group_top_two;
+    int32_t renormalize;
+    float scale;
+} moe_group_routing_options;
+
 /* Limits of this implementation (beyond them: MOE_ERR_UNSUPPORTED). */
 #define MOE_MAX_EXPERTS 4096   /* E */
 #define MOE_DIM_MULTIPLE 8     /* H and I of the expert products */
@@ -100,6 +113,30 @@ typedef struct moe_routing_options {
  */
 moe_status moe_route(const moe_tensor* logits, moe_routing_options options,
                      moe_tensor* indices, moe_tensor* weights, void* stream);
+
+/*
+ * moe_route_sigmoid_grouped -- group-limited sigmoid routing (section 10).
+ *   logits  [T,E]  F32 | F16 | BF16, read only; E 1..1024 (beyond:
+ *                  MOE_ERR_UNSUPPORTED).
+ *   bias    [E]    F32 correction, read only, or NULL for none.  It steers
+ *                  the choice only: corrected score c = sigmoid(l) + bias.
+ *   indices [T,k]  U32, written: the experts chosen as follows, in order
+ *                  of decreasing c, ties to the lower id.  The experts form
+ *                  `groups` contiguous groups of E/groups; a group scores
+ *                  its largest c (or, with group_top_two, the sum of its two
+ *                  largest); the selected_groups best groups are kept (ties
+ *                  to the lower group id); the top_k experts of the kept
+ *                  groups by c are chosen.
+ *   weights [T,k]  logits dtype, written: sigmoid(l) of the chosen experts
+ *                  (not c), divided by their FP32 sum when renormalize is
+ *                  set, times scale, rounded to nearest even.
+ * A row with a NaN in c (a NaN logit or bias) gets indices 0..k-1 and NaN
+ * weights.  Bad options: MOE_ERR_INVALID_ARGUMENT; top_k outside its range:
+ * MOE_ERR_TOP_K.
+ */
+moe_status moe_route_sigmoid_grouped(const moe_tensor* logits, const moe_tensor* bias,
+                                     moe_group_routing_options options, moe_tensor* indices,
+                                     moe_tensor* weights, void* stream);
 
 /* Workspace bytes moe_dispatch needs for T tokens, E experts, top_k. */
 size_t moe_dispatch_workspace_bytes(int64_t T, int64_t E, int32_t top_k);
@@ -220,6 +257,19 @@ moe_status moe_forward(const moe_tensor* gate, const moe_tensor* up, const moe_t
                        const moe_tensor* input, const moe_tensor* logits,
                        moe_routing_options options, moe_tensor* output,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * moe_forward_sigmoid_grouped -- moe_forward with group-limited sigmoid
+ * routing (section 10, forward_sigmoid_grouped): moe_route_sigmoid_grouped,
+ * then dispatch, experts and combine as moe_forward does them.
+ *   bias [E] F32 or NULL; options as for moe_route_sigmoid_grouped; the
+ *   other arguments as for moe_forward, with the workspace of
+ *   moe_forward_workspace_bytes(T, H, I, E, options.top_k, dtype).
+ */
+moe_status moe_forward_sigmoid_grouped(const moe_tensor* gate, const moe_tensor* up, const moe_tensor* down,
+                                       const moe_tensor* input, const moe_tensor* logits, const moe_tensor* bias,
+                                       moe_group_routing_options options, moe_tensor* output,
+                                       void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static text of a status code. */
 const char* moe_status_string(moe_status status);

@@ -29,6 +29,7 @@ DIM_MULTIPLE = 8
 # every function include/moe.h declares
 EXPORTS = (
     "moe_route",
+    "moe_route_sigmoid_grouped",
     "moe_dispatch_workspace_bytes",
     "moe_dispatch",
     "moe_experts_workspace_bytes",
@@ -39,6 +40,7 @@ EXPORTS = (
     "moe_combine",
     "moe_forward_workspace_bytes",
     "moe_forward",
+    "moe_forward_sigmoid_grouped",
     "moe_status_string",
 )
 
@@ -54,6 +56,11 @@ class MoeTensor(ctypes.Structure):
 
 class MoeRoutingOptions(ctypes.Structure):
     _fields_ = [("top_k", ctypes.c_int32), ("renormalize", ctypes.c_int32)]
+
+
+class MoeGroupRoutingOptions(ctypes.Structure):
+    _fields_ = [("top_k", ctypes.c_int32), ("groups", ctypes.c_int32), ("selected_groups", ctypes.c_int32),
+                ("group_top_two", ctypes.c_int32), ("renormalize", ctypes.c_int32), ("scale", ctypes.c_float)]
 
 
 class MoeError(RuntimeError):
@@ -80,6 +87,7 @@ def load() -> ctypes.CDLL:
     P = ctypes.POINTER(MoeTensor)
     vp, sz, i64, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int64, ctypes.c_int32
     L.moe_route.argtypes = [P, MoeRoutingOptions, P, P, vp]
+    L.moe_route_sigmoid_grouped.argtypes = [P, P, MoeGroupRoutingOptions, P, P, vp]
     L.moe_dispatch_workspace_bytes.argtypes = [i64, i64, i32]
     L.moe_dispatch_workspace_bytes.restype = sz
     L.moe_dispatch.argtypes = [P, P, i64, P, P, P, P, vp, sz, vp]
@@ -93,10 +101,12 @@ def load() -> ctypes.CDLL:
     L.moe_forward_workspace_bytes.argtypes = [i64, i64, i64, i64, i32, i32]
     L.moe_forward_workspace_bytes.restype = sz
     L.moe_forward.argtypes = [P, P, P, P, P, MoeRoutingOptions, P, vp, sz, vp]
+    L.moe_forward_sigmoid_grouped.argtypes = [P, P, P, P, P, P, MoeGroupRoutingOptions, P, vp, sz, vp]
     L.moe_status_string.argtypes = [i32]
     L.moe_status_string.restype = ctypes.c_char_p
-    for f in ("moe_route", "moe_dispatch", "moe_experts_forward", "moe_experts_gate_up",
-              "moe_experts_gate_up_gathered", "moe_experts_down", "moe_combine", "moe_forward"):
+    for f in ("moe_route", "moe_route_sigmoid_grouped", "moe_dispatch", "moe_experts_forward",
+              "moe_experts_gate_up", "moe_experts_gate_up_gathered", "moe_experts_down", "moe_combine",
+              "moe_forward", "moe_forward_sigmoid_grouped"):
         getattr(L, f).restype = i32
     _lib = L
     return L

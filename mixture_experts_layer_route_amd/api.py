@@ -19,7 +19,7 @@ from dataclasses import dataclass
 import torch
 
 from . import _lib
-from ._lib import MoeError, MoeRoutingOptions, MoeTensor
+from ._lib import MoeError, MoeGroupRoutingOptions, MoeRoutingOptions, MoeTensor
 
 _DTYPES = {
     torch.float32: _lib.MOE_F32,
@@ -72,6 +72,24 @@ class RoutingOptions:
         return MoeRoutingOptions(int(self.top_k), int(bool(self.renormalize)))
 
 
+@dataclass(frozen=True)
+class GroupRoutingOptions:
+    """Group-limited sigmoid routing (section 10): top_k in 1..64; `groups`
+    contiguous groups of E/groups experts (1..128); the `selected_groups` best
+    groups, scored by their largest corrected score or, with group_top_two,
+    the sum of their two largest; renormalize; a finite positive scale."""
+    top_k: int
+    groups: int
+    selected_groups: int
+    group_top_two: bool = True
+    renormalize: bool = True
+    scale: float = 1.0
+
+    def _c(self) -> MoeGroupRoutingOptions:
+        return MoeGroupRoutingOptions(int(self.top_k), int(self.groups), int(self.selected_groups),
+                                      int(bool(self.group_top_two)), int(bool(self.renormalize)), float(self.scale))
+
+
 def _workspace(nbytes: int, device) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
@@ -107,6 +125,23 @@ def route(logits: torch.Tensor, options: RoutingOptions) -> RoutingPlan:
     w = torch.empty((T, max(k, 0)), dtype=logits.dtype, device=logits.device)
     dl, di, dw = _desc(logits), _desc(idx), _desc(w)
     _lib.check(L.moe_route(_ref(dl), options._c(), _ref(di), _ref(dw), _stream(logits.device)), "moe_route")
+    return RoutingPlan(idx, w, E)
+
+
+def route_sigmoid_grouped(logits: torch.Tensor, bias: torch.Tensor | None,
+                          options: GroupRoutingOptions) -> RoutingPlan:
+    """Group-limited sigmoid routing of [T,E] logits with an optional FP32
+    correction bias [E] that steers the choice only (moe_route_sigmoid_grouped)."""
+    L = _lib.load()
+    T, E = logits.shape
+    k = int(options.top_k)
+    idx = torch.empty((T, max(k, 0)), dtype=torch.uint32, device=logits.device)
+    w = torch.empty((T, max(k, 0)), dtype=logits.dtype, device=logits.device)
+    dl, di, dw = _desc(logits), _desc(idx), _desc(w)
+    db = _desc(bias) if bias is not None else None
+    _lib.check(L.moe_route_sigmoid_grouped(_ref(dl), _ref(db) if db is not None else None, options._c(),
+                                           _ref(di), _ref(dw), _stream(logits.device)),
+               "moe_route_sigmoid_grouped")
     return RoutingPlan(idx, w, E)
 
 
@@ -196,6 +231,28 @@ class SwiGluExperts:
         st = L.moe_forward(_ref(g), _ref(u), _ref(d), _ref(dx), _ref(dl), options._c(), _ref(do),
                            ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), _stream(input.device))
         _lib.check(st, "moe_forward")
+        return out
+
+    def forward_sigmoid_grouped(self, input: torch.Tensor, logits: torch.Tensor, bias: torch.Tensor | None,
+                                options: GroupRoutingOptions, workspace: torch.Tensor | None = None,
+                                out: torch.Tensor | None = None) -> torch.Tensor:
+        """The whole local chain with group-limited sigmoid routing (moe_forward_sigmoid_grouped)."""
+        L = _lib.load()
+        T, H = input.shape
+        if out is None:
+            out = torch.empty((T, H), dtype=input.dtype, device=input.device)
+        need = L.moe_forward_workspace_bytes(T, self.hidden, self.intermediate, self.num_experts,
+                                             int(options.top_k), _dtype_code(input))
+        if workspace is None or workspace.numel() < need:
+            workspace = _workspace(need, input.device)
+        dx, dl, do = _desc(input), _desc(logits), _desc(out)
+        db = _desc(bias) if bias is not None else None
+        g, u, d = self._dw
+        st = L.moe_forward_sigmoid_grouped(_ref(g), _ref(u), _ref(d), _ref(dx), _ref(dl),
+                                           _ref(db) if db is not None else None, options._c(), _ref(do),
+                                           ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
+                                           _stream(input.device))
+        _lib.check(st, "moe_forward_sigmoid_grouped")
         return out
 
     def forward_workspace_bytes(self, T: int, top_k: int, dtype: torch.dtype) -> int:

@@ -145,6 +145,39 @@ moe_status check_route(const moe_tensor* logits, moe_routing_options opt, const 
     return MOE_OK;
 }
 
+moe_status check_group_options(moe_group_routing_options o, int64_t E) {
+    if (o.groups < 1 || o.groups > 128 || o.selected_groups < 1 || o.selected_groups > o.groups)
+        return MOE_ERR_INVALID_ARGUMENT;
+    if ((o.group_top_two != 0 && o.group_top_two != 1) || (o.renormalize != 0 && o.renormalize != 1))
+        return MOE_ERR_INVALID_ARGUMENT;
+    if (!(o.scale > 0.0f) || o.scale == INFINITY) return MOE_ERR_INVALID_ARGUMENT;
+    if (E % o.groups) return MOE_ERR_INVALID_ARGUMENT;
+    if (o.group_top_two && E / o.groups < 2) return MOE_ERR_INVALID_ARGUMENT;
+    return MOE_OK;
+}
+
+moe_status check_route_grouped(const moe_tensor* logits, const moe_tensor* bias, moe_group_routing_options opt,
+                               const moe_tensor* indices, const moe_tensor* weights) {
+    MOE_TRY(check_tensor(logits, 2));
+    if (bias) MOE_TRY(check_tensor(bias, 1));
+    MOE_TRY(check_tensor(indices, 2));
+    MOE_TRY(check_tensor(weights, 2));
+    const int64_t T = logits->dims[0], E = logits->dims[1];
+    if (E >= 1) MOE_TRY(check_group_options(opt, E));
+    if (!is_float(logits->dtype)) return MOE_ERR_DTYPE;
+    if (bias && bias->dtype != MOE_F32) return MOE_ERR_DTYPE;
+    if (indices->dtype != MOE_U32) return MOE_ERR_DTYPE;
+    if (weights->dtype != logits->dtype) return MOE_ERR_DTYPE;
+    if (E < 1) return MOE_ERR_SHAPE;
+    if (bias && bias->dims[0] != E) return MOE_ERR_SHAPE;
+    if (opt.top_k < 1 || opt.top_k > 64 || (int64_t)opt.top_k > (int64_t)opt.selected_groups * (E / opt.groups))
+        return MOE_ERR_TOP_K;
+    if (indices->dims[0] != T || indices->dims[1] != opt.top_k) return MOE_ERR_SHAPE;
+    if (weights->dims[0] != T || weights->dims[1] != opt.top_k) return MOE_ERR_SHAPE;
+    if (E > 1024) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
 moe_status check_dispatch(const moe_tensor* input, const moe_tensor* indices, int64_t E,
                           const moe_tensor* dispatched, const moe_tensor* offsets,
                           const moe_tensor* ros, const moe_tensor* tor) {
@@ -242,6 +275,25 @@ moe_status enqueue_route(const moe_tensor* logits, moe_routing_options opt, uint
     return launch_status(launch_route(a, s));
 }
 
+moe_status enqueue_route_grouped(const moe_tensor* logits, const moe_tensor* bias, moe_group_routing_options o,
+                                 uint32_t* idx, void* w, hipStream_t s) {
+    GroupRouteArgs a;
+    a.logits = logits->data;
+    a.ldtype = logits->dtype;
+    a.bias = bias ? (const float*)bias->data : nullptr;
+    a.T = logits->dims[0];
+    a.E = (int)logits->dims[1];
+    a.k = o.top_k;
+    a.groups = o.groups;
+    a.selected = o.selected_groups;
+    a.top_two = o.group_top_two;
+    a.renorm = o.renormalize;
+    a.scale = o.scale;
+    a.idx = idx;
+    a.w = w;
+    return launch_status(launch_route_grouped(a, s));
+}
+
 moe_status enqueue_dispatch(const void* x, int dtype, int64_t T, int64_t H, const uint32_t* idx, int k,
                             int64_t E, void* dispatched, uint32_t* offsets, uint32_t* ros, uint32_t* tor,
                             void* ws, hipStream_t s) {
@@ -329,6 +381,16 @@ moe_status moe_route(const moe_tensor* logits, moe_routing_options options, moe_
     hipStream_t s = (hipStream_t)stream;
     MOE_TRY(check_devices(s, {logits->data, indices->data, weights->data}));
     return enqueue_route(logits, options, (uint32_t*)indices->data, weights->data, s);
+}
+
+moe_status moe_route_sigmoid_grouped(const moe_tensor* logits, const moe_tensor* bias,
+                                     moe_group_routing_options options, moe_tensor* indices, moe_tensor* weights,
+                                     void* stream) {
+    MOE_TRY(check_route_grouped(logits, bias, options, indices, weights));
+    if (logits->dims[0] == 0) return MOE_OK;
+    hipStream_t s = (hipStream_t)stream;
+    MOE_TRY(check_devices(s, {logits->data, bias ? bias->data : logits->data, indices->data, weights->data}));
+    return enqueue_route_grouped(logits, bias, options, (uint32_t*)indices->data, weights->data, s);
 }
 
 size_t moe_dispatch_workspace_bytes(int64_t T, int64_t E, int32_t top_k) {
@@ -470,31 +532,32 @@ size_t moe_forward_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, i
     return forward_ws(T, H, I, E, top_k, dtype).total;
 }
 
-moe_status moe_forward(const moe_tensor* gate, const moe_tensor* up, const moe_tensor* down,
-                       const moe_tensor* input, const moe_tensor* logits, moe_routing_options options,
-                       moe_tensor* output, void* workspace, size_t workspace_bytes, void* stream) {
-    MOE_TRY(check_weights(gate, up, down));
-    MOE_TRY(check_tensor(input, 2));
-    MOE_TRY(check_tensor(logits, 2));
-    MOE_TRY(check_tensor(output, 2));
-    if (!is_float(logits->dtype)) return MOE_ERR_DTYPE;
-    if (input->dtype != gate->dtype || output->dtype != gate->dtype) return MOE_ERR_DTYPE;
+}  // extern "C"
+
+namespace {
+// The chain after the routing options were checked: shapes, limits and
+// workspace, then route (through `route`, which writes indices and weights
+// into the workspace), mapping-only dispatch, experts reading the tokens in
+// place, combine.
+template <typename RouteFn>
+moe_status forward_chain(const moe_tensor* gate, const moe_tensor* up, const moe_tensor* down,
+                         const moe_tensor* input, const moe_tensor* logits, const moe_tensor* bias, int64_t k,
+                         moe_tensor* output, void* workspace, size_t workspace_bytes, void* stream,
+                         RouteFn route) {
     const int64_t E = gate->dims[0], I = gate->dims[1], H = gate->dims[2];
     const int64_t T = input->dims[0];
     if (input->dims[1] != H) return MOE_ERR_SHAPE;
     if (logits->dims[0] != T || logits->dims[1] != E) return MOE_ERR_SHAPE;
     if (output->dims[0] != T || output->dims[1] != H) return MOE_ERR_SHAPE;
-    if (options.top_k < 1 || options.top_k > E) return MOE_ERR_TOP_K;
-    if (options.renormalize != 0 && options.renormalize != 1) return MOE_ERR_INVALID_ARGUMENT;
-    const int64_t k = options.top_k, N = T * k;
+    const int64_t N = T * k;
     if (N >= (int64_t)0x7FFFFFFF) return MOE_ERR_UNSUPPORTED;
     MOE_TRY(check_gemm_limits(E, H, I, N, {gate->data, up->data, down->data, input->data, output->data}));
     const ForwardWs l = forward_ws(T, H, I, E, k, gate->dtype);
     if (!workspace || workspace_bytes < l.total) return MOE_ERR_WORKSPACE;
     if (T == 0) return MOE_OK;
     hipStream_t s = (hipStream_t)stream;
-    MOE_TRY(check_devices(s, {gate->data, up->data, down->data, input->data, logits->data, output->data,
-                              workspace}));
+    MOE_TRY(check_devices(s, {gate->data, up->data, down->data, input->data, logits->data,
+                              bias ? bias->data : logits->data, output->data, workspace}));
     char* ws = (char*)workspace;
     uint32_t* idx = (uint32_t*)(ws + l.idx);
     void* w = ws + l.w;
@@ -502,7 +565,7 @@ moe_status moe_forward(const moe_tensor* gate, const moe_tensor* up, const moe_t
     uint32_t* ros = (uint32_t*)(ws + l.ros);
     uint32_t* tor = (uint32_t*)(ws + l.tor);
     void* y = ws + l.y;
-    MOE_TRY(enqueue_route(logits, options, idx, w, s));
+    MOE_TRY(route(idx, w, s));
     MOE_TRY(enqueue_dispatch(input->data, input->dtype, T, H, idx, (int)k, E, nullptr, offsets, ros, tor,
                              ws + l.dws, s));
     // the gate/up products read the token rows through token_of_row, so the
@@ -510,6 +573,53 @@ moe_status moe_forward(const moe_tensor* gate, const moe_tensor* up, const moe_t
     MOE_TRY(enqueue_experts(gate->dtype, E, H, I, gate->data, up->data, down->data, input->data, tor, T, N,
                             offsets, y, nullptr, ws + l.ews, s, kBoth));
     return enqueue_combine(y, input->dtype, N, ros, w, logits->dtype, T, (int)k, H, output->data, s);
+}
+
+moe_status check_forward_tensors(const moe_tensor* gate, const moe_tensor* up, const moe_tensor* down,
+                                 const moe_tensor* input, const moe_tensor* logits, const moe_tensor* output) {
+    MOE_TRY(check_weights(gate, up, down));
+    MOE_TRY(check_tensor(input, 2));
+    MOE_TRY(check_tensor(logits, 2));
+    MOE_TRY(check_tensor(output, 2));
+    if (!is_float(logits->dtype)) return MOE_ERR_DTYPE;
+    if (input->dtype != gate->dtype || output->dtype != gate->dtype) return MOE_ERR_DTYPE;
+    return MOE_OK;
+}
+}  // namespace
+
+extern "C" {
+
+moe_status moe_forward(const moe_tensor* gate, const moe_tensor* up, const moe_tensor* down,
+                       const moe_tensor* input, const moe_tensor* logits, moe_routing_options options,
+                       moe_tensor* output, void* workspace, size_t workspace_bytes, void* stream) {
+    MOE_TRY(check_forward_tensors(gate, up, down, input, logits, output));
+    const int64_t E = gate->dims[0];
+    if (logits->dims[1] == E && (options.top_k < 1 || options.top_k > E)) return MOE_ERR_TOP_K;
+    if (options.renormalize != 0 && options.renormalize != 1) return MOE_ERR_INVALID_ARGUMENT;
+    return forward_chain(gate, up, down, input, logits, nullptr, options.top_k, output, workspace, workspace_bytes,
+                         stream, [&](uint32_t* idx, void* w, hipStream_t s) {
+                             return enqueue_route(logits, options, idx, w, s);
+                         });
+}
+
+moe_status moe_forward_sigmoid_grouped(const moe_tensor* gate, const moe_tensor* up, const moe_tensor* down,
+                                       const moe_tensor* input, const moe_tensor* logits, const moe_tensor* bias,
+                                       moe_group_routing_options options, moe_tensor* output,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+    MOE_TRY(check_forward_tensors(gate, up, down, input, logits, output));
+    if (bias) MOE_TRY(check_tensor(bias, 1));
+    const int64_t E = gate->dims[0];
+    MOE_TRY(check_group_options(options, E));
+    if (bias && bias->dtype != MOE_F32) return MOE_ERR_DTYPE;
+    if (bias && bias->dims[0] != E) return MOE_ERR_SHAPE;
+    if (options.top_k < 1 || options.top_k > 64 ||
+        (int64_t)options.top_k > (int64_t)options.selected_groups * (E / options.groups))
+        return MOE_ERR_TOP_K;
+    if (E > 1024) return MOE_ERR_UNSUPPORTED;
+    return forward_chain(gate, up, down, input, logits, bias, options.top_k, output, workspace, workspace_bytes,
+                         stream, [&](uint32_t* idx, void* w, hipStream_t s) {
+                             return enqueue_route_grouped(logits, bias, options, idx, w, s);
+                         });
 }
 
 }  // extern "C"

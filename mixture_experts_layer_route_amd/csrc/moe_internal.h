@@ -102,6 +102,18 @@ struct RouteArgs {
 };
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
 
+struct GroupRouteArgs {
+    const void* logits;
+    int ldtype;         // moe_dtype of logits and weights
+    const float* bias;  // [E] FP32 or null
+    int64_t T;
+    int E, k, groups, selected, top_two, renorm;
+    float scale;
+    uint32_t* idx;
+    void* w;
+};
+hipError_t launch_route_grouped(const GroupRouteArgs& a, hipStream_t s);
+
 struct DispatchArgs {
     const void* x;
     int64_t T;

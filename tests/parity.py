@@ -114,3 +114,58 @@ def compare_dispatch(gpu: dict, o_offsets, o_ros, o_tor, o_rows, x_bits: np.ndar
         assert np.array_equal(np.sort(tor[a:b]), np.sort(otor[a:b])), f"token set of expert {e} differs"
     rows = gpu["rows"][:n]
     assert np.array_equal(rows, x_bits[tor]), "dispatched rows must be bit copies of their tokens"
+
+
+def compare_grouped_routing(gpu_idx: np.ndarray, gpu_w: np.ndarray, logits_bits: np.ndarray, ldt: str,
+                            bias: np.ndarray | None, top_k: int, groups: int, selected: int, top_two: bool,
+                            renorm: bool, scale: float, nthreads: int | None = None):
+    """Group-limited sigmoid routing against the oracle, with the near-tie
+    rule applied to the corrected scores: a slot may differ where the two
+    experts' corrected scores are within 1e-6 (unless logit and bias are
+    both identical, an exact tie), and a whole row may differ where the
+    oracle's group scores at the selection boundary are within 1e-6.
+    Returns (oracle result, near-tie token mask)."""
+    o_idx, o_w, _, corr = oracle.route_sigmoid_grouped(logits_bits, ldt, bias, top_k, groups, selected, top_two,
+                                                       renorm, scale, nthreads)
+    lg = oracle.widen(logits_bits, ldt)
+    T, E = corr.shape
+    k, G, gsz = top_k, groups, E // groups
+    b = np.zeros(E, np.float32) if bias is None else bias.astype(np.float32)
+    gi, oi = gpu_idx.astype(np.int64), o_idx.astype(np.int64)
+    assert gi.shape == (T, k)
+    nan_rows = np.isnan(corr).any(axis=1)
+    gw, ow = values(gpu_w, ldt), oracle.widen(o_w, ldt)
+    if nan_rows.any():
+        assert (gi[nan_rows] == np.arange(k)[None, :]).all(), "NaN rows must select experts 0..k-1"
+        assert np.isnan(gw[nan_rows]).all(), "NaN rows must keep NaN weights"
+    fin = ~nan_rows
+    assert not np.isnan(gw[fin]).any(), "finite rows must have finite weights"
+    assert ((gi >= 0) & (gi < E)).all()
+    assert (np.diff(np.sort(gi, axis=1), axis=1) > 0).all(), "indices of a token must be distinct"
+    # the oracle's group scores, to find rows whose group choice is a near tie
+    cf = np.where(np.isnan(corr), -np.inf, corr).astype(np.float64)
+    top = -np.sort(-cf.reshape(T, G, gsz), axis=2)
+    gsc = top[:, :, 0] + (top[:, :, 1] if top_two else 0.0)
+    gs_sorted = -np.sort(-gsc, axis=1)
+    near_group = np.zeros(T, bool)
+    if selected < G:
+        # an exact tie (gap 0) comes from identical inputs and must resolve
+        # to the lower group id on both sides, so it is not exempt
+        ggap = gs_sorted[:, selected - 1] - gs_sorted[:, selected]
+        near_group = (ggap > 0) & (ggap < NEAR_TIE)
+    near = near_group & fin
+    mism = (gi != oi) & fin[:, None] & ~near_group[:, None]
+    if mism.any():
+        t_ids, j_ids = np.nonzero(mism)
+        a, bb = oi[t_ids, j_ids], gi[t_ids, j_ids]
+        gap = np.abs(cf[t_ids, a] - cf[t_ids, bb])
+        exact = (lg[t_ids, a] == lg[t_ids, bb]) & (b[a] == b[bb])
+        bad = (gap >= NEAR_TIE) | exact
+        assert not bad.any(), (
+            f"index mismatch outside the near-tie rule at token {t_ids[bad][0]} slot {j_ids[bad][0]}: "
+            f"oracle {a[bad][0]} gpu {bb[bad][0]} gap {gap[bad][0]:.3g}")
+        near[t_ids] = True
+    same = fin & ~near
+    assert_close(gw[same], ow[same], ldt, "grouped routing weights")
+    assert near.mean() < 0.01, f"too many near-tie tokens: {int(near.sum())}"
+    return (o_idx, o_w), near

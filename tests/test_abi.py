@@ -242,3 +242,58 @@ def test_python_layer_rejects_non_contiguous():
     x = torch.zeros(4, 6)[:, ::2]
     with pytest.raises(moe.MoeError):
         moe.api._desc(x)
+
+
+def test_route_sigmoid_grouped_validation(L):
+    from mixture_experts_layer_route_amd._lib import MoeGroupRoutingOptions
+    T, E = 16, 64
+    lg = raw_tensor(FAKE, BF16, (T, E))
+    bias = raw_tensor(FAKE, F32, (E,))
+
+    def r(k=8, G=8, m=4, two=1, renorm=1, scale=2.5, lg=lg, bias=bias, idx=None, w=None):
+        idx = idx or raw_tensor(FAKE, U32, (T, k))
+        w = w or raw_tensor(FAKE, BF16, (T, k))
+        o = MoeGroupRoutingOptions(k, G, m, two, renorm, scale)
+        return L.moe_route_sigmoid_grouped(ctypes.byref(lg), ctypes.byref(bias) if bias is not None else None, o,
+                                           ctypes.byref(idx), ctypes.byref(w), None)
+
+    assert r(G=0) == INVALID and r(G=129) == INVALID and r(G=6) == INVALID   # 6 does not divide 64
+    assert r(m=0) == INVALID and r(m=9) == INVALID
+    assert r(two=2) == INVALID and r(renorm=2) == INVALID
+    assert r(G=64, m=8, two=1) == INVALID                                    # one expert per group
+    assert r(scale=0.0) == INVALID and r(scale=float("inf")) == INVALID and r(scale=float("nan")) == INVALID
+    assert r(bias=raw_tensor(FAKE, F16, (E,))) == DTYPE
+    assert r(lg=raw_tensor(FAKE, U32, (T, E))) == DTYPE
+    assert r(w=raw_tensor(FAKE, F32, (T, 8))) == DTYPE                      # weights follow the logits dtype
+    assert r(bias=raw_tensor(FAKE, F32, (E + 1,))) == SHAPE
+    assert r(k=0) == TOPK and r(k=65) == TOPK
+    assert r(k=33, m=4) == TOPK                                              # only 4 x 8 experts are kept
+    assert r(idx=raw_tensor(FAKE, U32, (T, 7))) == SHAPE
+    assert r(lg=raw_tensor(FAKE, BF16, (T, 2048)), bias=None) == UNSUPPORTED
+    assert r() == DEVICE and r(bias=None) == DEVICE
+
+
+def test_forward_sigmoid_grouped_validation(L):
+    from mixture_experts_layer_route_amd._lib import MoeGroupRoutingOptions
+    E, I, H, T, k = 16, 64, 32, 8, 2
+    g = raw_tensor(FAKE, BF16, (E, I, H))
+    u = raw_tensor(FAKE, BF16, (E, I, H))
+    d = raw_tensor(FAKE, BF16, (E, H, I))
+    x = raw_tensor(FAKE, BF16, (T, H))
+    lg = raw_tensor(FAKE, F32, (T, E))
+    out = raw_tensor(FAKE, BF16, (T, H))
+    ws = L.moe_forward_workspace_bytes(T, H, I, E, k, BF16)
+
+    def f(k=k, G=4, m=2, bias=None, lg=lg, wsb=ws):
+        o = MoeGroupRoutingOptions(k, G, m, 1, 1, 1.0)
+        return L.moe_forward_sigmoid_grouped(ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), ctypes.byref(x),
+                                             ctypes.byref(lg), ctypes.byref(bias) if bias is not None else None, o,
+                                             ctypes.byref(out), ctypes.c_void_p(FAKE), wsb, None)
+
+    assert f(G=3) == INVALID
+    assert f(k=9, m=2) == TOPK
+    assert f(bias=raw_tensor(FAKE, F32, (E - 1,))) == SHAPE
+    assert f(bias=raw_tensor(FAKE, BF16, (E,))) == DTYPE
+    assert f(lg=raw_tensor(FAKE, F32, (T, E + 4))) == SHAPE
+    assert f(wsb=ws - 1) == WORKSPACE
+    assert f() == DEVICE and f(bias=raw_tensor(FAKE, F32, (E,))) == DEVICE

@@ -15,7 +15,8 @@ import torch
 import mixture_experts_layer_route_amd as moe
 import moe_synth as S
 import oracle
-from parity import TOL, assert_close, compare_dispatch, compare_routing, host_bits, values
+from parity import (TOL, assert_close, compare_dispatch, compare_grouped_routing, compare_routing, host_bits,
+                    values)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -388,3 +389,89 @@ def test_gate_up_and_down_halves_equal_experts_forward(cfg):
     torch.cuda.synchronize()
     assert torch.equal(whole.view(torch.int16), y.view(torch.int16))
     assert_close(values(h, cfg.dtype), oracle.widen(h_ref, cfg.dtype), cfg.dtype, "activation h")
+
+
+# ------------------------------------------------------------------ group-limited sigmoid routing
+def grouped_case(name, T, E, dtype, k, G, m, top_two, renorm, scale, seed, bias="normal", ties=False,
+                 nan_rows=False):
+    return dict(name=name, T=T, E=E, dtype=dtype, k=k, G=G, m=m, top_two=top_two, renorm=renorm, scale=scale,
+                seed=seed, bias=bias, ties=ties, nan_rows=nan_rows)
+
+
+GROUPED_CASES = [
+    # the skewed workload's routing shape: 256 experts in 8 groups, the best 4
+    # by their top two corrected scores, top-8, renormalised, scaled 2.5
+    grouped_case("ds_bf16", 2048, 256, "bf16", 8, 8, 4, True, True, 2.5, 61),
+    grouped_case("ds_f32", 1024, 256, "f32", 8, 8, 4, True, True, 2.5, 62),
+    grouped_case("ds_f16_nobias", 1024, 256, "f16", 8, 8, 4, True, False, 1.0, 63, bias=None),
+    grouped_case("one_group_f32", 512, 64, "f32", 6, 1, 1, False, True, 1.0, 64),
+    grouped_case("max_shape_bf16", 256, 1024, "bf16", 64, 128, 32, True, True, 2.0, 65),
+    grouped_case("small_groups_f32", 700, 96, "f32", 5, 32, 3, False, False, 0.5, 66),
+    grouped_case("ties_f32", 2000, 16, "f32", 4, 4, 2, True, True, 1.0, 67, ties=True),
+    grouped_case("ties_max_bf16", 2000, 32, "bf16", 3, 8, 2, False, True, 1.0, 68, ties=True),
+    grouped_case("nan_rows_bf16", 600, 64, "bf16", 4, 8, 2, True, True, 1.0, 69, nan_rows=True),
+    grouped_case("odd_E_f32", 300, 40, "f32", 7, 5, 3, True, True, 1.5, 70),
+]
+
+
+def make_grouped_inputs(c):
+    g = torch.Generator().manual_seed(c["seed"])
+    if c["ties"]:
+        lg = torch.randint(-1, 2, (c["T"], c["E"]), generator=g).float()
+        bias = torch.tensor([0.0, 0.25, -0.25])[torch.randint(0, 3, (c["E"],), generator=g)]
+    else:
+        lg = torch.randn(c["T"], c["E"], generator=g)
+        bias = torch.randn(c["E"], generator=g) * 0.3
+    if c["nan_rows"]:
+        rows = torch.randperm(c["T"], generator=g)[: c["T"] // 10]
+        lg[rows[: len(rows) // 2], 3] = float("nan")
+        lg[rows[len(rows) // 2:], :] = float("inf")  # sigmoid 1 everywhere: ties, lower ids
+    lg = lg.to(S.TORCH_DT[c["dtype"]])
+    return lg, (None if c["bias"] is None else bias.float().contiguous())
+
+
+@pytest.mark.parametrize("c", GROUPED_CASES, ids=lambda c: c["name"])
+def test_route_sigmoid_grouped_parity(c):
+    log(f"grouped routing {c['name']}")
+    lg, bias = make_grouped_inputs(c)
+    opts = moe.GroupRoutingOptions(c["k"], c["G"], c["m"], c["top_two"], c["renorm"], c["scale"])
+    plan = moe.route_sigmoid_grouped(lg.to(DEV), None if bias is None else bias.to(DEV), opts)
+    torch.cuda.synchronize()
+    compare_grouped_routing(host_bits(plan.expert_indices()), plan.weights().cpu(), host_bits(lg), c["dtype"],
+                            None if bias is None else bias.numpy(), c["k"], c["G"], c["m"], c["top_two"],
+                            c["renorm"], c["scale"], NTHREADS)
+
+
+@pytest.mark.parametrize("cfg", [
+    S.small_config("grouped_fwd_bf16", T=700, H=128, I=192, E=32, top_k=4, dtype="bf16", seed=71),
+    S.small_config("grouped_fwd_f32", T=200, H=64, I=96, E=16, top_k=3, dtype="f32", seed=72),
+], ids=lambda c: c.name)
+def test_forward_sigmoid_grouped_parity(cfg):
+    """The chain with group-limited sigmoid routing against the oracle's
+    routing, dispatch, experts and combine, and bitwise against the split
+    calls fed by the same routing."""
+    log(f"grouped forward {cfg.name}")
+    x, lg = S.make_tokens(cfg)
+    W = S.make_weights(cfg)
+    bias = (torch.randn(cfg.E, generator=torch.Generator().manual_seed(cfg.seed)) * 0.3).float()
+    G, m = 4, 2
+    opts = moe.GroupRoutingOptions(cfg.top_k, G, m, True, True, 2.5)
+    ex = moe.SwiGluExperts(*[w.to(DEV) for w in W])
+    gx, glg, gb = x.to(DEV), lg.to(DEV), bias.to(DEV)
+    out = ex.forward_sigmoid_grouped(gx, glg, gb, opts)
+    plan = moe.route_sigmoid_grouped(glg, gb, opts)
+    d = plan.dispatch(gx)
+    split = d.combine(ex.forward_dispatched(d))
+    torch.cuda.synchronize()
+    bits = torch.int32 if out.dtype == torch.float32 else torch.int16
+    assert torch.equal(out.view(bits), split.view(bits))
+    (o_idx, o_w), near = compare_grouped_routing(host_bits(plan.expert_indices()), plan.weights().cpu(),
+                                                 host_bits(lg), cfg.logits_dtype, bias.numpy(), cfg.top_k, G, m,
+                                                 True, True, 2.5, NTHREADS)
+    Wb = [host_bits(w) for w in W]
+    xb = host_bits(x)
+    offsets, ros, _, rows = oracle.dispatch(o_idx, cfg.E, xb, cfg.dtype)
+    Y = oracle.experts(*Wb, cfg.dtype, rows, offsets, cfg.E, cfg.H, cfg.I, nthreads=NTHREADS)
+    ref = oracle.combine(Y, cfg.dtype, ros, o_w, cfg.logits_dtype, cfg.T, cfg.top_k, cfg.H, NTHREADS)
+    assert_close(values(out, cfg.dtype), oracle.widen(ref, cfg.dtype), cfg.dtype, f"grouped forward {cfg.name}",
+                 rows_mask=~near)
