@@ -13,7 +13,9 @@ inputs and weights already resident in HBM.  Prints one JSON line:
                stream it runs on, against the MI355X dense peak;
   stages_ms    per-stage times of the split calls (same kernels);
   cpu_baseline the CPU oracle timed on a bounded sample of the same workload;
-  secondary    the decode and skewed workloads, same measurement.
+  secondary    the decode and skewed workloads, same measurement;
+  grouped_routing  the skewed workload's forward with group-limited sigmoid
+               routing, and that routing kernel's HBM roofline.
 The pages publish no throughput for this chain, so vs_baseline is null.
 """
 from __future__ import annotations
@@ -48,6 +50,8 @@ def parse():
                     help="comma-separated extra workloads to measure ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--grouped", default="skewed_bf16",
+                    help="workload for the forward with group-limited sigmoid routing ('' to skip)")
     ap.add_argument("--only-forward", action="store_true",
                     help="time only the fused forward (for profiler runs)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -222,6 +226,56 @@ def cpu_baseline(name: str, target_s: float) -> dict:
                       f"combine), {dt:.1f} s"}
 
 
+def measure_grouped(name: str, steps: int, warmup: int) -> dict:
+    """The forward with group-limited sigmoid routing on workload `name`
+    (8 groups, the best 4 by their top-two corrected scores, renormalised,
+    scale 2.5, a small seeded FP32 correction bias), and the routing kernel
+    alone, both timed back to back with HIP events."""
+    import torch
+
+    import mixture_experts_layer_route_amd as moe
+    import moe_synth as S
+
+    cfg = S.CONFIGS[name]
+    dev = "cuda:0"
+    x, lg = S.make_tokens(cfg, device=dev)
+    W = S.make_weights(cfg, device=dev)
+    ex = moe.SwiGluExperts(*W)
+    bias = (torch.randn(cfg.E, generator=torch.Generator().manual_seed(cfg.seed)) * 0.1).float().to(dev)
+    opts = moe.GroupRoutingOptions(cfg.top_k, 8, 4, True, True, 2.5)
+    ws = torch.empty(ex.forward_workspace_bytes(cfg.T, cfg.top_k, x.dtype), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(x)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for _ in range(warmup):
+        ex.forward_sigmoid_grouped(x, lg, bias, opts, ws, out)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        ex.forward_sigmoid_grouped(x, lg, bias, opts, ws, out)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    reps = max(steps, 20)
+    for _ in range(warmup):
+        moe.route_sigmoid_grouped(lg, bias, opts)
+    ev[0].record()
+    for _ in range(reps):
+        plan = moe.route_sigmoid_grouped(lg, bias, opts)
+    ev[1].record()
+    torch.cuda.synchronize()
+    route_ms = ev[0].elapsed_time(ev[1]) / reps
+    ls = 2 if cfg.logits_dtype in ("bf16", "f16") else 4
+    nbytes = cfg.T * cfg.E * ls + cfg.E * 4 + cfg.T * cfg.top_k * (4 + ls)
+    ach = nbytes / (route_ms * 1e-3) / 1e9
+    idx = plan.expert_indices().view(torch.int32).long()
+    return {"workload": name, "routing": "group-limited sigmoid: 8 groups, best 4 by top-two, renormalised, scale 2.5",
+            "tokens_per_s": round(cfg.T / (ms * 1e-3), 1), "ms_per_step": round(ms, 4),
+            "tflops": round(cfg.flops() / (ms * 1e-3) / 1e12, 2),
+            "active_experts": int(torch.unique(idx).numel()),
+            "route_roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                               "frac": round(ach / PEAK_HBM_GBS, 4), "kernel": "route_grouped_kernel",
+                               "avg_launch_ms": round(route_ms, 4), "bytes_per_launch": nbytes}}
+
+
 def summary(res: dict) -> dict:
     cfg = res["cfg"]
     d = {"workload": res["workload"], "tokens_per_s": round(res["tokens_per_s"], 1),
@@ -287,6 +341,9 @@ def main():
             line["secondary"][s] = summary(r)
             del r
         torch.cuda.empty_cache()
+        if args.grouped:
+            line["grouped_routing"] = measure_grouped(args.grouped, args.steps, args.warmup)
+            torch.cuda.empty_cache()
         if not args.no_cpu_baseline:
             line["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_seconds)
     if args.calibrate_copy_mib > 0:
