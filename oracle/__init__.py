@@ -12,6 +12,10 @@ drop-free dispatch grouped by expert, SwiGLU experts
 Expert and combine sums are taken in binary64 (tiny-llm deep dive 5, the
 RMSNorm block's reason for wide accumulators).
 
+The first-order training functions follow the RUDA ruDNN library guide,
+section 12: router weights of a fixed selection and their logits gradient,
+the combine, expert and dispatch backward passes.
+
 Arrays are numpy: F32 data as ``float32``; F16 and BF16 data as their raw
 ``uint16`` bit patterns; indices and mappings as ``uint32``.
 """
@@ -74,6 +78,20 @@ def lib():
         L.oracle_experts.argtypes = [vp, vp, vp, i32, vp, vp, i64, i64, i64, vp, vp, i32]
         L.oracle_combine.restype = i32
         L.oracle_combine.argtypes = [vp, i32, vp, vp, i32, i64, i32, i64, vp, i32]
+        f32 = ctypes.c_float
+        L.oracle_router_weights.restype = i32
+        L.oracle_router_weights.argtypes = [vp, i32, vp, i64, i64, i32, i32, i32, f32, vp, i32]
+        L.oracle_router_backward.restype = i32
+        L.oracle_router_backward.argtypes = [vp, i32, vp, vp, i64, i64, i32, i32, i32, f32, vp, i32]
+        L.oracle_combine_backward.restype = i32
+        L.oracle_combine_backward.argtypes = [vp, i32, vp, vp, i32, vp, i64, i32, i64, i64, vp, vp, i32]
+        L.oracle_dispatch_backward.restype = i32
+        L.oracle_dispatch_backward.argtypes = [vp, i32, vp, i64, i32, i64, i64, vp, i32]
+        L.oracle_experts_train_forward.restype = i32
+        L.oracle_experts_train_forward.argtypes = [vp, vp, vp, i32, vp, vp, i64, i64, i64, vp, vp, vp, vp, i32]
+        L.oracle_experts_backward.restype = i32
+        L.oracle_experts_backward.argtypes = [vp, vp, vp, i32, vp, vp, i64, i64, i64, vp, vp, vp, vp, vp,
+                                              vp, vp, vp, i32]
         _lib = L
     return _lib
 
@@ -267,3 +285,160 @@ def forward(x: np.ndarray, logits: np.ndarray, gate, up, down, dt: str, ldt: str
     return {"indices": idx, "weights": w, "weights_f32": w32, "offsets": offsets,
             "row_of_slot": ros, "token_of_row": tor, "dispatched": rows, "h": h, "Y": Y,
             "output": out}
+
+
+# ---------------------------------------------------------------- training
+SCORING = {"softmax": 0, "sigmoid": 1}
+
+
+def _indices_i64(indices: np.ndarray) -> np.ndarray:
+    """U32, I32 or I64 indices as int64 values (a U32 index keeps its value)."""
+    a = np.asarray(indices)
+    if a.dtype not in (np.uint32, np.int32, np.int64):
+        raise TypeError(f"indices must be u32, i32 or i64, got {a.dtype}")
+    return np.ascontiguousarray(a.astype(np.int64))
+
+
+def router_weights(logits: np.ndarray, dt: str, indices: np.ndarray, scoring: str, renormalize: bool,
+                   scale: float, nthreads: int | None = None) -> np.ndarray:
+    """FP32 [T,k] weights of a fixed selection (RUDA ruDNN guide, section 12)."""
+    lg = _check(logits, dt, "logits")
+    T, E = lg.shape
+    idx = _indices_i64(indices)
+    k = idx.shape[1]
+    w = np.empty((T, k), dtype=np.float32)
+    rc = lib().oracle_router_weights(_ptr(lg), DT[dt], _ptr(idx), T, E, k, SCORING[scoring],
+                                     int(bool(renormalize)), float(scale), _ptr(w), nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_router_weights: bad arguments")
+    return w
+
+
+def router_backward(logits: np.ndarray, dt: str, indices: np.ndarray, grad_weights: np.ndarray, scoring: str,
+                    renormalize: bool, scale: float, nthreads: int | None = None) -> np.ndarray:
+    """[T,E] logits gradient in the logits dtype for FP32 weight gradients [T,k]."""
+    lg = _check(logits, dt, "logits")
+    T, E = lg.shape
+    idx = _indices_i64(indices)
+    k = idx.shape[1]
+    gw = np.ascontiguousarray(grad_weights, dtype=np.float32)
+    if gw.shape != (T, k):
+        raise ValueError("grad_weights must be [T,k]")
+    dl = np.empty((T, E), dtype=storage_dtype(dt))
+    rc = lib().oracle_router_backward(_ptr(lg), DT[dt], _ptr(idx), _ptr(gw), T, E, k, SCORING[scoring],
+                                      int(bool(renormalize)), float(scale), _ptr(dl), nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_router_backward: bad arguments")
+    return dl
+
+
+def combine_backward(Y: np.ndarray, dt: str, row_of_slot: np.ndarray, weights: np.ndarray, wdt: str,
+                     grad_output: np.ndarray, T: int, k: int, H: int, nthreads: int | None = None):
+    """Returns (dY [N,H] in the expert dtype, dweights [T,k] FP32)."""
+    N = Y.shape[0]
+    Ys = _check(Y, dt, "Y") if Y.size else np.empty((1, H), dtype=storage_dtype(dt))
+    ros = np.ascontiguousarray(row_of_slot, dtype=np.uint32)
+    w = _check(weights, wdt, "weights")
+    g = _check(grad_output, dt, "grad_output")
+    dY = np.empty((max(N, 1), H), dtype=storage_dtype(dt))
+    dw = np.empty((T, k), dtype=np.float32)
+    rc = lib().oracle_combine_backward(_ptr(Ys), DT[dt], _ptr(ros), _ptr(w), DT[wdt], _ptr(g), T, k, H, N,
+                                       _ptr(dY), _ptr(dw), nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_combine_backward: bad arguments")
+    return dY[:N], dw
+
+
+def dispatch_backward(dinput: np.ndarray, dt: str, row_of_slot: np.ndarray, T: int, k: int, H: int,
+                      nthreads: int | None = None) -> np.ndarray:
+    """dx [T,H]: each token's dispatched-row gradients summed, weights not applied."""
+    N = dinput.shape[0]
+    d = _check(dinput, dt, "dinput") if dinput.size else np.empty((1, H), dtype=storage_dtype(dt))
+    ros = np.ascontiguousarray(row_of_slot, dtype=np.uint32)
+    dx = np.empty((T, H), dtype=storage_dtype(dt))
+    rc = lib().oracle_dispatch_backward(_ptr(d), DT[dt], _ptr(ros), T, k, H, N, _ptr(dx),
+                                        nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_dispatch_backward: bad arguments")
+    return dx
+
+
+def experts_train_forward(gate, up, down, dt: str, rows: np.ndarray, offsets: np.ndarray, E: int, H: int, I: int,
+                          nthreads: int | None = None) -> dict:
+    """The experts' forward plus what their backward needs: the FP32
+    pre-activations g = gate x, u = up x and the stored activation h."""
+    keep: list = []
+    gp = _expert_ptrs(gate, E, dt, keep)
+    up_ = _expert_ptrs(up, E, dt, keep)
+    dp = _expert_ptrs(down, E, dt, keep)
+    r = _check(rows, dt, "rows") if rows.size else np.empty((1, H), dtype=storage_dtype(dt))
+    off = np.ascontiguousarray(offsets, dtype=np.uint32)
+    n = int(off[E])
+    m = max(n, 1)
+    out = np.empty((m, H), dtype=storage_dtype(dt))
+    h = np.empty((m, I), dtype=storage_dtype(dt))
+    g = np.empty((m, I), dtype=np.float32)
+    u = np.empty((m, I), dtype=np.float32)
+    rc = lib().oracle_experts_train_forward(ctypes.cast(gp, ctypes.c_void_p), ctypes.cast(up_, ctypes.c_void_p),
+                                            ctypes.cast(dp, ctypes.c_void_p), DT[dt], _ptr(r), _ptr(off),
+                                            E, H, I, _ptr(out), _ptr(h), _ptr(g), _ptr(u),
+                                            nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_experts_train_forward: a row's expert has no weights")
+    return {"output": out[:n], "h": h[:n], "g": g[:n], "u": u[:n]}
+
+
+def experts_backward(gate, up, down, dt: str, rows: np.ndarray, offsets: np.ndarray, E: int, H: int, I: int,
+                     g: np.ndarray, u: np.ndarray, h: np.ndarray, dY: np.ndarray, nthreads: int | None = None):
+    """Returns (dinput [N,H] in the expert dtype, dgate [E,I,H], dup [E,I,H], ddown [E,H,I] FP32)."""
+    keep: list = []
+    gp = _expert_ptrs(gate, E, dt, keep)
+    up_ = _expert_ptrs(up, E, dt, keep)
+    dp = _expert_ptrs(down, E, dt, keep)
+    off = np.ascontiguousarray(offsets, dtype=np.uint32)
+    n = int(off[E])
+    m = max(n, 1)
+
+    def pad(a, cols, storage):
+        a = np.ascontiguousarray(a, dtype=storage) if storage == np.float32 else _check(a, dt, "array")
+        return a if a.size else np.zeros((1, cols), dtype=storage)
+
+    r = pad(rows, H, storage_dtype(dt))
+    g_ = pad(g, I, np.float32)
+    u_ = pad(u, I, np.float32)
+    h_ = pad(h, I, storage_dtype(dt))
+    dy = pad(dY, H, storage_dtype(dt))
+    dx = np.empty((m, H), dtype=storage_dtype(dt))
+    dgate = np.empty((E, I, H), dtype=np.float32)
+    dup = np.empty((E, I, H), dtype=np.float32)
+    ddown = np.empty((E, H, I), dtype=np.float32)
+    rc = lib().oracle_experts_backward(ctypes.cast(gp, ctypes.c_void_p), ctypes.cast(up_, ctypes.c_void_p),
+                                       ctypes.cast(dp, ctypes.c_void_p), DT[dt], _ptr(r), _ptr(off), E, H, I,
+                                       _ptr(g_), _ptr(u_), _ptr(h_), _ptr(dy), _ptr(dx), _ptr(dgate), _ptr(dup),
+                                       _ptr(ddown), nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_experts_backward: a row's expert has no weights")
+    return dx[:n], dgate, dup, ddown
+
+
+def train_step(x: np.ndarray, logits: np.ndarray, gate, up, down, dt: str, ldt: str, top_k: int,
+               renormalize: bool, grad_output: np.ndarray, nthreads: int | None = None) -> dict:
+    """Forward of the chain with training caches, then the section's four
+    backward steps in order: combine, experts, dispatch, router."""
+    T, H = x.shape
+    E = logits.shape[1]
+    I = gate.shape[1]
+    idx, _, _ = route(logits, ldt, top_k, renormalize, nthreads)
+    w32 = router_weights(logits, ldt, idx, "softmax", renormalize, 1.0, nthreads)
+    offsets, ros, tor, rows = dispatch(idx, E, x, dt)
+    fw = experts_train_forward(gate, up, down, dt, rows, offsets, E, H, I, nthreads)
+    out = combine(fw["output"], dt, ros, w32, "f32", T, top_k, H, nthreads)
+    dY, dw = combine_backward(fw["output"], dt, ros, w32, "f32", grad_output, T, top_k, H, nthreads)
+    drows, dgate, dup, ddown = experts_backward(gate, up, down, dt, rows, offsets, E, H, I, fw["g"], fw["u"],
+                                                fw["h"], dY, nthreads)
+    dx = dispatch_backward(drows, dt, ros, T, top_k, H, nthreads)
+    dl = router_backward(logits, ldt, idx, dw, "softmax", renormalize, 1.0, nthreads)
+    return {"indices": idx, "weights_f32": w32, "offsets": offsets, "row_of_slot": ros, "dispatched": rows,
+            "Y": fw["output"], "h": fw["h"], "g": fw["g"], "u": fw["u"], "output": out, "dY": dY,
+            "dweights": dw, "drows": drows, "dgate": dgate, "dup": dup, "ddown": ddown, "dx": dx,
+            "dlogits": dl}

@@ -575,3 +575,390 @@ int oracle_combine(const void* Y, int dt, const uint32_t* row_of_slot, const voi
     parallel_rows(T, nthreads, combine_one, &c);
     return 0;
 }
+
+/* ------------------------------------------------------------------ */
+/* First-order MoE training (RUDA ruDNN library guide, section 12).     */
+/* ------------------------------------------------------------------ */
+
+/* Router weights of a fixed selection.  scoring 0: softmax over all E (the
+ * routing contract's FP32 softmax); 1: sigmoid of the selected logits.  The
+ * selected scores q_j (gathered: a repeated index is gathered twice) are
+ * divided by their FP32 sum in slot order when renorm is set, then
+ * multiplied by scale.  An index outside [0, E) makes the token's row NaN. */
+typedef struct {
+    const void* logits;
+    int dt;
+    const int64_t* idx;
+    const float* gw; /* [T,k] FP32 incoming gradient, backward only */
+    int64_t E;
+    int k, scoring, renorm;
+    float scale;
+    float* w;        /* [T,k] FP32 weights, forward only */
+    void* dl;        /* [T,E] gradient in the logits dtype, backward only */
+} rweights_ctx;
+
+static int row_indices_valid(const int64_t* idx, int k, int64_t E)
+{
+    for (int j = 0; j < k; ++j)
+        if (idx[j] < 0 || idx[j] >= E) return 0;
+    return 1;
+}
+
+static void router_scores(const rweights_ctx* c, int64_t t, float* p)
+{
+    if (c->scoring == 0) {
+        softmax_row_f32(c->logits, c->dt, t, c->E, p);
+    } else {
+        for (int64_t e = 0; e < c->E; ++e) p[e] = sigmoid_f32((float)load_elem(c->logits, c->dt, t * c->E + e));
+    }
+}
+
+static void rweights_one(void* vctx, int64_t t)
+{
+    rweights_ctx* c = (rweights_ctx*)vctx;
+    const int k = c->k;
+    const int64_t* idx = c->idx + t * k;
+    if (!row_indices_valid(idx, k, c->E)) {
+        for (int j = 0; j < k; ++j) c->w[t * k + j] = NAN;
+        return;
+    }
+    float* p = (float*)malloc(sizeof(float) * (size_t)c->E);
+    router_scores(c, t, p);
+    float S = 0.0f;
+    for (int j = 0; j < k; ++j) S += p[idx[j]];
+    for (int j = 0; j < k; ++j) {
+        float q = p[idx[j]];
+        if (c->renorm) q = q / S;
+        c->w[t * k + j] = q * c->scale;
+    }
+    free(p);
+}
+
+/* d loss / d logits from d loss / d weights, for the fixed selection: only
+ * the continuous weights are differentiated, not the choice.  Evaluated in
+ * double from the binary32 scores, rounded once to the logits dtype. */
+static void rbackward_one(void* vctx, int64_t t)
+{
+    rweights_ctx* c = (rweights_ctx*)vctx;
+    const int k = c->k;
+    const int64_t E = c->E;
+    const int64_t* idx = c->idx + t * k;
+    if (!row_indices_valid(idx, k, E)) {
+        for (int64_t e = 0; e < E; ++e) store_elem(c->dl, c->dt, t * E + e, NAN);
+        return;
+    }
+    float* p = (float*)malloc(sizeof(float) * (size_t)E);
+    double* dscore = (double*)calloc((size_t)E, sizeof(double));
+    router_scores(c, t, p);
+    double S = 0.0, dot = 0.0;
+    for (int j = 0; j < k; ++j) {
+        S += p[idx[j]];
+        dot += (double)c->gw[t * k + j] * p[idx[j]];
+    }
+    for (int j = 0; j < k; ++j) {
+        double g = (double)c->gw[t * k + j];
+        /* w_j = scale q_j / S (renorm) or scale q_j */
+        double dq = c->renorm ? c->scale * (g / S - dot / (S * S)) : c->scale * g;
+        dscore[idx[j]] += dq; /* gather: repeated indices add up */
+    }
+    if (c->scoring == 0) {
+        /* softmax Jacobian: dl_e = p_e (ds_e - sum_f p_f ds_f) */
+        double m = 0.0;
+        for (int64_t e = 0; e < E; ++e) m += (double)p[e] * dscore[e];
+        for (int64_t e = 0; e < E; ++e) store_elem(c->dl, c->dt, t * E + e, (double)p[e] * (dscore[e] - m));
+    } else {
+        for (int64_t e = 0; e < E; ++e) {
+            double s = p[e];
+            store_elem(c->dl, c->dt, t * E + e, dscore[e] * s * (1.0 - s));
+        }
+    }
+    free(dscore);
+    free(p);
+}
+
+int oracle_router_weights(const void* logits, int dt, const int64_t* idx, int64_t T, int64_t E, int k,
+                          int scoring, int renorm, float scale, float* w, int nthreads)
+{
+    if (T < 0 || E < 1 || k < 1 || k > 64 || k > E || (scoring != 0 && scoring != 1)) return -1;
+    if (!(scale > 0.0f) || isinf(scale)) return -1; /* a finite, positive scale */
+    rweights_ctx c = {logits, dt, idx, NULL, E, k, scoring, renorm, scale, w, NULL};
+    parallel_rows(T, nthreads, rweights_one, &c);
+    return 0;
+}
+
+int oracle_router_backward(const void* logits, int dt, const int64_t* idx, const float* gw, int64_t T,
+                           int64_t E, int k, int scoring, int renorm, float scale, void* dl, int nthreads)
+{
+    if (T < 0 || E < 1 || k < 1 || k > 64 || k > E || (scoring != 0 && scoring != 1)) return -1;
+    if (!(scale > 0.0f) || isinf(scale)) return -1;
+    rweights_ctx c = {logits, dt, idx, gw, E, k, scoring, renorm, scale, NULL, dl};
+    parallel_rows(T, nthreads, rbackward_one, &c);
+    return 0;
+}
+
+/* combine backward: for out[t] = sum_j w_j Y[row_j]:
+ *   dY[row_j] = w_j g_t (rounded to the expert dtype), dw_j = <Y[row_j], g_t>
+ * (double, rounded to FP32).  A token with a slot outside [0, N) -- NaN in
+ * the forward -- gets NaN weight gradients; its valid rows still get w g. */
+typedef struct {
+    const void* Y;
+    int dt;
+    const uint32_t* ros;
+    const void* w;
+    int wdt;
+    const void* gout;
+    int k;
+    int64_t H, N;
+    void* dY;
+    float* dw;
+} cback_ctx;
+
+static void cback_one(void* vctx, int64_t t)
+{
+    cback_ctx* c = (cback_ctx*)vctx;
+    const int k = c->k;
+    const int64_t H = c->H;
+    int invalid = 0;
+    for (int j = 0; j < k; ++j)
+        if ((int64_t)c->ros[t * k + j] >= c->N) invalid = 1;
+    for (int j = 0; j < k; ++j) {
+        const int64_t row = c->ros[t * k + j];
+        double dot = 0.0;
+        if (row < c->N) {
+            const double wj = load_elem(c->w, c->wdt, t * k + j);
+            for (int64_t col = 0; col < H; ++col) {
+                const double g = load_elem(c->gout, c->dt, t * H + col);
+                store_elem(c->dY, c->dt, row * H + col, wj * g);
+                dot += load_elem(c->Y, c->dt, row * H + col) * g;
+            }
+        }
+        c->dw[t * k + j] = invalid ? NAN : (float)dot;
+    }
+}
+
+int oracle_combine_backward(const void* Y, int dt, const uint32_t* ros, const void* w, int wdt, const void* gout,
+                            int64_t T, int k, int64_t H, int64_t N, void* dY, float* dw, int nthreads)
+{
+    if (T < 0 || k < 1 || H < 0 || N < 0) return -1;
+    cback_ctx c = {Y, dt, ros, w, wdt, gout, k, H, N, dY, dw};
+    parallel_rows(T, nthreads, cback_one, &c);
+    return 0;
+}
+
+/* dispatch backward: dx[t] = sum_j dinput[row_j] (double, slot order,
+ * rounded once); the routing weights are not applied again.  A token with a
+ * slot outside [0, N) gets a NaN row. */
+typedef struct {
+    const void* din;
+    int dt;
+    const uint32_t* ros;
+    int k;
+    int64_t H, N;
+    void* dx;
+} dback_ctx;
+
+static void dback_one(void* vctx, int64_t t)
+{
+    dback_ctx* c = (dback_ctx*)vctx;
+    int invalid = 0;
+    for (int j = 0; j < c->k; ++j)
+        if ((int64_t)c->ros[t * c->k + j] >= c->N) invalid = 1;
+    for (int64_t col = 0; col < c->H; ++col) {
+        double acc = 0.0;
+        if (invalid) {
+            acc = NAN;
+        } else {
+            for (int j = 0; j < c->k; ++j) acc += load_elem(c->din, c->dt, (int64_t)c->ros[t * c->k + j] * c->H + col);
+        }
+        store_elem(c->dx, c->dt, t * c->H + col, acc);
+    }
+}
+
+int oracle_dispatch_backward(const void* din, int dt, const uint32_t* ros, int64_t T, int k, int64_t H, int64_t N,
+                             void* dx, int nthreads)
+{
+    if (T < 0 || k < 1 || H < 0 || N < 0) return -1;
+    dback_ctx c = {din, dt, ros, k, H, N, dx};
+    parallel_rows(T, nthreads, dback_one, &c);
+    return 0;
+}
+
+/* Expert training forward and backward.  For row r of expert e:
+ *   g = gate_e x, u = up_e x            (the saved pre-activations, FP32)
+ *   h = silu(g) u  in the weight dtype  (as in the inference forward)
+ *   y = down_e h
+ * backward from dy:
+ *   dh = down_e^T dy
+ *   du = dh silu(g),  dg = dh u silu'(g),  silu'(g) = s (1 + g (1 - s)),
+ *        s = 1/(1+exp(-g)); both rounded to the weight dtype
+ *   dx = gate_e^T dg + up_e^T du        (rounded to the weight dtype)
+ *   dgate_e += dg x^T, dup_e += du x^T, ddown_e += dy h^T   (FP32)
+ * Sums in double, each result rounded once. */
+static double round_dt(double v, int dt)
+{
+    switch (dt) {
+    case O_F32: return oracle_round_f32(v);
+    case O_F16: return oracle_round_f16(v);
+    default: return oracle_round_bf16(v);
+    }
+}
+
+typedef struct {
+    const void* const* gate;
+    const void* const* up;
+    const void* const* down;
+    int dt;
+    const void* rows;
+    const uint32_t* offsets;
+    int64_t E, H, I;
+    void* out;   /* [N,H] */
+    void* h;     /* [N,I] weight dtype */
+    float* g;    /* [N,I] */
+    float* u;    /* [N,I] */
+    int* bad;
+} tfwd_ctx;
+
+static void tfwd_row(void* vctx, int64_t r)
+{
+    tfwd_ctx* c = (tfwd_ctx*)vctx;
+    const int64_t e = expert_of_row(c->offsets, c->E, r);
+    const int64_t H = c->H, I = c->I;
+    if (e < 0 || !c->gate[e] || !c->up[e] || !c->down[e]) {
+        *c->bad = 1;
+        return;
+    }
+    double* x = (double*)malloc(sizeof(double) * (size_t)H);
+    double* h = (double*)malloc(sizeof(double) * (size_t)I);
+    for (int64_t j = 0; j < H; ++j) x[j] = load_elem(c->rows, c->dt, r * H + j);
+    for (int64_t i = 0; i < I; ++i) {
+        double g = 0.0, u = 0.0;
+        for (int64_t j = 0; j < H; ++j) {
+            g += x[j] * load_elem(c->gate[e], c->dt, i * H + j);
+            u += x[j] * load_elem(c->up[e], c->dt, i * H + j);
+        }
+        c->g[r * I + i] = (float)g;
+        c->u[r * I + i] = (float)u;
+        h[i] = round_dt(oracle_silu(g) * u, c->dt);
+        store_elem(c->h, c->dt, r * I + i, h[i]);
+    }
+    for (int64_t j = 0; j < H; ++j) {
+        double y = 0.0;
+        for (int64_t i = 0; i < I; ++i) y += h[i] * load_elem(c->down[e], c->dt, j * I + i);
+        store_elem(c->out, c->dt, r * H + j, y);
+    }
+    free(h);
+    free(x);
+}
+
+int oracle_experts_train_forward(const void* const* gate, const void* const* up, const void* const* down, int dt,
+                                 const void* rows, const uint32_t* offsets, int64_t E, int64_t H, int64_t I,
+                                 void* out, void* h, float* g, float* u, int nthreads)
+{
+    if (E < 1 || H < 1 || I < 1) return -1;
+    int bad = 0;
+    tfwd_ctx c = {gate, up, down, dt, rows, offsets, E, H, I, out, h, g, u, &bad};
+    parallel_rows((int64_t)offsets[E], nthreads, tfwd_row, &c);
+    return bad ? -1 : 0;
+}
+
+typedef struct {
+    const void* const* gate;
+    const void* const* up;
+    const void* const* down;
+    int dt;
+    const void* rows;
+    const uint32_t* offsets;
+    int64_t E, H, I;
+    const float* g;
+    const float* u;
+    const void* dy;   /* [N,H] */
+    void* dx;         /* [N,H] */
+    double* dg;       /* [N,I] scratch: the rounded dg */
+    double* du;       /* [N,I] scratch */
+    int* bad;
+} tbwd_ctx;
+
+static void tbwd_row(void* vctx, int64_t r)
+{
+    tbwd_ctx* c = (tbwd_ctx*)vctx;
+    const int64_t e = expert_of_row(c->offsets, c->E, r);
+    const int64_t H = c->H, I = c->I;
+    if (e < 0 || !c->gate[e] || !c->up[e] || !c->down[e]) {
+        *c->bad = 1;
+        return;
+    }
+    for (int64_t i = 0; i < I; ++i) {
+        double dh = 0.0;
+        for (int64_t j = 0; j < H; ++j)
+            dh += load_elem(c->dy, c->dt, r * H + j) * load_elem(c->down[e], c->dt, j * I + i);
+        const double g = c->g[r * I + i], u = c->u[r * I + i];
+        const double s = 1.0 / (1.0 + exp(-g));
+        c->du[r * I + i] = round_dt(dh * g * s, c->dt);
+        c->dg[r * I + i] = round_dt(dh * u * s * (1.0 + g * (1.0 - s)), c->dt);
+    }
+    for (int64_t j = 0; j < H; ++j) {
+        double acc = 0.0;
+        for (int64_t i = 0; i < I; ++i)
+            acc += c->dg[r * I + i] * load_elem(c->gate[e], c->dt, i * H + j) +
+                   c->du[r * I + i] * load_elem(c->up[e], c->dt, i * H + j);
+        store_elem(c->dx, c->dt, r * H + j, acc);
+    }
+}
+
+typedef struct {
+    tbwd_ctx* b;
+    const void* h;
+    float* dgate; /* [E,I,H] */
+    float* dup;
+    float* ddown; /* [E,H,I] */
+} twgrad_ctx;
+
+/* one expert's weight gradients, summed over its rows in ascending order */
+static void twgrad_expert(void* vctx, int64_t e)
+{
+    twgrad_ctx* c = (twgrad_ctx*)vctx;
+    const tbwd_ctx* b = c->b;
+    const int64_t H = b->H, I = b->I;
+    const int64_t r0 = b->offsets[e], r1 = b->offsets[e + 1] > r0 ? b->offsets[e + 1] : r0;
+    for (int64_t i = 0; i < I; ++i) {
+        for (int64_t j = 0; j < H; ++j) {
+            double sg = 0.0, su = 0.0;
+            for (int64_t r = r0; r < r1; ++r) {
+                const double x = load_elem(b->rows, b->dt, r * H + j);
+                sg += b->dg[r * I + i] * x;
+                su += b->du[r * I + i] * x;
+            }
+            c->dgate[(e * I + i) * H + j] = (float)sg;
+            c->dup[(e * I + i) * H + j] = (float)su;
+        }
+    }
+    for (int64_t j = 0; j < H; ++j) {
+        for (int64_t i = 0; i < I; ++i) {
+            double sd = 0.0;
+            for (int64_t r = r0; r < r1; ++r)
+                sd += load_elem(b->dy, b->dt, r * H + j) * load_elem(c->h, b->dt, r * I + i);
+            c->ddown[(e * H + j) * I + i] = (float)sd;
+        }
+    }
+}
+
+int oracle_experts_backward(const void* const* gate, const void* const* up, const void* const* down, int dt,
+                            const void* rows, const uint32_t* offsets, int64_t E, int64_t H, int64_t I,
+                            const float* g, const float* u, const void* h, const void* dy, void* dx,
+                            float* dgate, float* dup, float* ddown, int nthreads)
+{
+    if (E < 1 || H < 1 || I < 1) return -1;
+    const int64_t N = offsets[E];
+    int bad = 0;
+    double* dg = (double*)malloc(sizeof(double) * (size_t)(N > 0 ? N * I : 1));
+    double* du = (double*)malloc(sizeof(double) * (size_t)(N > 0 ? N * I : 1));
+    tbwd_ctx b = {gate, up, down, dt, rows, offsets, E, H, I, g, u, dy, dx, dg, du, &bad};
+    parallel_rows(N, nthreads, tbwd_row, &b);
+    if (!bad) {
+        twgrad_ctx w = {&b, h, dgate, dup, ddown};
+        parallel_rows(E, nthreads, twgrad_expert, &w);
+    }
+    free(du);
+    free(dg);
+    return bad ? -1 : 0;
+}
