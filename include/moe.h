@@ -54,7 +54,9 @@ typedef enum moe_dtype {
     MOE_F32 = 0,
     MOE_F16 = 1,
     MOE_BF16 = 2,
-    MOE_U32 = 3
+    MOE_U32 = 3,
+    MOE_I32 = 4, /* router-training indices only */
+    MOE_I64 = 5  /* router-training indices only */
 } moe_dtype;
 
 typedef enum moe_status {
@@ -95,6 +97,20 @@ typedef struct moe_group_routing_options {
     int32_t renormalize;
     float scale;
 } moe_group_routing_options;
+
+/* Router-weight options of the training calls (RUDA guide, section 12):
+ *   scoring MOE_SCORING_SOFTMAX (FP32 softmax over all E experts) or
+ *   MOE_SCORING_SIGMOID (sigmoid of each logit); renormalize 0 or 1; scale
+ *   finite and > 0, applied last. */
+typedef enum moe_router_scoring {
+    MOE_SCORING_SOFTMAX = 0,
+    MOE_SCORING_SIGMOID = 1
+} moe_router_scoring;
+typedef struct moe_router_weight_options {
+    int32_t scoring;
+    int32_t renormalize;
+    float scale;
+} moe_router_weight_options;
 
 /* Limits of this implementation (beyond them: MOE_ERR_UNSUPPORTED). */
 #define MOE_MAX_EXPERTS 4096   /* E */
@@ -270,6 +286,120 @@ moe_status moe_forward_sigmoid_grouped(const moe_tensor* gate, const moe_tensor*
                                        const moe_tensor* input, const moe_tensor* logits, const moe_tensor* bias,
                                        moe_group_routing_options options, moe_tensor* output,
                                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------ */
+/* First-order training (RUDA ruDNN library guide, section 12).          */
+/* The forward keeps what the backward needs (the FP32 pre-activations   */
+/* and the activation); the backward then runs, in this order:           */
+/* moe_combine_backward, moe_experts_backward, moe_dispatch_backward and */
+/* moe_router_backward.  Only the weights of the fixed selection are     */
+/* differentiated: not the top-k choice, the group choice or a           */
+/* correction bias.  The saved inputs must not change before the         */
+/* backward.                                                             */
+/* ------------------------------------------------------------------ */
+
+/*
+ * moe_router_weights -- selected_router_weights: the weights of a fixed
+ * selection.
+ *   logits  [T,E]  F32 | F16 | BF16, read only.
+ *   indices [T,k]  U32 | I32 | I64, read only; 1 <= k <= min(E, 64).  A
+ *                  repeated index is gathered again.  An index outside
+ *                  [0, E) is not checked on the host: it makes the token's
+ *                  row NaN, with no access outside the logits.
+ *   weights [T,k]  F32, written: w_j = scale * q_j / S, with q_j the score
+ *                  (softmax probability or sigmoid) of expert indices[t,j]
+ *                  and S the FP32 sum of the row's q in slot order when
+ *                  renormalize is set (else w_j = scale * q_j).
+ */
+moe_status moe_router_weights(const moe_tensor* logits, const moe_tensor* indices,
+                              moe_router_weight_options options, moe_tensor* weights, void* stream);
+
+/*
+ * moe_router_backward -- selected_router_backward: d loss / d logits from
+ * the FP32 weight gradients, for the same selection and options.
+ *   grad_weights [T,k]  F32, read only.
+ *   grad_logits  [T,E]  logits dtype, written (every element; NaN rows for
+ *                       tokens with an index outside [0, E)).
+ *   Other arguments as for moe_router_weights.
+ */
+moe_status moe_router_backward(const moe_tensor* logits, const moe_tensor* indices,
+                               const moe_tensor* grad_weights, moe_router_weight_options options,
+                               moe_tensor* grad_logits, void* stream);
+
+/*
+ * moe_combine_backward -- step 1: the backward of moe_combine.
+ *   expert_out      [N,H]  F32 | F16 | BF16, read only (the forward's).
+ *   row_of_slot     [T*k]  U32, read only (moe_dispatch's).
+ *   weights         [T,k]  F32 | F16 | BF16, read only (the combine's).
+ *   grad_output     [T,H]  expert_out dtype, read only.
+ *   grad_expert_out [N,H]  expert_out dtype, written for every row some slot
+ *                          names: row_of_slot[t*k+j] gets weights[t,j] *
+ *                          grad_output[t], rounded once.
+ *   grad_weights    [T,k]  F32, written: <expert_out[row_of_slot[t*k+j]],
+ *                          grad_output[t]>, FP32 sums in a fixed order; NaN
+ *                          for every slot of a token with a row >= N.
+ */
+moe_status moe_combine_backward(const moe_tensor* expert_out, const moe_tensor* row_of_slot,
+                                const moe_tensor* weights, const moe_tensor* grad_output,
+                                moe_tensor* grad_expert_out, moe_tensor* grad_weights, void* stream);
+
+/*
+ * moe_experts_forward_training -- forward_dispatched_training: the experts
+ * forward (bit for bit moe_experts_forward's output) that also keeps the
+ * cache of the backward.
+ *   rows           [R,H]   weight dtype, read only: the N dispatched rows
+ *                          (token_of_row NULL, R = N), or the T token rows
+ *                          read in place through token_of_row.
+ *   token_of_row   [N]     U32 (moe_dispatch's) or NULL; an entry >= R is
+ *                          clamped to R-1.
+ *   expert_out     [N,H]   written for rows < expert_offsets[E].
+ *   preact         [N,2I]  F32, written: g = gate_e x in columns [0, I),
+ *                          u = up_e x in [I, 2I), FP32 accumulations.
+ *   h              [N,I]   weight dtype, written: silu(g) * u, rounded once.
+ *   workspace      >= moe_experts_workspace_bytes(N,H,I,E,dtype) bytes.
+ *   Other arguments as for moe_experts_forward.
+ */
+moe_status moe_experts_forward_training(const moe_tensor* gate, const moe_tensor* up, const moe_tensor* down,
+                                        const moe_tensor* rows, const moe_tensor* token_of_row,
+                                        const moe_tensor* expert_offsets, moe_tensor* expert_out,
+                                        moe_tensor* preact, moe_tensor* h, void* workspace,
+                                        size_t workspace_bytes, void* stream);
+
+/* Workspace bytes moe_experts_backward needs for N dispatched rows. */
+size_t moe_experts_backward_workspace_bytes(int64_t N, int64_t H, int64_t I, int64_t E, int32_t dtype);
+
+/*
+ * moe_experts_backward -- step 2 (cache.backward): for the rows r of expert
+ * e, with dh = grad_expert_out_r down_e, s = 1/(1+exp(-g)):
+ *   du = dh * g * s and dg = dh * u * s * (1 + g * (1 - s)), each rounded
+ *   to the weight dtype;
+ *   grad_rows_r = gate_e^T dg + up_e^T du   [N,H] weight dtype, written for
+ *                                            rows < expert_offsets[E];
+ *   grad_gate_e = sum_r dg x_r^T, grad_up_e = sum_r du x_r^T   [E,I,H] F32;
+ *   grad_down_e = sum_r grad_expert_out_r h_r^T                [E,H,I] F32;
+ *   FP32 accumulation; an expert without rows gets zero gradients.
+ *   rows, token_of_row, expert_offsets, preact, h: as given to (and written
+ *   by) moe_experts_forward_training; grad_expert_out [N,H] weight dtype.
+ *   workspace >= moe_experts_backward_workspace_bytes(N,H,I,E,dtype) bytes.
+ */
+moe_status moe_experts_backward(const moe_tensor* gate, const moe_tensor* up, const moe_tensor* down,
+                                const moe_tensor* rows, const moe_tensor* token_of_row,
+                                const moe_tensor* expert_offsets, const moe_tensor* preact, const moe_tensor* h,
+                                const moe_tensor* grad_expert_out, moe_tensor* grad_rows, moe_tensor* grad_gate,
+                                moe_tensor* grad_up, moe_tensor* grad_down, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/*
+ * moe_dispatch_backward -- step 3: grad_input[t] = the FP32 sum, in slot
+ * order, of grad_rows[row_of_slot[t*k+j]] over j < top_k, rounded once; the
+ * routing weights are not applied again.
+ *   grad_rows   [N,H]      F32 | F16 | BF16, read only.
+ *   row_of_slot [T*top_k]  U32, read only; a row >= N makes the token's
+ *                          grad_input row NaN.
+ *   grad_input  [T,H]      grad_rows dtype, written.
+ */
+moe_status moe_dispatch_backward(const moe_tensor* grad_rows, const moe_tensor* row_of_slot, int32_t top_k,
+                                 moe_tensor* grad_input, void* stream);
 
 /* Static text of a status code. */
 const char* moe_status_string(moe_status status);

@@ -11,7 +11,8 @@ import os
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe.so")
 
-MOE_F32, MOE_F16, MOE_BF16, MOE_U32 = 0, 1, 2, 3
+MOE_F32, MOE_F16, MOE_BF16, MOE_U32, MOE_I32, MOE_I64 = 0, 1, 2, 3, 4, 5
+MOE_SCORING_SOFTMAX, MOE_SCORING_SIGMOID = 0, 1
 STATUS = {
     0: "MOE_OK",
     1: "MOE_ERR_INVALID_ARGUMENT",
@@ -41,6 +42,13 @@ EXPORTS = (
     "moe_forward_workspace_bytes",
     "moe_forward",
     "moe_forward_sigmoid_grouped",
+    "moe_router_weights",
+    "moe_router_backward",
+    "moe_combine_backward",
+    "moe_experts_forward_training",
+    "moe_experts_backward_workspace_bytes",
+    "moe_experts_backward",
+    "moe_dispatch_backward",
     "moe_status_string",
 )
 
@@ -61,6 +69,10 @@ class MoeRoutingOptions(ctypes.Structure):
 class MoeGroupRoutingOptions(ctypes.Structure):
     _fields_ = [("top_k", ctypes.c_int32), ("groups", ctypes.c_int32), ("selected_groups", ctypes.c_int32),
                 ("group_top_two", ctypes.c_int32), ("renormalize", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+class MoeRouterWeightOptions(ctypes.Structure):
+    _fields_ = [("scoring", ctypes.c_int32), ("renormalize", ctypes.c_int32), ("scale", ctypes.c_float)]
 
 
 class MoeError(RuntimeError):
@@ -102,11 +114,21 @@ def load() -> ctypes.CDLL:
     L.moe_forward_workspace_bytes.restype = sz
     L.moe_forward.argtypes = [P, P, P, P, P, MoeRoutingOptions, P, vp, sz, vp]
     L.moe_forward_sigmoid_grouped.argtypes = [P, P, P, P, P, P, MoeGroupRoutingOptions, P, vp, sz, vp]
+    L.moe_router_weights.argtypes = [P, P, MoeRouterWeightOptions, P, vp]
+    L.moe_router_backward.argtypes = [P, P, P, MoeRouterWeightOptions, P, vp]
+    L.moe_combine_backward.argtypes = [P, P, P, P, P, P, vp]
+    L.moe_experts_forward_training.argtypes = [P, P, P, P, P, P, P, P, P, vp, sz, vp]
+    L.moe_experts_backward_workspace_bytes.argtypes = [i64, i64, i64, i64, i32]
+    L.moe_experts_backward_workspace_bytes.restype = sz
+    L.moe_experts_backward.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, P, vp, sz, vp]
+    L.moe_dispatch_backward.argtypes = [P, P, i32, P, vp]
     L.moe_status_string.argtypes = [i32]
     L.moe_status_string.restype = ctypes.c_char_p
     for f in ("moe_route", "moe_route_sigmoid_grouped", "moe_dispatch", "moe_experts_forward",
               "moe_experts_gate_up", "moe_experts_gate_up_gathered", "moe_experts_down", "moe_combine",
-              "moe_forward", "moe_forward_sigmoid_grouped"):
+              "moe_forward", "moe_forward_sigmoid_grouped", "moe_router_weights", "moe_router_backward",
+              "moe_combine_backward", "moe_experts_forward_training", "moe_experts_backward",
+              "moe_dispatch_backward"):
         getattr(L, f).restype = i32
     _lib = L
     return L

@@ -8,6 +8,14 @@ The objects mirror the ruDNN User Guide (ruDNN 0.1.5 on docs.rs), section 6
 whole chain from precomputed logits) or ``forward_dispatched``.  Errors come
 back as ``MoeError`` (the guide's section 3 error convention).
 
+First-order training follows the RUDA ruDNN library guide, section 12:
+``RoutingPlan.into_training(logits, options)`` keeps the selection and
+recomputes FP32 weights (``selected_router_weights``);
+``SwiGluExperts.forward_dispatched_training`` returns the output and an
+``ExpertsCache``; the backward then runs ``DispatchedTokens.combine_backward``,
+``ExpertsCache.backward``, ``DispatchedTokens.dispatch_backward`` and
+``RouterTrainingPlan.backward``, in that order.
+
 This module only allocates torch tensors and passes pointers and extents
 to the C ABI: every step of the chain runs in the HIP kernels.
 """
@@ -19,13 +27,15 @@ from dataclasses import dataclass
 import torch
 
 from . import _lib
-from ._lib import MoeError, MoeGroupRoutingOptions, MoeRoutingOptions, MoeTensor
+from ._lib import MoeError, MoeGroupRoutingOptions, MoeRouterWeightOptions, MoeRoutingOptions, MoeTensor
 
 _DTYPES = {
     torch.float32: _lib.MOE_F32,
     torch.float16: _lib.MOE_F16,
     torch.bfloat16: _lib.MOE_BF16,
     torch.uint32: _lib.MOE_U32,
+    torch.int32: _lib.MOE_I32,
+    torch.int64: _lib.MOE_I64,
 }
 
 
@@ -90,6 +100,22 @@ class GroupRoutingOptions:
                                       int(bool(self.group_top_two)), int(bool(self.renormalize)), float(self.scale))
 
 
+@dataclass(frozen=True)
+class RouterWeightOptions:
+    """Weights of a fixed selection (section 12): scoring "softmax" (FP32
+    softmax over all experts) or "sigmoid"; renormalize over the selection;
+    a finite positive scale applied last."""
+    scoring: str = "softmax"
+    renormalize: bool = True
+    scale: float = 1.0
+
+    def _c(self) -> MoeRouterWeightOptions:
+        codes = {"softmax": _lib.MOE_SCORING_SOFTMAX, "sigmoid": _lib.MOE_SCORING_SIGMOID}
+        if self.scoring not in codes:
+            raise MoeError(1, f"scoring must be 'softmax' or 'sigmoid', got {self.scoring!r}")
+        return MoeRouterWeightOptions(codes[self.scoring], int(bool(self.renormalize)), float(self.scale))
+
+
 def _workspace(nbytes: int, device) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
@@ -114,6 +140,54 @@ class RoutingPlan:
 
     def dispatch(self, input: torch.Tensor, copy_rows: bool = True) -> "DispatchedTokens":
         return dispatch(input, self._indices, self.num_experts, self._weights, copy_rows)
+
+    def into_training(self, logits: torch.Tensor, options: RouterWeightOptions) -> "RouterTrainingPlan":
+        """Keep this selection and recompute its weights in FP32 (selected_router_weights)."""
+        return RouterTrainingPlan(logits, self._indices, options)
+
+
+class RouterTrainingPlan:
+    """A fixed selection with FP32 weights recomputed from the logits; the
+    logits and indices are kept for the backward and must not change."""
+
+    def __init__(self, logits: torch.Tensor, indices: torch.Tensor, options: RouterWeightOptions):
+        self.logits, self.indices, self.options = logits, indices, options
+        self._weights = router_weights(logits, indices, options)
+
+    def weights(self) -> torch.Tensor:
+        return self._weights
+
+    def routing(self) -> RoutingPlan:
+        """The plan to dispatch and combine with (FP32 weights)."""
+        if self.indices.dtype != torch.uint32:
+            raise MoeError(2, "dispatch takes U32 indices")
+        return RoutingPlan(self.indices, self._weights, int(self.logits.shape[1]))
+
+    def backward(self, grad_weights: torch.Tensor) -> torch.Tensor:
+        """d loss / d logits (selected_router_backward)."""
+        return router_backward(self.logits, self.indices, grad_weights, self.options)
+
+
+def router_weights(logits: torch.Tensor, indices: torch.Tensor, options: RouterWeightOptions) -> torch.Tensor:
+    """FP32 [T,k] weights of the experts in `indices` (moe_router_weights)."""
+    L = _lib.load()
+    T, k = indices.shape
+    w = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    dl, di, dw = _desc(logits), _desc(indices), _desc(w)
+    _lib.check(L.moe_router_weights(_ref(dl), _ref(di), options._c(), _ref(dw), _stream(logits.device)),
+               "moe_router_weights")
+    return w
+
+
+def router_backward(logits: torch.Tensor, indices: torch.Tensor, grad_weights: torch.Tensor,
+                    options: RouterWeightOptions) -> torch.Tensor:
+    """[T,E] logits gradient in the logits dtype (moe_router_backward)."""
+    L = _lib.load()
+    dlog = torch.empty_like(logits)
+    d = [_desc(x) for x in (logits, indices, grad_weights, dlog)]
+    _lib.check(L.moe_router_backward(_ref(d[0]), _ref(d[1]), _ref(d[2]), options._c(), _ref(d[3]),
+                                     _stream(logits.device)), "moe_router_backward")
+    return dlog
 
 
 def route(logits: torch.Tensor, options: RoutingOptions) -> RoutingPlan:
@@ -163,6 +237,18 @@ class DispatchedTokens:
             raise MoeError(1, "combine needs routing weights")
         return combine(expert_output, self.row_of_slot, w)
 
+    def combine_backward(self, expert_output: torch.Tensor, grad_output: torch.Tensor,
+                         weights: torch.Tensor | None = None):
+        """Step 1 of the backward: (dexpert [N,H], FP32 dweights [T,k]) (moe_combine_backward)."""
+        w = self.routing_weights if weights is None else weights
+        if w is None:
+            raise MoeError(1, "combine_backward needs routing weights")
+        return combine_backward(expert_output, self.row_of_slot, w, grad_output)
+
+    def dispatch_backward(self, grad_rows: torch.Tensor) -> torch.Tensor:
+        """Step 3: each token's row gradients summed, weights not applied (moe_dispatch_backward)."""
+        return dispatch_backward(grad_rows, self.row_of_slot, self.top_k, self.num_tokens)
+
 
 def dispatch(input: torch.Tensor, indices: torch.Tensor, num_experts: int,
              weights: torch.Tensor | None = None, copy_rows: bool = True) -> DispatchedTokens:
@@ -196,6 +282,63 @@ def combine(expert_output: torch.Tensor, row_of_slot: torch.Tensor, weights: tor
     _lib.check(L.moe_combine(_ref(d[0]), _ref(d[1]), _ref(d[2]), _ref(d[3]), _stream(out.device)),
                "moe_combine")
     return out
+
+
+def combine_backward(expert_output: torch.Tensor, row_of_slot: torch.Tensor, weights: torch.Tensor,
+                     grad_output: torch.Tensor):
+    """(grad_expert_out [N,H], grad_weights [T,k] FP32) (moe_combine_backward)."""
+    L = _lib.load()
+    T, k = weights.shape
+    dy = torch.empty_like(expert_output)
+    dw = torch.empty((T, k), dtype=torch.float32, device=expert_output.device)
+    d = [_desc(x) for x in (expert_output, row_of_slot, weights, grad_output, dy, dw)]
+    _lib.check(L.moe_combine_backward(*[_ref(x) for x in d], _stream(expert_output.device)),
+               "moe_combine_backward")
+    return dy, dw
+
+
+def dispatch_backward(grad_rows: torch.Tensor, row_of_slot: torch.Tensor, top_k: int, num_tokens: int) -> torch.Tensor:
+    """[T,H] token gradients (moe_dispatch_backward)."""
+    L = _lib.load()
+    dx = torch.empty((num_tokens, grad_rows.shape[1]), dtype=grad_rows.dtype, device=grad_rows.device)
+    d = [_desc(x) for x in (grad_rows, row_of_slot, dx)]
+    _lib.check(L.moe_dispatch_backward(_ref(d[0]), _ref(d[1]), int(top_k), _ref(d[2]), _stream(dx.device)),
+               "moe_dispatch_backward")
+    return dx
+
+
+class ExpertsCache:
+    """What the experts backward needs: the product rows (dispatched, or the
+    tokens with token_of_row), the offsets, the FP32 pre-activations g | u
+    [N,2I] and the activation h [N,I]."""
+
+    def __init__(self, experts, rows, token_of_row, expert_offsets, preact, h):
+        self.experts = experts
+        self.rows, self.token_of_row, self.expert_offsets = rows, token_of_row, expert_offsets
+        self.preact, self.h = preact, h
+
+    def backward(self, grad_expert_out: torch.Tensor, workspace: torch.Tensor | None = None):
+        """Step 2: (grad_rows [N,H], grad_gate, grad_up [E,I,H], grad_down [E,H,I] FP32) (moe_experts_backward)."""
+        ex = self.experts
+        L = _lib.load()
+        N = self.h.shape[0]
+        dev = self.h.device
+        dx = torch.empty((N, ex.hidden), dtype=self.h.dtype, device=dev)
+        dg = torch.empty((ex.num_experts, ex.intermediate, ex.hidden), dtype=torch.float32, device=dev)
+        du = torch.empty_like(dg)
+        dd = torch.empty((ex.num_experts, ex.hidden, ex.intermediate), dtype=torch.float32, device=dev)
+        need = L.moe_experts_backward_workspace_bytes(N, ex.hidden, ex.intermediate, ex.num_experts,
+                                                      _dtype_code(self.h))
+        if workspace is None or workspace.numel() < need:
+            workspace = _workspace(need, dev)
+        tor = _desc(self.token_of_row) if self.token_of_row is not None else None
+        d = [_desc(x) for x in (self.rows, self.expert_offsets, self.preact, self.h, grad_expert_out, dx, dg, du, dd)]
+        g, u, w = ex._dw
+        st = L.moe_experts_backward(_ref(g), _ref(u), _ref(w), _ref(d[0]), _ref(tor) if tor is not None else None,
+                                    *[_ref(x) for x in d[1:]], ctypes.c_void_p(workspace.data_ptr()),
+                                    workspace.numel(), _stream(dev))
+        _lib.check(st, "moe_experts_backward")
+        return dx, dg, du, dd
 
 
 class SwiGluExperts:
@@ -277,6 +420,36 @@ class SwiGluExperts:
                                    ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(rows.device))
         _lib.check(st, "moe_experts_forward")
         return out
+
+    def forward_dispatched_training(self, dispatched: DispatchedTokens, input: torch.Tensor | None = None,
+                                    workspace: torch.Tensor | None = None):
+        """The experts forward plus its cache (moe_experts_forward_training):
+        on the dispatched copy, or -- with `input` -- on the token rows read
+        in place through token_of_row.  Returns (output [N,H], ExpertsCache)."""
+        L = _lib.load()
+        if input is None:
+            if dispatched.rows is None:
+                raise MoeError(1, "no dispatched rows: pass the token rows as `input`")
+            rows, tor = dispatched.rows, None
+        else:
+            rows, tor = input, dispatched.token_of_row
+        offsets = dispatched.expert_offsets
+        N = tor.shape[0] if tor is not None else rows.shape[0]
+        dev = rows.device
+        out = torch.empty((N, self.hidden), dtype=rows.dtype, device=dev)
+        preact = torch.empty((N, 2 * self.intermediate), dtype=torch.float32, device=dev)
+        h = torch.empty((N, self.intermediate), dtype=rows.dtype, device=dev)
+        need = L.moe_experts_workspace_bytes(N, self.hidden, self.intermediate, self.num_experts, _dtype_code(rows))
+        if workspace is None or workspace.numel() < need:
+            workspace = _workspace(need, dev)
+        dt = _desc(tor) if tor is not None else None
+        d = [_desc(x) for x in (rows, offsets, out, preact, h)]
+        g, u, w = self._dw
+        st = L.moe_experts_forward_training(_ref(g), _ref(u), _ref(w), _ref(d[0]), _ref(dt) if dt is not None else None,
+                                            *[_ref(x) for x in d[1:]], ctypes.c_void_p(workspace.data_ptr()),
+                                            workspace.numel(), _stream(dev))
+        _lib.check(st, "moe_experts_forward_training")
+        return out, ExpertsCache(self, rows, tor, offsets, preact, h)
 
     def gate_up(self, rows: torch.Tensor, expert_offsets: torch.Tensor,
                 workspace: torch.Tensor | None = None) -> torch.Tensor:

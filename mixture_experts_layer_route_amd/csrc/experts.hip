@@ -36,48 +36,11 @@
 #include <algorithm>
 #include <type_traits>
 
-#include "moe_internal.h"
+#include "mfma.h"
+#include "tiles.h"
 
 namespace moe {
 namespace {
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
-// One 16-byte operand chunk per lane and per fragment: 8 bf16/f16 values feed
-// one 16x16x32 MFMA; 4 f32 values feed four 16x16x4 MFMAs.  A and B always
-// take the same K elements in the same register slots, so the products sum
-// over exactly the right K indices.
-template <typename DT> struct mma;
-template <> struct mma<bf16_t> {
-    static __device__ __forceinline__ f32x4_t run(uint4 a, uint4 b, f32x4_t c) {
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                       __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-    }
-};
-template <> struct mma<f16_t> {
-    static __device__ __forceinline__ f32x4_t run(uint4 a, uint4 b, f32x4_t c) {
-        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
-                                                      __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
-    }
-};
-template <> struct mma<f32_t> {
-    static __device__ __forceinline__ f32x4_t run(uint4 a, uint4 b, f32x4_t c) {
-        c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x), c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), c, 0, 0, 0);
-        return c;
-    }
-};
-
-#ifndef MOE_GROUP_M
-#define MOE_GROUP_M 8
-#endif
-constexpr int kGroupM = MOE_GROUP_M;
-static_assert(kGroupM >= 1 && kGroupM < 64, "group size is packed in 6 bits");
-constexpr int64_t kMaxTiles = int64_t(1) << 26;  // tile index packed in 26 bits
 
 // ------------------------------------------------------------------ tile list
 // offsets are clamped to [0, N] and to be non-decreasing per expert, so even
@@ -146,63 +109,10 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const uint32_t* __res
     if (threadIdx.x == 0) *count = min(total, max_tiles);
 }
 
-// ------------------------------------------------------------------ tile order
-// Workgroup b -> (token tile, weight tile).  The grid is sized for the most
-// token tiles the routing could produce; only the first m_tiles (the count the
-// tile-list kernel wrote) exist.  The hardware hands workgroup b to XCD b % 8,
-// so the live workgroups are the first m_tiles * n_tiles ids, which every XCD
-// shares evenly; their ids are remapped to give each XCD a contiguous run of
-// logical tiles.  The run is walked group by group -- a group is a few token
-// tiles of ONE expert (at most kGroupM), taken token tile first, then weight
-// tile -- so the ~32 workgroups an XCD runs at once share that expert's weight
-// tiles and the group's token tiles in the XCD's L2.  A group of g token tiles
-// starting at tile f owns logical ids [f * n_tiles, (f + g) * n_tiles), so id
-// p belongs to the group recorded with token tile p / n_tiles.  Returns false
-// for a workgroup with no tile.
-__device__ __forceinline__ bool tile_of_block(int bid, int nblocks, int n_tiles, int m_tiles,
-                                              const int4* __restrict__ tiles, int* m_idx, int* n_idx) {
-    const int live = min(nblocks, m_tiles * n_tiles);
-    if (bid >= live) return false;
-    const int q = live / 8, rem = live % 8;
-    const int xcd = bid % 8, loc = bid / 8;
-    const int pid = (xcd < rem ? xcd * (q + 1) : rem * (q + 1) + (xcd - rem) * q) + loc;
-    const uint32_t g = (uint32_t)tiles[pid / n_tiles].w;
-    const int first_m = (int)(g & 0x3ffffffu);  // 26 bits of first tile, 6 of group size
-    const int gm = max(1, min((int)(g >> 26), m_tiles - first_m));
-    const int in_group = pid - first_m * n_tiles;
-    *m_idx = first_m + in_group % gm;
-    *n_idx = in_group / gm;
-    return true;
-}
 
 // ------------------------------------------------------------------ grouped GEMM
-// Source row of product row r: r itself, or (fused gather) the token row
-// a_rows[r], clamped into the token buffer.
-__device__ __forceinline__ int64_t src_row(const uint32_t* __restrict__ a_rows, int a_nrows, int r) {
-    return a_rows ? (int64_t)min(a_rows[r], (uint32_t)(a_nrows - 1)) : (int64_t)r;
-}
 
-// SiLU(g) * u in FP32: exp on the hardware exp2 unit and a hardware
-// reciprocal; the product is then rounded to the weight dtype, whose
-// precision (bf16/f16), or the f32 tolerance, dwarfs their few-ulp error.
-__device__ __forceinline__ float silu_mul(float g, float u) {
-    return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
-}
 
-template <typename DT> struct store4;
-template <> struct store4<f32_t> {
-    static __device__ __forceinline__ void run(float* p, const float* v) {
-        *(float4*)p = make_float4(v[0], v[1], v[2], v[3]);
-    }
-};
-template <typename DT> struct store4 {
-    static __device__ __forceinline__ void run(uint16_t* p, const float* v) {
-        uint2 w;
-        w.x = (uint32_t)fmt<DT>::store(v[0]) | ((uint32_t)fmt<DT>::store(v[1]) << 16);
-        w.y = (uint32_t)fmt<DT>::store(v[2]) | ((uint32_t)fmt<DT>::store(v[3]) << 16);
-        *(uint2*)p = w;
-    }
-};
 
 // MFMA operand roles: the weight rows are the A operand (16 rows of the
 // output's columns) and the token rows the B operand, so the 16x16 result
@@ -214,6 +124,7 @@ __global__ __launch_bounds__(WGM* WGN* kWave) void grouped_gemm_kernel(
     const typename DT::storage* __restrict__ B0,  // [E, NOUT, K]  (gate or down)
     const typename DT::storage* __restrict__ B1,  // [E, NOUT, K]  (up; GATEUP only)
     typename DT::storage* __restrict__ C,         // [rows, NOUT]
+    float* __restrict__ gu,                       // [rows, 2 NOUT] g | u (GATEUP) or null
     const uint32_t* __restrict__ a_rows, int a_nrows, const int4* __restrict__ tiles,
     const uint32_t* __restrict__ tile_count, int K, int NOUT,
     int n_tiles, int nblocks) {
@@ -366,6 +277,12 @@ __global__ __launch_bounds__(WGM* WGN* kWave) void grouped_gemm_kernel(
 #pragma unroll
                     for (int r = 0; r < 4; ++r) v[r] = silu_mul(acc[i][f][r], acc[i][f + NF / 2][r]);
                     store4<DT>::run(crow + col, v);
+                    if (gu) {
+                        const float g4[4] = {acc[i][f][0], acc[i][f][1], acc[i][f][2], acc[i][f][3]};
+                        const float u4[4] = {acc[i][f + NF / 2][0], acc[i][f + NF / 2][1], acc[i][f + NF / 2][2],
+                                             acc[i][f + NF / 2][3]};
+                        save_preact(gu, grow, NOUT, col, g4, u4);
+                    }
                 }
             }
         } else {
@@ -449,24 +366,7 @@ __device__ __forceinline__ void barrier_lds() { asm volatile("s_barrier" ::: "me
 // (the scheduler otherwise trades that latency slack for fewer registers).
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-// 32x32x16 matrix op: lane l supplies 8 K-values of row (l % 32) of each
-// operand, K group (l / 32); lane l receives column (l % 32) and rows
-// 8 (r / 4) + 4 (l / 32) + (r % 4) of the result in register r.
-template <typename DT> struct mma32;
-template <> struct mma32<bf16_t> {
-    static __device__ __forceinline__ f32x16_t run(uint4 a, uint4 b, f32x16_t c) {
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                       __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-    }
-};
-template <> struct mma32<f16_t> {
-    static __device__ __forceinline__ f32x16_t run(uint4 a, uint4 b, f32x16_t c) {
-        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
-                                                      __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
-    }
-};
 
 template <int N> __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 // lgkmcnt(0) through the builtin, so the compiler's own LDS-read tracking
@@ -479,7 +379,8 @@ __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F
 // past NOUT are not written.
 template <typename DT, bool GATEUP, int MB, int NB, int WTM, int WTN, int WCN>
 __device__ __forceinline__ void store_tile32(const f32x16_t (&acc)[MB][NB], typename DT::storage* __restrict__ C,
-                                             int r0, int r1, int n0, int wm, int wn, int NOUT, int lane) {
+                                             float* __restrict__ gu, int r0, int r1, int n0, int wm, int wn,
+                                             int NOUT, int lane) {
     using S = typename DT::storage;
     const int frow = lane & 31;
 #pragma unroll
@@ -500,6 +401,15 @@ __device__ __forceinline__ void store_tile32(const f32x16_t (&acc)[MB][NB], type
                         for (int r = 0; r < 4; ++r)
                             v[r] = silu_mul(acc[i][f][g * 4 + r], acc[i][f + NB / 2][g * 4 + r]);
                         store4<DT>::run(crow + col, v);
+                        if (gu) {
+                            float g4[4], u4[4];
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) {
+                                g4[r] = acc[i][f][g * 4 + r];
+                                u4[r] = acc[i][f + NB / 2][g * 4 + r];
+                            }
+                            save_preact(gu, grow, NOUT, col, g4, u4);
+                        }
                     }
                 }
             } else {
@@ -523,7 +433,7 @@ __device__ __forceinline__ void store_tile32(const f32x16_t (&acc)[MB][NB], type
 template <typename DT, bool GATEUP, int WGM, int WGN>
 __global__ __launch_bounds__(WGM* WGN* kWave, MOE_P_MINB) void grouped_gemm_pipe_kernel(
     const typename DT::storage* __restrict__ A, const typename DT::storage* __restrict__ B0,
-    const typename DT::storage* __restrict__ B1, typename DT::storage* __restrict__ C,
+    const typename DT::storage* __restrict__ B1, typename DT::storage* __restrict__ C, float* __restrict__ gu,
     const uint32_t* __restrict__ a_rows, int a_nrows, const int4* __restrict__ tiles,
     const uint32_t* __restrict__ tile_count, int K, int NOUT, int n_tiles,
     int nblocks) {
@@ -686,7 +596,7 @@ __global__ __launch_bounds__(WGM* WGN* kWave, MOE_P_MINB) void grouped_gemm_pipe
         wait_vm<0>();
     }
 
-    store_tile32<DT, GATEUP, MB, NB, WTM, WTN, WCN>(acc, C, r0, r1, n0, wm, wn, NOUT, lane);
+    store_tile32<DT, GATEUP, MB, NB, WTM, WTN, WCN>(acc, C, gu, r0, r1, n0, wm, wn, NOUT, lane);
 }
 
 // ------------------------------------------------------------------ pipelined grouped GEMM, 64-wide K stages
@@ -707,7 +617,7 @@ constexpr int kP64SlotsA = 2, kP64SlotsB = 3;
 template <typename DT, bool GATEUP, int WGM, int WGN>
 __global__ __launch_bounds__(WGM* WGN* kWave, 1) void grouped_gemm_pipe64_kernel(
     const typename DT::storage* __restrict__ A, const typename DT::storage* __restrict__ B0,
-    const typename DT::storage* __restrict__ B1, typename DT::storage* __restrict__ C,
+    const typename DT::storage* __restrict__ B1, typename DT::storage* __restrict__ C, float* __restrict__ gu,
     const uint32_t* __restrict__ a_rows, int a_nrows, const int4* __restrict__ tiles,
     const uint32_t* __restrict__ tile_count, int K, int NOUT, int n_tiles, int nblocks) {
     using S = typename DT::storage;
@@ -887,24 +797,14 @@ __global__ __launch_bounds__(WGM* WGN* kWave, 1) void grouped_gemm_pipe64_kernel
             setup(m_idx, n_idx);
             prologue_dma();
         }
-        store_tile32<DT, GATEUP, MB, NB, WTM, WTN, WCN>(acc, C, c_r0, c_r1, c_n0, wm, wn, NOUT, lane);
+        store_tile32<DT, GATEUP, MB, NB, WTM, WTN, WCN>(acc, C, gu, c_r0, c_r1, c_n0, wm, wn, NOUT, lane);
         if (!more) break;
     }
 }
 
-struct GemmShape {
-    int BM;
-};
-
-int64_t max_mtiles(int64_t N, int64_t E, int BM) {
-    if (N <= 0) return 0;
-    const int64_t bound = (N + E * (BM - 1)) / BM;
-    return bound < N ? bound : N;
-}
-
 template <typename DT, bool GATEUP, int BM, int BNB, int WGM, int WGN>
 hipError_t launch_gemm(const void* A, const uint32_t* a_rows, int64_t a_nrows, const void* B0, const void* B1,
-                       void* C, const int4* tiles, const uint32_t* count, int64_t mt, int K, int NOUT,
+                       void* C, float* gu, const int4* tiles, const uint32_t* count, int64_t mt, int K, int NOUT,
                        hipStream_t s) {
     using S = typename DT::storage;
     constexpr int BN_OUT = GATEUP ? BNB / 2 : BNB;
@@ -913,14 +813,14 @@ hipError_t launch_gemm(const void* A, const uint32_t* a_rows, int64_t a_nrows, c
     if (nb == 0) return hipSuccess;
     if (nb > 0x7fffffff) return hipErrorInvalidValue;
     grouped_gemm_kernel<DT, GATEUP, BM, BNB, WGM, WGN><<<(unsigned)nb, WGM * WGN * kWave, 0, s>>>(
-        (const S*)A, (const S*)B0, (const S*)B1, (S*)C, a_rows, (int)a_nrows, tiles, count, K, NOUT, n_tiles,
+        (const S*)A, (const S*)B0, (const S*)B1, (S*)C, gu, a_rows, (int)a_nrows, tiles, count, K, NOUT, n_tiles,
         (int)nb);
     return hipGetLastError();
 }
 
 template <typename DT, bool GATEUP, int WGM, int WGN>
 hipError_t launch_pipe(const void* A, const uint32_t* a_rows, int64_t a_nrows, const void* B0, const void* B1,
-                       void* C, const int4* tiles, const uint32_t* count, int64_t mt, int K, int NOUT,
+                       void* C, float* gu, const int4* tiles, const uint32_t* count, int64_t mt, int K, int NOUT,
                        hipStream_t s) {
     using S = typename DT::storage;
     constexpr int BN_OUT = GATEUP ? kPipeBN / 2 : kPipeBN;
@@ -929,15 +829,15 @@ hipError_t launch_pipe(const void* A, const uint32_t* a_rows, int64_t a_nrows, c
     if (nb == 0) return hipSuccess;
     if (nb > 0x7fffffff) return hipErrorInvalidValue;
     grouped_gemm_pipe_kernel<DT, GATEUP, WGM, WGN><<<(unsigned)nb, WGM * WGN * kWave, 0, s>>>(
-        (const S*)A, (const S*)B0, (const S*)B1, (S*)C, a_rows, (int)a_nrows, tiles, count, K, NOUT, n_tiles,
+        (const S*)A, (const S*)B0, (const S*)B1, (S*)C, gu, a_rows, (int)a_nrows, tiles, count, K, NOUT, n_tiles,
         (int)nb);
     return hipGetLastError();
 }
 
 template <typename DT, bool GATEUP>
 hipError_t launch_pipe64(const void* A, const uint32_t* a_rows, int64_t a_nrows, const void* B0, const void* B1,
-                         void* C, const int4* tiles, const uint32_t* count, int64_t mt, int K, int NOUT,
-                         hipStream_t s) {
+                         void* C, float* gu, const int4* tiles, const uint32_t* count, int64_t mt, int K,
+                         int NOUT, hipStream_t s) {
     using S = typename DT::storage;
     constexpr int BN_OUT = GATEUP ? kPipeBN / 2 : kPipeBN;
     const int n_tiles = (NOUT + BN_OUT - 1) / BN_OUT;
@@ -948,7 +848,7 @@ hipError_t launch_pipe64(const void* A, const uint32_t* a_rows, int64_t a_nrows,
     // multiple of 8 so each workgroup's tiles stay on one XCD
     const int64_t grid = MOE_P64_PERSIST ? std::min<int64_t>(nb, (int64_t)persistent_slots(s)) : nb;
     grouped_gemm_pipe64_kernel<DT, GATEUP, MOE_P64_WM, MOE_P64_WN><<<(unsigned)grid, MOE_P64_WM * MOE_P64_WN * kWave, 0, s>>>(
-        (const S*)A, (const S*)B0, (const S*)B1, (S*)C, a_rows, (int)a_nrows, tiles, count, K, NOUT, n_tiles,
+        (const S*)A, (const S*)B0, (const S*)B1, (S*)C, gu, a_rows, (int)a_nrows, tiles, count, K, NOUT, n_tiles,
         (int)nb);
     return hipGetLastError();
 }
@@ -982,46 +882,57 @@ hipError_t launch_typed(const ExpertsArgs& a, hipStream_t s, ExpertsPart part) {
     int4* tiles = (int4*)((char*)a.tiles + 256);
     uint32_t* count = (uint32_t*)a.tiles;
     const int64_t mt = max_mtiles(a.N, a.E, BM);
-    if (mt >= kMaxTiles) return hipErrorInvalidValue;
-    build_tiles_kernel<<<1, 1024, 0, s>>>(a.offsets, a.E, (uint32_t)a.N, BM, (uint32_t)mt, tiles, count);
-    hipError_t err = hipGetLastError();
+    hipError_t err = launch_build_tiles(a.offsets, a.E, a.N, BM, mt, tiles, count, s);
     if (err != hipSuccess) return err;
     const int H = (int)a.H, I = (int)a.I;
     if (pipe && MOE_P_BK64 && a.H % 64 == 0 && a.I % 64 == 0) {
         if constexpr (sizeof(typename DT::storage) == 2) {
             if (part != kDown) {
-                err = launch_pipe64<DT, true>(a.x, a.x_rows, a.x_nrows, a.gate, a.up, a.h, tiles, count, mt, H, I, s);
+                err = launch_pipe64<DT, true>(a.x, a.x_rows, a.x_nrows, a.gate, a.up, a.h, a.gu, tiles, count, mt, H, I, s);
                 if (err != hipSuccess) return err;
             }
             if (part != kGateUp)
-                err = launch_pipe64<DT, false>(a.h, nullptr, 0, a.down, nullptr, a.y, tiles, count, mt, I, H, s);
+                err = launch_pipe64<DT, false>(a.h, nullptr, 0, a.down, nullptr, a.y, nullptr, tiles, count, mt, I, H, s);
         }
         return err;
     }
     if (pipe) {
         if constexpr (sizeof(typename DT::storage) == 2) {
             if (part != kDown) {
-                err = launch_pipe<DT, true, MOE_P_WM, MOE_P_WN>(a.x, a.x_rows, a.x_nrows, a.gate, a.up, a.h, tiles, count, mt, H, I, s);
+                err = launch_pipe<DT, true, MOE_P_WM, MOE_P_WN>(a.x, a.x_rows, a.x_nrows, a.gate, a.up, a.h, a.gu, tiles, count, mt, H, I, s);
                 if (err != hipSuccess) return err;
             }
             if (part != kGateUp)
-                err = launch_pipe<DT, false, MOE_P_WM, MOE_P_WN>(a.h, nullptr, 0, a.down, nullptr, a.y, tiles, count, mt, I, H, s);
+                err = launch_pipe<DT, false, MOE_P_WM, MOE_P_WN>(a.h, nullptr, 0, a.down, nullptr, a.y, nullptr, tiles, count, mt, I, H, s);
         }
         return err;
     }
     if (part != kDown) {
-        err = small ? launch_gemm<DT, true, 16, MOE_S_BN, 1, MOE_S_WN>(a.x, a.x_rows, a.x_nrows, a.gate, a.up, a.h, tiles, count, mt, H, I, s)
-                    : launch_gemm<DT, true, MOE_L_BM, MOE_L_BN, MOE_L_WM, MOE_L_WN>(a.x, a.x_rows, a.x_nrows, a.gate, a.up, a.h, tiles, count, mt, H, I, s);
+        err = small ? launch_gemm<DT, true, 16, MOE_S_BN, 1, MOE_S_WN>(a.x, a.x_rows, a.x_nrows, a.gate, a.up, a.h, a.gu, tiles, count, mt, H, I, s)
+                    : launch_gemm<DT, true, MOE_L_BM, MOE_L_BN, MOE_L_WM, MOE_L_WN>(a.x, a.x_rows, a.x_nrows, a.gate, a.up, a.h, a.gu, tiles, count, mt, H, I, s);
         if (err != hipSuccess) return err;
     }
     if (part != kGateUp) {
-        err = small ? launch_gemm<DT, false, 16, MOE_S_BN, 1, MOE_S_WN>(a.h, nullptr, 0, a.down, nullptr, a.y, tiles, count, mt, I, H, s)
-                    : launch_gemm<DT, false, MOE_L_BM, MOE_L_BN, MOE_L_WM, MOE_L_WN>(a.h, nullptr, 0, a.down, nullptr, a.y, tiles, count, mt, I, H, s);
+        err = small ? launch_gemm<DT, false, 16, MOE_S_BN, 1, MOE_S_WN>(a.h, nullptr, 0, a.down, nullptr, a.y, nullptr, tiles, count, mt, I, H, s)
+                    : launch_gemm<DT, false, MOE_L_BM, MOE_L_BN, MOE_L_WM, MOE_L_WN>(a.h, nullptr, 0, a.down, nullptr, a.y, nullptr, tiles, count, mt, I, H, s);
     }
     return err;
 }
 
 }  // namespace
+
+int64_t max_mtiles(int64_t N, int64_t E, int BM) {
+    if (N <= 0) return 0;
+    const int64_t bound = (N + E * (BM - 1)) / BM;
+    return bound < N ? bound : N;
+}
+
+hipError_t launch_build_tiles(const uint32_t* offsets, int E, int64_t N, int BM, int64_t max_tiles, int4* tiles,
+                              uint32_t* count, hipStream_t s) {
+    if (max_tiles >= kMaxTiles || N >= (int64_t)0xFFFFFFFF) return hipErrorInvalidValue;
+    build_tiles_kernel<<<1, 1024, 0, s>>>(offsets, E, (uint32_t)N, BM, (uint32_t)max_tiles, tiles, count);
+    return hipGetLastError();
+}
 
 size_t experts_tile_bytes(int64_t N, int64_t E) {
     return 256 + 16 * (size_t)max_mtiles(N, E, kSmallBM);

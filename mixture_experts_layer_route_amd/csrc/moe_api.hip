@@ -318,7 +318,8 @@ moe_status enqueue_dispatch(const void* x, int dtype, int64_t T, int64_t H, cons
 // holds the x_nrows token rows the products read through it.
 moe_status enqueue_experts(int dtype, int64_t E, int64_t H, int64_t I, const void* gate, const void* up,
                            const void* down, const void* x, const uint32_t* x_rows, int64_t x_nrows, int64_t N,
-                           const uint32_t* offsets, void* y, void* h, void* ws, hipStream_t s, ExpertsPart part) {
+                           const uint32_t* offsets, void* y, void* h, void* ws, hipStream_t s, ExpertsPart part,
+                           float* gu = nullptr) {
     const ExpertsWs l = experts_ws(N, I, E, dtype);
     ExpertsArgs a;
     a.dtype = dtype;
@@ -331,6 +332,7 @@ moe_status enqueue_experts(int dtype, int64_t E, int64_t H, int64_t I, const voi
     a.offsets = offsets;
     a.y = y;
     a.h = h ? h : (char*)ws + l.h;
+    a.gu = gu;
     a.tiles = (char*)ws + l.tiles;
     a.N = N;
     a.H = H;
@@ -620,6 +622,280 @@ moe_status moe_forward_sigmoid_grouped(const moe_tensor* gate, const moe_tensor*
                          stream, [&](uint32_t* idx, void* w, hipStream_t s) {
                              return enqueue_route_grouped(logits, bias, options, idx, w, s);
                          });
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- first-order training
+namespace {
+
+bool is_index(int dt) { return dt == MOE_U32 || dt == MOE_I32 || dt == MOE_I64; }
+
+moe_status check_router_options(moe_router_weight_options o) {
+    if (o.scoring != MOE_SCORING_SOFTMAX && o.scoring != MOE_SCORING_SIGMOID) return MOE_ERR_INVALID_ARGUMENT;
+    if (o.renormalize != 0 && o.renormalize != 1) return MOE_ERR_INVALID_ARGUMENT;
+    if (!(o.scale > 0.0f) || o.scale == INFINITY) return MOE_ERR_INVALID_ARGUMENT;
+    return MOE_OK;
+}
+
+// logits [T,E], indices [T,k], a [T,k] F32 tensor (weights or their gradient)
+moe_status check_router_train(const moe_tensor* logits, const moe_tensor* indices, const moe_tensor* tk,
+                              moe_router_weight_options o) {
+    MOE_TRY(check_tensor(logits, 2));
+    MOE_TRY(check_tensor(indices, 2));
+    MOE_TRY(check_tensor(tk, 2));
+    MOE_TRY(check_router_options(o));
+    if (!is_float(logits->dtype)) return MOE_ERR_DTYPE;
+    if (!is_index(indices->dtype)) return MOE_ERR_DTYPE;
+    if (tk->dtype != MOE_F32) return MOE_ERR_DTYPE;
+    const int64_t T = logits->dims[0], E = logits->dims[1], k = indices->dims[1];
+    if (E < 1) return MOE_ERR_SHAPE;
+    if (indices->dims[0] != T) return MOE_ERR_SHAPE;
+    if (k < 1 || k > E || k > 64) return MOE_ERR_TOP_K;
+    if (tk->dims[0] != T || tk->dims[1] != k) return MOE_ERR_SHAPE;
+    if (E > MOE_MAX_EXPERTS) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+RouterWeightArgs router_args(const moe_tensor* logits, const moe_tensor* indices, moe_router_weight_options o) {
+    RouterWeightArgs a = {};
+    a.logits = logits->data;
+    a.ldtype = logits->dtype;
+    a.idx = indices->data;
+    a.idx_dtype = indices->dtype;
+    a.T = logits->dims[0];
+    a.E = (int)logits->dims[1];
+    a.k = (int)indices->dims[1];
+    a.scoring = o.scoring;
+    a.renorm = o.renormalize;
+    a.scale = o.scale;
+    return a;
+}
+
+// rows [R,H] with an optional token_of_row [N]: the product rows; *N gets N
+moe_status check_product_rows(const moe_tensor* rows, const moe_tensor* tor, int dtype, int64_t H, int64_t* N) {
+    MOE_TRY(check_tensor(rows, 2));
+    if (tor) MOE_TRY(check_tensor(tor, 1));
+    if (rows->dtype != dtype) return MOE_ERR_DTYPE;
+    if (tor && tor->dtype != MOE_U32) return MOE_ERR_DTYPE;
+    if (rows->dims[1] != H) return MOE_ERR_SHAPE;
+    *N = tor ? tor->dims[0] : rows->dims[0];
+    if (tor && *N > 0 && rows->dims[0] < 1) return MOE_ERR_SHAPE;
+    return MOE_OK;
+}
+
+moe_status check_2d(const moe_tensor* t, int dtype, int64_t d0, int64_t d1) {
+    MOE_TRY(check_tensor(t, 2));
+    if (t->dtype != dtype) return MOE_ERR_DTYPE;
+    if (t->dims[0] != d0 || t->dims[1] != d1) return MOE_ERR_SHAPE;
+    return MOE_OK;
+}
+
+moe_status check_3d(const moe_tensor* t, int dtype, int64_t d0, int64_t d1, int64_t d2) {
+    MOE_TRY(check_tensor(t, 3));
+    if (t->dtype != dtype) return MOE_ERR_DTYPE;
+    if (t->dims[0] != d0 || t->dims[1] != d1 || t->dims[2] != d2) return MOE_ERR_SHAPE;
+    return MOE_OK;
+}
+
+struct BackwardWs {
+    size_t tiles, dgu, total;
+};
+BackwardWs backward_ws(int64_t N, int64_t I, int64_t E, int dtype) {
+    BackwardWs w;
+    w.tiles = 0;
+    w.dgu = align_up(experts_backward_tile_bytes(N, E));
+    w.total = w.dgu + align_up((size_t)N * 2 * (size_t)I * elem_size(dtype));
+    return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_router_weights(const moe_tensor* logits, const moe_tensor* indices,
+                              moe_router_weight_options options, moe_tensor* weights, void* stream) {
+    MOE_TRY(check_router_train(logits, indices, weights, options));
+    if (logits->dims[0] == 0) return MOE_OK;
+    hipStream_t s = (hipStream_t)stream;
+    MOE_TRY(check_devices(s, {logits->data, indices->data, weights->data}));
+    RouterWeightArgs a = router_args(logits, indices, options);
+    a.w = (float*)weights->data;
+    return launch_status(launch_router_weights(a, s));
+}
+
+moe_status moe_router_backward(const moe_tensor* logits, const moe_tensor* indices,
+                               const moe_tensor* grad_weights, moe_router_weight_options options,
+                               moe_tensor* grad_logits, void* stream) {
+    MOE_TRY(check_router_train(logits, indices, grad_weights, options));
+    MOE_TRY(check_2d(grad_logits, logits->dtype, logits->dims[0], logits->dims[1]));
+    if (logits->dims[0] == 0) return MOE_OK;
+    hipStream_t s = (hipStream_t)stream;
+    MOE_TRY(check_devices(s, {logits->data, indices->data, grad_weights->data, grad_logits->data}));
+    RouterWeightArgs a = router_args(logits, indices, options);
+    a.gw = (const float*)grad_weights->data;
+    a.dl = grad_logits->data;
+    return launch_status(launch_router_backward(a, s));
+}
+
+moe_status moe_combine_backward(const moe_tensor* expert_out, const moe_tensor* row_of_slot,
+                                const moe_tensor* weights, const moe_tensor* grad_output,
+                                moe_tensor* grad_expert_out, moe_tensor* grad_weights, void* stream) {
+    MOE_TRY(check_tensor(expert_out, 2));
+    MOE_TRY(check_tensor(row_of_slot, 1));
+    MOE_TRY(check_tensor(weights, 2));
+    MOE_TRY(check_tensor(grad_output, 2));
+    MOE_TRY(check_tensor(grad_expert_out, 2));
+    MOE_TRY(check_tensor(grad_weights, 2));
+    if (!is_float(expert_out->dtype) || !is_float(weights->dtype)) return MOE_ERR_DTYPE;
+    if (row_of_slot->dtype != MOE_U32) return MOE_ERR_DTYPE;
+    if (grad_output->dtype != expert_out->dtype || grad_expert_out->dtype != expert_out->dtype)
+        return MOE_ERR_DTYPE;
+    if (grad_weights->dtype != MOE_F32) return MOE_ERR_DTYPE;
+    const int64_t N = expert_out->dims[0], H = expert_out->dims[1];
+    const int64_t T = weights->dims[0], k = weights->dims[1];
+    if (k < 1) return MOE_ERR_TOP_K;
+    if (row_of_slot->dims[0] != T * k) return MOE_ERR_SHAPE;
+    if (grad_output->dims[0] != T || grad_output->dims[1] != H) return MOE_ERR_SHAPE;
+    if (grad_expert_out->dims[0] != N || grad_expert_out->dims[1] != H) return MOE_ERR_SHAPE;
+    if (grad_weights->dims[0] != T || grad_weights->dims[1] != k) return MOE_ERR_SHAPE;
+    if (T == 0) return MOE_OK;
+    hipStream_t s = (hipStream_t)stream;
+    MOE_TRY(check_devices(s, {expert_out->data, row_of_slot->data, weights->data, grad_output->data,
+                              grad_expert_out->data, grad_weights->data}));
+    CombineBackwardArgs a;
+    a.y = expert_out->data;
+    a.dtype = expert_out->dtype;
+    a.N = N;
+    a.row_of_slot = (const uint32_t*)row_of_slot->data;
+    a.w = weights->data;
+    a.wdtype = weights->dtype;
+    a.g = grad_output->data;
+    a.T = T;
+    a.k = (int)k;
+    a.H = H;
+    a.dy = grad_expert_out->data;
+    a.dw = (float*)grad_weights->data;
+    return launch_status(launch_combine_backward(a, s));
+}
+
+moe_status moe_experts_forward_training(const moe_tensor* gate, const moe_tensor* up, const moe_tensor* down,
+                                        const moe_tensor* rows, const moe_tensor* token_of_row,
+                                        const moe_tensor* expert_offsets, moe_tensor* expert_out,
+                                        moe_tensor* preact, moe_tensor* h, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+    MOE_TRY(check_weights(gate, up, down));
+    const int dt = gate->dtype;
+    const int64_t E = gate->dims[0], I = gate->dims[1], H = gate->dims[2];
+    int64_t N = 0;
+    MOE_TRY(check_product_rows(rows, token_of_row, dt, H, &N));
+    MOE_TRY(check_tensor(expert_offsets, 1));
+    if (expert_offsets->dtype != MOE_U32) return MOE_ERR_DTYPE;
+    if (expert_offsets->dims[0] != E + 1) return MOE_ERR_SHAPE;
+    MOE_TRY(check_2d(expert_out, dt, N, H));
+    MOE_TRY(check_2d(preact, MOE_F32, N, 2 * I));
+    MOE_TRY(check_2d(h, dt, N, I));
+    MOE_TRY(check_gemm_limits(E, H, I, N, {gate->data, up->data, down->data, rows->data, expert_out->data,
+                                           preact->data, h->data}));
+    if (!workspace || workspace_bytes < experts_ws(N, I, E, dt).total) return MOE_ERR_WORKSPACE;
+    if (N == 0) return MOE_OK;
+    hipStream_t s = (hipStream_t)stream;
+    const uint32_t* tor = token_of_row ? (const uint32_t*)token_of_row->data : nullptr;
+    MOE_TRY(check_devices(s, {gate->data, up->data, down->data, rows->data, tor ? (const void*)tor : rows->data,
+                              expert_offsets->data, expert_out->data, preact->data, h->data, workspace}));
+    return enqueue_experts(dt, E, H, I, gate->data, up->data, down->data, rows->data, tor, rows->dims[0], N,
+                           (const uint32_t*)expert_offsets->data, expert_out->data, h->data, workspace, s, kBoth,
+                           (float*)preact->data);
+}
+
+size_t moe_experts_backward_workspace_bytes(int64_t N, int64_t H, int64_t I, int64_t E, int32_t dtype) {
+    (void)H;
+    if (N < 0 || I < 1 || E < 1 || !is_float(dtype)) return 0;
+    return backward_ws(N, I, E, dtype).total;
+}
+
+moe_status moe_experts_backward(const moe_tensor* gate, const moe_tensor* up, const moe_tensor* down,
+                                const moe_tensor* rows, const moe_tensor* token_of_row,
+                                const moe_tensor* expert_offsets, const moe_tensor* preact, const moe_tensor* h,
+                                const moe_tensor* grad_expert_out, moe_tensor* grad_rows, moe_tensor* grad_gate,
+                                moe_tensor* grad_up, moe_tensor* grad_down, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+    MOE_TRY(check_weights(gate, up, down));
+    const int dt = gate->dtype;
+    const int64_t E = gate->dims[0], I = gate->dims[1], H = gate->dims[2];
+    int64_t N = 0;
+    MOE_TRY(check_product_rows(rows, token_of_row, dt, H, &N));
+    MOE_TRY(check_tensor(expert_offsets, 1));
+    if (expert_offsets->dtype != MOE_U32) return MOE_ERR_DTYPE;
+    if (expert_offsets->dims[0] != E + 1) return MOE_ERR_SHAPE;
+    MOE_TRY(check_2d(preact, MOE_F32, N, 2 * I));
+    MOE_TRY(check_2d(h, dt, N, I));
+    MOE_TRY(check_2d(grad_expert_out, dt, N, H));
+    MOE_TRY(check_2d(grad_rows, dt, N, H));
+    MOE_TRY(check_3d(grad_gate, MOE_F32, E, I, H));
+    MOE_TRY(check_3d(grad_up, MOE_F32, E, I, H));
+    MOE_TRY(check_3d(grad_down, MOE_F32, E, H, I));
+    MOE_TRY(check_gemm_limits(E, H, I, N, {gate->data, up->data, down->data, rows->data, preact->data, h->data,
+                                           grad_expert_out->data, grad_rows->data, grad_gate->data, grad_up->data,
+                                           grad_down->data}));
+    const BackwardWs l = backward_ws(N, I, E, dt);
+    if (!workspace || workspace_bytes < l.total) return MOE_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    const uint32_t* tor = token_of_row ? (const uint32_t*)token_of_row->data : nullptr;
+    MOE_TRY(check_devices(s, {gate->data, up->data, down->data, rows->data, tor ? (const void*)tor : rows->data,
+                              expert_offsets->data, preact->data, h->data, grad_expert_out->data, grad_rows->data,
+                              grad_gate->data, grad_up->data, grad_down->data, workspace}));
+    ExpertsBackwardArgs a;
+    a.dtype = dt;
+    a.gate = gate->data;
+    a.up = up->data;
+    a.down = down->data;
+    a.x = rows->data;
+    a.x_rows = tor;
+    a.x_nrows = rows->dims[0];
+    a.offsets = (const uint32_t*)expert_offsets->data;
+    a.gu = (const float*)preact->data;
+    a.h = h->data;
+    a.dy = grad_expert_out->data;
+    a.dx = grad_rows->data;
+    a.dgate = (float*)grad_gate->data;
+    a.dup = (float*)grad_up->data;
+    a.ddown = (float*)grad_down->data;
+    a.dgu = (char*)workspace + l.dgu;
+    a.tiles = (char*)workspace + l.tiles;
+    a.N = N;
+    a.H = H;
+    a.I = I;
+    a.E = (int)E;
+    // N == 0 still runs: every expert's weight gradients are written as zeros
+    return launch_status(launch_experts_backward(a, s));
+}
+
+moe_status moe_dispatch_backward(const moe_tensor* grad_rows, const moe_tensor* row_of_slot, int32_t top_k,
+                                 moe_tensor* grad_input, void* stream) {
+    MOE_TRY(check_tensor(grad_rows, 2));
+    MOE_TRY(check_tensor(row_of_slot, 1));
+    MOE_TRY(check_tensor(grad_input, 2));
+    if (!is_float(grad_rows->dtype)) return MOE_ERR_DTYPE;
+    if (row_of_slot->dtype != MOE_U32) return MOE_ERR_DTYPE;
+    if (grad_input->dtype != grad_rows->dtype) return MOE_ERR_DTYPE;
+    if (top_k < 1) return MOE_ERR_TOP_K;
+    const int64_t N = grad_rows->dims[0], H = grad_rows->dims[1], T = grad_input->dims[0];
+    if (grad_input->dims[1] != H) return MOE_ERR_SHAPE;
+    if (row_of_slot->dims[0] != T * top_k) return MOE_ERR_SHAPE;
+    if (T == 0) return MOE_OK;
+    hipStream_t s = (hipStream_t)stream;
+    MOE_TRY(check_devices(s, {grad_rows->data, row_of_slot->data, grad_input->data}));
+    DispatchBackwardArgs a;
+    a.drows = grad_rows->data;
+    a.dtype = grad_rows->dtype;
+    a.N = N;
+    a.row_of_slot = (const uint32_t*)row_of_slot->data;
+    a.T = T;
+    a.k = top_k;
+    a.H = H;
+    a.dx = grad_input->data;
+    return launch_status(launch_dispatch_backward(a, s));
 }
 
 }  // extern "C"

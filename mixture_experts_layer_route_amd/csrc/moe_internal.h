@@ -140,6 +140,7 @@ struct ExpertsArgs {
     const uint32_t* offsets;
     void* y;        // [N,H]
     void* h;        // [N,I] workspace
+    float* gu;      // null, or [N,2I] FP32: the gate/up product saves g | u (training forward)
     void* tiles;    // tile list workspace
     int64_t N, H, I;
     int E;
@@ -162,5 +163,73 @@ struct CombineArgs {
     void* out;
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+
+// ------------------------------------------------------------------ training
+struct RouterWeightArgs {
+    const void* logits;
+    int ldtype;          // moe_dtype of logits (and of dlogits)
+    const void* idx;     // [T,k] U32, I32 or I64
+    int idx_dtype;
+    const float* gw;     // [T,k] FP32 weight gradients (backward only)
+    int64_t T;
+    int E, k, scoring, renorm;
+    float scale;
+    float* w;            // [T,k] FP32 weights (forward only)
+    void* dl;            // [T,E] logits gradient (backward only)
+};
+hipError_t launch_router_weights(const RouterWeightArgs& a, hipStream_t s);
+hipError_t launch_router_backward(const RouterWeightArgs& a, hipStream_t s);
+
+struct ExpertsBackwardArgs {
+    int dtype;
+    const void* gate;
+    const void* up;
+    const void* down;
+    const void* x;           // [N,H] dispatched rows, or [x_nrows,H] token rows picked by x_rows
+    const uint32_t* x_rows;  // null, or token_of_row [N]
+    int64_t x_nrows;
+    const uint32_t* offsets;
+    const float* gu;         // [N,2I] saved g | u
+    const void* h;           // [N,I] saved activation
+    const void* dy;          // [N,H] expert-output gradient
+    void* dx;                // [N,H] dispatched-row gradient
+    float* dgate;            // [E,I,H]
+    float* dup;              // [E,I,H]
+    float* ddown;            // [E,H,I]
+    void* dgu;               // [N,2I] workspace (weight dtype)
+    void* tiles;             // tile list workspace
+    int64_t N, H, I;
+    int E;
+};
+size_t experts_backward_tile_bytes(int64_t N, int64_t E);
+hipError_t launch_experts_backward(const ExpertsBackwardArgs& a, hipStream_t s);
+
+struct CombineBackwardArgs {
+    const void* y;       // [N,H] expert outputs
+    int dtype;
+    int64_t N;
+    const uint32_t* row_of_slot;
+    const void* w;       // [T,k]
+    int wdtype;
+    const void* g;       // [T,H] output gradient
+    int64_t T;
+    int k;
+    int64_t H;
+    void* dy;            // [N,H]
+    float* dw;           // [T,k]
+};
+hipError_t launch_combine_backward(const CombineBackwardArgs& a, hipStream_t s);
+
+struct DispatchBackwardArgs {
+    const void* drows;   // [N,H]
+    int dtype;
+    int64_t N;
+    const uint32_t* row_of_slot;
+    int64_t T;
+    int k;
+    int64_t H;
+    void* dx;            // [T,H]
+};
+hipError_t launch_dispatch_backward(const DispatchBackwardArgs& a, hipStream_t s);
 
 }  // namespace moe

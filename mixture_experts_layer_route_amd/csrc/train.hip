@@ -1,0 +1,563 @@
+// train.hip -- first-order training of the experts stage and the backward of
+// the combine and dispatch steps on CDNA4.
+//
+// Follows the RUDA ruDNN library guide, section 12 (first-order MoE
+// training): the combine backward gives the expert-output gradient and FP32
+// weight gradients; the experts backward gives the dispatched-row gradient
+// and FP32 dgate, dup and ddown; the dispatch backward adds each token's
+// row gradients without applying the routing weights again.
+//
+// Experts backward.  For the rows r of expert e, with the saved FP32
+// pre-activations g = gate_e x, u = up_e x and the stored activation
+// h = silu(g) u (weight dtype), from dy (rows x H):
+//   dh      = dy down_e                       rows x I    product DH, K = H
+//   du      = dh silu(g)                      in DH's epilogue, FP32,
+//   dg      = dh u silu'(g)                   stored in the weight dtype as
+//             silu'(g) = s (1 + g (1 - s)),   dgu = [dg | du] (rows x 2I)
+//             s = 1 / (1 + exp(-g))
+//   dx      = dgu [gate_e ; up_e]             rows x H    product DX, K = 2I
+//   [dgate_e ; dup_e] = dgu^T x               2I x H      product DWGU, K = rows
+//   ddown_e = dy^T h                          H x I       product DWD,  K = rows
+// FP32 accumulation throughout; dgate, dup and ddown are written in FP32.
+//
+// Operand layouts.  The MFMA takes, per lane, 8 (16-bit) or 4 (f32)
+// consecutive K values of one output row or column.  The forward products
+// have K contiguous in memory for both operands; here only the DH and DX row
+// operands (dy, dgu) do.  The others -- down_e, gate_e, up_e read along
+// their first index, and every operand of the weight gradients, whose K runs
+// over dispatched rows -- are K-outer: contiguous along the output index.
+// Those are staged through registers: each thread loads 4 K-rows x 16 bytes,
+// transposes the 4 x 8 (or 4 x 4) block in registers and writes 8-byte (or
+// 16-byte) K-runs to LDS, so every tile sits in LDS with K contiguous and the
+// fragment reads are the same 16-byte reads as in the forward.
+//
+// Tiles: 128 x 128 outputs, 4 waves of 64 x 64, 16x16 MFMAs, 128-byte K
+// stages (64 bf16/f16 or 32 f32 values) double buffered.  DH and DX walk the
+// forward's per-expert row-tile list; the weight gradients walk (expert,
+// row tile, column tile) over all experts, and an expert without rows gets
+// zero gradients.
+#include <algorithm>
+
+#include "mfma.h"
+#include "tiles.h"
+
+namespace moe {
+namespace {
+
+enum TrainProduct { kDH = 0, kDX = 1, kDWGU = 2, kDWD = 3 };
+
+struct TrainGemm {
+    const void* a;            // DH, DWD: dy [N,H]; DX, DWGU: dgu [N,2I]
+    const void* b0;           // DH: down [E,H,I]; DX: gate [E,I,H]; DWGU: x rows; DWD: h [N,I]
+    const void* b1;           // DX: up [E,I,H]
+    const uint32_t* b_rows;   // DWGU: token_of_row (x holds b_nrows token rows) or null
+    int b_nrows;
+    const float* gu;          // DH: saved g | u [N,2I]
+    void* c0;                 // DH: dgu; DX: dx [N,H]; DWGU: dgate; DWD: ddown
+    void* c1;                 // DWGU: dup
+    const int4* tiles;        // DH, DX: row-tile list and its length
+    const uint32_t* tile_count;
+    const uint32_t* offsets;  // DWGU, DWD: expert_offsets [E+1]
+    int N, H, I;
+    int n_tiles;              // output column tiles
+    int m_tiles;              // DWGU, DWD: output row tiles per expert
+    int nblocks;
+};
+
+constexpr int kTBM = 128, kTBN = 128, kTThreads = 256;
+constexpr int kTStride = 144;  // LDS bytes per operand row: 128 of K + 16 of padding
+constexpr int kTStage = (kTBM + kTBN) * kTStride;
+
+// Workgroup -> logical tile id: each XCD (workgroup b runs on XCD b % 8)
+// gets a contiguous run of ids, so neighbouring tiles share its L2.
+__device__ __forceinline__ int xcd_contiguous(int bid, int nblocks) {
+    const int q = nblocks / 8, rem = nblocks % 8;
+    const int xcd = bid % 8, loc = bid / 8;
+    return (xcd < rem ? xcd * (q + 1) : rem * (q + 1) + (xcd - rem) * q) + loc;
+}
+
+// 4 K-rows of V values each (w[j] = 16 bytes of K-row j) -> V K-runs of 4
+// values (out[i] = values (i, K-rows 0..3), the lower K-row in the lower bits).
+template <int ES> struct transpose4;
+template <> struct transpose4<2> {
+    static __device__ __forceinline__ void run(const uint4 (&w)[4], uint2 (&out)[8]) {
+        const uint32_t* r0 = (const uint32_t*)&w[0];
+        const uint32_t* r1 = (const uint32_t*)&w[1];
+        const uint32_t* r2 = (const uint32_t*)&w[2];
+        const uint32_t* r3 = (const uint32_t*)&w[3];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            out[2 * p].x = (r0[p] & 0xffffu) | (r1[p] << 16);
+            out[2 * p].y = (r2[p] & 0xffffu) | (r3[p] << 16);
+            out[2 * p + 1].x = (r0[p] >> 16) | (r1[p] & 0xffff0000u);
+            out[2 * p + 1].y = (r2[p] >> 16) | (r3[p] & 0xffff0000u);
+        }
+    }
+};
+template <> struct transpose4<4> {
+    static __device__ __forceinline__ void run(const uint4 (&w)[4], uint4 (&out)[4]) {
+        out[0] = make_uint4(w[0].x, w[1].x, w[2].x, w[3].x);
+        out[1] = make_uint4(w[0].y, w[1].y, w[2].y, w[3].y);
+        out[2] = make_uint4(w[0].z, w[1].z, w[2].z, w[3].z);
+        out[3] = make_uint4(w[0].w, w[1].w, w[2].w, w[3].w);
+    }
+};
+
+template <typename DT, int MODE>
+__global__ __launch_bounds__(kTThreads, 2) void train_gemm_kernel(TrainGemm p) {
+    using S = typename DT::storage;
+    constexpr int ES = (int)sizeof(S);
+    constexpr int KS = 128 / ES;   // K values per stage
+    constexpr int V = 16 / ES;     // values per 16-byte vector
+    constexpr int KQ = KS / 4;     // K-outer: 4-row groups per stage
+    constexpr bool A_KOUTER = MODE == kDWGU || MODE == kDWD;
+    constexpr int MF = 4, NF = 4;  // 16-row fragments per wave and side
+
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kTStage];
+
+    const int tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
+    const int wm = wid / 2, wn = wid % 2;
+    const int64_t I2 = 2 * (int64_t)p.I;
+
+    // ---- this workgroup's tile: expert e, output rows [m0, m1), columns
+    // [n0, n0 + 128), K range [kb, ke)
+    int e, m0, m1, n0, kb, ke, ncols, lda;
+    if constexpr (MODE == kDH || MODE == kDX) {
+        int mi, ni;
+        if (!tile_of_block(blockIdx.x, p.nblocks, p.n_tiles, (int)*p.tile_count, p.tiles, &mi, &ni)) return;
+        const int4 tl = p.tiles[mi];
+        e = tl.x;
+        m0 = tl.y;
+        m1 = tl.z;
+        n0 = ni * kTBN;
+        kb = 0;
+        ke = MODE == kDH ? p.H : 2 * p.I;
+        ncols = MODE == kDH ? p.I : p.H;
+        lda = ke;
+    } else {
+        const int pid = xcd_contiguous(blockIdx.x, p.nblocks);
+        const int per = p.m_tiles * p.n_tiles;
+        e = pid / per;
+        const int rem = pid - e * per;
+        const int mrows = MODE == kDWGU ? 2 * p.I : p.H;
+        m0 = (rem % p.m_tiles) * kTBM;
+        m1 = min(m0 + kTBM, mrows);
+        n0 = (rem / p.m_tiles) * kTBN;
+        kb = (int)min(p.offsets[e], (uint32_t)p.N);
+        ke = max((int)min(p.offsets[e + 1], (uint32_t)p.N), kb);
+        ncols = MODE == kDWGU ? p.H : p.I;
+        lda = mrows;
+    }
+    const S* A = (const S*)p.a;
+
+    // ---- K-outer row pointers: row k of the N-side operand (B), or of the
+    // M-side operand (A) of the weight gradients
+    auto b_row = [&](int k) -> const S* {
+        if constexpr (MODE == kDH) {
+            return (const S*)p.b0 + ((int64_t)e * p.H + k) * p.I;
+        } else if constexpr (MODE == kDX) {
+            return k < p.I ? (const S*)p.b0 + ((int64_t)e * p.I + k) * p.H
+                           : (const S*)p.b1 + ((int64_t)e * p.I + (k - p.I)) * p.H;
+        } else if constexpr (MODE == kDWGU) {
+            return (const S*)p.b0 + src_row(p.b_rows, p.b_nrows, k) * p.H;
+        } else {
+            return (const S*)p.b0 + (int64_t)k * p.I;
+        }
+    };
+
+    // ---- staging registers
+    uint4 ra[4], rb[4];
+    // K-contiguous M side (DH, DX): thread -> 16-byte chunk (tid % 8) of rows
+    // tid / 8 + 32 j
+    const int kc_ch = tid % 8, kc_row = tid / 8;
+    // K-outer operands: thread -> K-rows 4 (tid % KQ) + 0..3, values
+    // V (tid / KQ) + 0..V-1 of the 128 output rows/columns
+    const int ko_q = tid % KQ, ko_c = (tid / KQ) * V;
+
+    auto load_kouter = [&](uint4 (&r)[4], int kbase, int cbase, int climit, bool is_a) {
+        const int col = cbase + ko_c < climit ? cbase + ko_c : 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int k = kbase + ko_q * 4 + j;
+            const bool kin = k < ke;
+            const int kk = kin ? k : ke - 1;
+            const S* row;
+            if constexpr (A_KOUTER) {
+                row = is_a ? A + (int64_t)kk * lda : b_row(kk);
+            } else {
+                row = b_row(kk);
+            }
+            const uint4 v = *(const uint4*)(row + col);
+            r[j] = kin ? v : make_uint4(0, 0, 0, 0);
+        }
+    };
+    auto load_kcontig = [&](uint4 (&r)[4], int kbase) {
+        const int k = kbase + kc_ch * V;
+        const bool kin = k < ke;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int row = min(m0 + kc_row + 32 * j, m1 - 1);
+            const uint4 v = *(const uint4*)(A + (int64_t)row * lda + (kin ? k : 0));
+            r[j] = kin ? v : make_uint4(0, 0, 0, 0);
+        }
+    };
+    auto gload = [&](int kbase) {
+        if constexpr (A_KOUTER)
+            load_kouter(ra, kbase, m0, m1, true);
+        else
+            load_kcontig(ra, kbase);
+        load_kouter(rb, kbase, n0, ncols, false);
+    };
+    auto store_kouter = [&](unsigned char* base, const uint4 (&r)[4]) {
+        if constexpr (ES == 2) {
+            uint2 t[8];
+            transpose4<2>::run(r, t);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) *(uint2*)(base + (ko_c + i) * kTStride + ko_q * 8) = t[i];
+        } else {
+            uint4 t[4];
+            transpose4<4>::run(r, t);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) *(uint4*)(base + (ko_c + i) * kTStride + ko_q * 16) = t[i];
+        }
+    };
+    auto lstore = [&](int st) {
+        unsigned char* base = smem + st * kTStage;
+        if constexpr (A_KOUTER) {
+            store_kouter(base, ra);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) *(uint4*)(base + (kc_row + 32 * j) * kTStride + kc_ch * 16) = ra[j];
+        }
+        store_kouter(base + kTBM * kTStride, rb);
+    };
+
+    int fa[MF], fb[NF];
+#pragma unroll
+    for (int i = 0; i < MF; ++i) fa[i] = (wm * 64 + i * 16 + (lane & 15)) * kTStride + (lane >> 4) * 16;
+#pragma unroll
+    for (int f = 0; f < NF; ++f) fb[f] = (kTBM + wn * 64 + f * 16 + (lane & 15)) * kTStride + (lane >> 4) * 16;
+
+    f32x4_t acc[MF][NF];
+#pragma unroll
+    for (int i = 0; i < MF; ++i)
+#pragma unroll
+        for (int f = 0; f < NF; ++f) acc[i][f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    const int nk = (ke - kb + KS - 1) / KS;
+    if (nk > 0) {
+        gload(kb);
+        lstore(0);
+        __syncthreads();
+    }
+    for (int kt = 0; kt < nk; ++kt) {
+        const int st = kt & 1;
+        if (kt + 1 < nk) gload(kb + (kt + 1) * KS);
+        const unsigned char* base = smem + st * kTStage;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            uint4 av[MF], bv[NF];
+#pragma unroll
+            for (int i = 0; i < MF; ++i) av[i] = *(const uint4*)(base + fa[i] + kk * 64);
+#pragma unroll
+            for (int f = 0; f < NF; ++f) bv[f] = *(const uint4*)(base + fb[f] + kk * 64);
+#pragma unroll
+            for (int i = 0; i < MF; ++i)
+#pragma unroll
+                for (int f = 0; f < NF; ++f) acc[i][f] = mma<DT>::run(bv[f], av[i], acc[i][f]);
+        }
+        if (kt + 1 < nk) lstore(st ^ 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue: lane holds output row (lane % 16) of each M fragment and
+    // columns 4 (lane / 16) + 0..3 of each N fragment
+#pragma unroll
+    for (int i = 0; i < MF; ++i) {
+        const int m = m0 + wm * 64 + i * 16 + (lane & 15);
+        if (m >= m1) continue;
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+            const int col = n0 + wn * 64 + f * 16 + (lane >> 4) * 4;
+            if (col >= ncols) continue;
+            if constexpr (MODE == kDH) {
+                const float* gr = p.gu + (int64_t)m * I2 + col;
+                const float4 g4 = *(const float4*)gr;
+                const float4 u4 = *(const float4*)(gr + p.I);
+                const float gv[4] = {g4.x, g4.y, g4.z, g4.w}, uv[4] = {u4.x, u4.y, u4.z, u4.w};
+                float dg[4], du[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float dh = acc[i][f][r];
+                    const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-gv[r]));
+                    du[r] = dh * (gv[r] * sg);
+                    dg[r] = dh * uv[r] * (sg * (1.0f + gv[r] * (1.0f - sg)));
+                }
+                S* out = (S*)p.c0 + (int64_t)m * I2 + col;
+                store4<DT>::run(out, dg);
+                store4<DT>::run(out + p.I, du);
+            } else if constexpr (MODE == kDX) {
+                const float v[4] = {acc[i][f][0], acc[i][f][1], acc[i][f][2], acc[i][f][3]};
+                store4<DT>::run((S*)p.c0 + (int64_t)m * p.H + col, v);
+            } else {
+                float* out;
+                if constexpr (MODE == kDWGU)
+                    out = m < p.I ? (float*)p.c0 + ((int64_t)e * p.I + m) * p.H + col
+                                  : (float*)p.c1 + ((int64_t)e * p.I + (m - p.I)) * p.H + col;
+                else
+                    out = (float*)p.c0 + ((int64_t)e * p.H + m) * p.I + col;
+                *(float4*)out = make_float4(acc[i][f][0], acc[i][f][1], acc[i][f][2], acc[i][f][3]);
+            }
+        }
+    }
+}
+
+template <typename DT, int MODE>
+hipError_t launch_train_gemm(TrainGemm p, int64_t blocks, hipStream_t s) {
+    if (blocks == 0) return hipSuccess;
+    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+    p.nblocks = (int)blocks;
+    train_gemm_kernel<DT, MODE><<<(unsigned)blocks, kTThreads, 0, s>>>(p);
+    return hipGetLastError();
+}
+
+template <typename DT>
+hipError_t experts_backward_typed(const ExpertsBackwardArgs& a, hipStream_t s) {
+    const int E = a.E, H = (int)a.H, I = (int)a.I, N = (int)a.N;
+    int4* tiles = (int4*)((char*)a.tiles + 256);
+    uint32_t* count = (uint32_t*)a.tiles;
+    const int64_t mt = max_mtiles(a.N, a.E, kTBM);
+    hipError_t err = launch_build_tiles(a.offsets, E, a.N, kTBM, mt, tiles, count, s);
+    if (err != hipSuccess) return err;
+
+    TrainGemm p = {};
+    p.N = N;
+    p.H = H;
+    p.I = I;
+    p.tiles = tiles;
+    p.tile_count = count;
+    p.offsets = a.offsets;
+
+    // dh -> dgu = [dg | du]
+    p.a = a.dy;
+    p.b0 = a.down;
+    p.gu = a.gu;
+    p.c0 = a.dgu;
+    p.n_tiles = (I + kTBN - 1) / kTBN;
+    err = launch_train_gemm<DT, kDH>(p, mt * p.n_tiles, s);
+    if (err != hipSuccess) return err;
+
+    // dx = dgu [gate ; up]
+    p.a = a.dgu;
+    p.b0 = a.gate;
+    p.b1 = a.up;
+    p.c0 = a.dx;
+    p.n_tiles = (H + kTBN - 1) / kTBN;
+    err = launch_train_gemm<DT, kDX>(p, mt * p.n_tiles, s);
+    if (err != hipSuccess) return err;
+
+    // [dgate ; dup] = dgu^T x
+    p.a = a.dgu;
+    p.b0 = a.x;
+    p.b1 = nullptr;
+    p.b_rows = a.x_rows;
+    p.b_nrows = (int)a.x_nrows;
+    p.c0 = a.dgate;
+    p.c1 = a.dup;
+    p.m_tiles = (2 * I + kTBM - 1) / kTBM;
+    p.n_tiles = (H + kTBN - 1) / kTBN;
+    err = launch_train_gemm<DT, kDWGU>(p, (int64_t)E * p.m_tiles * p.n_tiles, s);
+    if (err != hipSuccess) return err;
+
+    // ddown = dy^T h
+    p.a = a.dy;
+    p.b0 = a.h;
+    p.b_rows = nullptr;
+    p.b_nrows = 0;
+    p.c0 = a.ddown;
+    p.c1 = nullptr;
+    p.m_tiles = (H + kTBM - 1) / kTBM;
+    p.n_tiles = (I + kTBN - 1) / kTBN;
+    return launch_train_gemm<DT, kDWD>(p, (int64_t)E * p.m_tiles * p.n_tiles, s);
+}
+
+// ------------------------------------------------------------------ combine / dispatch backward
+// One wavefront per token, 4 tokens per workgroup; lane -> 16-byte column
+// chunks c = lane, lane + 64, ... of the token's rows (or single values when
+// H is not a whole number of chunks).
+
+// dY[row_j] = w_j g (rounded to the expert dtype), dw_j = <Y[row_j], g> in
+// FP32; a token with a slot row >= N gets NaN weight gradients.
+template <typename DT, typename WT, int VEC>
+__global__ __launch_bounds__(256) void combine_backward_kernel(
+    const typename DT::storage* __restrict__ Y, int64_t N, const uint32_t* __restrict__ row_of_slot,
+    const typename WT::storage* __restrict__ w, const typename DT::storage* __restrict__ g, int64_t T, int k,
+    int64_t H, typename DT::storage* __restrict__ dY, float* __restrict__ dw) {
+    using S = typename DT::storage;
+    const int lane = lane_id();
+    const int64_t t = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
+    if (t >= T) return;
+    const uint32_t* rs = row_of_slot + t * k;
+    bool invalid = false;
+    for (int j = 0; j < k; ++j) invalid |= (int64_t)rs[j] >= N;
+    const S* gt = g + t * H;
+    const int64_t chunks = H / VEC;
+    for (int j = 0; j < k; ++j) {
+        const int64_t row = rs[j];
+        float dot = 0.0f;
+        if (row < N) {
+            const float wj = fmt<WT>::load(w[t * k + j]);
+            const S* yr = Y + row * H;
+            S* dr = dY + row * H;
+            for (int64_t c = lane; c < chunks; c += kWave) {
+                S gv[VEC], yv[VEC], ov[VEC];
+                if constexpr (VEC * sizeof(S) == 16) {
+                    *(uint4*)gv = *(const uint4*)(gt + c * VEC);
+                    *(uint4*)yv = *(const uint4*)(yr + c * VEC);
+                } else {
+                    gv[0] = gt[c];
+                    yv[0] = yr[c];
+                }
+#pragma unroll
+                for (int v = 0; v < VEC; ++v) {
+                    const float gf = fmt<DT>::load(gv[v]);
+                    dot = fmaf(fmt<DT>::load(yv[v]), gf, dot);
+                    ov[v] = fmt<DT>::store(wj * gf);
+                }
+                if constexpr (VEC * sizeof(S) == 16)
+                    *(uint4*)(dr + c * VEC) = *(const uint4*)ov;
+                else
+                    dr[c] = ov[0];
+            }
+        }
+        dot = wave_sum(dot);
+        if (lane == 0) dw[t * k + j] = invalid ? __uint_as_float(0x7fc00000u) : dot;
+    }
+}
+
+// dx[t] = sum_j drows[row_j] in FP32, slot order, rounded once; a token with
+// a slot row >= N gets a NaN row.
+template <typename DT, int VEC>
+__global__ __launch_bounds__(256) void dispatch_backward_kernel(const typename DT::storage* __restrict__ drows,
+                                                                int64_t N, const uint32_t* __restrict__ row_of_slot,
+                                                                int64_t T, int k, int64_t H,
+                                                                typename DT::storage* __restrict__ dx) {
+    using S = typename DT::storage;
+    const int lane = lane_id();
+    const int64_t t = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
+    if (t >= T) return;
+    const uint32_t* rs = row_of_slot + t * k;
+    bool invalid = false;
+    for (int j = 0; j < k; ++j) invalid |= (int64_t)rs[j] >= N;
+    const int64_t chunks = H / VEC;
+    for (int64_t c = lane; c < chunks; c += kWave) {
+        float acc[VEC];
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) acc[v] = invalid ? __uint_as_float(0x7fc00000u) : 0.0f;
+        if (!invalid) {
+            for (int j = 0; j < k; ++j) {
+                S rv[VEC];
+                const S* src = drows + (int64_t)rs[j] * H + c * VEC;
+                if constexpr (VEC * sizeof(S) == 16)
+                    *(uint4*)rv = *(const uint4*)src;
+                else
+                    rv[0] = *src;
+#pragma unroll
+                for (int v = 0; v < VEC; ++v) acc[v] += fmt<DT>::load(rv[v]);
+            }
+        }
+        S ov[VEC];
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) ov[v] = fmt<DT>::store(acc[v]);
+        if constexpr (VEC * sizeof(S) == 16)
+            *(uint4*)(dx + t * H + c * VEC) = *(const uint4*)ov;
+        else
+            dx[t * H + c] = ov[0];
+    }
+}
+
+bool wide_rows(int64_t H, int es, std::initializer_list<const void*> ptrs) {
+    if (H % (16 / es)) return false;
+    for (const void* q : ptrs)
+        if ((uintptr_t)q % 16) return false;
+    return true;
+}
+
+template <typename DT, typename WT>
+hipError_t combine_backward_typed(const CombineBackwardArgs& a, hipStream_t s) {
+    using S = typename DT::storage;
+    using W = typename WT::storage;
+    constexpr int V16 = 16 / sizeof(S);
+    const dim3 grid((unsigned)((a.T + 3) / 4)), block(256);
+    if (wide_rows(a.H, sizeof(S), {a.y, a.g, a.dy}))
+        combine_backward_kernel<DT, WT, V16><<<grid, block, 0, s>>>((const S*)a.y, a.N, a.row_of_slot, (const W*)a.w,
+                                                                   (const S*)a.g, a.T, a.k, a.H, (S*)a.dy, a.dw);
+    else
+        combine_backward_kernel<DT, WT, 1><<<grid, block, 0, s>>>((const S*)a.y, a.N, a.row_of_slot, (const W*)a.w,
+                                                                 (const S*)a.g, a.T, a.k, a.H, (S*)a.dy, a.dw);
+    return hipGetLastError();
+}
+
+template <typename DT>
+hipError_t combine_backward_w(const CombineBackwardArgs& a, hipStream_t s) {
+    switch (a.wdtype) {
+    case MOE_F32: return combine_backward_typed<DT, f32_t>(a, s);
+    case MOE_F16: return combine_backward_typed<DT, f16_t>(a, s);
+    case MOE_BF16: return combine_backward_typed<DT, bf16_t>(a, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <typename DT>
+hipError_t dispatch_backward_typed(const DispatchBackwardArgs& a, hipStream_t s) {
+    using S = typename DT::storage;
+    constexpr int V16 = 16 / sizeof(S);
+    const dim3 grid((unsigned)((a.T + 3) / 4)), block(256);
+    if (wide_rows(a.H, sizeof(S), {a.drows, a.dx}))
+        dispatch_backward_kernel<DT, V16><<<grid, block, 0, s>>>((const S*)a.drows, a.N, a.row_of_slot, a.T, a.k,
+                                                                a.H, (S*)a.dx);
+    else
+        dispatch_backward_kernel<DT, 1><<<grid, block, 0, s>>>((const S*)a.drows, a.N, a.row_of_slot, a.T, a.k, a.H,
+                                                              (S*)a.dx);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t experts_backward_tile_bytes(int64_t N, int64_t E) { return 256 + 16 * (size_t)max_mtiles(N, E, kTBM); }
+
+hipError_t launch_experts_backward(const ExpertsBackwardArgs& a, hipStream_t s) {
+    if (a.E < 1) return hipErrorInvalidValue;
+    if ((int64_t)a.E * ((2 * a.I + kTBM - 1) / kTBM) * ((a.H + kTBN - 1) / kTBN) > 0x7fffffff)
+        return hipErrorInvalidValue;
+    switch (a.dtype) {
+    case MOE_F32: return experts_backward_typed<f32_t>(a, s);
+    case MOE_F16: return experts_backward_typed<f16_t>(a, s);
+    case MOE_BF16: return experts_backward_typed<bf16_t>(a, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_combine_backward(const CombineBackwardArgs& a, hipStream_t s) {
+    if (a.T == 0) return hipSuccess;
+    if ((a.T + 3) / 4 > 0x7fffffff) return hipErrorInvalidValue;
+    switch (a.dtype) {
+    case MOE_F32: return combine_backward_w<f32_t>(a, s);
+    case MOE_F16: return combine_backward_w<f16_t>(a, s);
+    case MOE_BF16: return combine_backward_w<bf16_t>(a, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_dispatch_backward(const DispatchBackwardArgs& a, hipStream_t s) {
+    if (a.T == 0) return hipSuccess;
+    if ((a.T + 3) / 4 > 0x7fffffff) return hipErrorInvalidValue;
+    switch (a.dtype) {
+    case MOE_F32: return dispatch_backward_typed<f32_t>(a, s);
+    case MOE_F16: return dispatch_backward_typed<f16_t>(a, s);
+    case MOE_BF16: return dispatch_backward_typed<bf16_t>(a, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace moe

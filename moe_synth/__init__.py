@@ -15,6 +15,7 @@ Recipe (the same for every consumer):
   * the routing edge workload rounds its logits to integers (half to even)
     clamped to [-3, 3] and plants, in a seeded random set of rows, one NaN
     (5% of rows), one +inf (5%) or a row of -inf (2%);
+  * the training step's output gradient is N(0, 1) [T,H] in the input dtype;
   * the skewed workload adds to every logit column e the bias
     2 * ln(w_(e+1)) with Zipf weights w_r = r^-1.1 / sum_j j^-1.1 (expert e
     has Zipf rank e + 1), so a few low-id experts are hot.
@@ -33,7 +34,7 @@ import torch
 TORCH_DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 
 # tensor ids of the per-tensor streams
-_X, _LOGITS, _GATE, _UP, _DOWN, _EDGE = 1, 2, 3, 4, 5, 6
+_X, _LOGITS, _GATE, _UP, _DOWN, _EDGE, _GRAD_OUT = 1, 2, 3, 4, 5, 6, 7
 
 
 @dataclass(frozen=True)
@@ -150,6 +151,13 @@ def make_weights(cfg: MoeConfig, device="cpu", seed: int | None = None):
         up[e].copy_(u)
         down[e].copy_(d)
     return gate, up, down
+
+
+def make_grad_output(cfg: MoeConfig, device="cpu", seed: int | None = None, T: int | None = None):
+    """d loss / d output [T,H] of one training step, N(0, 1) in cfg.dtype."""
+    seed = cfg.seed if seed is None else seed
+    T = cfg.T if T is None else T
+    return _normal((T, cfg.H), device, seed, _GRAD_OUT).to(TORCH_DT[cfg.dtype])
 
 
 def to_bits(t: torch.Tensor) -> np.ndarray:

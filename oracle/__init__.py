@@ -422,14 +422,19 @@ def experts_backward(gate, up, down, dt: str, rows: np.ndarray, offsets: np.ndar
 
 
 def train_step(x: np.ndarray, logits: np.ndarray, gate, up, down, dt: str, ldt: str, top_k: int,
-               renormalize: bool, grad_output: np.ndarray, nthreads: int | None = None) -> dict:
+               renormalize: bool, grad_output: np.ndarray, nthreads: int | None = None,
+               indices: np.ndarray | None = None, scoring: str = "softmax", scale: float = 1.0) -> dict:
     """Forward of the chain with training caches, then the section's four
-    backward steps in order: combine, experts, dispatch, router."""
+    backward steps in order: combine, experts, dispatch, router.  The
+    selection is the softmax route's unless ``indices`` [T,k] (U32) is given."""
     T, H = x.shape
     E = logits.shape[1]
     I = gate.shape[1]
-    idx, _, _ = route(logits, ldt, top_k, renormalize, nthreads)
-    w32 = router_weights(logits, ldt, idx, "softmax", renormalize, 1.0, nthreads)
+    if indices is None:
+        idx, _, _ = route(logits, ldt, top_k, renormalize, nthreads)
+    else:
+        idx = np.ascontiguousarray(indices, dtype=np.uint32)
+    w32 = router_weights(logits, ldt, idx, scoring, renormalize, scale, nthreads)
     offsets, ros, tor, rows = dispatch(idx, E, x, dt)
     fw = experts_train_forward(gate, up, down, dt, rows, offsets, E, H, I, nthreads)
     out = combine(fw["output"], dt, ros, w32, "f32", T, top_k, H, nthreads)
@@ -437,7 +442,7 @@ def train_step(x: np.ndarray, logits: np.ndarray, gate, up, down, dt: str, ldt: 
     drows, dgate, dup, ddown = experts_backward(gate, up, down, dt, rows, offsets, E, H, I, fw["g"], fw["u"],
                                                 fw["h"], dY, nthreads)
     dx = dispatch_backward(drows, dt, ros, T, top_k, H, nthreads)
-    dl = router_backward(logits, ldt, idx, dw, "softmax", renormalize, 1.0, nthreads)
+    dl = router_backward(logits, ldt, idx, dw, scoring, renormalize, scale, nthreads)
     return {"indices": idx, "weights_f32": w32, "offsets": offsets, "row_of_slot": ros, "dispatched": rows,
             "Y": fw["output"], "h": fw["h"], "g": fw["g"], "u": fw["u"], "output": out, "dY": dY,
             "dweights": dw, "drows": drows, "dgate": dgate, "dup": dup, "ddown": ddown, "dx": dx,

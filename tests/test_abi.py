@@ -297,3 +297,125 @@ def test_forward_sigmoid_grouped_validation(L):
     assert f(lg=raw_tensor(FAKE, F32, (T, E + 4))) == SHAPE
     assert f(wsb=ws - 1) == WORKSPACE
     assert f() == DEVICE and f(bias=raw_tensor(FAKE, F32, (E,))) == DEVICE
+
+
+# ---------------------------------------------------------------- first-order training
+I32, I64 = _lib.MOE_I32, _lib.MOE_I64
+
+
+def _rw(L, lg, idx, w, scoring=0, renorm=1, scale=1.0):
+    return L.moe_router_weights(ctypes.byref(lg), ctypes.byref(idx), _lib.MoeRouterWeightOptions(scoring, renorm, scale),
+                                ctypes.byref(w), None)
+
+
+def _rb(L, lg, idx, gw, dl, scoring=0, renorm=1, scale=1.0):
+    return L.moe_router_backward(ctypes.byref(lg), ctypes.byref(idx), ctypes.byref(gw),
+                                 _lib.MoeRouterWeightOptions(scoring, renorm, scale), ctypes.byref(dl), None)
+
+
+def test_router_training_validation(L):
+    T, E, k = 16, 8, 2
+    lg = raw_tensor(FAKE, BF16, (T, E))
+    idx = raw_tensor(FAKE, I64, (T, k))
+    w = raw_tensor(FAKE, F32, (T, k))
+    dl = raw_tensor(FAKE, BF16, (T, E))
+    assert _rw(L, lg, raw_tensor(FAKE, F32, (T, k)), w) == DTYPE                 # float indices
+    assert _rw(L, raw_tensor(FAKE, U32, (T, E)), idx, w) == DTYPE                # integer logits
+    assert _rw(L, lg, idx, raw_tensor(FAKE, BF16, (T, k))) == DTYPE              # weights are F32
+    assert _rw(L, lg, idx, w, scoring=2) == INVALID
+    assert _rw(L, lg, idx, w, renorm=2) == INVALID
+    for bad in (0.0, -1.0, float("inf"), float("nan")):
+        assert _rw(L, lg, idx, w, scale=bad) == INVALID
+    assert _rw(L, lg, raw_tensor(FAKE, U32, (T + 1, k)), w) == SHAPE
+    assert _rw(L, lg, idx, raw_tensor(FAKE, F32, (T, k + 1))) == SHAPE
+    assert _rw(L, lg, raw_tensor(FAKE, I32, (T, E + 1)), raw_tensor(FAKE, F32, (T, E + 1))) == TOPK
+    big = raw_tensor(FAKE, F32, (T, 128))
+    assert _rw(L, big, raw_tensor(FAKE, U32, (T, 65)), raw_tensor(FAKE, F32, (T, 65))) == TOPK  # k <= 64
+    assert _rw(L, raw_tensor(FAKE, F32, (T, 5000)), idx, w) == UNSUPPORTED
+    for dt in (U32, I32, I64):
+        assert _rw(L, lg, raw_tensor(FAKE, dt, (T, k)), w) == DEVICE             # valid up to the device check
+    assert _rb(L, lg, idx, w, dl) == DEVICE
+    assert _rb(L, lg, idx, w, raw_tensor(FAKE, F32, (T, E))) == DTYPE            # gradient in the logits dtype
+    assert _rb(L, lg, idx, w, raw_tensor(FAKE, BF16, (T, E + 1))) == SHAPE
+    assert _rb(L, lg, idx, raw_tensor(FAKE, BF16, (T, k)), dl) == DTYPE          # grad_weights are F32
+
+
+def test_combine_and_dispatch_backward_validation(L):
+    T, k, H, N = 8, 2, 64, 16
+    y = raw_tensor(FAKE, BF16, (N, H))
+    ros = raw_tensor(FAKE, U32, (T * k,))
+    w = raw_tensor(FAKE, F32, (T, k))
+    g = raw_tensor(FAKE, BF16, (T, H))
+    dy = raw_tensor(FAKE, BF16, (N, H))
+    dw = raw_tensor(FAKE, F32, (T, k))
+
+    def cb(*a):
+        return L.moe_combine_backward(*[ctypes.byref(x) for x in a], None)
+
+    assert cb(y, ros, w, g, dy, dw) == DEVICE
+    assert cb(y, ros, w, raw_tensor(FAKE, F32, (T, H)), dy, dw) == DTYPE
+    assert cb(y, ros, w, g, dy, raw_tensor(FAKE, BF16, (T, k))) == DTYPE
+    assert cb(y, raw_tensor(FAKE, U32, (T * k + 1,)), w, g, dy, dw) == SHAPE
+    assert cb(y, ros, w, g, raw_tensor(FAKE, BF16, (N + 1, H)), dw) == SHAPE
+    assert cb(y, ros, w, raw_tensor(FAKE, BF16, (T, H + 8)), dy, dw) == SHAPE
+
+    def db(rows, r, kk, dx):
+        return L.moe_dispatch_backward(ctypes.byref(rows), ctypes.byref(r), kk, ctypes.byref(dx), None)
+
+    dx = raw_tensor(FAKE, BF16, (T, H))
+    assert db(dy, ros, k, dx) == DEVICE
+    assert db(dy, ros, 0, dx) == TOPK
+    assert db(dy, ros, k + 1, dx) == SHAPE
+    assert db(dy, ros, k, raw_tensor(FAKE, F16, (T, H))) == DTYPE
+    assert db(dy, ros, k, raw_tensor(FAKE, BF16, (T, H + 8))) == SHAPE
+    assert db(dy, raw_tensor(None, U32, (0,)), k, raw_tensor(None, BF16, (0, H))) == OK  # T = 0
+
+
+def test_experts_training_validation(L):
+    E, I, H, N, T = 4, 64, 128, 32, 16
+    gate = raw_tensor(FAKE, BF16, (E, I, H))
+    up = raw_tensor(FAKE, BF16, (E, I, H))
+    down = raw_tensor(FAKE, BF16, (E, H, I))
+    rows = raw_tensor(FAKE, BF16, (T, H))
+    tor = raw_tensor(FAKE, U32, (N,))
+    off = raw_tensor(FAKE, U32, (E + 1,))
+    out = raw_tensor(FAKE, BF16, (N, H))
+    pre = raw_tensor(FAKE, F32, (N, 2 * I))
+    h = raw_tensor(FAKE, BF16, (N, I))
+    ws_n = L.moe_experts_workspace_bytes(N, H, I, E, BF16)
+
+    def fwd(rows_, tor_, out_, pre_, h_, ws=ws_n):
+        return L.moe_experts_forward_training(ctypes.byref(gate), ctypes.byref(up), ctypes.byref(down),
+                                              ctypes.byref(rows_), ctypes.byref(tor_) if tor_ is not None else None,
+                                              ctypes.byref(off), ctypes.byref(out_), ctypes.byref(pre_),
+                                              ctypes.byref(h_), FAKE, ws, None)
+
+    assert fwd(rows, tor, out, pre, h) == DEVICE
+    assert fwd(rows, None, out, pre, h) == SHAPE                       # rows are then the N dispatched rows
+    assert fwd(raw_tensor(FAKE, BF16, (N, H)), None, out, pre, h) == DEVICE
+    assert fwd(rows, tor, out, raw_tensor(FAKE, BF16, (N, 2 * I)), h) == DTYPE   # preact is F32
+    assert fwd(rows, tor, out, raw_tensor(FAKE, F32, (N, I)), h) == SHAPE
+    assert fwd(rows, tor, out, pre, raw_tensor(FAKE, F32, (N, I))) == DTYPE
+    assert fwd(rows, tor, out, pre, h, ws=ws_n - 1) == WORKSPACE
+    assert fwd(rows, tor, out, pre, raw_tensor(FAKE + 8, BF16, (N, I))) == UNSUPPORTED  # misaligned
+
+    ws_b = L.moe_experts_backward_workspace_bytes(N, H, I, E, BF16)
+    assert ws_b >= N * 2 * I * 2
+    assert L.moe_experts_backward_workspace_bytes(N, H, I, E, U32) == 0
+    dy = raw_tensor(FAKE, BF16, (N, H))
+    dx = raw_tensor(FAKE, BF16, (N, H))
+    dg = raw_tensor(FAKE, F32, (E, I, H))
+    du = raw_tensor(FAKE, F32, (E, I, H))
+    dd = raw_tensor(FAKE, F32, (E, H, I))
+
+    def bwd(dg_=dg, du_=du, dd_=dd, dy_=dy, ws=ws_b):
+        return L.moe_experts_backward(ctypes.byref(gate), ctypes.byref(up), ctypes.byref(down), ctypes.byref(rows),
+                                      ctypes.byref(tor), ctypes.byref(off), ctypes.byref(pre), ctypes.byref(h),
+                                      ctypes.byref(dy_), ctypes.byref(dx), ctypes.byref(dg_), ctypes.byref(du_),
+                                      ctypes.byref(dd_), FAKE, ws, None)
+
+    assert bwd() == DEVICE
+    assert bwd(dg_=raw_tensor(FAKE, BF16, (E, I, H))) == DTYPE          # weight gradients are F32
+    assert bwd(dd_=raw_tensor(FAKE, F32, (E, I, H))) == SHAPE           # ddown is [E,H,I]
+    assert bwd(dy_=raw_tensor(FAKE, BF16, (N + 1, H))) == SHAPE
+    assert bwd(ws=ws_b - 1) == WORKSPACE
