@@ -15,7 +15,12 @@ inputs and weights already resident in HBM.  Prints one JSON line:
   cpu_baseline the CPU oracle timed on a bounded sample of the same workload;
   secondary    the decode and skewed workloads, same measurement;
   grouped_routing  the skewed workload's forward with group-limited sigmoid
-               routing, and that routing kernel's HBM roofline.
+               routing, and that routing kernel's HBM roofline;
+  training     one first-order training step on the prefill workload (route,
+               FP32 router weights, dispatch, experts forward with its cache,
+               combine, then the combine, experts, dispatch and router
+               backward), its stage times, the experts backward's MFMA
+               roofline and the oracle's step on a bounded token sample.
 The pages publish no throughput for this chain, so vs_baseline is null.
 """
 from __future__ import annotations
@@ -52,6 +57,10 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--grouped", default="skewed_bf16",
                     help="workload for the forward with group-limited sigmoid routing ('' to skip)")
+    ap.add_argument("--training", default="prefill_bf16",
+                    help="workload of the training-step measurement ('' to skip)")
+    ap.add_argument("--only-training", action="store_true",
+                    help="measure only the training step (for profiler runs)")
     ap.add_argument("--only-forward", action="store_true",
                     help="time only the fused forward (for profiler runs)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -276,6 +285,121 @@ def measure_grouped(name: str, steps: int, warmup: int) -> dict:
                                "avg_launch_ms": round(route_ms, 4), "bytes_per_launch": nbytes}}
 
 
+def training_step(moe, ex, x, lg, gout, cfg, opt, marks=None):
+    """One first-order training step through the public calls; with `marks`
+    (a list) HIP events are recorded between the stages on the current stream."""
+    import torch
+
+    def mark():
+        if marks is not None:
+            e = torch.cuda.Event(enable_timing=True)
+            e.record()
+            marks.append(e)
+
+    mark()
+    plan = moe.route(lg, moe.RoutingOptions(cfg.top_k, cfg.renormalize))
+    tp = plan.into_training(lg, opt)
+    mark()
+    d = tp.routing().dispatch(x, copy_rows=False)
+    mark()
+    y, cache = ex.forward_dispatched_training(d, input=x)
+    mark()
+    d.combine(y)
+    mark()
+    dy, dw = d.combine_backward(y, gout)
+    mark()
+    grads = cache.backward(dy)
+    mark()
+    d.dispatch_backward(grads[0])
+    mark()
+    tp.backward(dw)
+    mark()
+    return plan
+
+
+TRAIN_STAGES = ["route_and_weights", "dispatch", "experts_forward_training", "combine", "combine_backward",
+                "experts_backward", "dispatch_backward", "router_backward"]
+
+
+def measure_training(name: str, steps: int, warmup: int, cpu_seconds: float | None) -> dict:
+    """Whole training steps back to back (wall time, one sync), then the
+    same steps with HIP events between the stages (on the stream they are
+    launched on), then the oracle's step on the first tokens of the batch."""
+    import torch
+
+    import mixture_experts_layer_route_amd as moe
+    import moe_synth as S
+
+    cfg = S.CONFIGS[name]
+    dev = "cuda:0"
+    x, lg = S.make_tokens(cfg, device=dev)
+    W = S.make_weights(cfg, device=dev)
+    gout = S.make_grad_output(cfg, device=dev)
+    ex = moe.SwiGluExperts(*W)
+    opt = moe.RouterWeightOptions("softmax", cfg.renormalize, 1.0)
+    for _ in range(warmup):
+        training_step(moe, ex, x, lg, gout, cfg, opt)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        plan = training_step(moe, ex, x, lg, gout, cfg, opt)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    all_marks = []
+    for _ in range(steps):
+        m = []
+        training_step(moe, ex, x, lg, gout, cfg, opt, m)
+        all_marks.append(m)
+    torch.cuda.synchronize()
+    st = {n: sum(m[i].elapsed_time(m[i + 1]) for m in all_marks) / steps for i, n in enumerate(TRAIN_STAGES)}
+    # algorithmic FLOPs: forward 6 N H I (gate, up, down), backward 12 N H I
+    # (dh, dx over K = 2I, dgate + dup, ddown)
+    nhi = float(cfg.N) * cfg.H * cfg.I
+    t_bwd = st["experts_backward"] * 1e-3
+    ach = 12.0 * nhi / t_bwd / 1e12
+    idx = plan.expert_indices().view(torch.int32).long()
+    out = {"workload": f"{name}: {cfg.description}", "ms_per_step": round(ms, 4),
+           "tokens_per_s": round(cfg.T / (ms * 1e-3), 1), "tflops": round(18.0 * nhi / (ms * 1e-3) / 1e12, 2),
+           "active_experts": int(torch.unique(idx).numel()),
+           "stages_ms": {k: round(v, 4) for k, v in st.items()},
+           "roofline": {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                        "kernel": "train_gemm_kernel x4 (experts backward: dh, dx, dgate+dup, ddown)",
+                        "avg_launch_ms": round(st["experts_backward"], 4), "flops_per_launch": 12.0 * nhi,
+                        "traffic": None}}
+    del W, ex
+    torch.cuda.empty_cache()
+    if cpu_seconds:
+        out["cpu_baseline"] = cpu_training_baseline(cfg, cpu_seconds)
+    return out
+
+
+def cpu_training_baseline(cfg, target_s: float) -> dict:
+    """The oracle's training step (forward with caches and the four
+    backward steps) on the first n tokens of the same batch."""
+    import moe_synth as S
+    import oracle
+
+    threads = min(16, oracle.default_threads())
+    x, lg = S.make_tokens(cfg, device="cuda:0")
+    gout = S.make_grad_output(cfg, device="cuda:0")
+    Wb = [S.to_bits(w) for w in S.make_weights(cfg, device="cuda:0")]
+    xb, lgb, gb = S.to_bits(x), S.to_bits(lg), S.to_bits(gout)
+
+    def run(n):
+        t0 = time.perf_counter()
+        oracle.train_step(xb[:n], lgb[:n], *Wb, cfg.dtype, cfg.logits_dtype, cfg.top_k, cfg.renormalize, gb[:n],
+                          threads)
+        return time.perf_counter() - t0
+
+    probe = 8
+    dt = run(probe)
+    n = int(max(probe, min(cfg.T, probe * target_s / max(dt, 1e-3))))
+    dt = run(n)
+    return {"value": round(n / dt, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n} of {cfg.T} tokens, whole training step, {dt:.1f} s"}
+
+
 def summary(res: dict) -> dict:
     cfg = res["cfg"]
     d = {"workload": res["workload"], "tokens_per_s": round(res["tokens_per_s"], 1),
@@ -306,6 +430,10 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     moe.load()
+    if args.only_training:
+        print(json.dumps({"training": measure_training(args.training or args.workload, args.steps, args.warmup,
+                                                       None)}), flush=True)
+        return
     res = measure(args.workload, args.steps, args.warmup, args.only_forward)
     head = summary(res)
     cfg = res["cfg"]
@@ -343,6 +471,10 @@ def main():
         torch.cuda.empty_cache()
         if args.grouped:
             line["grouped_routing"] = measure_grouped(args.grouped, args.steps, args.warmup)
+            torch.cuda.empty_cache()
+        if args.training:
+            line["training"] = measure_training(args.training, args.steps, args.warmup,
+                                                None if args.no_cpu_baseline else args.cpu_seconds)
             torch.cuda.empty_cache()
         if not args.no_cpu_baseline:
             line["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_seconds)
