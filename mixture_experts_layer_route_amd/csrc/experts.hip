@@ -317,20 +317,6 @@ __global__ __launch_bounds__(WGM* WGN* kWave) void grouped_gemm_kernel(
 #ifndef MOE_P64_PERSIST
 #define MOE_P64_PERSIST 0
 #endif
-// Workgroups that fit on the stream's device at one per CU, rounded down to a
-// multiple of 8 XCDs (256 on MI355X); cached per device.
-int persistent_slots(hipStream_t s) {
-    static int cached[64] = {0};
-    int dev = 0;
-    if (hipStreamGetDevice(s, &dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-    if (!cached[dev]) {
-        int cus = 0;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8)
-            cus = 256;
-        cached[dev] = cus / 8 * 8;
-    }
-    return cached[dev];
-}
 #ifndef MOE_P64_WM
 #define MOE_P64_WM 2   // waves along token rows of the 64-K kernel's tile
 #define MOE_P64_WN 4   // waves along weight rows
@@ -341,37 +327,6 @@ int persistent_slots(hipStream_t s) {
 constexpr int kPipeBM = 256, kPipeBN = MOE_P_BN, kPipeBK = 32, kPipeStages = MOE_P_STAGES;
 constexpr int kPipeAhead = kPipeStages - 1;  // K steps of DMA in flight ahead of the reads
 
-// The stage ring is driven by hand: the DMA loads, the vmcnt waits and the
-// barriers below are the whole ordering protocol of the pipeline, so they
-// are written as volatile asm that the compiler neither reorders memory
-// around nor pads with waits of its own (it would otherwise drain every DMA
-// before each fragment read, since it cannot tell the stages apart).
-__device__ __forceinline__ uint32_t lds_offset(const void* p) {
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-// 16 bytes per lane from global address g into LDS at m0 + 16 * lane.
-// m0 is written here and nowhere else in these kernels.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds_base) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g),
-                 "s"(__builtin_amdgcn_readfirstlane(lds_base))
-                 : "memory", "m0");
-}
-#pragma clang diagnostic pop
-__device__ __forceinline__ void barrier_lds() { asm volatile("s_barrier" ::: "memory"); }
-// Keeps the instruction scheduler from moving anything across this point.
-// Placed after the fragment reads of a K half, so they are issued a whole
-// K half of MFMAs before their first use instead of being sunk next to it
-// (the scheduler otherwise trades that latency slack for fewer registers).
-__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
-
-
-
-template <int N> __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
-// lgkmcnt(0) through the builtin, so the compiler's own LDS-read tracking
-// knows the fragment registers are complete
-__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 // Epilogue of the 32x32-block kernels: lane holds token (lane % 32) of each
 // token block and output columns 8 (r / 4) + 4 (lane / 32) + (r % 4) of each
@@ -920,6 +875,21 @@ hipError_t launch_typed(const ExpertsArgs& a, hipStream_t s, ExpertsPart part) {
 }
 
 }  // namespace
+
+// Workgroups that fit on the stream's device at one per CU, rounded down to a
+// multiple of 8 XCDs (256 on MI355X); cached per device.
+int persistent_slots(hipStream_t s) {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipStreamGetDevice(s, &dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (!cached[dev]) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8)
+            cus = 256;
+        cached[dev] = cus / 8 * 8;
+    }
+    return cached[dev];
+}
 
 int64_t max_mtiles(int64_t N, int64_t E, int BM) {
     if (N <= 0) return 0;

@@ -86,4 +86,44 @@ __device__ __forceinline__ void save_preact(float* __restrict__ gu, int64_t row,
     *(float4*)(p + I) = make_float4(u[0], u[1], u[2], u[3]);
 }
 
+// ------------------------------------------------------------------ LDS pipelines
+// The stage ring is driven by hand: the DMA loads, the vmcnt waits and the
+// barriers below are the whole ordering protocol of the pipeline, so they
+// are written as volatile asm that the compiler neither reorders memory
+// around nor pads with waits of its own (it would otherwise drain every DMA
+// before each fragment read, since it cannot tell the stages apart).
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+// 16 bytes per lane from global address g into LDS at m0 + 16 * lane.
+// m0 is written here and nowhere else in these kernels.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g),
+                 "s"(__builtin_amdgcn_readfirstlane(lds_base))
+                 : "memory", "m0");
+}
+// The same from a wave-uniform base address plus a 32-bit per-lane byte
+// offset (one VGPR per load instead of a 64-bit address).
+__device__ __forceinline__ void lds_dma16_so(const void* base, uint32_t voff, uint32_t lds_base) {
+    const uint64_t b = (uint64_t)(uintptr_t)base;
+    const uint64_t sb = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                        (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sb),
+                 "s"(__builtin_amdgcn_readfirstlane(lds_base))
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+__device__ __forceinline__ void barrier_lds() { asm volatile("s_barrier" ::: "memory"); }
+// Keeps the instruction scheduler from moving anything across this point.
+// Placed after the fragment reads of a K half, so they are issued a whole
+// K half of MFMAs before their first use instead of being sunk next to it
+// (the scheduler otherwise trades that latency slack for fewer registers).
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+template <int N> __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+// lgkmcnt(0) through the builtin, so the compiler's own LDS-read tracking
+// knows the fragment registers are complete
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
 }  // namespace moe

@@ -699,13 +699,14 @@ moe_status check_3d(const moe_tensor* t, int dtype, int64_t d0, int64_t d1, int6
 }
 
 struct BackwardWs {
-    size_t tiles, dgu, total;
+    size_t tiles, dgu, xg, total;
 };
-BackwardWs backward_ws(int64_t N, int64_t I, int64_t E, int dtype) {
+BackwardWs backward_ws(int64_t N, int64_t H, int64_t I, int64_t E, int dtype) {
     BackwardWs w;
     w.tiles = 0;
     w.dgu = align_up(experts_backward_tile_bytes(N, E));
-    w.total = w.dgu + align_up((size_t)N * 2 * (size_t)I * elem_size(dtype));
+    w.xg = w.dgu + align_up((size_t)N * 2 * (size_t)I * elem_size(dtype));
+    w.total = w.xg + align_up((size_t)N * (size_t)H * elem_size(dtype));
     return w;
 }
 
@@ -809,9 +810,8 @@ moe_status moe_experts_forward_training(const moe_tensor* gate, const moe_tensor
 }
 
 size_t moe_experts_backward_workspace_bytes(int64_t N, int64_t H, int64_t I, int64_t E, int32_t dtype) {
-    (void)H;
-    if (N < 0 || I < 1 || E < 1 || !is_float(dtype)) return 0;
-    return backward_ws(N, I, E, dtype).total;
+    if (N < 0 || H < 1 || I < 1 || E < 1 || !is_float(dtype)) return 0;
+    return backward_ws(N, H, I, E, dtype).total;
 }
 
 moe_status moe_experts_backward(const moe_tensor* gate, const moe_tensor* up, const moe_tensor* down,
@@ -838,7 +838,7 @@ moe_status moe_experts_backward(const moe_tensor* gate, const moe_tensor* up, co
     MOE_TRY(check_gemm_limits(E, H, I, N, {gate->data, up->data, down->data, rows->data, preact->data, h->data,
                                            grad_expert_out->data, grad_rows->data, grad_gate->data, grad_up->data,
                                            grad_down->data}));
-    const BackwardWs l = backward_ws(N, I, E, dt);
+    const BackwardWs l = backward_ws(N, H, I, E, dt);
     if (!workspace || workspace_bytes < l.total) return MOE_ERR_WORKSPACE;
     hipStream_t s = (hipStream_t)stream;
     const uint32_t* tor = token_of_row ? (const uint32_t*)token_of_row->data : nullptr;
@@ -862,6 +862,7 @@ moe_status moe_experts_backward(const moe_tensor* gate, const moe_tensor* up, co
     a.dup = (float*)grad_up->data;
     a.ddown = (float*)grad_down->data;
     a.dgu = (char*)workspace + l.dgu;
+    a.xg = (char*)workspace + l.xg;
     a.tiles = (char*)workspace + l.tiles;
     a.N = N;
     a.H = H;

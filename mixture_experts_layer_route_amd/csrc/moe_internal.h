@@ -197,6 +197,7 @@ struct ExpertsBackwardArgs {
     float* dup;              // [E,I,H]
     float* ddown;            // [E,H,I]
     void* dgu;               // [N,2I] workspace (weight dtype)
+    void* xg;                // [N,H] workspace: token rows gathered through x_rows
     void* tiles;             // tile list workspace
     int64_t N, H, I;
     int E;

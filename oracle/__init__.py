@@ -91,7 +91,7 @@ def lib():
         L.oracle_experts_train_forward.argtypes = [vp, vp, vp, i32, vp, vp, i64, i64, i64, vp, vp, vp, vp, i32]
         L.oracle_experts_backward.restype = i32
         L.oracle_experts_backward.argtypes = [vp, vp, vp, i32, vp, vp, i64, i64, i64, vp, vp, vp, vp, vp,
-                                              vp, vp, vp, i32]
+                                              vp, vp, vp, vp, i32]
         _lib = L
     return _lib
 
@@ -389,8 +389,10 @@ def experts_train_forward(gate, up, down, dt: str, rows: np.ndarray, offsets: np
 
 
 def experts_backward(gate, up, down, dt: str, rows: np.ndarray, offsets: np.ndarray, E: int, H: int, I: int,
-                     g: np.ndarray, u: np.ndarray, h: np.ndarray, dY: np.ndarray, nthreads: int | None = None):
-    """Returns (dinput [N,H] in the expert dtype, dgate [E,I,H], dup [E,I,H], ddown [E,H,I] FP32)."""
+                     g: np.ndarray, u: np.ndarray, h: np.ndarray, dY: np.ndarray, nthreads: int | None = None,
+                     with_dgu: bool = False):
+    """Returns (dinput [N,H] in the expert dtype, dgate [E,I,H], dup [E,I,H], ddown [E,H,I] FP32), and with
+    ``with_dgu`` also the rounded intermediates dg | du [N,2I] as float64."""
     keep: list = []
     gp = _expert_ptrs(gate, E, dt, keep)
     up_ = _expert_ptrs(up, E, dt, keep)
@@ -412,12 +414,15 @@ def experts_backward(gate, up, down, dt: str, rows: np.ndarray, offsets: np.ndar
     dgate = np.empty((E, I, H), dtype=np.float32)
     dup = np.empty((E, I, H), dtype=np.float32)
     ddown = np.empty((E, H, I), dtype=np.float32)
+    dgu = np.empty((m, 2 * I), dtype=np.float64) if with_dgu else None
     rc = lib().oracle_experts_backward(ctypes.cast(gp, ctypes.c_void_p), ctypes.cast(up_, ctypes.c_void_p),
                                        ctypes.cast(dp, ctypes.c_void_p), DT[dt], _ptr(r), _ptr(off), E, H, I,
                                        _ptr(g_), _ptr(u_), _ptr(h_), _ptr(dy), _ptr(dx), _ptr(dgate), _ptr(dup),
-                                       _ptr(ddown), nthreads or default_threads())
+                                       _ptr(ddown), _ptr(dgu) if with_dgu else None, nthreads or default_threads())
     if rc != 0:
         raise ValueError("oracle_experts_backward: a row's expert has no weights")
+    if with_dgu:
+        return dx[:n], dgate, dup, ddown, dgu[:n]
     return dx[:n], dgate, dup, ddown
 
 
@@ -439,11 +444,11 @@ def train_step(x: np.ndarray, logits: np.ndarray, gate, up, down, dt: str, ldt: 
     fw = experts_train_forward(gate, up, down, dt, rows, offsets, E, H, I, nthreads)
     out = combine(fw["output"], dt, ros, w32, "f32", T, top_k, H, nthreads)
     dY, dw = combine_backward(fw["output"], dt, ros, w32, "f32", grad_output, T, top_k, H, nthreads)
-    drows, dgate, dup, ddown = experts_backward(gate, up, down, dt, rows, offsets, E, H, I, fw["g"], fw["u"],
-                                                fw["h"], dY, nthreads)
+    drows, dgate, dup, ddown, dgu = experts_backward(gate, up, down, dt, rows, offsets, E, H, I, fw["g"],
+                                                     fw["u"], fw["h"], dY, nthreads, with_dgu=True)
     dx = dispatch_backward(drows, dt, ros, T, top_k, H, nthreads)
     dl = router_backward(logits, ldt, idx, dw, scoring, renormalize, scale, nthreads)
     return {"indices": idx, "weights_f32": w32, "offsets": offsets, "row_of_slot": ros, "dispatched": rows,
             "Y": fw["output"], "h": fw["h"], "g": fw["g"], "u": fw["u"], "output": out, "dY": dY,
-            "dweights": dw, "drows": drows, "dgate": dgate, "dup": dup, "ddown": ddown, "dx": dx,
+            "dweights": dw, "drows": drows, "dgu": dgu, "dgate": dgate, "dup": dup, "ddown": ddown, "dx": dx,
             "dlogits": dl}

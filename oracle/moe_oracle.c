@@ -942,10 +942,11 @@ static void twgrad_expert(void* vctx, int64_t e)
     }
 }
 
+/* dgu_out: NULL, or [N,2I] doubles that receive the rounded dg | du. */
 int oracle_experts_backward(const void* const* gate, const void* const* up, const void* const* down, int dt,
                             const void* rows, const uint32_t* offsets, int64_t E, int64_t H, int64_t I,
                             const float* g, const float* u, const void* h, const void* dy, void* dx,
-                            float* dgate, float* dup, float* ddown, int nthreads)
+                            float* dgate, float* dup, float* ddown, double* dgu_out, int nthreads)
 {
     if (E < 1 || H < 1 || I < 1) return -1;
     const int64_t N = offsets[E];
@@ -957,6 +958,13 @@ int oracle_experts_backward(const void* const* gate, const void* const* up, cons
     if (!bad) {
         twgrad_ctx w = {&b, h, dgate, dup, ddown};
         parallel_rows(E, nthreads, twgrad_expert, &w);
+    }
+    if (!bad && dgu_out) {
+        for (int64_t r = 0; r < N; ++r)
+            for (int64_t i = 0; i < I; ++i) {
+                dgu_out[r * 2 * I + i] = dg[r * I + i];
+                dgu_out[r * 2 * I + I + i] = du[r * I + i];
+            }
     }
     free(du);
     free(dg);

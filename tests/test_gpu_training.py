@@ -10,8 +10,11 @@ workload runs at full size with sampled checks.
 
 Tolerances: values computed in FP32 from F32 data (router weights, the
 pre-activation cache, F32 chains) use 1e-4 * (1 + |ref|); results whose
-inputs are BF16/F16 use 2e-2 * (1 + |ref|), also for the FP32-stored weight
-gradients, since their terms carry the 16-bit rounding of dg, du and h.
+inputs are BF16/F16 use 2e-2 * (1 + |ref|).  The FP32 weight gradients are
+sums over an expert's rows of products whose 16-bit factor (dg, du or h) both
+sides round separately; they must stay within 2e-2 * (1 + |ref|) plus one
+rounding step of that factor times the sum of |terms|, with at most 0.1% of
+elements beyond the plain 2e-2 * (1 + |ref|).
 """
 import sys
 import zlib
@@ -23,7 +26,7 @@ import torch
 import mixture_experts_layer_route_amd as moe
 import moe_synth as S
 import oracle
-from parity import TOL, assert_close, host_bits, values
+from parity import TOL, assert_close, assert_close_sum, host_bits, values
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -49,6 +52,26 @@ def u32(a: np.ndarray) -> torch.Tensor:
 
 def f32_close(got, ref, what):
     assert_close(np.asarray(got, np.float64), np.asarray(ref, np.float64), "f32", what)
+
+
+def wgrad_l1(offsets, dgu, rows, dY, h, dt, E, I):
+    """Sums of |terms| of the weight gradients, per element: |dg|^T |x|,
+    |du|^T |x| (per expert, [E,I,H]) and |dy|^T |h| ([E,H,I])."""
+    x, y, hh = (np.abs(oracle.widen(a, dt)) for a in (rows, dY, h))
+    H = x.shape[1]
+    lg, lu, ld = np.zeros((E, I, H)), np.zeros((E, I, H)), np.zeros((E, H, I))
+    for e in range(E):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if b > a:
+            lg[e] = np.abs(dgu[a:b, :I]).T @ x[a:b]
+            lu[e] = np.abs(dgu[a:b, I:]).T @ x[a:b]
+            ld[e] = y[a:b].T @ hh[a:b]
+    return lg, lu, ld
+
+
+def check_wgrads(got, ref, l1, dt, tag):
+    for gt, rf, m, what in zip(got, ref, l1, ("grad_gate", "grad_up", "grad_down")):
+        assert_close_sum(gt.cpu().double().numpy(), rf, m, dt, f"{what} {tag}")
 
 
 # ------------------------------------------------------------------ router weights
@@ -151,6 +174,9 @@ EXPERT_CASES = [
     S.small_config("ex_pipe64_bf16", T=600, H=192, I=128, E=6, top_k=2, dtype="bf16", seed=405),
     S.small_config("ex_long_k_bf16", T=1500, H=128, I=64, E=2, top_k=1, dtype="bf16", seed=406),
     S.small_config("ex_f32_odd", T=90, H=48, I=40, E=3, top_k=2, dtype="f32", seed=407),
+    # more 256 x 256 weight-gradient tiles (16 x 4 x 8) than workgroups: the
+    # persistent loop stores one tile while the next one loads
+    S.small_config("ex_persistent_bf16", T=1100, H=2048, I=512, E=16, top_k=2, dtype="bf16", seed=409),
 ]
 
 
@@ -174,8 +200,8 @@ def compare_experts_training(cfg, x_bits, idx, W, gathered: bool):
     rows = x_bits[tor]
     Wb = [host_bits(w) for w in W]
     fw = oracle.experts_train_forward(*Wb, cfg.dtype, rows, offsets, E, H, I, NTHREADS)
-    odx, odg, odu, odd = oracle.experts_backward(*Wb, cfg.dtype, rows, offsets, E, H, I, fw["g"], fw["u"], fw["h"],
-                                                 dY[:n], NTHREADS)
+    odx, odg, odu, odd, odgu = oracle.experts_backward(*Wb, cfg.dtype, rows, offsets, E, H, I, fw["g"], fw["u"],
+                                                       fw["h"], dY[:n], NTHREADS, with_dgu=True)
     tag = f"{cfg.name} {'gathered' if gathered else 'copied'}"
     dt = cfg.dtype
     assert_close(values(y[:n], dt), oracle.widen(fw["output"], dt), dt, f"output {tag}")
@@ -184,8 +210,7 @@ def compare_experts_training(cfg, x_bits, idx, W, gathered: bool):
     f32_close(pre[:, I:], fw["u"], f"saved u {tag}")
     assert_close(values(cache.h[:n], dt), oracle.widen(fw["h"], dt), dt, f"saved h {tag}")
     assert_close(values(gdx[:n], dt), oracle.widen(odx, dt), dt, f"grad_rows {tag}")
-    for got, ref, what in ((gdg, odg, "grad_gate"), (gdu, odu, "grad_up"), (gdd, odd, "grad_down")):
-        assert_close(got.cpu().double().numpy(), ref, dt, f"{what} {tag}")
+    check_wgrads((gdg, gdu, gdd), (odg, odu, odd), wgrad_l1(offsets, odgu, rows, dY[:n], fw["h"], dt, E, I), dt, tag)
     # the cache's forward is the plain forward, bit for bit
     if not gathered:
         y_plain = ex.forward_dispatched(d)
@@ -268,8 +293,8 @@ def test_training_step_parity(cfg, scoring):
         assert_close(g["dweights"].cpu().double().numpy(), r["dweights"], dt, "step dweights")
     assert_close(values(g["dlogits"], cfg.logits_dtype), oracle.widen(r["dlogits"], cfg.logits_dtype),
                  cfg.logits_dtype if dt == "f32" else dt, "step dlogits")
-    for k in ("dgate", "dup", "ddown"):
-        assert_close(g[k].cpu().double().numpy(), r[k], dt, f"step {k}")
+    l1 = wgrad_l1(r["offsets"], r["dgu"], r["dispatched"], r["dY"], r["h"], dt, cfg.E, cfg.I)
+    check_wgrads((g["dgate"], g["dup"], g["ddown"]), (r["dgate"], r["dup"], r["ddown"]), l1, dt, "step")
 
 
 def test_training_step_with_group_limited_sigmoid_routing():
@@ -286,8 +311,8 @@ def test_training_step_with_group_limited_sigmoid_routing():
                           host_bits(gout), NTHREADS, indices=g["indices"], scoring="sigmoid", scale=2.5)
     for k, dt in (("output", "bf16"), ("dx", "bf16"), ("dlogits", "bf16")):
         assert_close(values(g[k], dt), oracle.widen(r[k], dt), dt, f"grouped step {k}")
-    for k in ("dgate", "dup", "ddown"):
-        assert_close(g[k].cpu().double().numpy(), r[k], "bf16", f"grouped step {k}")
+    l1 = wgrad_l1(r["offsets"], r["dgu"], r["dispatched"], r["dY"], r["h"], "bf16", cfg.E, cfg.I)
+    check_wgrads((g["dgate"], g["dup"], g["ddown"]), (r["dgate"], r["dup"], r["ddown"]), l1, "bf16", "grouped step")
 
 
 # ------------------------------------------------------------------ full size, sampled
@@ -359,8 +384,11 @@ def test_training_step_full_size_sampled():
         off1 = np.array([0, b - a], np.uint32)
         dy_e = host_bits(dy[a:b])
         fw = oracle.experts_train_forward(gate_s, up_s, down_s, "bf16", rows_e, off1, 1, H, len(cols), NTHREADS)
-        _, odg, odu, odd = oracle.experts_backward(gate_s, up_s, down_s, "bf16", rows_e, off1, 1, H, len(cols),
-                                                   fw["g"], fw["u"], fw["h"], dy_e, NTHREADS)
-        assert_close(dgate[e, cols].cpu().double().numpy(), odg[0], "bf16", f"full-size dgate expert {e}")
-        assert_close(dup[e, cols].cpu().double().numpy(), odu[0], "bf16", f"full-size dup expert {e}")
-        assert_close(ddown[e][:, cols].cpu().double().numpy(), odd[0], "bf16", f"full-size ddown expert {e}")
+        _, odg, odu, odd, odgu = oracle.experts_backward(gate_s, up_s, down_s, "bf16", rows_e, off1, 1, H,
+                                                         len(cols), fw["g"], fw["u"], fw["h"], dy_e, NTHREADS,
+                                                         with_dgu=True)
+        lg, lu, ld = wgrad_l1(off1, odgu, rows_e, dy_e, fw["h"], "bf16", 1, len(cols))
+        assert_close_sum(dgate[e, cols].cpu().double().numpy(), odg[0], lg[0], "bf16", f"full-size dgate expert {e}")
+        assert_close_sum(dup[e, cols].cpu().double().numpy(), odu[0], lu[0], "bf16", f"full-size dup expert {e}")
+        assert_close_sum(ddown[e][:, cols].cpu().double().numpy(), odd[0], ld[0], "bf16",
+                         f"full-size ddown expert {e}")
