@@ -179,7 +179,8 @@ def roofline(res: dict) -> dict:
         ach = flops / t / 1e12
         r = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
              "frac": round(ach / PEAK_BF16_TFLOPS, 4)}
-    r["kernel"] = "grouped_gemm_kernel (gate/up, fused SiLU*mul)"
+    r["kernel"] = ("grouped_gemm_kernel, 16-row tile (gate/up, fused SiLU*mul)" if res["workload"] == "decode_bf16"
+                   else "grouped_gemm_pipe64_kernel (gate/up, fused SiLU*mul)")
     r["avg_launch_ms"] = round(res["stages_ms"]["experts_gate_up"], 4)
     r["traffic"] = traffic_for(res["workload"])
     return r
@@ -364,7 +365,7 @@ def measure_training(name: str, steps: int, warmup: int, cpu_seconds: float | No
            "stages_ms": {k: round(v, 4) for k, v in st.items()},
            "roofline": {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                         "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-                        "kernel": "train_gemm_kernel x4 (experts backward: dh, dx, dgate+dup, ddown)",
+                        "kernel": "train_pipe_kernel x4 (experts backward: dh, dx, dgate+dup, ddown)",
                         "avg_launch_ms": round(st["experts_backward"], 4), "flops_per_launch": 12.0 * nhi,
                         "traffic": None}}
     del W, ex

@@ -26,16 +26,22 @@
 // operands (dy, dgu) do.  The others -- down_e, gate_e, up_e read along
 // their first index, and every operand of the weight gradients, whose K runs
 // over dispatched rows -- are K-outer: contiguous along the output index.
-// Those are staged through registers: each thread loads 4 K-rows x 16 bytes,
-// transposes the 4 x 8 (or 4 x 4) block in registers and writes 8-byte (or
-// 16-byte) K-runs to LDS, so every tile sits in LDS with K contiguous and the
-// fragment reads are the same 16-byte reads as in the forward.
 //
-// Tiles: 128 x 128 outputs, 4 waves of 64 x 64, 16x16 MFMAs, 128-byte K
-// stages (64 bf16/f16 or 32 f32 values) double buffered.  DH and DX walk the
-// forward's per-expert row-tile list; the weight gradients walk (expert,
-// row tile, column tile) over all experts, and an expert without rows gets
-// zero gradients.
+// Two kernels:
+//   train_pipe_kernel (bf16/f16, enough rows per expert): 256 x 256 tiles on
+//     8 waves of 32x32x16 MFMAs, 64-K steps loaded straight into LDS by
+//     global_load_lds in the forward's ring (two row-operand and three
+//     column-operand slots); K-outer operands land in their natural layout
+//     and are read with the gfx950 LDS transpose read ds_read_b64_tr_b16.
+//     One workgroup per CU walks several tiles and loads the next tile
+//     while it stores the last.
+//   train_gemm_kernel (f32, and few rows per expert): 128 x 128 tiles on 4
+//     waves of 16x16 MFMAs; K-outer operands are staged through registers,
+//     each thread transposing 4 K-rows x 16 bytes before writing K-runs to
+//     LDS, double buffered.
+// Both walk the forward's per-expert row-tile list for DH and DX, and
+// (expert, row tile, column tile) over all experts for the weight gradients;
+// an expert without rows gets zero gradients.
 #include <algorithm>
 #include <type_traits>
 
