@@ -24,7 +24,13 @@
 // M-tiles any routing could produce; only the live ones get workgroup ids,
 // spread over the 8 XCDs, each XCD walking groups of one expert's tiles.
 //
-// Two kernels:
+// Three kernels:
+//   grouped_gemm_pipe64_kernel (bf16/f16, H and I multiples of 64; the
+//     default for prefill-sized batches): 256x256 tiles on 8 waves of
+//     32x32x16 MFMAs; 64-element K steps filled by direct global->LDS loads
+//     into two token-row slots and three weight-row slots of 32 KB, the
+//     weight rows issued two steps ahead and the token rows one, each step's
+//     loads spread over the MFMAs of its last 16-K sub-step.
 //   grouped_gemm_pipe_kernel (bf16/f16, K a multiple of 32): 256x256 tiles on
 //     8 waves of 32x32x16 MFMAs; 32-element K stages filled by direct
 //     global->LDS loads in a 4-stage ring, issued three stages ahead and
