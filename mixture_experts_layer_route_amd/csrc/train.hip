@@ -27,8 +27,11 @@
 // their first index, and every operand of the weight gradients, whose K runs
 // over dispatched rows -- are K-outer: contiguous along the output index.
 //
-// Two kernels:
-//   train_pipe_kernel (bf16/f16, enough rows per expert): 256 x 256 tiles on
+// Three kernels:
+//   train_pipe2_kernel (bf16/f16, enough rows per expert; the default): 128 x
+//     256 tiles on 4 waves with 32-K steps in a 64 KB ring, so two
+//     workgroups share a CU and one computes while the other stores;
+//   train_pipe_kernel (the same with one workgroup per CU): 256 x 256 tiles on
 //     8 waves of 32x32x16 MFMAs, 64-K steps loaded straight into LDS by
 //     global_load_lds in the forward's ring (two row-operand and three
 //     column-operand slots); K-outer operands land in their natural layout
@@ -348,7 +351,7 @@ hipError_t launch_train_gemm(TrainGemm p, int64_t blocks, hipStream_t s) {
 // clamped to the last valid K-row or chunk, and the fragments of the last
 // step zero every value past the end on both operands.
 #ifndef MOE_TRAIN_PIPE
-#define MOE_TRAIN_PIPE 1    // the pipelined kernel for 16-bit types
+#define MOE_TRAIN_PIPE 2    // 16-bit types: 1 = one 256x256 workgroup per CU, 2 = two 128x256 per CU
 #endif
 #ifndef MOE_TP_PERSIST
 #define MOE_TP_PERSIST 1    // one workgroup per CU walking several tiles
@@ -732,6 +735,318 @@ hipError_t launch_train_pipe(TrainGemm p, int64_t blocks, hipStream_t s) {
     return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ pipelined training GEMM, two per CU
+// The same products on 128 x 256 tiles of 4 waves (each 128 x 64, 32x32x16
+// MFMAs) with 32-K steps in a 64 KB ring (two row-operand slots of 8 KB,
+// three column-operand slots of 16 KB), so two workgroups share a CU and one
+// computes while the other stores its tile.  Layouts per slot:
+//   K-contiguous row operand: 128 rows x 64 bytes, chunk c of row r at
+//     c ^ ((r >> 1) & 3);
+//   K-outer row operand (weight gradients): 32 K-rows x 256 bytes (128
+//     values), chunk c of K-row r at c ^ (4 (r & 3));
+//   K-outer column operand: 32 K-rows x 512 bytes, chunk c at c ^ ((r & 7) << 2).
+// K-outer operands are read with ds_read_b64_tr_b16 as in train_pipe_kernel.
+constexpr int kT2BM = 128, kT2BN = 256, kT2Waves = 4;
+constexpr int kT2SlotA = 8 * 1024, kT2SlotB = 16 * 1024;
+constexpr int kT2SlotsA = 2, kT2SlotsB = 3;
+constexpr int kT2LPA = kT2SlotA / 1024 / kT2Waves, kT2LPB = kT2SlotB / 1024 / kT2Waves;  // 2 and 4 pieces
+
+template <typename DT, int MODE>
+__global__ __launch_bounds__(kT2Waves* kWave, 2) void train_pipe2_kernel(TrainGemm p) {
+    using S = typename DT::storage;
+    constexpr bool A_KOUTER = MODE == kDWGU || MODE == kDWD;
+    constexpr bool ROWS = MODE == kDH || MODE == kDX;
+    constexpr int WTN = 64, MB = 4, NB = 2, NM = MB * NB;
+    constexpr int LPA = kT2LPA, LPB = kT2LPB, NA = kT2SlotsA, NB_ = kT2SlotsB;
+    constexpr int RA = A_KOUTER ? 2 * MB : MB;
+    constexpr int NR = RA + 2 * NB;
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[NA * kT2SlotA + NB_ * kT2SlotB];
+
+    const int lane = lane_id(), wid = threadIdx.x / kWave;  // wid = the wave's 64-column group
+    const int64_t I2 = 2 * (int64_t)p.I;
+    const S* A = (const S*)p.a;
+    const int ncols = (MODE == kDH || MODE == kDWD) ? p.I : p.H;
+    const int mrows = MODE == kDWGU ? 2 * p.I : p.H;
+    const int lda = MODE == kDH ? p.H : (MODE == kDWD ? p.H : 2 * p.I);
+
+    // ---- tile: expert e, output rows [m0, m1), columns [n0, n0 + 256), K [kb, ke)
+    int e, m0, m1, n0, kb, ke;
+    if constexpr (ROWS) {
+        int mi, ni;
+        if (!tile_of_block(blockIdx.x, p.nblocks, p.n_tiles, (int)*p.tile_count, p.tiles, &mi, &ni)) return;
+        const int4 tl = p.tiles[mi];
+        e = tl.x;
+        m0 = tl.y;
+        m1 = tl.z;
+        n0 = ni * kT2BN;
+        kb = 0;
+        ke = lda;
+    } else {
+        const int pid = xcd_contiguous(blockIdx.x, p.nblocks);
+        const int per = p.m_tiles * p.n_tiles;
+        e = pid / per;
+        const int rem = pid - e * per;
+        m0 = (rem % p.m_tiles) * kT2BM;
+        m1 = min(m0 + kT2BM, mrows);
+        n0 = (rem / p.m_tiles) * kT2BN;
+        kb = (int)min(p.offsets[e], (uint32_t)p.N);
+        ke = max((int)min(p.offsets[e + 1], (uint32_t)p.N), kb);
+    }
+    e = __builtin_amdgcn_readfirstlane(e);
+    m0 = __builtin_amdgcn_readfirstlane(m0);
+    m1 = __builtin_amdgcn_readfirstlane(m1);
+    n0 = __builtin_amdgcn_readfirstlane(n0);
+    kb = __builtin_amdgcn_readfirstlane(kb);
+    ke = __builtin_amdgcn_readfirstlane(ke);
+    const int nk = (ke - kb + 31) / 32;
+
+    // ---- loads: a wave-uniform base plus a 32-bit byte offset (the launcher
+    // keeps offsets below 2^31); steps past the end re-load the last step
+    const uint32_t lds_a = lds_offset(smem) + wid * LPA * 1024;
+    const uint32_t lds_b = lds_offset(smem) + NA * kT2SlotA + wid * LPB * 1024;
+    auto dma_a = [&](int kt, int j) __attribute__((always_inline)) {
+        const int s = min(kt, nk - 1);
+        const S* base;
+        uint32_t off;
+        if constexpr (A_KOUTER) {
+            // 4 K-rows x 256 bytes per piece
+            const int r = (wid * LPA + j) * 4 + (lane >> 4);
+            const int c = m0 + 8 * ((lane & 15) ^ (4 * (r & 3)));
+            const int k = min(32 * s + r, ke - kb - 1);
+            base = A + (int64_t)kb * lda;
+            off = (uint32_t)(k * lda + (c < m1 ? c : 0)) * (uint32_t)sizeof(S);
+        } else {
+            // 16 rows x 64 bytes per piece
+            const int row = (wid * LPA + j) * 16 + (lane >> 2);
+            const int lc = (lane & 3) ^ ((row >> 1) & 3);
+            base = A + (int64_t)m0 * lda;
+            off = (uint32_t)(min(row, m1 - m0 - 1) * lda) * (uint32_t)sizeof(S) +
+                  (uint32_t)min(64 * s + lc * 16, ke * (int)sizeof(S) - 16);
+        }
+        lds_dma16_so(base, off, lds_a + (kt % NA) * kT2SlotA + j * 1024);
+    };
+    auto dma_b = [&](int kt, int j) __attribute__((always_inline)) {
+        const int s = min(kt, nk - 1);
+        const int r = (wid * LPB + j) * 2 + (lane >> 5);  // 2 K-rows x 512 bytes per piece
+        const int c = n0 + 8 * ((lane & 31) ^ ((r & 7) << 2));
+        const int col = c < ncols ? c : 0;
+        const int k = min(32 * s + r, ke - kb - 1);     // K-row past kb
+        const uint32_t lds = lds_b + (kt % NB_) * kT2SlotB + j * 1024;
+        const S* base;
+        uint32_t off;
+        if constexpr (MODE == kDX) {
+            // gate rows, then up rows; a piece's two K-rows lie in one tensor (I is even)
+            const int kpair = __builtin_amdgcn_readfirstlane(min(32 * s + (wid * LPB + j) * 2, ke - 1));
+            const bool in_up = kpair >= p.I;
+            base = (const S*)(in_up ? p.b1 : p.b0) + (int64_t)e * p.I * p.H;
+            off = (uint32_t)((k - (in_up ? p.I : 0)) * p.H + col) * (uint32_t)sizeof(S);
+        } else if constexpr (MODE == kDH) {
+            base = (const S*)p.b0 + (int64_t)e * p.H * p.I;
+            off = (uint32_t)(k * p.I + col) * (uint32_t)sizeof(S);
+        } else if constexpr (MODE == kDWGU) {
+            base = (const S*)p.b0 + (int64_t)kb * p.H;
+            off = (uint32_t)(k * p.H + col) * (uint32_t)sizeof(S);
+        } else {
+            base = (const S*)p.b0 + (int64_t)kb * p.I;
+            off = (uint32_t)(k * p.I + col) * (uint32_t)sizeof(S);
+        }
+        lds_dma16_so(base, off, lds);
+    };
+
+    // ---- fragment addresses
+    const int frow = lane & 31, kg = lane >> 5;
+    const int g16 = lane >> 4, s16 = lane & 15;
+    // column operand (512-byte K-rows): per (h, block f) at q = 0; q adds 16 K-rows
+    int kob[2][NB];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int kk = 4 * h + (s16 >> 2);
+        const int rowoff = (8 * (g16 >> 1) + kk) * 512 + (2 * (g16 & 1) + ((s16 & 3) >> 1)) * 16 + (s16 & 1) * 8;
+#pragma unroll
+        for (int f = 0; f < NB; ++f) kob[h][f] = rowoff + 64 * ((2 * wid + f) ^ kk);
+    }
+    // K-outer row operand (256-byte K-rows): physical chunk 4 (i ^ (s16 / 4)) + 2 (g16 & 1) + (s16 & 3) / 2
+    int koa[2][MB];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int rowoff = (8 * (g16 >> 1) + 4 * h + (s16 >> 2)) * 256 + (2 * (g16 & 1) + ((s16 & 3) >> 1)) * 16 +
+                           (s16 & 1) * 8;
+#pragma unroll
+        for (int i = 0; i < MB; ++i) koa[h][i] = rowoff + 64 * (i ^ (s16 >> 2));
+    }
+    // K-contiguous row operand: row 32 i + frow, logical chunk 2 q + kg
+    int kca[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) kca[q] = frow * 64 + (((2 * q + kg) ^ ((frow >> 1) & 3)) * 16);
+
+    f32x16_t acc[MB][NB];
+    uint4 av[2][MB], bv[2][NB];
+    auto read_one = [&](int kt, int q, int set, int r) __attribute__((always_inline)) {
+        const int kv = ke - kb - 32 * kt;  // valid K values of step kt (32 or fewer on the last)
+        if (r < RA) {
+            const unsigned char* base = smem + (kt % NA) * kT2SlotA;
+            if constexpr (A_KOUTER) {
+                const int i = r >> 1, h = r & 1;
+                uint2 v = lds_read_tr16(base + koa[h][i] + q * 16 * 256);
+                if (kv < 32) v = keep_first(v, kv - (16 * q + 8 * (g16 >> 1) + 4 * h));
+                if (h == 0) {
+                    av[set][i].x = v.x;
+                    av[set][i].y = v.y;
+                } else {
+                    av[set][i].z = v.x;
+                    av[set][i].w = v.y;
+                }
+            } else {
+                // rows 32 r + frow keep (row >> 1) & 3 of frow
+                uint4 v = *(const uint4*)(base + kca[q] + r * 32 * 64);
+                if (kv < 32 && 16 * q + 8 * kg >= kv) v = make_uint4(0, 0, 0, 0);
+                av[set][r] = v;
+            }
+        } else {
+            const int rr = r - RA, f = rr >> 1, h = rr & 1;
+            const unsigned char* base = smem + NA * kT2SlotA + (kt % NB_) * kT2SlotB;
+            uint2 v = lds_read_tr16(base + kob[h][f] + q * 16 * 512);
+            if (kv < 32) v = keep_first(v, kv - (16 * q + 8 * (g16 >> 1) + 4 * h));
+            if (h == 0) {
+                bv[set][f].x = v.x;
+                bv[set][f].y = v.y;
+            } else {
+                bv[set][f].z = v.x;
+                bv[set][f].w = v.y;
+            }
+        }
+    };
+    int rows_live = kT2BM;
+    auto substep = [&](auto nd, int set, int rkt, int rq, auto&& dma) __attribute__((always_inline)) {
+        constexpr int ND = decltype(nd)::value, H1 = NM / 2, H2 = NM - NM / 2;
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+            const int i = m / NB, f = m % NB;
+            if (!ROWS || i * 32 < rows_live) acc[i][f] = mma32<DT>::run(bv[set][f], av[set][i], acc[i][f]);
+            if (m < H1) {
+#pragma unroll
+                for (int r = (m * NR) / H1; r < ((m + 1) * NR) / H1; ++r) read_one(rkt, rq, set ^ 1, r);
+            } else {
+                const int q = m - H1;
+#pragma unroll
+                for (int d = (q * ND) / H2; d < ((q + 1) * ND) / H2; ++d) dma(d);
+            }
+            sched_fence();
+        }
+    };
+    using no_dma = std::integral_constant<int, 0>;
+    using step_dma = std::integral_constant<int, LPA + LPB>;
+    auto none = [](int) __attribute__((always_inline)) {};
+
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int f = 0; f < NB; ++f)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][f][r] = 0.0f;
+    if (nk > 0) {
+        if constexpr (ROWS) rows_live = m1 - m0;
+        // issue order A0 B0 A1 B1 B2: step 0 has landed once the pieces after B0 may be in flight
+#pragma unroll
+        for (int j = 0; j < LPA; ++j) dma_a(0, j);
+#pragma unroll
+        for (int j = 0; j < LPB; ++j) dma_b(0, j);
+#pragma unroll
+        for (int j = 0; j < LPA; ++j) dma_a(1, j);
+#pragma unroll
+        for (int j = 0; j < LPB; ++j) dma_b(1, j);
+#pragma unroll
+        for (int j = 0; j < LPB; ++j) dma_b(2, j);
+        wait_vm<LPA + 2 * LPB>();
+        barrier_lds();
+#pragma unroll
+        for (int r = 0; r < NR; ++r) read_one(0, 0, 0, r);
+        for (int kt = 0; kt < nk; ++kt) {
+            wait_lgkm0();
+            substep(no_dma{}, 0, kt, 1, none);
+            // step kt+1 landed (only the column operand of kt+2 was issued after
+            // it); every wave is done reading step kt once past the barrier
+            wait_vm<LPB>();
+            wait_lgkm0();
+            barrier_lds();
+            substep(step_dma{}, 1, kt + 1, 0, [&](int d) __attribute__((always_inline)) {
+                if (d < LPA) dma_a(kt + 2, d); else dma_b(kt + 3, d - LPA);
+            });
+        }
+        wait_vm<0>();
+        wait_lgkm0();
+    }
+
+    // ---- epilogue: lane holds output row (lane % 32) of each row block and
+    // columns 8 g + 4 (lane / 32) + 0..3 (g = 0..3) of each column block
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+        const int m = m0 + 32 * i + frow;
+        if (m >= m1) continue;
+#pragma unroll
+        for (int f = 0; f < NB; ++f) {
+            const int cb = n0 + wid * WTN + 32 * f + 4 * kg;
+            if constexpr (MODE == kDH) {
+                float4 g4[4], u4[4];
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int col = cb + 8 * g;
+                    const float* gr = p.gu + (int64_t)m * I2 + (col < ncols ? col : 0);
+                    g4[g] = *(const float4*)gr;
+                    u4[g] = *(const float4*)(gr + p.I);
+                }
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int col = cb + 8 * g;
+                    if (col >= ncols) continue;
+                    const float gv[4] = {g4[g].x, g4[g].y, g4[g].z, g4[g].w};
+                    const float uv[4] = {u4[g].x, u4[g].y, u4[g].z, u4[g].w};
+                    float dg[4], du[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float dh = acc[i][f][4 * g + r];
+                        const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-gv[r]));
+                        du[r] = dh * (gv[r] * sg);
+                        dg[r] = dh * uv[r] * (sg * (1.0f + gv[r] * (1.0f - sg)));
+                    }
+                    S* out = (S*)p.c0 + (int64_t)m * I2 + col;
+                    store4<DT>::run(out, dg);
+                    store4<DT>::run(out + p.I, du);
+                }
+            } else {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int col = cb + 8 * g;
+                    if (col >= ncols) continue;
+                    const float v0 = acc[i][f][4 * g], v1 = acc[i][f][4 * g + 1], v2 = acc[i][f][4 * g + 2],
+                                v3 = acc[i][f][4 * g + 3];
+                    if constexpr (MODE == kDX) {
+                        const float v[4] = {v0, v1, v2, v3};
+                        store4<DT>::run((S*)p.c0 + (int64_t)m * p.H + col, v);
+                    } else {
+                        float* out;
+                        if constexpr (MODE == kDWGU)
+                            out = m < p.I ? (float*)p.c0 + ((int64_t)e * p.I + m) * p.H + col
+                                          : (float*)p.c1 + ((int64_t)e * p.I + (m - p.I)) * p.H + col;
+                        else
+                            out = (float*)p.c0 + ((int64_t)e * p.H + m) * p.I + col;
+                        *(float4*)out = make_float4(v0, v1, v2, v3);
+                    }
+                }
+            }
+        }
+    }
+}
+
+template <typename DT, int MODE>
+hipError_t launch_train_pipe2(TrainGemm p, int64_t blocks, hipStream_t s) {
+    if (blocks == 0) return hipSuccess;
+    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+    p.nblocks = (int)blocks;
+    train_pipe2_kernel<DT, MODE><<<(unsigned)blocks, kT2Waves * kWave, 0, s>>>(p);
+    return hipGetLastError();
+}
+
 // rows[r] = x[token_of_row[r]] (the token index clamped into x), one
 // wavefront per row, 16-byte chunks
 __global__ __launch_bounds__(256) void gather_rows_kernel(const uint4* __restrict__ x, const uint32_t* __restrict__ tor,
@@ -752,7 +1067,8 @@ hipError_t experts_backward_typed(const ExpertsBackwardArgs& a, hipStream_t s) {
     const bool offsets32 = a.N * 2 * a.I * es < lim && a.N * a.H * es < lim && a.H * a.I * es < lim &&
                            256 * std::max(a.H, 2 * a.I) * es < lim;
     const bool pipe = MOE_TRAIN_PIPE && es == 2 && offsets32 && a.N >= 64 * (int64_t)a.E;
-    const int BM = pipe ? kTPBM : kTBM, BN = pipe ? kTPBN : kTBN;
+    const bool two = pipe && MOE_TRAIN_PIPE == 2;
+    const int BM = two ? kT2BM : (pipe ? kTPBM : kTBM), BN = two ? kT2BN : (pipe ? kTPBN : kTBN);
     int4* tiles = (int4*)((char*)a.tiles + 256);
     uint32_t* count = (uint32_t*)a.tiles;
     const int64_t mt = max_mtiles(a.N, a.E, BM);
@@ -761,6 +1077,7 @@ hipError_t experts_backward_typed(const ExpertsBackwardArgs& a, hipStream_t s) {
     auto launch = [&](auto mode, const TrainGemm& q, int64_t blocks) {
         constexpr int M = decltype(mode)::value;
         if constexpr (sizeof(typename DT::storage) == 2) {
+            if (two) return launch_train_pipe2<DT, M>(q, blocks, s);
             if (pipe) return launch_train_pipe<DT, M>(q, blocks, s);
         }
         return launch_train_gemm<DT, M>(q, blocks, s);
