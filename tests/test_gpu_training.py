@@ -316,79 +316,156 @@ def test_training_step_with_group_limited_sigmoid_routing():
 
 
 # ------------------------------------------------------------------ full size, sampled
-def test_training_step_full_size_sampled():
-    """Prefill BF16 (T=8192, H=2048, I=1408, E=64, top_k=6) through the same
-    calls the benchmark times.  Sampled checks the oracle computes one by one:
-    dx and dlogits of a few tokens (each token's rows run through the oracle
-    with the full expert weights), and dgate / dup / ddown on a few
-    intermediate columns of a few experts (the gradient of column i of gate,
-    up and down depends only on column i of g, u, h and dh, so a sliced expert
-    gives them exactly)."""
-    cfg = S.CONFIGS["prefill_bf16"]
-    log("training full size: prefill_bf16")
+def run_step_on_device(cfg):
+    """The benchmark's training step on device-drawn inputs; returns every result."""
     x, lg = S.make_tokens(cfg, device=DEV)
     W = S.make_weights(cfg, device=DEV)
     gout = S.make_grad_output(cfg, device=DEV)
-    opt = moe.RouterWeightOptions("softmax", True, 1.0)
-    gx, glg = x, lg
+    opt = moe.RouterWeightOptions("softmax", cfg.renormalize, 1.0)
     ex = moe.SwiGluExperts(*W)
-    plan = moe.route(glg, moe.RoutingOptions(cfg.top_k, True))
-    tp = plan.into_training(glg, opt)
-    d = tp.routing().dispatch(gx, copy_rows=False)
-    y, cache = ex.forward_dispatched_training(d, input=gx)
+    plan = moe.route(lg, moe.RoutingOptions(cfg.top_k, cfg.renormalize))
+    tp = plan.into_training(lg, opt)
+    d = tp.routing().dispatch(x, copy_rows=False)
+    y, cache = ex.forward_dispatched_training(d, input=x)
     dy, dw = d.combine_backward(y, gout)
     drows, dgate, dup, ddown = cache.backward(dy)
     dx = d.dispatch_backward(drows)
     dlg = tp.backward(dw)
     torch.cuda.synchronize()
-    log("  device step done; sampling")
+    return dict(x=x, lg=lg, W=W, gout=gout, plan=plan, d=d, dy=dy, drows=drows, dgate=dgate, dup=dup,
+                ddown=ddown, dx=dx, dlg=dlg)
+
+
+def check_sampled(cfg, r, tokens, experts, n_cols, rng):
+    """Sampled checks the oracle computes one by one: dx and dlogits of some
+    tokens (each token's rows through the oracle with the full expert
+    weights), and dgate / dup / ddown on some intermediate columns of some
+    experts (column i of those gradients depends only on column i of g, u, h
+    and dh, so a sliced expert gives them exactly)."""
     E, H, I, k = cfg.E, cfg.H, cfg.I, cfg.top_k
-    idx = host_bits(plan.expert_indices())
-    offsets = host_bits(d.expert_offsets)
-    tor = host_bits(d.token_of_row)
-    ros = host_bits(d.row_of_slot)
-    xb, lb, gb = host_bits(x), host_bits(lg), host_bits(gout)
+    W = r["W"]
+    idx = host_bits(r["plan"].expert_indices())
+    offsets = host_bits(r["d"].expert_offsets)
+    tor = host_bits(r["d"].token_of_row)
+    ros = host_bits(r["d"].row_of_slot)
+    xb, lb, gb = host_bits(r["x"]), host_bits(r["lg"]), host_bits(r["gout"])
+    ldt = cfg.logits_dtype
     assert int(offsets[E]) == cfg.T * k
-    rng = np.random.default_rng(9)
-    # tokens: dx and dlogits
-    for t in rng.choice(cfg.T, size=6, replace=False):
+    for t in tokens:
         rows_t = ros[t * k:(t + 1) * k]
-        w32 = oracle.router_weights(lb[t:t + 1], "bf16", idx[t:t + 1], "softmax", True, 1.0)
+        w32 = oracle.router_weights(lb[t:t + 1], ldt, idx[t:t + 1], "softmax", cfg.renormalize, 1.0)
         gdx_t = np.zeros(H)
         dw_t = np.zeros((1, k), np.float32)
         for j in range(k):
             e = int(idx[t, j])
             We = [host_bits(w[e:e + 1]) for w in W]
             off1 = np.array([0, 1], np.uint32)
-            fw = oracle.experts_train_forward(*We, "bf16", xb[t:t + 1], off1, 1, H, I)
-            ody, odw = oracle.combine_backward(fw["output"], "bf16", np.array([0], np.uint32), w32[:, j:j + 1],
+            fw = oracle.experts_train_forward(*We, cfg.dtype, xb[t:t + 1], off1, 1, H, I)
+            ody, odw = oracle.combine_backward(fw["output"], cfg.dtype, np.array([0], np.uint32), w32[:, j:j + 1],
                                                "f32", gb[t:t + 1], 1, 1, H)
-            odx, _, _, _ = oracle.experts_backward(*We, "bf16", xb[t:t + 1], off1, 1, H, I, fw["g"], fw["u"],
+            odx, _, _, _ = oracle.experts_backward(*We, cfg.dtype, xb[t:t + 1], off1, 1, H, I, fw["g"], fw["u"],
                                                    fw["h"], ody)
-            gdx_t += oracle.widen(odx, "bf16")[0]
+            gdx_t += oracle.widen(odx, cfg.dtype)[0]
             dw_t[0, j] = odw[0, 0]
-            assert_close(values(drows[int(rows_t[j])], "bf16"), oracle.widen(odx, "bf16")[0], "bf16",
-                         f"full-size grad_rows token {t} slot {j}")
-        odl = oracle.router_backward(lb[t:t + 1], "bf16", idx[t:t + 1], dw_t, "softmax", True, 1.0)
-        assert_close(values(dx[t], "bf16"), oracle.widen(oracle.narrow(gdx_t, "bf16"), "bf16"), "bf16",
-                     f"full-size dx token {t}")
-        assert_close(values(dlg[t], "bf16"), oracle.widen(odl, "bf16")[0], "bf16", f"full-size dlogits token {t}")
-    # weight gradients: a few columns of a few experts, sliced experts
-    for e in rng.choice(E, size=2, replace=False):
+            assert_close(values(r["drows"][int(rows_t[j])], cfg.dtype), oracle.widen(odx, cfg.dtype)[0], cfg.dtype,
+                         f"{cfg.name} grad_rows token {t} slot {j}")
+        odl = oracle.router_backward(lb[t:t + 1], ldt, idx[t:t + 1], dw_t, "softmax", cfg.renormalize, 1.0)
+        assert_close(values(r["dx"][t], cfg.dtype), oracle.widen(oracle.narrow(gdx_t, cfg.dtype), cfg.dtype),
+                     cfg.dtype, f"{cfg.name} dx token {t}")
+        assert_close(values(r["dlg"][t], ldt), oracle.widen(odl, ldt)[0], cfg.dtype, f"{cfg.name} dlogits token {t}")
+    for e in experts:
         a, b = int(offsets[e]), int(offsets[e + 1])
-        cols = np.sort(rng.choice(I, size=8, replace=False))
+        cols = np.sort(rng.choice(I, size=n_cols, replace=False))
         gate_s = host_bits(W[0][e, cols])[None]
         up_s = host_bits(W[1][e, cols])[None]
         down_s = np.ascontiguousarray(host_bits(W[2][e][:, cols]))[None]
         rows_e = xb[tor[a:b]]
         off1 = np.array([0, b - a], np.uint32)
-        dy_e = host_bits(dy[a:b])
-        fw = oracle.experts_train_forward(gate_s, up_s, down_s, "bf16", rows_e, off1, 1, H, len(cols), NTHREADS)
-        _, odg, odu, odd, odgu = oracle.experts_backward(gate_s, up_s, down_s, "bf16", rows_e, off1, 1, H,
+        dy_e = host_bits(r["dy"][a:b])
+        fw = oracle.experts_train_forward(gate_s, up_s, down_s, cfg.dtype, rows_e, off1, 1, H, len(cols), NTHREADS)
+        _, odg, odu, odd, odgu = oracle.experts_backward(gate_s, up_s, down_s, cfg.dtype, rows_e, off1, 1, H,
                                                          len(cols), fw["g"], fw["u"], fw["h"], dy_e, NTHREADS,
                                                          with_dgu=True)
-        lg, lu, ld = wgrad_l1(off1, odgu, rows_e, dy_e, fw["h"], "bf16", 1, len(cols))
-        assert_close_sum(dgate[e, cols].cpu().double().numpy(), odg[0], lg[0], "bf16", f"full-size dgate expert {e}")
-        assert_close_sum(dup[e, cols].cpu().double().numpy(), odu[0], lu[0], "bf16", f"full-size dup expert {e}")
-        assert_close_sum(ddown[e][:, cols].cpu().double().numpy(), odd[0], ld[0], "bf16",
-                         f"full-size ddown expert {e}")
+        lg, lu, ld = wgrad_l1(off1, odgu, rows_e, dy_e, fw["h"], cfg.dtype, 1, len(cols))
+        tag = f"{cfg.name} expert {e} ({b - a} rows)"
+        assert_close_sum(r["dgate"][e, cols].cpu().double().numpy(), odg[0], lg[0], cfg.dtype, f"dgate {tag}")
+        assert_close_sum(r["dup"][e, cols].cpu().double().numpy(), odu[0], lu[0], cfg.dtype, f"dup {tag}")
+        assert_close_sum(r["ddown"][e][:, cols].cpu().double().numpy(), odd[0], ld[0], cfg.dtype, f"ddown {tag}")
+
+
+def test_training_step_full_size_sampled():
+    """Prefill BF16 (T=8192, H=2048, I=1408, E=64, top_k=6) through the same
+    calls the benchmark times, checked on sampled tokens and gradient columns."""
+    cfg = S.CONFIGS["prefill_bf16"]
+    log("training full size: prefill_bf16")
+    r = run_step_on_device(cfg)
+    log("  device step done; sampling")
+    rng = np.random.default_rng(9)
+    check_sampled(cfg, r, rng.choice(cfg.T, size=6, replace=False), rng.choice(cfg.E, size=2, replace=False), 8, rng)
+
+
+def test_training_step_skewed_routing_sampled():
+    """Zipf(1.1)-skewed routing over 256 experts (the skewed workload's
+    routing at H=1024, I=512): the hottest expert owns thousands of rows, so
+    the weight-gradient products run long K loops and the row products many
+    tiles of one expert, while cold experts own a few rows or none."""
+    cfg = S.small_config("skewed_train_bf16", T=8192, H=1024, I=512, E=256, top_k=8, dtype="bf16", zipf_s=1.1,
+                         seed=1104)
+    log("training skewed routing: T=8192 H=1024 I=512 E=256 k=8")
+    r = run_step_on_device(cfg)
+    off = host_bits(r["d"].expert_offsets).astype(np.int64)
+    counts = np.diff(off)
+    log(f"  rows per expert: max {counts.max()}, median {int(np.median(counts))}, empty {int((counts == 0).sum())}")
+    assert counts[0] > 2000
+    rng = np.random.default_rng(10)
+    experts = [0, int(np.argmin(np.where(counts > 0, counts, 1 << 30))), int(rng.integers(1, cfg.E))]
+    check_sampled(cfg, r, rng.choice(cfg.T, size=4, replace=False), experts, 6, rng)
+    empty = np.nonzero(counts == 0)[0]
+    for e in empty[:3]:
+        assert float(r["dgate"][e].abs().max()) == 0.0 and float(r["ddown"][e].abs().max()) == 0.0
+
+
+def test_training_all_tokens_to_one_expert():
+    """Every token picks expert 3 first: one expert owns a third of the rows
+    (a K loop of 2048 rows in its weight gradients) and the others share the
+    rest."""
+    cfg = S.small_config("one_hot_train_bf16", T=2048, H=256, I=192, E=8, top_k=3, dtype="bf16", seed=1105)
+    log("training with one dominant expert")
+    x, lg = S.make_tokens(cfg)
+    lg[:, 3] = 30.0
+    W = S.make_weights(cfg)
+    gout = S.make_grad_output(cfg)
+    opt = moe.RouterWeightOptions("softmax", True, 1.0)
+    g = gpu_train_step(cfg, x, lg, W, gout, opt)
+    assert (g["indices"][:, 0] == 3).all()
+    r = oracle.train_step(host_bits(x), host_bits(lg), *[host_bits(w) for w in W], "bf16", "bf16", 3, True,
+                          host_bits(gout), NTHREADS, indices=g["indices"])
+    for k, dt in (("output", "bf16"), ("dx", "bf16"), ("dlogits", "bf16")):
+        assert_close(values(g[k], dt), oracle.widen(r[k], dt), dt, f"one-hot step {k}")
+    l1 = wgrad_l1(r["offsets"], r["dgu"], r["dispatched"], r["dY"], r["h"], "bf16", cfg.E, cfg.I)
+    check_wgrads((g["dgate"], g["dup"], g["ddown"]), (r["dgate"], r["dup"], r["ddown"]), l1, "bf16", "one-hot step")
+
+
+def test_training_empty_batch_and_single_token():
+    """T = 0: no rows, every weight gradient is written as zeros; T = 1."""
+    E, H, I = 4, 64, 64
+    cfg = S.small_config("t1_bf16", T=1, H=H, I=I, E=E, top_k=2, dtype="bf16", seed=1106)
+    W = [w.to(DEV) for w in S.make_weights(cfg)]
+    ex = moe.SwiGluExperts(*W)
+    x0 = torch.empty((0, H), dtype=torch.bfloat16, device=DEV)
+    d0 = moe.dispatch(x0, torch.empty((0, 2), dtype=torch.uint32, device=DEV), E, copy_rows=False)
+    y0, cache0 = ex.forward_dispatched_training(d0, input=x0)
+    grads = cache0.backward(torch.empty((0, H), dtype=torch.bfloat16, device=DEV))
+    torch.cuda.synchronize()
+    assert y0.shape == (0, H) and grads[0].shape == (0, H)
+    for gw in grads[1:]:
+        assert float(gw.abs().max()) == 0.0
+    x, lg = S.make_tokens(cfg)
+    gout = S.make_grad_output(cfg)
+    g = gpu_train_step(cfg, x, lg, [w.cpu() for w in W], gout, moe.RouterWeightOptions("softmax", True, 1.0))
+    r = oracle.train_step(host_bits(x), host_bits(lg), *[host_bits(w) for w in W], "bf16", "bf16", 2, True,
+                          host_bits(gout), NTHREADS, indices=g["indices"])
+    for k in ("output", "dx", "dlogits"):
+        assert_close(values(g[k], "bf16"), oracle.widen(r[k], "bf16"), "bf16", f"single token {k}")
+    l1 = wgrad_l1(r["offsets"], r["dgu"], r["dispatched"], r["dY"], r["h"], "bf16", E, I)
+    check_wgrads((g["dgate"], g["dup"], g["ddown"]), (r["dgate"], r["dup"], r["ddown"]), l1, "bf16", "single token")
