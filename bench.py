@@ -365,7 +365,7 @@ def measure_training(name: str, steps: int, warmup: int, cpu_seconds: float | No
            "stages_ms": {k: round(v, 4) for k, v in st.items()},
            "roofline": {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                         "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-                        "kernel": "train_pipe_kernel x4 (experts backward: dh, dx, dgate+dup, ddown)",
+                        "kernel": "train_pipe2_kernel x4 (experts backward: dh, dx, dgate+dup, ddown)",
                         "avg_launch_ms": round(st["experts_backward"], 4), "flops_per_launch": 12.0 * nhi,
                         "traffic": None}}
     del W, ex
