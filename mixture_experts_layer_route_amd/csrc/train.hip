@@ -439,18 +439,6 @@ __global__ __launch_bounds__(kTPWaves* kWave, 1) void train_pipe_kernel(TrainGem
     // ---- DMA sources.  K-outer piece j: K-row r = 2 (wid LPO + j) + lane / 32
     // of the slot, physical chunk lane % 32 holding logical chunk
     // (lane % 32) ^ ((r & 7) << 2), i.e. columns c0 + 8 * that.
-    auto b_row = [&](int k) __attribute__((always_inline)) -> const S* {
-        if constexpr (MODE == kDH) {
-            return (const S*)p.b0 + ((int64_t)e * p.H + k) * p.I;
-        } else if constexpr (MODE == kDX) {
-            return k < p.I ? (const S*)p.b0 + ((int64_t)e * p.I + k) * p.H
-                           : (const S*)p.b1 + ((int64_t)e * p.I + (k - p.I)) * p.H;
-        } else if constexpr (MODE == kDWGU) {
-            return (const S*)p.b0 + (int64_t)k * p.H;
-        } else {
-            return (const S*)p.b0 + (int64_t)k * p.I;
-        }
-    };
     const uint32_t lds_a = lds_offset(smem) + wid * LPO * 1024;
     const uint32_t lds_b = lds_a + NA * kTPSlot;
     // Addresses are formed at issue time from the tile's (uniform) extents,
