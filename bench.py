@@ -11,7 +11,9 @@ inputs and weights already resident in HBM.  Prints one JSON line:
                algorithmic FLOPs (or bytes, at decode) per launch over its
                average launch time, measured with HIP events recorded on the
                stream it runs on, against the MI355X dense peak;
-  stages_ms    per-stage times of the split calls (same kernels);
+  stages_ms    per-stage times of the split calls (same kernels), and the
+               algorithmic HBM GB/s of routing, dispatch (mapping only, and
+               the split API's copying dispatch) and combine;
   cpu_baseline the CPU oracle timed on a bounded sample of the same workload;
   secondary    the decode and skewed workloads, same measurement;
   grouped_routing  the skewed workload's forward with group-limited sigmoid
@@ -157,6 +159,15 @@ def measure(name: str, steps: int, warmup: int, only_forward: bool = False) -> d
         for i, n in enumerate(names):
             acc[n] += evs[i].elapsed_time(evs[i + 1])
     res["stages_ms"] = {n: acc[n] / steps for n in names}
+    # the split API's dispatch, which also copies the rows grouped by expert
+    for _ in range(warmup):
+        plan.dispatch(x)
+    e0.record()
+    for _ in range(steps):
+        plan.dispatch(x)
+    e1.record()
+    torch.cuda.synchronize()
+    res["dispatch_copy_ms"] = e0.elapsed_time(e1) / steps
     idx = plan.expert_indices().view(torch.int32).long()
     res["active_experts"] = int(torch.unique(idx).numel())
     return res
@@ -401,6 +412,28 @@ def cpu_training_baseline(cfg, target_s: float) -> dict:
             "sample": f"first {n} of {cfg.T} tokens, whole training step, {dt:.1f} s"}
 
 
+def stage_gbs(res: dict) -> dict:
+    """Algorithmic HBM GB/s of the memory-bound stages: routing reads the
+    logits and writes indices and weights; the mapping-only dispatch reads
+    the indices and writes the offsets and both mappings; the copying
+    dispatch also reads the tokens and writes their k copies; combine reads
+    the expert rows, the mapping and the weights and writes the output."""
+    cfg = res["cfg"]
+    es = 2 if cfg.dtype in ("bf16", "f16") else 4
+    ls = 2 if cfg.logits_dtype in ("bf16", "f16") else 4
+    T, N, E, H = cfg.T, cfg.N, cfg.E, cfg.H
+    st = res["stages_ms"]
+    nbytes = {
+        "route": T * E * ls + N * (4 + ls),
+        "dispatch": N * 4 + 2 * N * 4 + (E + 1) * 4,
+        "dispatch_copy": N * 4 + T * H * es + N * H * es + 2 * N * 4 + (E + 1) * 4,
+        "combine": N * H * es + N * (4 + ls) + T * H * es,
+    }
+    ms = {"route": st["route"], "dispatch": st["dispatch"], "dispatch_copy": res["dispatch_copy_ms"],
+          "combine": st["combine"]}
+    return {k: round(nbytes[k] / (ms[k] * 1e-3) / 1e9, 1) for k in nbytes}
+
+
 def summary(res: dict) -> dict:
     cfg = res["cfg"]
     d = {"workload": res["workload"], "tokens_per_s": round(res["tokens_per_s"], 1),
@@ -410,6 +443,8 @@ def summary(res: dict) -> dict:
         d["stages_ms"] = {k: round(v, 4) for k, v in res["stages_ms"].items()}
         d["active_experts"] = res["active_experts"]
         d["hbm_gbs_forward"] = round(hbm_bytes_forward(res) / (res["ms_per_step"] * 1e-3) / 1e9, 1)
+        d["dispatch_copy_ms"] = round(res["dispatch_copy_ms"], 4)
+        d["stage_hbm_gbs"] = stage_gbs(res)
         d["roofline"] = roofline(res)
     d["config"] = {"T": cfg.T, "H": cfg.H, "I": cfg.I, "E": cfg.E, "top_k": cfg.top_k,
                    "renormalize": cfg.renormalize, "dtype": cfg.dtype}
@@ -460,6 +495,8 @@ def main():
         line["roofline"] = head["roofline"]
         line["stages_ms"] = head["stages_ms"]
         line["hbm_gbs_forward"] = head["hbm_gbs_forward"]
+        line["dispatch_copy_ms"] = head["dispatch_copy_ms"]
+        line["stage_hbm_gbs"] = head["stage_hbm_gbs"]
         line["active_experts"] = head["active_experts"]
     if not args.only_forward:
         sec = [s for s in args.secondary.split(",") if s and s != args.workload]
