@@ -29,8 +29,8 @@
 //     default for prefill-sized batches): 256x256 tiles on 8 waves of
 //     32x32x16 MFMAs; 64-element K steps filled by direct global->LDS loads
 //     into two token-row slots and three weight-row slots of 32 KB, the
-//     weight rows issued two steps ahead and the token rows one, each step's
-//     loads spread over the MFMAs of its last 16-K sub-step.
+//     weight rows issued about two steps ahead, a quarter per 16-K sub-step,
+//     and the token rows one step ahead, in the last sub-step of a step.
 //   grouped_gemm_pipe_kernel (bf16/f16, K a multiple of 32): 256x256 tiles on
 //     8 waves of 32x32x16 MFMAs; 32-element K stages filled by direct
 //     global->LDS loads in a 4-stage ring, issued three stages ahead and
@@ -572,8 +572,10 @@ __global__ __launch_bounds__(WGM* WGN* kWave, MOE_P_MINB) void grouped_gemm_pipe
 // read during the current one.  The barrier sits between sub-steps 2 and 3
 // of step kt: by then every wave has read all of step kt and landed its DMA
 // of step kt+1, so sub-step 3 reads the first fragments of kt+1 and starts
-// the DMA of the token rows of kt+2 and the weight rows of kt+3 into the
-// slots step kt leaves.  Requires K % 64 == 0.
+// the DMA of the token rows of kt+2 and of a quarter of the weight rows of
+// kt+3 into the slots step kt leaves; the other weight rows of kt+3 follow,
+// a quarter per sub-step, over sub-steps 0-2 of step kt+1.  Requires
+// K % 64 == 0.
 constexpr int kP64SlotsA = 2, kP64SlotsB = 3;
 template <typename DT, bool GATEUP, int WGM, int WGN>
 __global__ __launch_bounds__(WGM* WGN* kWave, 1) void grouped_gemm_pipe64_kernel(
@@ -594,7 +596,7 @@ __global__ __launch_bounds__(WGM* WGN* kWave, 1) void grouped_gemm_pipe64_kernel
     constexpr int WCN = BN_OUT / WGN;
     constexpr int NM = MB * NB, NR = MB + NB;                   // MFMAs and fragment reads per sub-step
     static_assert(!GATEUP || NB % 2 == 0, "gate and up blocks pair up");
-    static_assert(2 * LPO <= NM, "at most one DMA piece per MFMA of a sub-step");
+    static_assert(LPO + LPO / 4 <= 2 * (NM - NM / 2), "at most two DMA pieces per MFMA of a sub-step");
     static_assert(NA == 2 && NB_ == 3, "the vmcnt waits below are counted for 2 token and 3 weight slots");
     __shared__ __attribute__((aligned(1024))) unsigned char smem[(NA + NB_) * SLOT];
 
@@ -668,20 +670,28 @@ __global__ __launch_bounds__(WGM* WGN* kWave, 1) void grouped_gemm_pipe64_kernel
     auto dma_b = [&](int kt, int j) {
         lds_dma16(srcb[j] + min(kt, nk - 1) * ROWB, lds_b + (kt % NB_) * SLOT + j * 1024);
     };
-    // issue order A0 B0 A1 B1 B2: step 0 has landed once the 3 * LPO pieces
-    // after B0 may still be in flight
+    // Weight rows of step kt+2 go out a quarter step (BQ pieces) per sub-step,
+    // from sub-step 3 of step kt-1 to sub-step 2 of step kt, into the slot the
+    // barrier of step kt-1 freed; token rows of step kt+2 go out whole in
+    // sub-step 3 of step kt, the first moment their slot is free.  Spreading
+    // the weight rows keeps the DMA issue of a step from queueing up behind
+    // one sub-step.  Before step 0 the pieces that schedule would have issued
+    // go out in its order: A0 B0 B1 A1 B2[0, BQ).
+    constexpr int BQ = LPO / 4;
+    static_assert(LPO % 4 == 0, "weight-row pieces spread over four sub-steps");
     auto prologue_dma = [&]() {
 #pragma unroll
         for (int j = 0; j < LPO; ++j) dma_a(0, j);
 #pragma unroll
         for (int j = 0; j < LPO; ++j) dma_b(0, j);
 #pragma unroll
-        for (int j = 0; j < LPO; ++j) dma_a(1, j);
-#pragma unroll
         for (int j = 0; j < LPO; ++j) dma_b(1, j);
 #pragma unroll
-        for (int j = 0; j < LPO; ++j) dma_b(2, j);
+        for (int j = 0; j < LPO; ++j) dma_a(1, j);
+#pragma unroll
+        for (int j = 0; j < BQ; ++j) dma_b(2, j);
     };
+    constexpr int kPrologueAfter0 = 2 * LPO + BQ;  // pieces issued after B0
     // the MFMAs of sub-step (set), the reads of the next sub-step (rkt, rq)
     // into the other set over the first half of them, and `nd` DMA pieces
     // over the second half
@@ -704,27 +714,25 @@ __global__ __launch_bounds__(WGM* WGN* kWave, 1) void grouped_gemm_pipe64_kernel
             sched_fence();
         }
     };
-    using no_dma = std::integral_constant<int, 0>;
-    using step_dma = std::integral_constant<int, 2 * LPO>;
-    auto none = [](int) {};
+    using q_dma = std::integral_constant<int, BQ>;
+    using q3_dma = std::integral_constant<int, LPO + BQ>;
     auto main_loop = [&](auto full) {
         for (int kt = 0; kt < nk; ++kt) {
             wait_lgkm0();
-            substep(full, no_dma{}, 0, kt, 1, none);
+            substep(full, q_dma{}, 0, kt, 1, [&](int d) { dma_b(kt + 2, BQ + d); });
             wait_lgkm0();
-            substep(full, no_dma{}, 1, kt, 2, none);
+            substep(full, q_dma{}, 1, kt, 2, [&](int d) { dma_b(kt + 2, 2 * BQ + d); });
             wait_lgkm0();
-            substep(full, no_dma{}, 0, kt, 3, none);
-            // step kt+1 landed: its weight rows went out a step before its
-            // token rows, and only the weight rows of kt+2 (LPO pieces) were
-            // issued after them.  The reads of step kt complete before the
-            // barrier, so its slots can be refilled once every wave has
-            // passed it.
+            substep(full, q_dma{}, 0, kt, 3, [&](int d) { dma_b(kt + 2, 3 * BQ + d); });
+            // step kt+1 landed: its weight rows all went out before its token
+            // rows, and only the LPO weight-row pieces of kt+2 after them.
+            // The reads of step kt complete before the barrier, so its slots
+            // can be refilled once every wave has passed it.
             wait_vm<LPO>();
             wait_lgkm0();
             barrier_lds();
-            // token rows of kt+2 first, then weight rows of kt+3
-            substep(full, step_dma{}, 1, kt + 1, 0,
+            // token rows of kt+2, then the first weight rows of kt+3
+            substep(full, q3_dma{}, 1, kt + 1, 0,
                     [&](int d) { if (d < LPO) dma_a(kt + 2, d); else dma_b(kt + 3, d - LPO); });
         }
     };
@@ -738,7 +746,7 @@ __global__ __launch_bounds__(WGM* WGN* kWave, 1) void grouped_gemm_pipe64_kernel
             for (int f = 0; f < NB; ++f)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[i][f][r] = 0.0f;
-        wait_vm<3 * LPO>();
+        wait_vm<kPrologueAfter0>();
         barrier_lds();
 #pragma unroll
         for (int r = 0; r < NR; ++r) read_one(0, 0, 0, r);
