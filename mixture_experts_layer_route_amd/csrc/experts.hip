@@ -388,6 +388,59 @@ __device__ __forceinline__ void store_tile32(const f32x16_t (&acc)[MB][NB], type
     }
 }
 
+// The down product's epilogue staged through LDS (2-byte outputs): each wave
+// writes its WTM-token x WTN-column block into its own LDS region (`stage`,
+// WTM * WTN * 2 bytes that no other wave touches before the next barrier),
+// row by row, then reads it back a 16-byte chunk per lane, so a store
+// instruction writes whole 128-byte row segments of 8 token rows instead of
+// 8 bytes of 32 rows (5% of the down product's time on the prefill
+// workload).  Staged row t holds its 16-byte chunk c at c ^ ((t / 2) % 8),
+// which spreads both the 8-byte writes and the 16-byte reads over all 64
+// banks.  (The gate/up epilogue gains nothing from staging: its cost is the
+// SiLU arithmetic, not the stores.)
+template <typename DT, int MB, int NB, int WTM, int WTN>
+__device__ __forceinline__ void store_tile32_staged(const f32x16_t (&acc)[MB][NB],
+                                                    typename DT::storage* __restrict__ C, int r0, int r1, int n0,
+                                                    int wm, int wn, int NOUT, int lane, unsigned char* stage) {
+    using S = typename DT::storage;
+    constexpr int RB = WTN * 2;     // bytes per staged row
+    constexpr int CPR = RB / 16;    // 16-byte chunks per row
+    constexpr int RPS = 256 / RB;   // rows per sweep of the 64 banks
+    static_assert(sizeof(S) == 2 && RB == 128, "2-byte outputs, 64 per wave row");
+    // an opaque copy of the lane id keeps the compiler from computing the
+    // staging addresses before the K loop and holding them through it
+    asm volatile("" : "+v"(lane));
+    const int frow = lane & 31, half = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+        const int t = i * 32 + frow;
+        const int sw = (t / RPS) % CPR;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+#pragma unroll
+            for (int f = 0; f < NB; ++f) {
+                const int col = f * 32 + g * 8 + half * 4;
+                uint2 w;
+                w.x = (uint32_t)fmt<DT>::store(acc[i][f][g * 4]) | ((uint32_t)fmt<DT>::store(acc[i][f][g * 4 + 1]) << 16);
+                w.y = (uint32_t)fmt<DT>::store(acc[i][f][g * 4 + 2]) |
+                      ((uint32_t)fmt<DT>::store(acc[i][f][g * 4 + 3]) << 16);
+                *(uint2*)(stage + t * RB + (((col >> 3) ^ sw) << 4) + half * 8) = w;
+            }
+        }
+    }
+    wait_lgkm0();
+    constexpr int RPI = 64 / CPR;  // staged rows per store instruction
+    const int c = lane % CPR, rr = lane / CPR;
+    const int col = n0 + wn * WTN + c * 8;
+#pragma unroll
+    for (int t0 = 0; t0 < WTM; t0 += RPI) {
+        const int t = t0 + rr;
+        const uint4 v = *(const uint4*)(stage + t * RB + ((c ^ ((t / RPS) % CPR)) << 4));
+        const int grow = r0 + wm * WTM + t;
+        if (grow < r1 && col < NOUT) *(uint4*)(C + (int64_t)grow * NOUT + col) = v;
+    }
+}
+
 #ifndef MOE_P_MINB
 #define MOE_P_MINB 1   // workgroups per CU the register budget must allow
 #endif
@@ -598,9 +651,12 @@ __global__ __launch_bounds__(WGM* WGN* kWave, 1) void grouped_gemm_pipe64_kernel
     static_assert(!GATEUP || NB % 2 == 0, "gate and up blocks pair up");
     static_assert(LPO + LPO / 4 <= 2 * (NM - NM / 2), "at most two DMA pieces per MFMA of a sub-step");
     static_assert(NA == 2 && NB_ == 3, "the vmcnt waits below are counted for 2 token and 3 weight slots");
+    static_assert(GATEUP || NW * WTM * WTN * 2 <= (NA + NB_) * SLOT, "the staged outputs fit the LDS");
     __shared__ __attribute__((aligned(1024))) unsigned char smem[(NA + NB_) * SLOT];
 
-    const int lane = lane_id(), wid = threadIdx.x / kWave;
+    // the wave id is wave-uniform: in a scalar register the DMA's LDS
+    // addresses are scalar arithmetic, with no per-piece readfirstlane
+    const int lane = lane_id(), wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int wm = wid / WGN, wn = wid % WGN;
     const int live_m = (int)*tile_count;
     const int nk = K / 64;
@@ -613,9 +669,14 @@ __global__ __launch_bounds__(WGM* WGN* kWave, 1) void grouped_gemm_pipe64_kernel
     int e, r0, r1, n0;
     // DMA piece j of this wave, per operand: rows (wid * LPO + j) * 8 + lane / 8
     // of the operand tile, the lane's 16-byte physical slot (lane & 7) holding
-    // logical chunk slot ^ (row & 7)
-    const char* srca[LPO];
-    const char* srcb[LPO];
+    // logical chunk slot ^ (row & 7).  Each piece is addressed as a
+    // wave-uniform base in scalar registers (the token buffer, or the weight
+    // matrix's rows of this tile), advanced a step at a time, plus a 32-bit
+    // per-lane offset; the host only picks this kernel when every offset fits
+    // 32 bits.  (64-bit per-lane addresses cost a vector add per piece and
+    // step: 2-3% of the product's time.)
+    const char* basb[LPO];
+    uint32_t voffa[LPO], voffb[LPO];
     auto setup = [&](int mi, int ni) {
         const int4 tl = tiles[mi];
         e = tl.x;
@@ -624,15 +685,14 @@ __global__ __launch_bounds__(WGM* WGN* kWave, 1) void grouped_gemm_pipe64_kernel
         n0 = ni * BN_OUT;
 #pragma unroll
         for (int j = 0; j < LPO; ++j) {
-            const int row = (wid * LPO + j) * 8 + (lane >> 3);
+            const int prow0 = (wid * LPO + j) * 8;  // first row of the piece (wave-uniform)
+            const int row = prow0 + (lane >> 3);
             const int lc = (lane & 7) ^ (row & 7);
-            srca[j] = (const char*)(A + src_row(a_rows, a_nrows, min(r0 + row, r1 - 1)) * K) + lc * 16;
-            const S* p;
-            if (GATEUP)
-                p = (row < BN_OUT ? B0 : B1) + ((int64_t)e * NOUT + min(n0 + (row % BN_OUT), NOUT - 1)) * K;
-            else
-                p = B0 + ((int64_t)e * NOUT + min(n0 + row, NOUT - 1)) * K;
-            srcb[j] = (const char*)p + lc * 16;
+            voffa[j] = (uint32_t)(src_row(a_rows, a_nrows, min(r0 + row, r1 - 1)) * K * (int64_t)sizeof(S)) + lc * 16;
+            const S* m = (GATEUP && prow0 >= BN_OUT) ? B1 : B0;
+            basb[j] = (const char*)(m + ((int64_t)e * NOUT + n0) * K);
+            const int brow = GATEUP ? row % BN_OUT : row;
+            voffb[j] = (uint32_t)((int64_t)(min(n0 + brow, NOUT - 1) - n0) * K * (int64_t)sizeof(S)) + lc * 16;
         }
     };
     setup(m_idx, n_idx);
@@ -665,10 +725,10 @@ __global__ __launch_bounds__(WGM* WGN* kWave, 1) void grouped_gemm_pipe64_kernel
     };
     // steps past the end re-load the last step into a slot nobody reads again
     auto dma_a = [&](int kt, int j) {
-        lds_dma16(srca[j] + min(kt, nk - 1) * ROWB, lds_a + (kt % NA) * SLOT + j * 1024);
+        lds_dma16_so((const char*)A + min(kt, nk - 1) * ROWB, voffa[j], lds_a + (kt % NA) * SLOT + j * 1024);
     };
     auto dma_b = [&](int kt, int j) {
-        lds_dma16(srcb[j] + min(kt, nk - 1) * ROWB, lds_b + (kt % NB_) * SLOT + j * 1024);
+        lds_dma16_so(basb[j] + min(kt, nk - 1) * ROWB, voffb[j], lds_b + (kt % NB_) * SLOT + j * 1024);
     };
     // Weight rows of step kt+2 go out a quarter step (BQ pieces) per sub-step,
     // from sub-step 3 of step kt-1 to sub-step 2 of step kt, into the slot the
@@ -755,19 +815,23 @@ __global__ __launch_bounds__(WGM* WGN* kWave, 1) void grouped_gemm_pipe64_kernel
         else
             main_loop(std::false_type{});
         // every DMA of this tile landed and every wave finished its reads:
-        // the next tile's first steps can be loaded while this one is stored
+        // the LDS is free to stage this tile's outputs (down product)
         wait_vm<0>();
         wait_lgkm0();
         barrier_lds();
-        const int c_r0 = r0, c_r1 = r1, c_n0 = n0;
+        if constexpr (GATEUP)
+            store_tile32<DT, GATEUP, MB, NB, WTM, WTN, WCN>(acc, C, gu, r0, r1, n0, wm, wn, NOUT, lane);
+        else
+            store_tile32_staged<DT, MB, NB, WTM, WTN>(acc, C, r0, r1, n0, wm, wn, NOUT, lane,
+                                                      smem + wid * (WTM * WTN * (int)sizeof(S)));
         t += gridDim.x;
-        const bool more = tile_of_block(t, nblocks, n_tiles, live_m, tiles, &m_idx, &n_idx);
-        if (more) {
-            setup(m_idx, n_idx);
-            prologue_dma();
-        }
-        store_tile32<DT, GATEUP, MB, NB, WTM, WTN, WCN>(acc, C, gu, c_r0, c_r1, c_n0, wm, wn, NOUT, lane);
-        if (!more) break;
+        if (!tile_of_block(t, nblocks, n_tiles, live_m, tiles, &m_idx, &n_idx)) break;
+        // every wave has read back its staged outputs before the next
+        // tile's loads overwrite the LDS
+        wait_lgkm0();
+        barrier_lds();
+        setup(m_idx, n_idx);
+        prologue_dma();
     }
 }
 
@@ -854,7 +918,11 @@ hipError_t launch_typed(const ExpertsArgs& a, hipStream_t s, ExpertsPart part) {
     hipError_t err = launch_build_tiles(a.offsets, a.E, a.N, BM, mt, tiles, count, s);
     if (err != hipSuccess) return err;
     const int H = (int)a.H, I = (int)a.I;
-    if (pipe && MOE_P_BK64 && a.H % 64 == 0 && a.I % 64 == 0) {
+    // the 64-K kernel addresses each operand row as a scalar base plus a
+    // 32-bit per-lane offset: the row operands must span less than 4 GiB
+    const int64_t x_rows = a.x_rows ? a.x_nrows : a.N, esz = (int64_t)sizeof(typename DT::storage);
+    const bool fits32 = x_rows * a.H * esz < (int64_t(1) << 32) - 256 && a.N * a.I * esz < (int64_t(1) << 32) - 256;
+    if (pipe && MOE_P_BK64 && a.H % 64 == 0 && a.I % 64 == 0 && fits32) {
         if constexpr (sizeof(typename DT::storage) == 2) {
             if (part != kDown) {
                 err = launch_pipe64<DT, true>(a.x, a.x_rows, a.x_nrows, a.gate, a.up, a.h, a.gu, tiles, count, mt, H, I, s);
