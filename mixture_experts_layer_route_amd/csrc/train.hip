@@ -388,7 +388,8 @@ __global__ __launch_bounds__(kTPWaves* kWave, 1) void train_pipe_kernel(TrainGem
     constexpr int NR = RA + 2 * NB;
     __shared__ __attribute__((aligned(1024))) unsigned char smem[(NA + NB_) * kTPSlot];
 
-    const int lane = lane_id(), wid = threadIdx.x / kWave;
+    // wave-uniform, so the DMA's LDS addresses are scalar arithmetic
+    const int lane = lane_id(), wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int wm = wid / WGN, wn = wid % WGN;
     const int64_t I2 = 2 * (int64_t)p.I;
     const S* A = (const S*)p.a;
@@ -750,7 +751,9 @@ __global__ __launch_bounds__(kT2Waves* kWave, 2) void train_pipe2_kernel(TrainGe
     constexpr int NR = RA + 2 * NB;
     __shared__ __attribute__((aligned(1024))) unsigned char smem[NA * kT2SlotA + NB_ * kT2SlotB];
 
-    const int lane = lane_id(), wid = threadIdx.x / kWave;  // wid = the wave's 64-column group
+    // wid = the wave's 64-column group; wave-uniform, so the DMA's LDS
+    // addresses are scalar arithmetic
+    const int lane = lane_id(), wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int64_t I2 = 2 * (int64_t)p.I;
     const S* A = (const S*)p.a;
     const int ncols = (MODE == kDH || MODE == kDWD) ? p.I : p.H;
@@ -869,14 +872,17 @@ __global__ __launch_bounds__(kT2Waves* kWave, 2) void train_pipe2_kernel(TrainGe
 
     f32x16_t acc[MB][NB];
     uint4 av[2][MB], bv[2][NB];
-    auto read_one = [&](int kt, int q, int set, int r) __attribute__((always_inline)) {
+    // MASK: step kt may be the last, partial one; its K values past ke are
+    // zeroed (the loads repeat the last valid K-row there)
+    auto read_one = [&](int kt, int q, int set, int r, auto mask) __attribute__((always_inline)) {
+        constexpr bool MASK = decltype(mask)::value;
         const int kv = ke - kb - 32 * kt;  // valid K values of step kt (32 or fewer on the last)
         if (r < RA) {
             const unsigned char* base = smem + (kt % NA) * kT2SlotA;
             if constexpr (A_KOUTER) {
                 const int i = r >> 1, h = r & 1;
                 uint2 v = lds_read_tr16(base + koa[h][i] + q * 16 * 256);
-                if (kv < 32) v = keep_first(v, kv - (16 * q + 8 * (g16 >> 1) + 4 * h));
+                if (MASK && kv < 32) v = keep_first(v, kv - (16 * q + 8 * (g16 >> 1) + 4 * h));
                 if (h == 0) {
                     av[set][i].x = v.x;
                     av[set][i].y = v.y;
@@ -887,14 +893,14 @@ __global__ __launch_bounds__(kT2Waves* kWave, 2) void train_pipe2_kernel(TrainGe
             } else {
                 // rows 32 r + frow keep (row >> 1) & 3 of frow
                 uint4 v = *(const uint4*)(base + kca[q] + r * 32 * 64);
-                if (kv < 32 && 16 * q + 8 * kg >= kv) v = make_uint4(0, 0, 0, 0);
+                if (MASK && kv < 32 && 16 * q + 8 * kg >= kv) v = make_uint4(0, 0, 0, 0);
                 av[set][r] = v;
             }
         } else {
             const int rr = r - RA, f = rr >> 1, h = rr & 1;
             const unsigned char* base = smem + NA * kT2SlotA + (kt % NB_) * kT2SlotB;
             uint2 v = lds_read_tr16(base + kob[h][f] + q * 16 * 512);
-            if (kv < 32) v = keep_first(v, kv - (16 * q + 8 * (g16 >> 1) + 4 * h));
+            if (MASK && kv < 32) v = keep_first(v, kv - (16 * q + 8 * (g16 >> 1) + 4 * h));
             if (h == 0) {
                 bv[set][f].x = v.x;
                 bv[set][f].y = v.y;
@@ -905,15 +911,18 @@ __global__ __launch_bounds__(kT2Waves* kWave, 2) void train_pipe2_kernel(TrainGe
         }
     };
     int rows_live = kT2BM;
-    auto substep = [&](auto nd, int set, int rkt, int rq, auto&& dma) __attribute__((always_inline)) {
+    // FULL: every row block of the tile is live (no per-MFMA row check)
+    auto substep = [&](auto nd, int set, int rkt, int rq, auto&& dma, auto mask, auto full)
+                       __attribute__((always_inline)) {
         constexpr int ND = decltype(nd)::value, H1 = NM / 2, H2 = NM - NM / 2;
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
             const int i = m / NB, f = m % NB;
-            if (!ROWS || i * 32 < rows_live) acc[i][f] = mma32<DT>::run(bv[set][f], av[set][i], acc[i][f]);
+            if (!ROWS || decltype(full)::value || i * 32 < rows_live)
+                acc[i][f] = mma32<DT>::run(bv[set][f], av[set][i], acc[i][f]);
             if (m < H1) {
 #pragma unroll
-                for (int r = (m * NR) / H1; r < ((m + 1) * NR) / H1; ++r) read_one(rkt, rq, set ^ 1, r);
+                for (int r = (m * NR) / H1; r < ((m + 1) * NR) / H1; ++r) read_one(rkt, rq, set ^ 1, r, mask);
             } else {
                 const int q = m - H1;
 #pragma unroll
@@ -947,11 +956,14 @@ __global__ __launch_bounds__(kT2Waves* kWave, 2) void train_pipe2_kernel(TrainGe
         for (int j = 0; j < LPB; ++j) dma_b(2, j);
         wait_vm<LPA + 2 * LPB>();
         barrier_lds();
-#pragma unroll
-        for (int r = 0; r < NR; ++r) read_one(0, 0, 0, r);
-        for (int kt = 0; kt < nk; ++kt) {
+        // Step kt reads step kt (second half) and step kt+1 (first half):
+        // only the last two steps can touch a partial last step, so the steps
+        // before them run without the K-tail masking.
+        const bool tail = (ke - kb) % 32 != 0;
+        const int nk_plain = tail ? max(nk - 2, 0) : nk;
+        auto step = [&](int kt, auto mask, auto full) __attribute__((always_inline)) {
             wait_lgkm0();
-            substep(no_dma{}, 0, kt, 1, none);
+            substep(no_dma{}, 0, kt, 1, none, mask, full);
             // step kt+1 landed (only the column operand of kt+2 was issued after
             // it); every wave is done reading step kt once past the barrier
             wait_vm<LPB>();
@@ -959,8 +971,21 @@ __global__ __launch_bounds__(kT2Waves* kWave, 2) void train_pipe2_kernel(TrainGe
             barrier_lds();
             substep(step_dma{}, 1, kt + 1, 0, [&](int d) __attribute__((always_inline)) {
                 if (d < LPA) dma_a(kt + 2, d); else dma_b(kt + 3, d - LPA);
-            });
+            }, mask, full);
+        };
+        if (tail && nk == 1) {
+#pragma unroll
+            for (int r = 0; r < NR; ++r) read_one(0, 0, 0, r, std::true_type{});
+        } else {
+#pragma unroll
+            for (int r = 0; r < NR; ++r) read_one(0, 0, 0, r, std::false_type{});
         }
+        int kt = 0;
+        if (!ROWS || rows_live >= kT2BM)
+            for (; kt < nk_plain; ++kt) step(kt, std::false_type{}, std::true_type{});
+        else
+            for (; kt < nk_plain; ++kt) step(kt, std::false_type{}, std::false_type{});
+        for (; kt < nk; ++kt) step(kt, std::true_type{}, std::false_type{});
         wait_vm<0>();
         wait_lgkm0();
     }
