@@ -366,6 +366,36 @@ def test_full_size_sampled(name, n_sample):
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
 
 
+def test_token_buffer_over_4gib_sampled():
+    """A token buffer of 4.4 GB: the 64-K kernel addresses token rows with
+    32-bit offsets, so the host must send this size to the 64-bit kernel.  A
+    wrapped offset would read a lower row of the same buffer (wrong values,
+    no access outside it), which the sampled tokens past 2^32 bytes catch."""
+    cfg = S.small_config("tokens_over_4gib_bf16", T=270000, H=8192, I=64, E=4, top_k=1, dtype="bf16", seed=61)
+    assert cfg.T * cfg.H * 2 > 1 << 32
+    log(f"{cfg.name}: generating {cfg.T * cfg.H * 2 / 1e9:.1f} GB of tokens on the GPU")
+    x, lg = S.make_tokens(cfg, device=DEV)
+    W = S.make_weights(cfg, device=DEV)
+    ex = moe.SwiGluExperts(*W)
+    opts = moe.RoutingOptions(cfg.top_k, cfg.renormalize)
+    out = ex.forward(x, lg, opts)
+    torch.cuda.synchronize()
+    # tokens whose rows start past 2^32 bytes, and a few below
+    first_high = (1 << 32) // (cfg.H * 2)
+    rng = np.random.default_rng(cfg.seed)
+    sample = np.sort(np.concatenate([rng.choice(np.arange(first_high, cfg.T), 12, replace=False),
+                                     rng.choice(first_high, 4, replace=False)]))
+    st = torch.from_numpy(sample).to(DEV)
+    log(f"{cfg.name}: oracle on {len(sample)} sampled tokens")
+    g = {e: host_bits(W[0][e]) for e in range(cfg.E)}
+    u = {e: host_bits(W[1][e]) for e in range(cfg.E)}
+    dn = {e: host_bits(W[2][e]) for e in range(cfg.E)}
+    res = oracle.forward(host_bits(x[st]), host_bits(lg[st]), g, u, dn, cfg.dtype, cfg.logits_dtype, cfg.top_k,
+                         cfg.renormalize, NTHREADS)
+    assert_close(values(out[st], cfg.dtype), oracle.widen(res["output"], cfg.dtype), cfg.dtype,
+                 f"forward {cfg.name} (sampled tokens)")
+
+
 @pytest.mark.parametrize("cfg", [
     S.small_config("halves_bf16", T=300, H=128, I=192, E=6, top_k=2, dtype="bf16", seed=51),
     S.small_config("halves_small_f16", T=20, H=64, I=96, E=16, top_k=4, dtype="f16", seed=52),
