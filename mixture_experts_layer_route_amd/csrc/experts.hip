@@ -388,58 +388,6 @@ __device__ __forceinline__ void store_tile32(const f32x16_t (&acc)[MB][NB], type
     }
 }
 
-// The down product's epilogue staged through LDS (2-byte outputs): each wave
-// writes its WTM-token x WTN-column block into its own LDS region (`stage`,
-// WTM * WTN * 2 bytes that no other wave touches before the next barrier),
-// row by row, then reads it back a 16-byte chunk per lane, so a store
-// instruction writes whole 128-byte row segments of 8 token rows instead of
-// 8 bytes of 32 rows (5% of the down product's time on the prefill
-// workload).  Staged row t holds its 16-byte chunk c at c ^ ((t / 2) % 8),
-// which spreads both the 8-byte writes and the 16-byte reads over all 64
-// banks.  (The gate/up epilogue gains nothing from staging: its cost is the
-// SiLU arithmetic, not the stores.)
-template <typename DT, int MB, int NB, int WTM, int WTN>
-__device__ __forceinline__ void store_tile32_staged(const f32x16_t (&acc)[MB][NB],
-                                                    typename DT::storage* __restrict__ C, int r0, int r1, int n0,
-                                                    int wm, int wn, int NOUT, int lane, unsigned char* stage) {
-    using S = typename DT::storage;
-    constexpr int RB = WTN * 2;     // bytes per staged row
-    constexpr int CPR = RB / 16;    // 16-byte chunks per row
-    constexpr int RPS = 256 / RB;   // rows per sweep of the 64 banks
-    static_assert(sizeof(S) == 2 && RB == 128, "2-byte outputs, 64 per wave row");
-    // an opaque copy of the lane id keeps the compiler from computing the
-    // staging addresses before the K loop and holding them through it
-    asm volatile("" : "+v"(lane));
-    const int frow = lane & 31, half = lane >> 5;
-#pragma unroll
-    for (int i = 0; i < MB; ++i) {
-        const int t = i * 32 + frow;
-        const int sw = (t / RPS) % CPR;
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-#pragma unroll
-            for (int f = 0; f < NB; ++f) {
-                const int col = f * 32 + g * 8 + half * 4;
-                uint2 w;
-                w.x = fmt<DT>::store2(acc[i][f][g * 4], acc[i][f][g * 4 + 1]);
-                w.y = fmt<DT>::store2(acc[i][f][g * 4 + 2], acc[i][f][g * 4 + 3]);
-                *(uint2*)(stage + t * RB + (((col >> 3) ^ sw) << 4) + half * 8) = w;
-            }
-        }
-    }
-    wait_lgkm0();
-    constexpr int RPI = 64 / CPR;  // staged rows per store instruction
-    const int c = lane % CPR, rr = lane / CPR;
-    const int col = n0 + wn * WTN + c * 8;
-#pragma unroll
-    for (int t0 = 0; t0 < WTM; t0 += RPI) {
-        const int t = t0 + rr;
-        const uint4 v = *(const uint4*)(stage + t * RB + ((c ^ ((t / RPS) % CPR)) << 4));
-        const int grow = r0 + wm * WTM + t;
-        if (grow < r1 && col < NOUT) *(uint4*)(C + (int64_t)grow * NOUT + col) = v;
-    }
-}
-
 #ifndef MOE_P_MINB
 #define MOE_P_MINB 1   // workgroups per CU the register budget must allow
 #endif

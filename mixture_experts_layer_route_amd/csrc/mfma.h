@@ -126,4 +126,55 @@ template <int N> __device__ __forceinline__ void wait_vm() { asm volatile("s_wai
 // knows the fragment registers are complete
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
+// An epilogue of 2-byte outputs staged through LDS: each wave
+// writes its WTM-token x WTN-column block into its own LDS region (`stage`,
+// WTM * WTN * 2 bytes that no other wave touches before the next barrier),
+// row by row, then reads it back a 16-byte chunk per lane, so a store
+// instruction writes whole 128-byte row segments of 8 rows instead of 8 bytes
+// of 32 rows.  Staged row t holds its 16-byte chunk c at c ^ ((t / 2) % 8),
+// which spreads both the 8-byte writes and the 16-byte reads over all 64
+// banks.  The lane layout is the 32x32 MFMA result's: row (lane % 32) of each
+// 32-row block, columns 8 g + 4 (lane / 32) + 0..3 of each 32-column block.
+template <typename DT, int MB, int NB, int WTM, int WTN>
+__device__ __forceinline__ void store_tile32_staged(const f32x16_t (&acc)[MB][NB],
+                                                    typename DT::storage* __restrict__ C, int r0, int r1, int n0,
+                                                    int wm, int wn, int NOUT, int lane, unsigned char* stage) {
+    using S = typename DT::storage;
+    constexpr int RB = WTN * 2;     // bytes per staged row
+    constexpr int CPR = RB / 16;    // 16-byte chunks per row
+    constexpr int RPS = 256 / RB;   // rows per sweep of the 64 banks
+    static_assert(sizeof(S) == 2 && RB == 128, "2-byte outputs, 64 per wave row");
+    // an opaque copy of the lane id keeps the compiler from computing the
+    // staging addresses before the K loop and holding them through it
+    asm volatile("" : "+v"(lane));
+    const int frow = lane & 31, half = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+        const int t = i * 32 + frow;
+        const int sw = (t / RPS) % CPR;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+#pragma unroll
+            for (int f = 0; f < NB; ++f) {
+                const int col = f * 32 + g * 8 + half * 4;
+                uint2 w;
+                w.x = fmt<DT>::store2(acc[i][f][g * 4], acc[i][f][g * 4 + 1]);
+                w.y = fmt<DT>::store2(acc[i][f][g * 4 + 2], acc[i][f][g * 4 + 3]);
+                *(uint2*)(stage + t * RB + (((col >> 3) ^ sw) << 4) + half * 8) = w;
+            }
+        }
+    }
+    wait_lgkm0();
+    constexpr int RPI = 64 / CPR;  // staged rows per store instruction
+    const int c = lane % CPR, rr = lane / CPR;
+    const int col = n0 + wn * WTN + c * 8;
+#pragma unroll
+    for (int t0 = 0; t0 < WTM; t0 += RPI) {
+        const int t = t0 + rr;
+        const uint4 v = *(const uint4*)(stage + t * RB + ((c ^ ((t / RPS) % CPR)) << 4));
+        const int grow = r0 + wm * WTM + t;
+        if (grow < r1 && col < NOUT) *(uint4*)(C + (int64_t)grow * NOUT + col) = v;
+    }
+}
+
 }  // namespace moe

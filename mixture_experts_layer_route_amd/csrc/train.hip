@@ -992,6 +992,59 @@ __global__ __launch_bounds__(kT2Waves* kWave, 2) void train_pipe2_kernel(TrainGe
 
     // ---- epilogue: lane holds output row (lane % 32) of each row block and
     // columns 8 g + 4 (lane / 32) + 0..3 (g = 0..3) of each column block
+    if constexpr (MODE == kDWGU || MODE == kDWD) {
+        // FP32 weight gradients, staged through LDS: each wave writes 64 of
+        // its 128 rows x 64 columns (256-byte rows, 16-byte chunk c of row t
+        // at c ^ (t % 16)) into its own 16 KB, then reads them back a chunk
+        // per lane, so each store instruction writes 4 whole 256-byte row
+        // segments instead of 16 bytes of 32 rows; two rounds.  The barrier
+        // makes sure every wave is done with the operand slots first.
+        barrier_lds();
+        unsigned char* stage = smem + wid * 16384;
+        const int c = lane & 15, rr = lane >> 4;
+        const int col = n0 + wid * WTN + 4 * c;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+#pragma unroll
+            for (int ii = 0; ii < 2; ++ii) {
+                const int t = 32 * ii + frow;
+#pragma unroll
+                for (int f = 0; f < NB; ++f)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const f32x16_t& a = acc[2 * half + ii][f];
+                        *(float4*)(stage + t * 256 + (((8 * f + 2 * g + kg) ^ (t & 15)) << 4)) =
+                            make_float4(a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]);
+                    }
+            }
+            wait_lgkm0();
+#pragma unroll
+            for (int t0 = 0; t0 < 64; t0 += 4) {
+                const int t = t0 + rr;
+                const float4 v = *(const float4*)(stage + t * 256 + ((c ^ (t & 15)) << 4));
+                const int m = m0 + 64 * half + t;
+                if (m < m1 && col < ncols) {
+                    float* out;
+                    if constexpr (MODE == kDWGU)
+                        out = m < p.I ? (float*)p.c0 + ((int64_t)e * p.I + m) * p.H + col
+                                      : (float*)p.c1 + ((int64_t)e * p.I + (m - p.I)) * p.H + col;
+                    else
+                        out = (float*)p.c0 + ((int64_t)e * p.H + m) * p.I + col;
+                    *(float4*)out = v;
+                }
+            }
+            wait_lgkm0();
+        }
+        return;
+    }
+    if constexpr (MODE == kDX) {
+        // dx rows staged through LDS (each wave's 128 x 64 block in its own
+        // 16 KB) so that stores write whole 128-byte row segments
+        barrier_lds();
+        store_tile32_staged<DT, MB, NB, kT2BM, WTN>(acc, (S*)p.c0, m0, m1, n0, 0, wid, p.H, lane,
+                                                    smem + wid * (kT2BM * WTN * (int)sizeof(S)));
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
         const int m = m0 + 32 * i + frow;
