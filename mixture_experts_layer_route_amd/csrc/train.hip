@@ -1037,6 +1037,81 @@ __global__ __launch_bounds__(kT2Waves* kWave, 2) void train_pipe2_kernel(TrainGe
         }
         return;
     }
+    if constexpr (MODE == kDH) {
+        // dg = dh u s (1 + g (1 - s)), du = dh g s from the saved FP32 g, u.
+        // Per 32-row block: the block's g and u (32 rows x 64 columns, 256
+        // bytes a row each) come into this wave's 16 KB of LDS by direct
+        // loads of whole rows (chunk c of row t at c ^ (t % 16)); each lane
+        // reads its values back in the MFMA layout, and dg, du go out through
+        // the same LDS (128-byte rows, chunk c at c ^ ((t / 2) % 8)) so the
+        // stores write whole row segments.
+        barrier_lds();
+        unsigned char* stage = smem + wid * 16384;
+        const uint32_t lds_stage = lds_offset(stage);
+        const int c16 = lane & 15, r16 = lane >> 4;  // DMA: 4 rows x 16 chunks per instruction
+        const int c8 = lane & 7, r8 = lane >> 3;     // stores: 8 rows x 8 chunks per instruction
+#pragma unroll
+        for (int i = 0; i < MB; ++i) {
+            // g to [0, 8 KB), u to [8 KB, 16 KB)
+#pragma unroll
+            for (int d = 0; d < 8; ++d) {
+                const int t = 4 * d + r16;
+                const int m = min(m0 + 32 * i + t, m1 - 1);
+                const int col = n0 + wid * WTN + 4 * (c16 ^ (t & 15));
+                const uint32_t off = (uint32_t)(m * I2 + (col < ncols ? col : 0)) * 4u;
+                lds_dma16_so(p.gu, off, lds_stage + d * 1024);
+                lds_dma16_so(p.gu, off + (uint32_t)p.I * 4u, lds_stage + 8192 + d * 1024);
+            }
+            wait_vm<0>();
+            float dg[NB][16], du[NB][16];
+#pragma unroll
+            for (int f = 0; f < NB; ++f)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int ch = 8 * f + 2 * g + kg;
+                    const int a = frow * 256 + ((ch ^ (frow & 15)) << 4);
+                    const float4 g4 = *(const float4*)(stage + a);
+                    const float4 u4 = *(const float4*)(stage + 8192 + a);
+                    const float gv[4] = {g4.x, g4.y, g4.z, g4.w}, uv[4] = {u4.x, u4.y, u4.z, u4.w};
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float dh = acc[i][f][4 * g + r];
+                        const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-gv[r]));
+                        du[f][4 * g + r] = dh * (gv[r] * sg);
+                        dg[f][4 * g + r] = dh * uv[r] * (sg * (1.0f + gv[r] * (1.0f - sg)));
+                    }
+                }
+            wait_lgkm0();  // the g, u reads are done before the region is rewritten
+            // dg to [0, 4 KB), du to [4 KB, 8 KB): row frow, 8-byte half kg of chunk 4 f + g
+#pragma unroll
+            for (int f = 0; f < NB; ++f)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int a = frow * 128 + (((4 * f + g) ^ ((frow >> 1) & 7)) << 4) + kg * 8;
+                    *(uint2*)(stage + a) = make_uint2(fmt<DT>::store2(dg[f][4 * g], dg[f][4 * g + 1]),
+                                                      fmt<DT>::store2(dg[f][4 * g + 2], dg[f][4 * g + 3]));
+                    *(uint2*)(stage + 4096 + a) = make_uint2(fmt<DT>::store2(du[f][4 * g], du[f][4 * g + 1]),
+                                                             fmt<DT>::store2(du[f][4 * g + 2], du[f][4 * g + 3]));
+                }
+            wait_lgkm0();
+            const int col = n0 + wid * WTN + 8 * c8;
+#pragma unroll
+            for (int t0 = 0; t0 < 32; t0 += 8) {
+                const int t = t0 + r8;
+                const int a = t * 128 + ((c8 ^ ((t >> 1) & 7)) << 4);
+                const uint4 vg = *(const uint4*)(stage + a);
+                const uint4 vu = *(const uint4*)(stage + 4096 + a);
+                const int m = m0 + 32 * i + t;
+                if (m < m1 && col < ncols) {
+                    S* out = (S*)p.c0 + (int64_t)m * I2 + col;
+                    *(uint4*)out = vg;
+                    *(uint4*)(out + p.I) = vu;
+                }
+            }
+            wait_lgkm0();  // read back before the next block's loads land
+        }
+        return;
+    }
     if constexpr (MODE == kDX) {
         // dx rows staged through LDS (each wave's 128 x 64 block in its own
         // 16 KB) so that stores write whole 128-byte row segments
