@@ -388,6 +388,53 @@ __device__ __forceinline__ void store_tile32(const f32x16_t (&acc)[MB][NB], type
     }
 }
 
+// The training forward's FP32 pre-activations of the gate/up product (g at
+// columns [0, I) of a row of gu, u at [I, 2I)), staged through LDS: per
+// round of 64 token rows each wave writes its 64 x 32 g and u values into its
+// own 16 KB (128-byte rows, 16-byte chunk c of row t at c ^ ((t / 2) % 8)),
+// then reads them back a chunk per lane, so a store instruction writes 8
+// whole 128-byte row segments instead of 16 bytes of 32 rows.
+template <int MB, int NB, int WTM, int WCN>
+__device__ __forceinline__ void save_preact_staged(const f32x16_t (&acc)[MB][NB], float* __restrict__ gu, int r0,
+                                                   int r1, int n0, int wm, int wn, int I, int lane,
+                                                   unsigned char* stage) {
+    static_assert(WCN == 32 && NB == 2 && MB % 2 == 0, "one gate and one up block of 32 columns per wave");
+    asm volatile("" : "+v"(lane));  // keeps the addresses out of the K loop
+    const int frow = lane & 31, kg = lane >> 5;
+    const int c = lane & 7, rr = lane >> 3;
+    const int col = n0 + wn * WCN + 4 * c;
+#pragma unroll
+    for (int h = 0; h < MB / 2; ++h) {
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii) {
+            const int t = 32 * ii + frow, sw = (t >> 1) & 7;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const f32x16_t& ga = acc[2 * h + ii][0];
+                const f32x16_t& ua = acc[2 * h + ii][1];
+                const int a = t * 128 + (((2 * g + kg) ^ sw) << 4);
+                *(float4*)(stage + a) = make_float4(ga[4 * g], ga[4 * g + 1], ga[4 * g + 2], ga[4 * g + 3]);
+                *(float4*)(stage + 8192 + a) = make_float4(ua[4 * g], ua[4 * g + 1], ua[4 * g + 2], ua[4 * g + 3]);
+            }
+        }
+        wait_lgkm0();
+#pragma unroll
+        for (int t0 = 0; t0 < 64; t0 += 8) {
+            const int t = t0 + rr;
+            const int a = t * 128 + ((c ^ ((t >> 1) & 7)) << 4);
+            const float4 g4 = *(const float4*)(stage + a);
+            const float4 u4 = *(const float4*)(stage + 8192 + a);
+            const int grow = r0 + wm * WTM + 64 * h + t;
+            if (grow < r1 && col < I) {
+                float* p = gu + (int64_t)grow * 2 * I + col;
+                *(float4*)p = g4;
+                *(float4*)(p + I) = u4;
+            }
+        }
+        wait_lgkm0();  // read back before the next round rewrites the region
+    }
+}
+
 #ifndef MOE_P_MINB
 #define MOE_P_MINB 1   // workgroups per CU the register budget must allow
 #endif
@@ -599,6 +646,7 @@ __global__ __launch_bounds__(WGM* WGN* kWave, 1) void grouped_gemm_pipe64_kernel
     static_assert(LPO + LPO / 4 <= 2 * (NM - NM / 2), "at most two DMA pieces per MFMA of a sub-step");
     static_assert(NA == 2 && NB_ == 3, "the vmcnt waits below are counted for 2 token and 3 weight slots");
     static_assert(GATEUP || NW * WTM * WTN * 2 <= (NA + NB_) * SLOT, "the staged outputs fit the LDS");
+    static_assert(!GATEUP || NW * 16384 <= (NA + NB_) * SLOT, "the staged pre-activations fit the LDS");
     __shared__ __attribute__((aligned(1024))) unsigned char smem[(NA + NB_) * SLOT];
 
     // the wave id is wave-uniform: in a scalar register the DMA's LDS
@@ -766,9 +814,11 @@ __global__ __launch_bounds__(WGM* WGN* kWave, 1) void grouped_gemm_pipe64_kernel
         wait_vm<0>();
         wait_lgkm0();
         barrier_lds();
-        if constexpr (GATEUP)
-            store_tile32<DT, GATEUP, MB, NB, WTM, WTN, WCN>(acc, C, gu, r0, r1, n0, wm, wn, NOUT, lane);
-        else
+        if constexpr (GATEUP) {
+            store_tile32<DT, GATEUP, MB, NB, WTM, WTN, WCN>(acc, C, nullptr, r0, r1, n0, wm, wn, NOUT, lane);
+            if (gu)
+                save_preact_staged<MB, NB, WTM, WCN>(acc, gu, r0, r1, n0, wm, wn, NOUT, lane, smem + wid * 16384);
+        } else
             store_tile32_staged<DT, MB, NB, WTM, WTN>(acc, C, r0, r1, n0, wm, wn, NOUT, lane,
                                                       smem + wid * (WTM * WTN * (int)sizeof(S)));
         t += gridDim.x;
