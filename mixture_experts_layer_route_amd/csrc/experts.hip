@@ -320,9 +320,6 @@ __global__ __launch_bounds__(WGM* WGN* kWave) void grouped_gemm_kernel(
 #ifndef MOE_P_BK64
 #define MOE_P_BK64 1
 #endif
-#ifndef MOE_P64_PERSIST
-#define MOE_P64_PERSIST 0
-#endif
 #ifndef MOE_P64_WM
 #define MOE_P64_WM 2   // waves along token rows of the 64-K kernel's tile
 #define MOE_P64_WN 4   // waves along weight rows
@@ -656,11 +653,8 @@ __global__ __launch_bounds__(WGM* WGN* kWave, 1) void grouped_gemm_pipe64_kernel
     const int live_m = (int)*tile_count;
     const int nk = K / 64;
 
-    // The workgroup walks tiles t = blockIdx.x, + gridDim.x, ...; gridDim.x is
-    // a multiple of 8, so every tile of a workgroup stays on its XCD and the
-    // XCD still walks a contiguous run of logical tiles.
-    int t = blockIdx.x, m_idx, n_idx;
-    if (!tile_of_block(t, nblocks, n_tiles, live_m, tiles, &m_idx, &n_idx)) return;
+    int m_idx, n_idx;
+    if (!tile_of_block(blockIdx.x, nblocks, n_tiles, live_m, tiles, &m_idx, &n_idx)) return;
     int e, r0, r1, n0;
     // DMA piece j of this wave, per operand: rows (wid * LPO + j) * 8 + lane / 8
     // of the operand tile, the lane's 16-byte physical slot (lane & 7) holding
@@ -793,42 +787,32 @@ __global__ __launch_bounds__(WGM* WGN* kWave, 1) void grouped_gemm_pipe64_kernel
     };
 
     prologue_dma();
-    while (true) {
-        rows_live = __builtin_amdgcn_readfirstlane(r1 - r0) - __builtin_amdgcn_readfirstlane(wm) * WTM;
+    rows_live = __builtin_amdgcn_readfirstlane(r1 - r0) - __builtin_amdgcn_readfirstlane(wm) * WTM;
 #pragma unroll
-        for (int i = 0; i < MB; ++i)
+    for (int i = 0; i < MB; ++i)
 #pragma unroll
-            for (int f = 0; f < NB; ++f)
+        for (int f = 0; f < NB; ++f)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) acc[i][f][r] = 0.0f;
-        wait_vm<kPrologueAfter0>();
-        barrier_lds();
+            for (int r = 0; r < 16; ++r) acc[i][f][r] = 0.0f;
+    wait_vm<kPrologueAfter0>();
+    barrier_lds();
 #pragma unroll
-        for (int r = 0; r < NR; ++r) read_one(0, 0, 0, r);
-        if (rows_live >= MB * 32)
-            main_loop(std::true_type{});
-        else
-            main_loop(std::false_type{});
-        // every DMA of this tile landed and every wave finished its reads:
-        // the LDS is free to stage this tile's outputs (down product)
-        wait_vm<0>();
-        wait_lgkm0();
-        barrier_lds();
-        if constexpr (GATEUP) {
-            store_tile32<DT, GATEUP, MB, NB, WTM, WTN, WCN>(acc, C, nullptr, r0, r1, n0, wm, wn, NOUT, lane);
-            if (gu)
-                save_preact_staged<MB, NB, WTM, WCN>(acc, gu, r0, r1, n0, wm, wn, NOUT, lane, smem + wid * 16384);
-        } else
-            store_tile32_staged<DT, MB, NB, WTM, WTN>(acc, C, r0, r1, n0, wm, wn, NOUT, lane,
-                                                      smem + wid * (WTM * WTN * (int)sizeof(S)));
-        t += gridDim.x;
-        if (!tile_of_block(t, nblocks, n_tiles, live_m, tiles, &m_idx, &n_idx)) break;
-        // every wave has read back its staged outputs before the next
-        // tile's loads overwrite the LDS
-        wait_lgkm0();
-        barrier_lds();
-        setup(m_idx, n_idx);
-        prologue_dma();
+    for (int r = 0; r < NR; ++r) read_one(0, 0, 0, r);
+    if (rows_live >= MB * 32)
+        main_loop(std::true_type{});
+    else
+        main_loop(std::false_type{});
+    // every DMA of this tile landed and every wave finished its reads: the
+    // LDS is free to stage the outputs
+    wait_vm<0>();
+    wait_lgkm0();
+    barrier_lds();
+    if constexpr (GATEUP) {
+        store_tile32<DT, GATEUP, MB, NB, WTM, WTN, WCN>(acc, C, nullptr, r0, r1, n0, wm, wn, NOUT, lane);
+        if (gu) save_preact_staged<MB, NB, WTM, WCN>(acc, gu, r0, r1, n0, wm, wn, NOUT, lane, smem + wid * 16384);
+    } else {
+        store_tile32_staged<DT, MB, NB, WTM, WTN>(acc, C, r0, r1, n0, wm, wn, NOUT, lane,
+                                                  smem + wid * (WTM * WTN * (int)sizeof(S)));
     }
 }
 
@@ -874,10 +858,7 @@ hipError_t launch_pipe64(const void* A, const uint32_t* a_rows, int64_t a_nrows,
     const int64_t nb = mt * n_tiles;
     if (nb == 0) return hipSuccess;
     if (nb > 0x7fffffff) return hipErrorInvalidValue;
-    // persistent: one workgroup per CU (the kernel takes the whole LDS), a
-    // multiple of 8 so each workgroup's tiles stay on one XCD
-    const int64_t grid = MOE_P64_PERSIST ? std::min<int64_t>(nb, (int64_t)persistent_slots(s)) : nb;
-    grouped_gemm_pipe64_kernel<DT, GATEUP, MOE_P64_WM, MOE_P64_WN><<<(unsigned)grid, MOE_P64_WM * MOE_P64_WN * kWave, 0, s>>>(
+    grouped_gemm_pipe64_kernel<DT, GATEUP, MOE_P64_WM, MOE_P64_WN><<<(unsigned)nb, MOE_P64_WM * MOE_P64_WN * kWave, 0, s>>>(
         (const S*)A, (const S*)B0, (const S*)B1, (S*)C, gu, a_rows, (int)a_nrows, tiles, count, K, NOUT, n_tiles,
         (int)nb);
     return hipGetLastError();
