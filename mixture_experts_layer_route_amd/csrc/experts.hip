@@ -936,21 +936,6 @@ hipError_t launch_typed(const ExpertsArgs& a, hipStream_t s, ExpertsPart part) {
 
 }  // namespace
 
-// Workgroups that fit on the stream's device at one per CU, rounded down to a
-// multiple of 8 XCDs (256 on MI355X); cached per device.
-int persistent_slots(hipStream_t s) {
-    static int cached[64] = {0};
-    int dev = 0;
-    if (hipStreamGetDevice(s, &dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-    if (!cached[dev]) {
-        int cus = 0;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8)
-            cus = 256;
-        cached[dev] = cus / 8 * 8;
-    }
-    return cached[dev];
-}
-
 int64_t max_mtiles(int64_t N, int64_t E, int BM) {
     if (N <= 0) return 0;
     const int64_t bound = (N + E * (BM - 1)) / BM;

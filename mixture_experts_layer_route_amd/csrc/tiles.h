@@ -13,9 +13,6 @@ constexpr int kGroupM = MOE_GROUP_M;
 static_assert(kGroupM >= 1 && kGroupM < 64, "group size is packed in 6 bits");
 constexpr int64_t kMaxTiles = int64_t(1) << 26;  // tile index packed in 26 bits
 
-// Workgroups that fit on the stream's device at one per CU, rounded down to
-// a multiple of 8 XCDs (256 on MI355X).
-int persistent_slots(hipStream_t s);
 // Upper bound of the M-tiles of BM rows that N rows over E experts produce.
 int64_t max_mtiles(int64_t N, int64_t E, int BM);
 // Writes the (expert, row_begin, row_end, group) M-tile list of BM-row tiles

@@ -27,17 +27,13 @@
 // their first index, and every operand of the weight gradients, whose K runs
 // over dispatched rows -- are K-outer: contiguous along the output index.
 //
-// Three kernels:
-//   train_pipe2_kernel (bf16/f16, enough rows per expert; the default): 128 x
-//     256 tiles on 4 waves with 32-K steps in a 64 KB ring, so two
-//     workgroups share a CU and one computes while the other stores;
-//   train_pipe_kernel (the same with one workgroup per CU): 256 x 256 tiles on
-//     8 waves of 32x32x16 MFMAs, 64-K steps loaded straight into LDS by
-//     global_load_lds in the forward's ring (two row-operand and three
-//     column-operand slots); K-outer operands land in their natural layout
-//     and are read with the gfx950 LDS transpose read ds_read_b64_tr_b16.
-//     One workgroup per CU walks several tiles and loads the next tile
-//     while it stores the last.
+// Two kernels:
+//   train_pipe2_kernel (bf16/f16, enough rows per expert): 128 x 256 tiles
+//     on 4 waves of 32x32x16 MFMAs, 32-K steps loaded straight into LDS by
+//     global_load_lds in a 64 KB ring, so two workgroups share a CU and one
+//     computes while the other stores; K-outer operands land in their
+//     natural layout and are read with the gfx950 LDS transpose read
+//     ds_read_b64_tr_b16;
 //   train_gemm_kernel (f32, and few rows per expert): 128 x 128 tiles on 4
 //     waves of 16x16 MFMAs; K-outer operands are staged through registers,
 //     each thread transposing 4 K-rows x 16 bytes before writing K-runs to
@@ -332,35 +328,13 @@ hipError_t launch_train_gemm(TrainGemm p, int64_t blocks, hipStream_t s) {
 }
 
 
-// ------------------------------------------------------------------ pipelined training GEMM (16-bit)
-// 256 x 256 output tiles on 8 waves of 128 x 64 (32x32x16 MFMAs), 64-K steps
-// filled by direct global->LDS loads (two row-operand slots and three
-// column-operand slots of 32 KB, as in the forward's 64-K kernel).
-//
-// K-contiguous operand (the DH / DX row operand): 256 rows x 128 bytes per
-// slot, 16-byte chunk c of row r at chunk c ^ (r & 7), read with 16-byte
-// fragment reads.
-// K-outer operand: 64 K-rows x 512 bytes (256 values) per slot, 16-byte chunk
-// c of K-row r at chunk c ^ ((r & 7) << 2), read with ds_read_b64_tr_b16:
-// within each 16-lane group, lane s gives the address of 4 values (K-row
-// k0 + s / 4, columns n0 + 4 (s % 4) .. + 3) and receives column n0 + s's
-// values of K-rows k0 .. k0 + 3.  Two such reads give a lane the 8
-// consecutive K values of one operand row that a 32x32x16 MFMA takes; the
-// swizzle spreads the 16 K-rows of a read over all banks.
-// K tails (an expert's last rows, or K not a multiple of 64): loads are
-// clamped to the last valid K-row or chunk, and the fragments of the last
-// step zero every value past the end on both operands.
-#ifndef MOE_TRAIN_PIPE
-#define MOE_TRAIN_PIPE 2    // 16-bit types: 1 = one 256x256 workgroup per CU, 2 = two 128x256 per CU
-#endif
-#ifndef MOE_TP_PERSIST
-#define MOE_TP_PERSIST 1    // one workgroup per CU walking several tiles
-#endif
-constexpr int kTPBM = 256, kTPBN = 256;
-constexpr int kTPSlot = 32 * 1024;
-constexpr int kTPSlotsA = 2, kTPSlotsB = 3;
-constexpr int kTPWaves = 8, kTPLPO = kTPSlot / 1024 / kTPWaves;  // 4 DMA pieces per wave and operand
-
+// ------------------------------------------------------------------ LDS transpose read
+// A K-outer operand lands in LDS in its natural layout (K-rows of
+// consecutive output indices) and is read with ds_read_b64_tr_b16: within
+// each 16-lane group, lane s gives the address of 4 values (K-row k0 + s / 4,
+// columns n0 + 4 (s % 4) .. + 3) and receives column n0 + s's values of
+// K-rows k0 .. k0 + 3.  Two such reads give a lane the 8 consecutive K values
+// of one operand row that a 32x32x16 MFMA takes.
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint2 lds_read_tr16(const unsigned char* p) {
     const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -377,355 +351,8 @@ __device__ __forceinline__ uint2 keep_first(uint2 v, int n) {
     return v;
 }
 
-template <typename DT, int MODE>
-__global__ __launch_bounds__(kTPWaves* kWave, 1) void train_pipe_kernel(TrainGemm p) {
-    using S = typename DT::storage;
-    constexpr bool A_KOUTER = MODE == kDWGU || MODE == kDWD;
-    constexpr int WGN = 4, WTM = 128, WTN = 64;
-    constexpr int MB = WTM / 32, NB = WTN / 32, NM = MB * NB;
-    constexpr int LPO = kTPLPO, NA = kTPSlotsA, NB_ = kTPSlotsB;
-    constexpr int RA = A_KOUTER ? 2 * MB : MB;  // fragment reads per sub-step, row operand
-    constexpr int NR = RA + 2 * NB;
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[(NA + NB_) * kTPSlot];
-
-    // wave-uniform, so the DMA's LDS addresses are scalar arithmetic
-    const int lane = lane_id(), wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int wm = wid / WGN, wn = wid % WGN;
-    const int64_t I2 = 2 * (int64_t)p.I;
-    const S* A = (const S*)p.a;
-    constexpr bool ROWS = MODE == kDH || MODE == kDX;
-    const int ncols = (MODE == kDH || MODE == kDWD) ? p.I : p.H;
-    const int mrows = MODE == kDWGU ? 2 * p.I : p.H;  // weight-gradient rows
-    const int lda = MODE == kDH ? p.H : (MODE == kDWD ? p.H : 2 * p.I);
-    const int live_m = ROWS ? (int)*p.tile_count : 0;
-
-    // ---- the current tile: expert e, output rows [m0, m1), columns
-    // [n0, n0 + 256), K range [kb, ke) in nk steps of 64.  The workgroup walks
-    // tiles blockIdx.x, + gridDim.x, ...; gridDim.x is a multiple of 8, so
-    // all of a workgroup's tiles are on its XCD, which walks a contiguous run.
-    int e = 0, m0 = 0, m1 = 0, n0 = 0, kb = 0, ke = 0, nk = 0;
-    auto tile = [&](int t) __attribute__((always_inline)) {
-        if constexpr (ROWS) {
-            int mi, ni;
-            if (!tile_of_block(t, p.nblocks, p.n_tiles, live_m, p.tiles, &mi, &ni)) return false;
-            const int4 tl = p.tiles[mi];
-            e = tl.x;
-            m0 = tl.y;
-            m1 = tl.z;
-            n0 = ni * kTPBN;
-            kb = 0;
-            ke = lda;
-        } else {
-            if (t >= p.nblocks) return false;
-            const int pid = xcd_contiguous(t, p.nblocks);
-            const int per = p.m_tiles * p.n_tiles;
-            e = pid / per;
-            const int rem = pid - e * per;
-            m0 = (rem % p.m_tiles) * kTPBM;
-            m1 = min(m0 + kTPBM, mrows);
-            n0 = (rem / p.m_tiles) * kTPBN;
-            kb = (int)min(p.offsets[e], (uint32_t)p.N);
-            ke = max((int)min(p.offsets[e + 1], (uint32_t)p.N), kb);
-        }
-        e = __builtin_amdgcn_readfirstlane(e);
-        m0 = __builtin_amdgcn_readfirstlane(m0);
-        m1 = __builtin_amdgcn_readfirstlane(m1);
-        n0 = __builtin_amdgcn_readfirstlane(n0);
-        kb = __builtin_amdgcn_readfirstlane(kb);
-        ke = __builtin_amdgcn_readfirstlane(ke);
-        nk = (ke - kb + 63) / 64;
-        return true;
-    };
-
-    // ---- DMA sources.  K-outer piece j: K-row r = 2 (wid LPO + j) + lane / 32
-    // of the slot, physical chunk lane % 32 holding logical chunk
-    // (lane % 32) ^ ((r & 7) << 2), i.e. columns c0 + 8 * that.
-    const uint32_t lds_a = lds_offset(smem) + wid * LPO * 1024;
-    const uint32_t lds_b = lds_a + NA * kTPSlot;
-    // Addresses are formed at issue time from the tile's (uniform) extents,
-    // so no per-lane state of the next tile is live during an epilogue.
-    // K-outer piece j: slot K-row r, logical chunk of the lane's physical chunk
-    auto ko_row = [&](int j) __attribute__((always_inline)) { return 2 * (wid * LPO + j) + (lane >> 5); };
-    auto ko_col = [&](int j, int c0, int climit) __attribute__((always_inline)) {
-        const int c = c0 + 8 * ((lane & 31) ^ ((ko_row(j) & 7) << 2));
-        return c < climit ? c : 0;
-    };
-    // Loads take a wave-uniform base (the tile's first row of the operand, or
-    // the expert's weights) plus a 32-bit byte offset; the launcher keeps
-    // every offset below 2^31.  Steps past the end re-load the last step into
-    // a slot nobody reads again.
-    auto dma_a = [&](int kt, int j) __attribute__((always_inline)) {
-        const int s = min(kt, nk - 1);
-        uint32_t off;
-        const S* base;
-        if constexpr (A_KOUTER) {
-            base = A + (int64_t)kb * lda;
-            const int k = min(64 * s + ko_row(j), ke - kb - 1);
-            off = (uint32_t)(k * lda + ko_col(j, m0, m1)) * (uint32_t)sizeof(S);
-        } else {
-            // K-contiguous row operand (DH, DX): as the forward's 64-K kernel
-            base = A + (int64_t)m0 * lda;
-            const int row = (wid * LPO + j) * 8 + (lane >> 3);
-            const int coff = ((lane & 7) ^ (row & 7)) * 16;
-            off = (uint32_t)(min(row, m1 - m0 - 1) * lda) * (uint32_t)sizeof(S) +
-                  (uint32_t)min(128 * s + coff, ke * (int)sizeof(S) - 16);
-        }
-        lds_dma16_so(base, off, lds_a + (kt % NA) * kTPSlot + j * 1024);
-    };
-    auto dma_b = [&](int kt, int j) __attribute__((always_inline)) {
-        const int s = min(kt, nk - 1);
-        const int k = min(64 * s + ko_row(j), ke - kb - 1);  // K-row past kb
-        const uint32_t lds = lds_b + (kt % NB_) * kTPSlot + j * 1024;
-        const int col = ko_col(j, n0, ncols);
-        if constexpr (MODE == kDX) {
-            // gate rows, then up rows.  An instruction loads K-rows 2 q and
-            // 2 q + 1 of the slot, and I is even, so both lie in one tensor.
-            const int kpair = __builtin_amdgcn_readfirstlane(min(64 * s + 2 * (wid * LPO + j), ke - 1));
-            const bool in_up = kpair >= p.I;
-            const S* base = (const S*)(in_up ? p.b1 : p.b0) + (int64_t)e * p.I * p.H;
-            lds_dma16_so(base, (uint32_t)((k - (in_up ? p.I : 0)) * p.H + col) * (uint32_t)sizeof(S), lds);
-        } else {
-            const S* base;
-            int ld;
-            if constexpr (MODE == kDH) {
-                base = (const S*)p.b0 + (int64_t)e * p.H * p.I;
-                ld = p.I;
-            } else if constexpr (MODE == kDWGU) {
-                base = (const S*)p.b0 + (int64_t)kb * p.H;
-                ld = p.H;
-            } else {
-                base = (const S*)p.b0 + (int64_t)kb * p.I;
-                ld = p.I;
-            }
-            lds_dma16_so(base, (uint32_t)(k * ld + col) * (uint32_t)sizeof(S), lds);
-        }
-    };
-
-    // ---- fragment addresses (byte offsets inside a slot)
-    const int frow = lane & 31, kg = lane >> 5;
-    const int g16 = lane >> 4, s16 = lane & 15;
-    // K-outer reads: read h of sub-step q for the 32-wide operand block blk
-    // (columns 32 blk ..) takes K-row 16 q + 8 (g16 >> 1) + 4 h + s16 / 4 and
-    // logical chunk 4 blk + 2 (g16 & 1) + (s16 & 3) / 2, half s16 & 1; the
-    // swizzle XORs the chunk with 4 kk, kk = 4 h + s16 / 4 = K-row & 7, so the
-    // physical chunk is 4 (blk ^ kk) + 2 (g16 & 1) + (s16 & 3) / 2.  Per lane
-    // one byte offset per (h, block) at q = 0; q adds 16 K-rows (8 KB).
-    int kob[2][NB], koa[2][MB];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int kk = 4 * h + (s16 >> 2);
-        const int rowoff = (8 * (g16 >> 1) + kk) * 512 + (2 * (g16 & 1) + ((s16 & 3) >> 1)) * 16 + (s16 & 1) * 8;
-#pragma unroll
-        for (int f = 0; f < NB; ++f) kob[h][f] = rowoff + 64 * ((2 * wn + f) ^ kk);
-#pragma unroll
-        for (int i = 0; i < MB; ++i) koa[h][i] = rowoff + 64 * ((4 * wm + i) ^ kk);
-    }
-    const int fa0 = (wm * WTM + frow) * 128;
-    int csw[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) csw[q] = ((2 * q + kg) ^ (frow & 7)) * 16;
-
-    f32x16_t acc[MB][NB];
-    uint4 av[2][MB], bv[2][NB];
-    // fragment read r of sub-step q of step kt into register set `set`; on
-    // the last step, values past the end of K are zeroed
-    auto read_one = [&](int kt, int q, int set, int r) __attribute__((always_inline)) {
-        const int kv = ke - kb - 64 * kt;
-        if (r < RA) {
-            const unsigned char* base = smem + (kt % NA) * kTPSlot;
-            if constexpr (A_KOUTER) {
-                const int i = r >> 1, h = r & 1;
-                uint2 v = lds_read_tr16(base + koa[h][i] + q * 8192);
-                if (kv < 64) v = keep_first(v, kv - (16 * q + 8 * (g16 >> 1) + 4 * h));
-                if (h == 0) {
-                    av[set][i].x = v.x;
-                    av[set][i].y = v.y;
-                } else {
-                    av[set][i].z = v.x;
-                    av[set][i].w = v.y;
-                }
-            } else {
-                uint4 v = *(const uint4*)(base + csw[q] + fa0 + r * 32 * 128);
-                if (kv < 64 && 16 * q + 8 * kg >= kv) v = make_uint4(0, 0, 0, 0);
-                av[set][r] = v;
-            }
-        } else {
-            const int rr = r - RA, f = rr >> 1, h = rr & 1;
-            const unsigned char* base = smem + NA * kTPSlot + (kt % NB_) * kTPSlot;
-            uint2 v = lds_read_tr16(base + kob[h][f] + q * 8192);
-            if (kv < 64) v = keep_first(v, kv - (16 * q + 8 * (g16 >> 1) + 4 * h));
-            if (h == 0) {
-                bv[set][f].x = v.x;
-                bv[set][f].y = v.y;
-            } else {
-                bv[set][f].z = v.x;
-                bv[set][f].w = v.y;
-            }
-        }
-    };
-    auto prologue_dma = [&]() __attribute__((always_inline)) {
-#pragma unroll
-        for (int j = 0; j < LPO; ++j) dma_a(0, j);
-#pragma unroll
-        for (int j = 0; j < LPO; ++j) dma_b(0, j);
-#pragma unroll
-        for (int j = 0; j < LPO; ++j) dma_a(1, j);
-#pragma unroll
-        for (int j = 0; j < LPO; ++j) dma_b(1, j);
-#pragma unroll
-        for (int j = 0; j < LPO; ++j) dma_b(2, j);
-    };
-    int rows_live = 256;
-    auto substep = [&](auto full, auto nd, int set, int rkt, int rq, auto&& dma) __attribute__((always_inline)) {
-        constexpr int ND = decltype(nd)::value, H1 = NM / 2, H2 = NM - NM / 2;
-#pragma unroll
-        for (int m = 0; m < NM; ++m) {
-            const int i = m / NB, f = m % NB;
-            // row blocks past the tile's last row are skipped (rows_live is
-            // wave-uniform); the weight gradients always have full blocks
-            if (!ROWS || i * 32 < rows_live) acc[i][f] = mma32<DT>::run(bv[set][f], av[set][i], acc[i][f]);
-            if (m < H1) {
-#pragma unroll
-                for (int r = (m * NR) / H1; r < ((m + 1) * NR) / H1; ++r) read_one(rkt, rq, set ^ 1, r);
-            } else {
-                const int q = m - H1;
-#pragma unroll
-                for (int d = (q * ND) / H2; d < ((q + 1) * ND) / H2; ++d) dma(d);
-            }
-            sched_fence();
-        }
-    };
-    using no_dma = std::integral_constant<int, 0>;
-    using step_dma = std::integral_constant<int, 2 * LPO>;
-    auto none = [](int) __attribute__((always_inline)) {};
-    auto main_loop = [&](auto full) __attribute__((always_inline)) {
-        for (int kt = 0; kt < nk; ++kt) {
-            wait_lgkm0();
-            substep(full, no_dma{}, 0, kt, 1, none);
-            wait_lgkm0();
-            substep(full, no_dma{}, 1, kt, 2, none);
-            wait_lgkm0();
-            substep(full, no_dma{}, 0, kt, 3, none);
-            // step kt+1 landed (only the column operand of kt+2 was issued
-            // after it); every wave is done reading step kt once past the barrier
-            wait_vm<LPO>();
-            wait_lgkm0();
-            barrier_lds();
-            substep(full, step_dma{}, 1, kt + 1, 0,
-                    [&](int d) __attribute__((always_inline)) {
-                        if (d < LPO) dma_a(kt + 2, d); else dma_b(kt + 3, d - LPO);
-                    });
-        }
-    };
-
-    int t = blockIdx.x;
-    if (!tile(t)) return;
-    if (nk > 0) prologue_dma();
-    while (true) {
-#pragma unroll
-        for (int i = 0; i < MB; ++i)
-#pragma unroll
-            for (int f = 0; f < NB; ++f)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[i][f][r] = 0.0f;
-        if (nk > 0) {
-            if constexpr (ROWS)
-                rows_live = __builtin_amdgcn_readfirstlane(m1 - m0) - __builtin_amdgcn_readfirstlane(wm) * WTM;
-            wait_vm<3 * LPO>();
-            barrier_lds();
-#pragma unroll
-            for (int r = 0; r < NR; ++r) read_one(0, 0, 0, r);
-            main_loop(std::true_type{});
-            // every DMA of this tile landed and every wave finished its reads
-            wait_vm<0>();
-            wait_lgkm0();
-            barrier_lds();
-        }
-        // the next tile's first steps load while this one is stored
-        const int c_e = e, c_m0 = m0, c_m1 = m1, c_n0 = n0;
-        t += gridDim.x;
-        const bool more = tile(t);
-        if (more && nk > 0) prologue_dma();
-
-        // ---- epilogue: lane holds output row (lane % 32) of each row block
-        // and columns 8 g + 4 (lane / 32) + 0..3 (g = 0..3) of each column block
-#pragma unroll
-        for (int i = 0; i < MB; ++i) {
-            const int m = c_m0 + wm * WTM + 32 * i + frow;
-            if (m >= c_m1) continue;
-#pragma unroll
-            for (int f = 0; f < NB; ++f) {
-                const int cb = c_n0 + wn * WTN + 32 * f + 4 * kg;
-                if constexpr (MODE == kDH) {
-                    // the block's saved g and u are loaded before any store,
-                    // so the 8 loads are in flight together
-                    float4 g4[4], u4[4];
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const int col = cb + 8 * g;
-                        const float* gr = p.gu + (int64_t)m * I2 + (col < ncols ? col : 0);
-                        g4[g] = *(const float4*)gr;
-                        u4[g] = *(const float4*)(gr + p.I);
-                    }
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const int col = cb + 8 * g;
-                        if (col >= ncols) continue;
-                        const float gv[4] = {g4[g].x, g4[g].y, g4[g].z, g4[g].w};
-                        const float uv[4] = {u4[g].x, u4[g].y, u4[g].z, u4[g].w};
-                        float dg[4], du[4];
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const float dh = acc[i][f][4 * g + r];
-                            const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-gv[r]));
-                            du[r] = dh * (gv[r] * sg);
-                            dg[r] = dh * uv[r] * (sg * (1.0f + gv[r] * (1.0f - sg)));
-                        }
-                        S* out = (S*)p.c0 + (int64_t)m * I2 + col;
-                        store4<DT>::run(out, dg);
-                        store4<DT>::run(out + p.I, du);
-                    }
-                } else {
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const int col = cb + 8 * g;
-                        if (col >= ncols) continue;
-                        const float v0 = acc[i][f][4 * g], v1 = acc[i][f][4 * g + 1], v2 = acc[i][f][4 * g + 2],
-                                    v3 = acc[i][f][4 * g + 3];
-                        if constexpr (MODE == kDX) {
-                            const float v[4] = {v0, v1, v2, v3};
-                            store4<DT>::run((S*)p.c0 + (int64_t)m * p.H + col, v);
-                        } else {
-                            float* out;
-                            if constexpr (MODE == kDWGU)
-                                out = m < p.I ? (float*)p.c0 + ((int64_t)c_e * p.I + m) * p.H + col
-                                              : (float*)p.c1 + ((int64_t)c_e * p.I + (m - p.I)) * p.H + col;
-                            else
-                                out = (float*)p.c0 + ((int64_t)c_e * p.H + m) * p.I + col;
-                            *(float4*)out = make_float4(v0, v1, v2, v3);
-                        }
-                    }
-                }
-            }
-        }
-        if (!more) break;
-    }
-}
-
-template <typename DT, int MODE>
-hipError_t launch_train_pipe(TrainGemm p, int64_t blocks, hipStream_t s) {
-    if (blocks == 0) return hipSuccess;
-    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-    p.nblocks = (int)blocks;
-    // persistent: one workgroup per CU (it takes the whole LDS), a multiple
-    // of 8 so each workgroup's tiles stay on one XCD
-    const int64_t grid = MOE_TP_PERSIST ? std::min<int64_t>(blocks, (int64_t)persistent_slots(s)) : blocks;
-    train_pipe_kernel<DT, MODE><<<(unsigned)grid, kTPWaves * kWave, 0, s>>>(p);
-    return hipGetLastError();
-}
-
-// ------------------------------------------------------------------ pipelined training GEMM, two per CU
-// The same products on 128 x 256 tiles of 4 waves (each 128 x 64, 32x32x16
+// ------------------------------------------------------------------ pipelined training GEMM (16-bit)
+// The four products on 128 x 256 tiles of 4 waves (each 128 x 64, 32x32x16
 // MFMAs) with 32-K steps in a 64 KB ring (two row-operand slots of 8 KB,
 // three column-operand slots of 16 KB), so two workgroups share a CU and one
 // computes while the other stores its tile.  Layouts per slot:
@@ -734,7 +361,11 @@ hipError_t launch_train_pipe(TrainGemm p, int64_t blocks, hipStream_t s) {
 //   K-outer row operand (weight gradients): 32 K-rows x 256 bytes (128
 //     values), chunk c of K-row r at c ^ (4 (r & 3));
 //   K-outer column operand: 32 K-rows x 512 bytes, chunk c at c ^ ((r & 7) << 2).
-// K-outer operands are read with ds_read_b64_tr_b16 as in train_pipe_kernel.
+// K-outer operands are read with the transpose read above; the swizzles put
+// the K-rows of one read on distinct banks.  K tails (an expert's last rows,
+// K not a multiple of 32): loads are clamped to the last valid K-row or
+// chunk, and the fragments of the last step zero every value past the end
+// on both operands.
 constexpr int kT2BM = 128, kT2BN = 256, kT2Waves = 4;
 constexpr int kT2SlotA = 8 * 1024, kT2SlotB = 16 * 1024;
 constexpr int kT2SlotsA = 2, kT2SlotsB = 3;
@@ -1207,9 +838,8 @@ hipError_t experts_backward_typed(const ExpertsBackwardArgs& a, hipStream_t s) {
     const int64_t lim = int64_t(1) << 31, es = (int64_t)sizeof(typename DT::storage);
     const bool offsets32 = a.N * 2 * a.I * es < lim && a.N * a.H * es < lim && a.H * a.I * es < lim &&
                            256 * std::max(a.H, 2 * a.I) * es < lim;
-    const bool pipe = MOE_TRAIN_PIPE && es == 2 && offsets32 && a.N >= 64 * (int64_t)a.E;
-    const bool two = pipe && MOE_TRAIN_PIPE == 2;
-    const int BM = two ? kT2BM : (pipe ? kTPBM : kTBM), BN = two ? kT2BN : (pipe ? kTPBN : kTBN);
+    const bool pipe = es == 2 && offsets32 && a.N >= 64 * (int64_t)a.E;
+    const int BM = pipe ? kT2BM : kTBM, BN = pipe ? kT2BN : kTBN;
     int4* tiles = (int4*)((char*)a.tiles + 256);
     uint32_t* count = (uint32_t*)a.tiles;
     const int64_t mt = max_mtiles(a.N, a.E, BM);
@@ -1218,8 +848,7 @@ hipError_t experts_backward_typed(const ExpertsBackwardArgs& a, hipStream_t s) {
     auto launch = [&](auto mode, const TrainGemm& q, int64_t blocks) {
         constexpr int M = decltype(mode)::value;
         if constexpr (sizeof(typename DT::storage) == 2) {
-            if (two) return launch_train_pipe2<DT, M>(q, blocks, s);
-            if (pipe) return launch_train_pipe<DT, M>(q, blocks, s);
+            if (pipe) return launch_train_pipe2<DT, M>(q, blocks, s);
         }
         return launch_train_gemm<DT, M>(q, blocks, s);
     };
