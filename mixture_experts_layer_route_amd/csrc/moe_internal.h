@@ -103,6 +103,20 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
     return v;
 }
 
+// ------------------------------------------------------------------ streaming access
+// 16-byte loads and stores with the non-temporal hint (global_load/store ...
+// nt), for data a kernel touches exactly once: it streams past the caches
+// instead of displacing lines that other rows still reuse.
+typedef unsigned int u32x4_nt_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_nt16(const void* p) {
+    const u32x4_nt_t v = __builtin_nontemporal_load((const u32x4_nt_t*)p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void store_nt16(void* p, uint4 v) {
+    const u32x4_nt_t w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, (u32x4_nt_t*)p);
+}
+
 // ------------------------------------------------------------------ launchers
 // Each returns hipSuccess or the launch error.  Shapes are checked by the
 // caller (moe_api.hip) before these run.

@@ -820,14 +820,24 @@ hipError_t launch_train_pipe2(TrainGemm p, int64_t blocks, hipStream_t s) {
 }
 
 // rows[r] = x[token_of_row[r]] (the token index clamped into x), one
-// wavefront per row, 16-byte chunks
+// wavefront per row, 16-byte chunks, four loads in flight per lane.  A token
+// row is read once per slot and stays cached; the gathered rows are written
+// once (non-temporal).
 __global__ __launch_bounds__(256) void gather_rows_kernel(const uint4* __restrict__ x, const uint32_t* __restrict__ tor,
                                                           int64_t x_rows, int64_t N, int64_t chunks,
                                                           uint4* __restrict__ rows) {
     const int64_t r = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
     if (r >= N) return;
     const int64_t t = min((int64_t)tor[r], x_rows - 1);
-    for (int64_t c = lane_id(); c < chunks; c += kWave) rows[r * chunks + c] = x[t * chunks + c];
+    for (int64_t c = lane_id(); c < chunks; c += 4 * kWave) {
+        uint4 v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (c + i * kWave < chunks) v[i] = x[t * chunks + c + i * kWave];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (c + i * kWave < chunks) store_nt16(rows + r * chunks + c + i * kWave, v[i]);
+    }
 }
 
 template <typename DT>
@@ -970,45 +980,57 @@ __global__ __launch_bounds__(256) void combine_backward_kernel(
     }
 }
 
-// dx[t] = sum_j drows[row_j] in FP32, slot order, rounded once; a token with
-// a slot row >= N gets a NaN row.
+// dx[t] = sum_j drows[row_j] in FP32, slot order j = 0..k-1, rounded once; a
+// token with a slot row >= N gets a NaN row.  grid (tokens, column chunks):
+// thread -> VEC consecutive columns of one token.  The token's k rows are
+// wave-uniform and their loads go out in batches of 8 before the adds, so
+// the loads of a thread overlap.  Every row of drows is read once and every
+// row of dx written once: the 16-byte accesses are non-temporal.
 template <typename DT, int VEC>
 __global__ __launch_bounds__(256) void dispatch_backward_kernel(const typename DT::storage* __restrict__ drows,
                                                                 int64_t N, const uint32_t* __restrict__ row_of_slot,
-                                                                int64_t T, int k, int64_t H,
+                                                                int k, int64_t H,
                                                                 typename DT::storage* __restrict__ dx) {
     using S = typename DT::storage;
-    const int lane = lane_id();
-    const int64_t t = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
-    if (t >= T) return;
+    const int64_t t = blockIdx.x;
+    const int64_t c0 = ((int64_t)blockIdx.y * blockDim.x + threadIdx.x) * VEC;
+    if (c0 >= H) return;
     const uint32_t* rs = row_of_slot + t * k;
     bool invalid = false;
     for (int j = 0; j < k; ++j) invalid |= (int64_t)rs[j] >= N;
-    const int64_t chunks = H / VEC;
-    for (int64_t c = lane; c < chunks; c += kWave) {
-        float acc[VEC];
+    float acc[VEC];
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) acc[v] = invalid ? __uint_as_float(0x7fc00000u) : 0.0f;
-        if (!invalid) {
-            for (int j = 0; j < k; ++j) {
-                S rv[VEC];
-                const S* src = drows + (int64_t)rs[j] * H + c * VEC;
-                if constexpr (VEC * sizeof(S) == 16)
-                    *(uint4*)rv = *(const uint4*)src;
-                else
-                    rv[0] = *src;
+    for (int v = 0; v < VEC; ++v) acc[v] = invalid ? __uint_as_float(0x7fc00000u) : 0.0f;
+    if (!invalid) {
+        constexpr int B = 8;
+        for (int j0 = 0; j0 < k; j0 += B) {
+            S vals[B][VEC];
 #pragma unroll
-                for (int v = 0; v < VEC; ++v) acc[v] += fmt<DT>::load(rv[v]);
+            for (int b = 0; b < B; ++b) {
+                if (j0 + b < k) {
+                    const S* src = drows + (int64_t)rs[j0 + b] * H + c0;
+                    if constexpr (VEC * sizeof(S) == 16)
+                        *(uint4*)vals[b] = load_nt16(src);
+                    else
+                        vals[b][0] = *src;
+                }
+            }
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                if (j0 + b < k) {
+#pragma unroll
+                    for (int v = 0; v < VEC; ++v) acc[v] += fmt<DT>::load(vals[b][v]);
+                }
             }
         }
-        S ov[VEC];
-#pragma unroll
-        for (int v = 0; v < VEC; ++v) ov[v] = fmt<DT>::store(acc[v]);
-        if constexpr (VEC * sizeof(S) == 16)
-            *(uint4*)(dx + t * H + c * VEC) = *(const uint4*)ov;
-        else
-            dx[t * H + c] = ov[0];
     }
+    S ov[VEC];
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) ov[v] = fmt<DT>::store(acc[v]);
+    if constexpr (VEC * sizeof(S) == 16)
+        store_nt16(dx + t * H + c0, *(const uint4*)ov);
+    else
+        dx[t * H + c0] = ov[0];
 }
 
 bool wide_rows(int64_t H, int es, std::initializer_list<const void*> ptrs) {
@@ -1047,12 +1069,16 @@ template <typename DT>
 hipError_t dispatch_backward_typed(const DispatchBackwardArgs& a, hipStream_t s) {
     using S = typename DT::storage;
     constexpr int V16 = 16 / sizeof(S);
-    const dim3 grid((unsigned)((a.T + 3) / 4)), block(256);
-    if (wide_rows(a.H, sizeof(S), {a.drows, a.dx}))
-        dispatch_backward_kernel<DT, V16><<<grid, block, 0, s>>>((const S*)a.drows, a.N, a.row_of_slot, a.T, a.k,
-                                                                a.H, (S*)a.dx);
+    const bool wide = wide_rows(a.H, sizeof(S), {a.drows, a.dx});
+    const int64_t chunks = ((wide ? a.H / V16 : a.H) + 255) / 256;
+    if (a.T > 0x7fffffff || chunks > 65535) return hipErrorInvalidValue;
+    if (chunks == 0) return hipSuccess;
+    const dim3 grid((unsigned)a.T, (unsigned)chunks), block(256);
+    if (wide)
+        dispatch_backward_kernel<DT, V16><<<grid, block, 0, s>>>((const S*)a.drows, a.N, a.row_of_slot, a.k, a.H,
+                                                                (S*)a.dx);
     else
-        dispatch_backward_kernel<DT, 1><<<grid, block, 0, s>>>((const S*)a.drows, a.N, a.row_of_slot, a.T, a.k, a.H,
+        dispatch_backward_kernel<DT, 1><<<grid, block, 0, s>>>((const S*)a.drows, a.N, a.row_of_slot, a.k, a.H,
                                                               (S*)a.dx);
     return hipGetLastError();
 }
@@ -1086,7 +1112,6 @@ hipError_t launch_combine_backward(const CombineBackwardArgs& a, hipStream_t s) 
 
 hipError_t launch_dispatch_backward(const DispatchBackwardArgs& a, hipStream_t s) {
     if (a.T == 0) return hipSuccess;
-    if ((a.T + 3) / 4 > 0x7fffffff) return hipErrorInvalidValue;
     switch (a.dtype) {
     case MOE_F32: return dispatch_backward_typed<f32_t>(a, s);
     case MOE_F16: return dispatch_backward_typed<f16_t>(a, s);

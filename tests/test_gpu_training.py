@@ -136,6 +136,8 @@ BWD_CASES = [
     S.small_config("cb_ragged_bf16", T=301, H=200, I=8, E=5, top_k=3, dtype="bf16", seed=302),
     S.small_config("cb_odd_h_f16", T=77, H=36, I=8, E=3, top_k=2, dtype="f16", logits_dtype="f32", seed=303),
     S.small_config("cb_wide_bf16", T=129, H=7168, I=8, E=16, top_k=8, dtype="bf16", seed=304),
+    # more slots than one batch of row loads (8) in the dispatch backward
+    S.small_config("cb_many_slots_bf16", T=50, H=64, I=8, E=24, top_k=11, dtype="bf16", seed=305),
 ]
 
 
@@ -174,9 +176,9 @@ EXPERT_CASES = [
     S.small_config("ex_pipe64_bf16", T=600, H=192, I=128, E=6, top_k=2, dtype="bf16", seed=405),
     S.small_config("ex_long_k_bf16", T=1500, H=128, I=64, E=2, top_k=1, dtype="bf16", seed=406),
     S.small_config("ex_f32_odd", T=90, H=48, I=40, E=3, top_k=2, dtype="f32", seed=407),
-    # more 256 x 256 weight-gradient tiles (16 x 4 x 8) than workgroups: the
-    # persistent loop stores one tile while the next one loads
-    S.small_config("ex_persistent_bf16", T=1100, H=2048, I=512, E=16, top_k=2, dtype="bf16", seed=409),
+    # more weight-gradient tiles (16 experts x 8 x 8 of 128 x 256) than the
+    # GPU runs at once
+    S.small_config("ex_many_tiles_bf16", T=1100, H=2048, I=512, E=16, top_k=2, dtype="bf16", seed=409),
 ]
 
 
