@@ -192,34 +192,35 @@ __global__ __launch_bounds__(WGM* WGN* kWave) void grouped_gemm_kernel(
     }
 
     uint4 ra[A_CH], rb[B_CH];
-    // loads never branch: a chunk past K reads a valid address and is zeroed
+    // Loads never branch on K: a chunk past K reads a valid address (step 0's)
+    // and is zeroed when it is written to LDS, once it has arrived.  (Zeroing
+    // it at the load made the compiler clear the register and load into it
+    // under a mask, and wait for each load before issuing the next: two
+    // memory round trips per step.)
     auto gload = [&](int kt) {
         const int kb = kt * ROWB;
-        const bool kin = kb + my_ch * 16 < kbytes;
-        const int off = kin ? kb : 0;
-#pragma unroll
-        for (int i = 0; i < A_CH; ++i) {
-            if (A_CHUNKS % NT == 0 || tid + i * NT < A_CHUNKS) {
-                uint4 v = *(const uint4*)(a_src[i] + off);
-                ra[i] = kin ? v : make_uint4(0, 0, 0, 0);
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < B_CH; ++i) {
-            if (B_CHUNKS % NT == 0 || tid + i * NT < B_CHUNKS) {
-                uint4 v = *(const uint4*)(b_src[i] + off);
-                rb[i] = kin ? v : make_uint4(0, 0, 0, 0);
-            }
-        }
-    };
-    auto lstore = [&](int st) {
-        unsigned char* base = smem + st * STAGE;
+        const int off = kb + my_ch * 16 < kbytes ? kb : 0;
 #pragma unroll
         for (int i = 0; i < A_CH; ++i)
-            if (A_CHUNKS % NT == 0 || tid + i * NT < A_CHUNKS) *(uint4*)(base + a_lds[i]) = ra[i];
+            if (A_CHUNKS % NT == 0 || tid + i * NT < A_CHUNKS) ra[i] = *(const uint4*)(a_src[i] + off);
 #pragma unroll
         for (int i = 0; i < B_CH; ++i)
-            if (B_CHUNKS % NT == 0 || tid + i * NT < B_CHUNKS) *(uint4*)(base + b_lds[i]) = rb[i];
+            if (B_CHUNKS % NT == 0 || tid + i * NT < B_CHUNKS) rb[i] = *(const uint4*)(b_src[i] + off);
+    };
+    auto lstore = [&](int st, int kt) {
+        unsigned char* base = smem + st * STAGE;
+        // a select per 32-bit word: a select of whole uint4 values would
+        // pick between their addresses and move the arrays to scratch
+        const uint32_t keep = kt * ROWB + my_ch * 16 < kbytes ? ~0u : 0u;
+        auto masked = [keep](const uint4& v) {
+            return make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
+        };
+#pragma unroll
+        for (int i = 0; i < A_CH; ++i)
+            if (A_CHUNKS % NT == 0 || tid + i * NT < A_CHUNKS) *(uint4*)(base + a_lds[i]) = masked(ra[i]);
+#pragma unroll
+        for (int i = 0; i < B_CH; ++i)
+            if (B_CHUNKS % NT == 0 || tid + i * NT < B_CHUNKS) *(uint4*)(base + b_lds[i]) = masked(rb[i]);
     };
 
     const int lane = lane_id(), wid = tid / kWave;
@@ -245,7 +246,7 @@ __global__ __launch_bounds__(WGM* WGN* kWave) void grouped_gemm_kernel(
 
     const int nk = (kbytes + ROWB - 1) / ROWB;
     gload(0);
-    lstore(0);
+    lstore(0, 0);
     __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
         const int st = kt & 1;
@@ -263,7 +264,7 @@ __global__ __launch_bounds__(WGM* WGN* kWave) void grouped_gemm_kernel(
 #pragma unroll
                 for (int f = 0; f < NF; ++f) acc[i][f] = mma<DT>::run(bv[f], av[i], acc[i][f]);
         }
-        if (kt + 1 < nk) lstore(st ^ 1);
+        if (kt + 1 < nk) lstore(st ^ 1, kt + 1);
         __syncthreads();
     }
 
