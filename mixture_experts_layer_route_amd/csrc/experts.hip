@@ -31,7 +31,9 @@
 //     into two token-row slots and three weight-row slots of 32 KB, the
 //     weight rows issued about two steps ahead, a quarter per 16-K sub-step,
 //     and the token rows one step ahead, in the last sub-step of a step.
-//   grouped_gemm_pipe_kernel (bf16/f16, K a multiple of 32): 256x256 tiles on
+//   grouped_gemm_pipe_kernel (bf16/f16, K a multiple of 32 but not of 64, or
+//     a row-operand buffer of 4 GiB or more, which the 64-K kernel's 32-bit
+//     offsets cannot span): 256x256 tiles on
 //     8 waves of 32x32x16 MFMAs; 32-element K stages filled by direct
 //     global->LDS loads in a 4-stage ring, issued three stages ahead and
 //     interleaved with the MFMAs and the next fragment reads.
