@@ -932,51 +932,83 @@ hipError_t experts_backward_typed(const ExpertsBackwardArgs& a, hipStream_t s) {
 // H is not a whole number of chunks).
 
 // dY[row_j] = w_j g (rounded to the expert dtype), dw_j = <Y[row_j], g> in
-// FP32; a token with a slot row >= N gets NaN weight gradients.
+// FP32; a token with a slot row >= N gets NaN weight gradients.  One
+// workgroup per token: thread -> VEC-column groups c = tid, tid + 256, ...
+// of the row.  Slots go in batches of 8: the thread's g values are loaded
+// once per batch and its Y loads for the batch's slots go out together.  Each
+// dw_j is reduced in a fixed order (the thread's columns in order, a
+// butterfly over the wave, then the 4 waves in order), so it does not depend
+// on timing.
 template <typename DT, typename WT, int VEC>
 __global__ __launch_bounds__(256) void combine_backward_kernel(
     const typename DT::storage* __restrict__ Y, int64_t N, const uint32_t* __restrict__ row_of_slot,
-    const typename WT::storage* __restrict__ w, const typename DT::storage* __restrict__ g, int64_t T, int k,
-    int64_t H, typename DT::storage* __restrict__ dY, float* __restrict__ dw) {
+    const typename WT::storage* __restrict__ w, const typename DT::storage* __restrict__ g, int k, int64_t H,
+    typename DT::storage* __restrict__ dY, float* __restrict__ dw) {
     using S = typename DT::storage;
-    const int lane = lane_id();
-    const int64_t t = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
-    if (t >= T) return;
+    constexpr int B = 8, NWAVE = 256 / kWave;
+    __shared__ float part[NWAVE][B];
+    const int64_t t = blockIdx.x;
+    const int tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
     const uint32_t* rs = row_of_slot + t * k;
     bool invalid = false;
     for (int j = 0; j < k; ++j) invalid |= (int64_t)rs[j] >= N;
     const S* gt = g + t * H;
     const int64_t chunks = H / VEC;
-    for (int j = 0; j < k; ++j) {
-        const int64_t row = rs[j];
-        float dot = 0.0f;
-        if (row < N) {
-            const float wj = fmt<WT>::load(w[t * k + j]);
-            const S* yr = Y + row * H;
-            S* dr = dY + row * H;
-            for (int64_t c = lane; c < chunks; c += kWave) {
-                S gv[VEC], yv[VEC], ov[VEC];
-                if constexpr (VEC * sizeof(S) == 16) {
-                    *(uint4*)gv = *(const uint4*)(gt + c * VEC);
-                    *(uint4*)yv = *(const uint4*)(yr + c * VEC);
-                } else {
-                    gv[0] = gt[c];
-                    yv[0] = yr[c];
-                }
+    for (int j0 = 0; j0 < k; j0 += B) {
+        float dot[B], wj[B];
+        int64_t row[B];
 #pragma unroll
-                for (int v = 0; v < VEC; ++v) {
-                    const float gf = fmt<DT>::load(gv[v]);
-                    dot = fmaf(fmt<DT>::load(yv[v]), gf, dot);
-                    ov[v] = fmt<DT>::store(wj * gf);
+        for (int b = 0; b < B; ++b) {
+            dot[b] = 0.0f;
+            row[b] = j0 + b < k ? (int64_t)rs[j0 + b] : N;  // N: no slot, or a slot past the rows
+            wj[b] = row[b] < N ? fmt<WT>::load(w[t * k + j0 + b]) : 0.0f;
+        }
+        for (int64_t c = tid; c < chunks; c += 256) {
+            S gv[VEC], yv[B][VEC];
+            if constexpr (VEC * sizeof(S) == 16)
+                *(uint4*)gv = *(const uint4*)(gt + c * VEC);
+            else
+                gv[0] = gt[c];
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                if (row[b] < N) {
+                    if constexpr (VEC * sizeof(S) == 16)
+                        *(uint4*)yv[b] = *(const uint4*)(Y + row[b] * H + c * VEC);
+                    else
+                        yv[b][0] = Y[row[b] * H + c];
                 }
-                if constexpr (VEC * sizeof(S) == 16)
-                    *(uint4*)(dr + c * VEC) = *(const uint4*)ov;
-                else
-                    dr[c] = ov[0];
+            }
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                if (row[b] < N) {
+                    S ov[VEC];
+#pragma unroll
+                    for (int v = 0; v < VEC; ++v) {
+                        const float gf = fmt<DT>::load(gv[v]);
+                        dot[b] = fmaf(fmt<DT>::load(yv[b][v]), gf, dot[b]);
+                        ov[v] = fmt<DT>::store(wj[b] * gf);
+                    }
+                    if constexpr (VEC * sizeof(S) == 16)
+                        *(uint4*)(dY + row[b] * H + c * VEC) = *(const uint4*)ov;
+                    else
+                        dY[row[b] * H + c] = ov[0];
+                }
             }
         }
-        dot = wave_sum(dot);
-        if (lane == 0) dw[t * k + j] = invalid ? __uint_as_float(0x7fc00000u) : dot;
+#pragma unroll
+        for (int b = 0; b < B; ++b) dot[b] = wave_sum(dot[b]);
+        if (lane == 0) {
+#pragma unroll
+            for (int b = 0; b < B; ++b) part[wid][b] = dot[b];
+        }
+        __syncthreads();
+        if (tid < B && j0 + tid < k) {
+            float sum = part[0][tid];
+#pragma unroll
+            for (int q = 1; q < NWAVE; ++q) sum += part[q][tid];
+            dw[t * k + j0 + tid] = invalid ? __uint_as_float(0x7fc00000u) : sum;
+        }
+        __syncthreads();
     }
 }
 
@@ -1045,13 +1077,14 @@ hipError_t combine_backward_typed(const CombineBackwardArgs& a, hipStream_t s) {
     using S = typename DT::storage;
     using W = typename WT::storage;
     constexpr int V16 = 16 / sizeof(S);
-    const dim3 grid((unsigned)((a.T + 3) / 4)), block(256);
+    if (a.T > 0x7fffffff) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)a.T), block(256);
     if (wide_rows(a.H, sizeof(S), {a.y, a.g, a.dy}))
         combine_backward_kernel<DT, WT, V16><<<grid, block, 0, s>>>((const S*)a.y, a.N, a.row_of_slot, (const W*)a.w,
-                                                                   (const S*)a.g, a.T, a.k, a.H, (S*)a.dy, a.dw);
+                                                                   (const S*)a.g, a.k, a.H, (S*)a.dy, a.dw);
     else
         combine_backward_kernel<DT, WT, 1><<<grid, block, 0, s>>>((const S*)a.y, a.N, a.row_of_slot, (const W*)a.w,
-                                                                 (const S*)a.g, a.T, a.k, a.H, (S*)a.dy, a.dw);
+                                                                 (const S*)a.g, a.k, a.H, (S*)a.dy, a.dw);
     return hipGetLastError();
 }
 
@@ -1101,7 +1134,6 @@ hipError_t launch_experts_backward(const ExpertsBackwardArgs& a, hipStream_t s) 
 
 hipError_t launch_combine_backward(const CombineBackwardArgs& a, hipStream_t s) {
     if (a.T == 0) return hipSuccess;
-    if ((a.T + 3) / 4 > 0x7fffffff) return hipErrorInvalidValue;
     switch (a.dtype) {
     case MOE_F32: return combine_backward_w<f32_t>(a, s);
     case MOE_F16: return combine_backward_w<f16_t>(a, s);
