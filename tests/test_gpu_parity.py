@@ -58,6 +58,9 @@ def small_cases():
         # and several steps with ragged tiles in f16
         S.small_config("pipe64_one_step_bf16", T=600, H=64, I=64, E=3, top_k=2, dtype="bf16", seed=20),
         S.small_config("pipe64_f16", T=900, H=192, I=128, E=6, top_k=2, dtype="f16", seed=27),
+        # few rows per expert (the 16-row tile) with a partial last K slice on
+        # both products: K = 72 and 40 values of f16
+        S.small_config("small_tile_k_tail_f16", T=40, H=72, I=40, E=8, top_k=2, dtype="f16", seed=28),
     ]
 
 
