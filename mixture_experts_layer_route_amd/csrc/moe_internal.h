@@ -69,9 +69,25 @@ template <> struct fmt<bf16_t> {
 // ------------------------------------------------------------------ wave helpers
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
 
+// Cross-lane moves inside a row of 16 lanes (DPP): swap neighbours, swap
+// pairs, mirror within 8 lanes, mirror within 16.  Applied in that order,
+// each step pairs every lane with one holding the other half of the lanes
+// reduced so far, so a max over the row ends in all 16 lanes; the last two
+// steps (across rows) use permutes.  Only order-free reductions (max) use
+// this: a sum keeps its xor butterfly so its rounding does not change.
+constexpr int kDppSwap1 = 0xB1, kDppSwap2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
+    v = fmaxf(v, __uint_as_float(dpp_u32<kDppSwap1>(__float_as_uint(v))));
+    v = fmaxf(v, __uint_as_float(dpp_u32<kDppSwap2>(__float_as_uint(v))));
+    v = fmaxf(v, __uint_as_float(dpp_u32<kDppHalfMirror>(__float_as_uint(v))));
+    v = fmaxf(v, __uint_as_float(dpp_u32<kDppMirror>(__float_as_uint(v))));
+    v = fmaxf(v, __shfl_xor(v, 16, kWave));
+    v = fmaxf(v, __shfl_xor(v, 32, kWave));
     return v;
 }
 
@@ -81,9 +97,19 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
+template <int CTRL>
+__device__ __forceinline__ uint64_t max_dpp_u64(uint64_t v) {
+    const uint64_t o = ((uint64_t)dpp_u32<CTRL>((uint32_t)(v >> 32)) << 32) | dpp_u32<CTRL>((uint32_t)v);
+    return o > v ? o : v;
+}
+
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+    v = max_dpp_u64<kDppSwap1>(v);
+    v = max_dpp_u64<kDppSwap2>(v);
+    v = max_dpp_u64<kDppHalfMirror>(v);
+    v = max_dpp_u64<kDppMirror>(v);
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
+    for (int m = 16; m <= 32; m <<= 1) {
         uint32_t lo = __shfl_xor((uint32_t)v, m, kWave);
         uint32_t hi = __shfl_xor((uint32_t)(v >> 32), m, kWave);
         uint64_t o = ((uint64_t)hi << 32) | lo;
