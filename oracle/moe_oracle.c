@@ -17,8 +17,7 @@
  *   - same guide, section 5 "Expert weights and dispatch": x is [T,H], gate
  *     and up are [E,I,H], down is [E,H,I]; dispatch drops no token; a saved
  *     mapping restores token order.
- *   - tiny-llm deep dive 5 (ops.rs), "softmax" block: max-shifted softmax;
- *     "SiLU" block: silu(z) = z / (1 + exp(-z)) and the SwiGLU FFN
+ *   - tiny-llm deep dive 5 (ops.rs), "SiLU" block: silu(z) = z / (1 + exp(-z)) and the SwiGLU FFN
  *     W_down(SiLU(W_gate x) * W_up x); "RMSNorm" block: why sums are kept
  *     in double; "matvec" block: rows are independent, so rows may be
  *     split over threads without locks.
@@ -191,23 +190,24 @@ static void parallel_rows(int64_t n, int nthreads, row_fn fn, void* ctx)
 /* Routing (ruDNN User Guide, section 4 "Routing contract").            */
 /* ------------------------------------------------------------------ */
 
-/* FP32 softmax of one row, max-shifted as in the tiny-llm softmax block.
- * A NaN never wins "v > m"; a NaN, a +inf (inf - inf) or an all -inf row
- * (-inf - -inf) therefore gives NaN in d, so S and every p become NaN:
- * the plain arithmetic itself yields the NaN rows the contract keeps. */
+/* The routing contract's probabilities of one row: the logits widened to
+ * binary32, then p_e = exp(l_e - m) / S over all E experts, with m the row
+ * maximum (the shift leaves p unchanged in exact arithmetic and keeps exp
+ * finite) and S the sum of exp(l_j - m).  Each exp is rounded once to
+ * binary32; S is summed in ascending expert id; p_e is one IEEE division.
+ * Rows the contract turns into NaN rows need no test of their own: m
+ * ignores NaN ("l > m" is false for it), so a NaN logit, a +inf logit
+ * (inf - inf) or a row of only -inf (-inf - -inf) puts a NaN into some
+ * l_e - m, which reaches S and from there every p_e. */
 static void softmax_row_f32(const void* logits, int dt, int64_t row, int64_t E, float* p)
 {
+    for (int64_t e = 0; e < E; ++e) p[e] = (float)load_elem(logits, dt, row * E + e);
     float m = -INFINITY;
-    for (int64_t e = 0; e < E; ++e) {
-        float v = (float)load_elem(logits, dt, row * E + e);
-        if (v > m) m = v;
-    }
+    for (int64_t e = 0; e < E; ++e) m = p[e] > m ? p[e] : m;
     float S = 0.0f;
     for (int64_t e = 0; e < E; ++e) {
-        float d = (float)load_elem(logits, dt, row * E + e) - m;
-        float q = (float)exp((double)d); /* exp rounded once to binary32 */
-        p[e] = q;
-        S += q; /* sequential, ascending expert id */
+        p[e] = (float)exp((double)(p[e] - m)); /* exp(l_e - m), rounded once */
+        S += p[e];
     }
     for (int64_t e = 0; e < E; ++e) p[e] = p[e] / S;
 }

@@ -442,6 +442,49 @@ def test_no_token_is_dropped(oracle_lib):
     assert off[4] - off[3] == T and off[7] - off[6] == T and off[E] == T * k
 
 
+@pytest.mark.parametrize("ldt", ["bf16", "f16", "f32"])
+def test_combine_uses_the_cast_weights(oracle_lib, ldt):
+    """Section 6 (Call MoE): the combine sums the expert rows with the routing
+    weights, and section 4 makes those weights the logits dtype.  Two experts
+    whose outputs are exactly +256 and -256 (a SiLU input of 128 saturates to
+    128 in every dtype, times a down weight of +-2) make the output of a token
+    256 (w0 - w1) rounded once: with the cast weights this is one value, with
+    the FP32 weights before the cast another, and the oracle must give the
+    first on every token.  For F32 logits the two coincide."""
+    T, H, I, E = 256, 8, 1, 2
+    x = np.zeros((T, H), np.float32)
+    x[:, 0] = 1.0
+    gate = np.zeros((E, I, H), np.float32)
+    gate[:, 0, 0] = 128.0
+    up = np.zeros((E, I, H), np.float32)
+    up[:, 0, 0] = 1.0
+    down = np.zeros((E, H, I), np.float32)
+    down[0, :, 0] = 2.0
+    down[1, :, 0] = -2.0
+    to = lambda a, dt: S.to_bits(torch.from_numpy(a).to(S.TORCH_DT[dt]))
+    a = np.linspace(-0.1, 0.1, T).astype(np.float32)  # w0 - w1 near 0: a fine output grid
+    lg = np.stack([a, np.zeros(T, np.float32)], axis=1)
+    res = oracle_lib.forward(to(x, "bf16"), to(lg, ldt), to(gate, "bf16"), to(up, "bf16"), to(down, "bf16"),
+                             "bf16", ldt, 2, True)
+    Y = oracle_lib.widen(res["Y"], "bf16")
+    y_of_expert = np.where(np.arange(T * 2) < res["offsets"][1], 256.0, -256.0)
+    assert np.array_equal(Y, np.repeat(y_of_expert[:, None], H, axis=1))
+    # the stored weights are the FP32 weights rounded to the logits dtype
+    w32 = res["weights_f32"].reshape(T, 2).astype(np.float64)
+    wc = torch.from_numpy(res["weights_f32"]).to(S.TORCH_DT[ldt]).double().numpy().reshape(T, 2)
+    rnd = lambda v: torch.from_numpy(v).to(torch.bfloat16).double().numpy()
+    sign = np.where(res["indices"].reshape(T, 2) == 0, 256.0, -256.0)  # slot j's expert output
+    want = rnd((sign * wc).sum(axis=1))       # two exact terms: exact in double, rounded once
+    other = rnd((sign * w32).sum(axis=1))
+    got = oracle_lib.widen(res["output"], "bf16")
+    assert np.array_equal(got, np.repeat(want[:, None], H, axis=1))
+    differ = int((want != other).sum())
+    if ldt == "f32":
+        assert differ == 0
+    else:
+        assert differ > T // 8, f"the case must tell the two readings apart ({differ} tokens differ)"
+
+
 # ------------------------------------------------------------------ generator sanity
 def test_edge_workload_has_the_planted_rows():
     cfg = S.CONFIGS["edge_f32"]
