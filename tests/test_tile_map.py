@@ -1,0 +1,138 @@
+"""The grouped GEMMs' work decomposition, modelled on the CPU.
+
+The expert products walk a list of (expert, row range) token tiles that one
+workgroup builds on the device from expert_offsets, and map each workgroup
+id to one (token tile, weight tile) pair, group by group, in runs per XCD
+(csrc/experts.hip build_tiles_kernel, csrc/tiles.h tile_of_block).  These
+tests restate both in Python, integer for integer, and check on random
+routings -- Zipf-skewed, uniform, empty experts, one hot expert -- that
+every row of every expert lies in exactly one token tile of at most BM rows
+and that the launched grid computes every (token tile, weight tile) pair
+exactly once.  Section 5 of the ruDNN user guide requires the dispatch to
+drop no token; a hole or a double count here would drop or double rows.
+"""
+import numpy as np
+import pytest
+
+MAX_TILE_BITS = 26
+
+
+def max_mtiles(N, E, BM):
+    if N <= 0:
+        return 0
+    return min((N + E * (BM - 1)) // BM, N)
+
+
+def build_tiles(offsets, E, N, BM, max_tiles, G):
+    """build_tiles_kernel: per expert, ceil(rows / BM) tiles in ascending
+    expert order, split into ceil(n / G) groups of near-equal size (the first
+    n % ng groups one tile larger); each tile records its group's first tile
+    (26 bits) and size (6 bits)."""
+    tiles = []
+    t = 0
+    for e in range(E):
+        b = min(int(offsets[e]), N)
+        en = max(min(int(offsets[e + 1]), N), b)
+        n = (en - b + BM - 1) // BM
+        ng = (n + G - 1) // G
+        sz = n // ng if ng else 0
+        big = n % ng if ng else 0
+        for j in range(n):
+            if j < big * (sz + 1):
+                first = j // (sz + 1) * (sz + 1)
+                gm = sz + 1
+            else:
+                first = big * (sz + 1) + (j - big * (sz + 1)) // sz * sz
+                gm = sz
+            r = b + j * BM
+            if t < max_tiles:
+                tiles.append((e, r, min(r + BM, en), (t - j + first) | (gm << MAX_TILE_BITS)))
+            t += 1
+    return tiles, min(t, max_tiles)
+
+
+def tile_of_block(bid, nblocks, n_tiles, m_tiles, tiles):
+    live = min(nblocks, m_tiles * n_tiles)
+    if bid >= live:
+        return None
+    q, rem = live // 8, live % 8
+    xcd, loc = bid % 8, bid // 8
+    pid = (xcd * (q + 1) if xcd < rem else rem * (q + 1) + (xcd - rem) * q) + loc
+    g = tiles[pid // n_tiles][3]
+    first_m = g & ((1 << MAX_TILE_BITS) - 1)
+    gm = max(1, min(g >> MAX_TILE_BITS, m_tiles - first_m))
+    in_group = pid - first_m * n_tiles
+    return first_m + in_group % gm, in_group // gm
+
+
+def routing_counts(rng, kind, E, N):
+    if kind == "zipf":
+        w = np.arange(1, E + 1, dtype=np.float64) ** -rng.uniform(0.5, 1.6)
+        return rng.multinomial(N, w / w.sum())
+    if kind == "uniform":
+        return rng.multinomial(N, np.full(E, 1.0 / E))
+    if kind == "holes":
+        w = rng.random(E) * (rng.random(E) < 0.4)
+        if w.sum() == 0:
+            w[rng.integers(E)] = 1.0
+        return rng.multinomial(N, w / w.sum())
+    c = np.zeros(E, np.int64)  # one hot expert
+    c[rng.integers(E)] = N
+    return c
+
+
+def check_cover(counts, BM, G, n_tiles):
+    E = len(counts)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    N = int(offsets[-1])
+    mt = max_mtiles(N, E, BM)
+    tiles, count = build_tiles(offsets, E, N, BM, mt, G)
+    assert count == len(tiles) <= mt
+    # token tiles: every row of every expert exactly once, in its own expert
+    seen = np.zeros(N, np.int64)
+    for e, r0, r1, _ in tiles:
+        assert offsets[e] <= r0 < r1 <= offsets[e + 1] and r1 - r0 <= BM
+        seen[r0:r1] += 1
+    assert (seen == 1).all()
+    # groups: consecutive tiles of one expert, at most G of them
+    for m, (e, _, _, g) in enumerate(tiles):
+        first, gm = g & ((1 << MAX_TILE_BITS) - 1), g >> MAX_TILE_BITS
+        assert 1 <= gm <= G and first <= m < first + gm
+        assert all(tiles[i][0] == e for i in range(first, min(first + gm, count)))
+    # the launched grid: every (token tile, weight tile) pair exactly once
+    nblocks = mt * n_tiles
+    hits = np.zeros((max(count, 1), n_tiles), np.int64)
+    for b in range(nblocks):
+        r = tile_of_block(b, nblocks, n_tiles, count, tiles)
+        if r is not None:
+            hits[r] += 1
+    assert (hits[:count] == 1).all()
+
+
+@pytest.mark.parametrize("G", range(1, 9))
+@pytest.mark.parametrize("kind", ["zipf", "uniform", "holes", "hot"])
+def test_tiles_cover_every_row_and_pair_once(G, kind):
+    rng = np.random.default_rng(100 * G + len(kind))
+    for _ in range(12):
+        E = int(rng.choice([1, 3, 8, 64, 256]))
+        N = int(rng.integers(0, 6000))
+        BM = int(rng.choice([16, 128, 256]))
+        n_tiles = int(rng.integers(1, 20))
+        check_cover(routing_counts(rng, kind, E, N), BM, G, n_tiles)
+
+
+def test_prefill_and_skewed_shapes():
+    """The benchmark's shapes: 49152 rows over 64 experts (11 and 8 weight
+    tiles), 65536 rows over 256 Zipf-skewed experts (16 and 28)."""
+    rng = np.random.default_rng(7)
+    check_cover(routing_counts(rng, "uniform", 64, 49152), 256, 8, 11)
+    check_cover(routing_counts(rng, "uniform", 64, 49152), 256, 8, 8)
+    w = np.arange(1, 257, dtype=np.float64) ** -2.2
+    c = rng.multinomial(65536, w / w.sum())
+    check_cover(c, 256, 8, 16)
+    check_cover(c, 256, 8, 28)
+
+
+def test_group_bits_hold_the_largest_list():
+    # the host refuses lists of 2^26 tiles or more; 6 bits hold sizes up to 63
+    assert max_mtiles((1 << 31) - 1, 4096, 128) < (1 << MAX_TILE_BITS)
