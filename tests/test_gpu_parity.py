@@ -64,6 +64,18 @@ def small_cases():
     ]
 
 
+def deep_cases():
+    """The 64-K kernel's steady state and long tile groups, element by
+    element: H and I multiples of 64 with 6-8 K steps each way (both rings
+    wrap several times, the two-steps-ahead weight loads land in reused
+    slots), and experts owning 9-12 token tiles of 256 rows, so the tile
+    list splits them into two groups of 5-6."""
+    return [
+        S.small_config("pipe64_deep_bf16", T=5000, H=512, I=448, E=2, top_k=1, dtype="bf16", seed=81),
+        S.small_config("pipe64_deep_f16", T=4500, H=448, I=384, E=3, top_k=2, dtype="f16", seed=82),
+    ]
+
+
 # ------------------------------------------------------------------ routing
 @pytest.mark.parametrize("cfg", [
     S.CONFIGS["tiny_f32"],
@@ -157,7 +169,7 @@ def test_invalid_indices_give_nan_rows_without_oob():
 
 
 # ------------------------------------------------------------------ experts
-@pytest.mark.parametrize("cfg", small_cases() + [S.CONFIGS["edge_f32"]], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", small_cases() + deep_cases() + [S.CONFIGS["edge_f32"]], ids=lambda c: c.name)
 def test_experts_parity(cfg):
     log(f"experts parity {cfg.name}")
     x, lg = S.make_tokens(cfg)
@@ -258,7 +270,7 @@ def run_forward_case(cfg, repeat_check=True):
     return out
 
 
-@pytest.mark.parametrize("cfg", small_cases() + [
+@pytest.mark.parametrize("cfg", small_cases() + deep_cases() + [
     S.CONFIGS["edge_f32"],
     S.small_config("edge_norenorm", T=1024, H=256, I=512, E=16, top_k=4, renormalize=False, edge_rows=True,
                    seed=1001),
@@ -323,9 +335,32 @@ def test_errors_surface_as_moeerror():
     assert e.value.name == "MOE_ERR_DEVICE"
 
 
-# ------------------------------------------------------------------ full-size workloads, sampled
-@pytest.mark.parametrize("name,n_sample", [("prefill_bf16", 24), ("decode_bf16", 32), ("skewed_bf16", 12)])
-def test_full_size_sampled(name, n_sample):
+# ------------------------------------------------------------------ full-size workloads
+def tile_covering_tokens(offsets, tor, BM=256):
+    """One token at the first and one at the last row of every BM-row token
+    tile of every expert (the tiles the expert products walk), so every live
+    (expert, token tile) pair of the forward has checked rows."""
+    pick = set()
+    for e in range(len(offsets) - 1):
+        for r0 in range(int(offsets[e]), int(offsets[e + 1]), BM):
+            r1 = min(r0 + BM, int(offsets[e + 1]))
+            pick.add(int(tor[r0]))
+            pick.add(int(tor[r1 - 1]))
+    return np.array(sorted(pick), dtype=np.int64)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["prefill_bf16", "decode_bf16", "skewed_bf16"])
+def test_full_size(name):
+    """The benchmark's workloads at full size, on the kernels and launch
+    configuration the benchmark times.  The fused forward is run, then the
+    same chain as split calls (route, mapping-only dispatch, gate/up through
+    token_of_row, down, combine), whose mapping the test keeps: the two must
+    agree bit for bit, so the split run's tiles are the fused run's.  Routing
+    and dispatch are compared in full; the output is compared against the
+    oracle on every token for prefill and decode, and for the skewed workload
+    on the tokens at the first and last row of every token tile of every
+    expert."""
     cfg = S.CONFIGS[name]
     log(f"full-size {name}: generating inputs on the GPU")
     x, lg = S.make_tokens(cfg, device=DEV)
@@ -334,7 +369,12 @@ def test_full_size_sampled(name, n_sample):
     opts = moe.RoutingOptions(cfg.top_k, cfg.renormalize)
     out = ex.forward(x, lg, opts)
     plan = moe.route(lg, opts)
+    m = plan.dispatch(x, copy_rows=False)
+    h = ex.gate_up_gathered(x, m.token_of_row, m.expert_offsets)
+    split = m.combine(ex.down_proj(h, m.expert_offsets))
     torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), split.view(torch.int16)), "fused and split forwards differ"
+    del h, split
     log(f"full-size {name}: routing parity over all {cfg.T} tokens")
     lgb = host_bits(lg)
     (o_idx, _), near = compare_routing(host_bits(plan.expert_indices()), plan.weights().cpu(), lgb,
@@ -350,18 +390,22 @@ def test_full_size_sampled(name, n_sample):
            "row_of_slot": host_bits(d.row_of_slot), "token_of_row": host_bits(d.token_of_row)}
     compare_dispatch(gpu, *o, xb, gidx, cfg.E)
     del d, gpu, o
-    rng = np.random.default_rng(cfg.seed)
-    cand = np.nonzero(~near)[0]
-    sample = np.sort(rng.choice(cand, size=min(n_sample, len(cand)), replace=False))
+    if name == "skewed_bf16":
+        sample = tile_covering_tokens(host_bits(m.expert_offsets), host_bits(m.token_of_row))
+    else:
+        sample = np.arange(cfg.T)
+    sample = sample[~near[sample]]
     experts = sorted(set(o_idx[sample].reshape(-1).tolist()))
-    log(f"full-size {name}: oracle on {len(sample)} sampled tokens, {len(experts)} experts")
+    log(f"full-size {name}: oracle on {len(sample)} of {cfg.T} tokens, {len(experts)} experts, "
+        f"{NTHREADS} threads")
     g = {e: host_bits(W[0][e]) for e in experts}
     u = {e: host_bits(W[1][e]) for e in experts}
     dn = {e: host_bits(W[2][e]) for e in experts}
     res = oracle.forward(xb[sample], lgb[sample], g, u, dn, cfg.dtype, cfg.logits_dtype, cfg.top_k,
                          cfg.renormalize, NTHREADS)
     assert_close(values(out, cfg.dtype)[sample], oracle.widen(res["output"], cfg.dtype), cfg.dtype,
-                 f"forward {name} (sampled tokens)")
+                 f"forward {name} ({len(sample)} tokens)")
+    log(f"full-size {name}: {len(sample)} tokens match")
     # properties at every token: finite output, bitwise reproducible
     assert torch.isfinite(out.float()).all()
     out2 = ex.forward(x, lg, opts)
