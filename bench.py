@@ -43,7 +43,9 @@ METRIC = "MoE forward tokens/s + TFLOP/s (% bf16 MFMA peak) / HBM GB/s at decode
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
-GEMM_SRC = os.path.join(ROOT, "mixture_experts_layer_route_amd", "csrc", "experts.hip")
+_CSRC = os.path.join(ROOT, "mixture_experts_layer_route_amd", "csrc")
+# every source compiled into the expert GEMM kernels
+GEMM_SRCS = [os.path.join(_CSRC, f) for f in ("experts.hip", "mfma.h", "tiles.h", "moe_internal.h")]
 
 
 def parse():
@@ -76,14 +78,17 @@ def parse():
 
 
 def kernel_hash() -> str:
-    """sha256 prefix of the GEMM source with comments and blank space
-    removed, so an edit of a comment does not retire the counters."""
-    with open(GEMM_SRC) as f:
-        src = f.read()
-    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
-    src = re.sub(r"//[^\n]*", " ", src)
-    src = " ".join(src.split())
-    return hashlib.sha256(src.encode()).hexdigest()[:16]
+    """sha256 prefix of the GEMM kernels' sources (the kernel file and the
+    headers compiled into it) with comments and blank space removed, so an
+    edit of a comment does not retire the counters."""
+    parts = []
+    for path in GEMM_SRCS:
+        with open(path) as f:
+            src = f.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        parts.append(" ".join(src.split()))
+    return hashlib.sha256("\n".join(parts).encode()).hexdigest()[:16]
 
 
 def traffic_for(workload: str):
@@ -114,28 +119,46 @@ def measure(name: str, steps: int, warmup: int, only_forward: bool = False) -> d
     opts = moe.RoutingOptions(cfg.top_k, cfg.renormalize)
     ws = torch.empty(ex.forward_workspace_bytes(cfg.T, cfg.top_k, x.dtype), dtype=torch.uint8, device=dev)
     out = torch.empty_like(x)
+    res = {"workload": name, "cfg": cfg}
+    if not only_forward:
+        res.update(stage_times(moe, ex, x, lg, opts, cfg, steps, warmup))
+
+    # The timed region: W untimed fused forwards, then exactly K, bracketed
+    # by synchronisations; an event before each step gives per-step device
+    # times (their median sits next to the wall-clock mean).  The stage loop
+    # above runs first, so the timed steps do not fall into the first ~30
+    # forwards after the GPU starts working, whose clock is still settling
+    # (a kernel trace of 30 fused, 30 split and 30 fused forwards: gate/up
+    # 606, 554 and 550 us on average).
     for _ in range(warmup):
         ex.forward(x, lg, opts, ws, out)
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     t0 = time.perf_counter()
-    e0.record()
-    for _ in range(steps):
+    for i in range(steps):
+        evs[i].record()
         ex.forward(x, lg, opts, ws, out)
-    e1.record()
+    evs[steps].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    per = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(steps))
     ms_step = wall * 1e3 / steps
-    res = {"workload": name, "cfg": cfg, "ms_per_step": ms_step, "event_ms_per_step": e0.elapsed_time(e1) / steps,
-           "tokens_per_s": cfg.T * steps / wall}
+    res.update({"ms_per_step": ms_step, "event_ms_mean": sum(per) / steps,
+                "event_ms_median": (per[(steps - 1) // 2] + per[steps // 2]) / 2,
+                "tokens_per_s": cfg.T * steps / wall})
     res["tflops"] = cfg.flops() / (ms_step * 1e-3) / 1e12
-    if only_forward:
-        return res
+    return res
 
-    # stage times: the split calls run the kernels of the fused forward
-    # (mapping-only dispatch, gate/up reading the tokens in place), back to
-    # back like the forward steps, with events on the stream every call is
-    # launched on (torch's current stream) and one synchronisation at the end
+
+def stage_times(moe, ex, x, lg, opts, cfg, steps: int, warmup: int) -> dict:
+    """Per-stage times: the split calls run the kernels of the fused forward
+    (mapping-only dispatch, gate/up reading the tokens in place), back to
+    back like the forward steps, with events on the stream every call is
+    launched on (torch's current stream) and one synchronisation at the end;
+    then the split API's copying dispatch alone."""
+    import torch
+
+    dev = x.device
     names = ["route", "dispatch", "experts_gate_up", "experts_down", "combine"]
     acc = {n: 0.0 for n in names}
     ews = torch.empty(moe.load().moe_experts_workspace_bytes(cfg.N, cfg.H, cfg.I, cfg.E, 2 if cfg.dtype == "bf16"
@@ -162,8 +185,8 @@ def measure(name: str, steps: int, warmup: int, only_forward: bool = False) -> d
     for evs in marks:
         for i, n in enumerate(names):
             acc[n] += evs[i].elapsed_time(evs[i + 1])
-    res["stages_ms"] = {n: acc[n] / steps for n in names}
-    # the split API's dispatch, which also copies the rows grouped by expert
+    res = {"stages_ms": {n: acc[n] / steps for n in names}}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     for _ in range(warmup):
         plan.dispatch(x)
     e0.record()
@@ -214,28 +237,29 @@ def hbm_bytes_forward(res: dict) -> float:
     return w + io + inter
 
 
+def oracle_threads() -> int:
+    """Every core this process may run on."""
+    return len(os.sched_getaffinity(0))
+
+
 def cpu_baseline(name: str, target_s: float) -> dict:
+    """The oracle's whole forward on the first n tokens of workload `name`
+    (n sized for about target_s seconds), on every core this process may run
+    on; then its per-stage times on every workload (cpu_stages)."""
     import torch
 
     import moe_synth as S
     import oracle
 
     cfg = S.CONFIGS[name]
-    threads = min(16, oracle.default_threads())
+    threads = oracle_threads()
     x, lg = S.make_tokens(cfg, device="cuda:0")
-    W = S.make_weights(cfg, device="cuda:0")
     xb, lgb = S.to_bits(x), S.to_bits(lg)
     cache = {}
 
     def run(n):
         idx, _, _ = oracle.route(lgb[:n], cfg.logits_dtype, cfg.top_k, cfg.renormalize, threads)
-        need = sorted(set(idx.reshape(-1).tolist()))
-        for e in need:
-            if e not in cache:
-                cache[e] = tuple(S.to_bits(w[e]) for w in W)
-        g = {e: cache[e][0] for e in need}
-        u = {e: cache[e][1] for e in need}
-        d = {e: cache[e][2] for e in need}
+        g, u, d = expert_bits(cfg, sorted(set(idx.reshape(-1).tolist())), cache)
         t0 = time.perf_counter()
         oracle.forward(xb[:n], lgb[:n], g, u, d, cfg.dtype, cfg.logits_dtype, cfg.top_k, cfg.renormalize, threads)
         return time.perf_counter() - t0
@@ -244,11 +268,65 @@ def cpu_baseline(name: str, target_s: float) -> dict:
     dt = run(probe)
     n = int(max(probe, min(cfg.T, probe * target_s / max(dt, 1e-3))))
     dt = run(n)
-    del W
+    cache.clear()
     torch.cuda.empty_cache()
     return {"value": round(n / dt, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"first {n} of {cfg.T} tokens of {name}, whole forward (route, dispatch, experts, "
-                      f"combine), {dt:.1f} s"}
+                      f"combine), {dt:.1f} s on {threads} threads",
+            "stages": cpu_stages(threads)}
+
+
+def expert_bits(cfg, experts, cache):
+    """Host bits of the gate, up and down matrices of `experts`, each drawn on
+    the GPU from its own stream (the values make_weights draws)."""
+    import moe_synth as S
+
+    for e in experts:
+        if e not in cache:
+            cache[e] = tuple(S.to_bits(w) for w in S.make_expert(cfg, e, device="cuda:0"))
+    return ({e: cache[e][0] for e in experts}, {e: cache[e][1] for e in experts},
+            {e: cache[e][2] for e in experts})
+
+
+# tokens of each workload the per-stage oracle timing covers: the small
+# workloads whole, the large ones on their first tokens (seconds each)
+CPU_STAGE_TOKENS = {"tiny_f32": 64, "edge_f32": 1024, "prefill_bf16": 1024, "decode_bf16": 32,
+                    "skewed_bf16": 64}
+
+
+def cpu_stages(threads: int) -> dict:
+    """Wall seconds of each oracle stage (route, dispatch, experts, combine)
+    on every workload, on the first CPU_STAGE_TOKENS tokens of each."""
+    import moe_synth as S
+    import oracle
+
+    out = {}
+    for name, n in CPU_STAGE_TOKENS.items():
+        cfg = S.CONFIGS[name]
+        x, lg = S.make_tokens(cfg, device="cuda:0")
+        n = min(n, cfg.T)
+        xb, lgb = S.to_bits(x[:n]), S.to_bits(lg[:n])
+        t = {}
+        t0 = time.perf_counter()
+        idx, w, _ = oracle.route(lgb, cfg.logits_dtype, cfg.top_k, cfg.renormalize, threads)
+        t["route"] = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        offsets, ros, _, rows = oracle.dispatch(idx, cfg.E, xb, cfg.dtype)
+        t["dispatch"] = time.perf_counter() - t0
+        experts = sorted(e for e in set(idx.reshape(-1).tolist()) if e < cfg.E)
+        g, u, d = expert_bits(cfg, experts, {})
+        t0 = time.perf_counter()
+        Y = oracle.experts(g, u, d, cfg.dtype, rows, offsets, cfg.E, cfg.H, cfg.I, nthreads=threads)
+        t["experts"] = time.perf_counter() - t0
+        del g, u, d
+        t0 = time.perf_counter()
+        oracle.combine(Y, cfg.dtype, ros, w, cfg.logits_dtype, n, cfg.top_k, cfg.H, threads)
+        t["combine"] = time.perf_counter() - t0
+        total = sum(t.values())
+        out[name] = {"tokens": n, "of": cfg.T, "active_experts": len(experts),
+                     "seconds": {k: round(v, 4) for k, v in t.items()}, "total_s": round(total, 4),
+                     "tokens_per_s": round(n / total, 2)}
+    return out
 
 
 def measure_grouped(name: str, steps: int, warmup: int) -> dict:
@@ -396,7 +474,7 @@ def cpu_training_baseline(cfg, target_s: float) -> dict:
     import moe_synth as S
     import oracle
 
-    threads = min(16, oracle.default_threads())
+    threads = oracle_threads()
     x, lg = S.make_tokens(cfg, device="cuda:0")
     gout = S.make_grad_output(cfg, device="cuda:0")
     Wb = [S.to_bits(w) for w in S.make_weights(cfg, device="cuda:0")]
@@ -441,7 +519,9 @@ def stage_gbs(res: dict) -> dict:
 def summary(res: dict) -> dict:
     cfg = res["cfg"]
     d = {"workload": res["workload"], "tokens_per_s": round(res["tokens_per_s"], 1),
-         "ms_per_step": round(res["ms_per_step"], 4), "tflops": round(res["tflops"], 2),
+         "ms_per_step": round(res["ms_per_step"], 4),
+         "event_ms_per_step": {"mean": round(res["event_ms_mean"], 4), "median": round(res["event_ms_median"], 4)},
+         "tflops": round(res["tflops"], 2),
          "pct_bf16_peak": round(100 * res["tflops"] / PEAK_BF16_TFLOPS, 2)}
     if "stages_ms" in res:
         d["stages_ms"] = {k: round(v, 4) for k, v in res["stages_ms"].items()}
@@ -453,6 +533,10 @@ def summary(res: dict) -> dict:
     d["config"] = {"T": cfg.T, "H": cfg.H, "I": cfg.I, "E": cfg.E, "top_k": cfg.top_k,
                    "renormalize": cfg.renormalize, "dtype": cfg.dtype}
     return d
+
+
+def progress(msg: str) -> None:
+    print(f"bench: {msg}", file=sys.stderr, flush=True)
 
 
 def main():
@@ -474,6 +558,7 @@ def main():
         print(json.dumps({"training": measure_training(args.training or args.workload, args.steps, args.warmup,
                                                        None)}), flush=True)
         return
+    progress(f"measuring {args.workload}")
     res = measure(args.workload, args.steps, args.warmup, args.only_forward)
     head = summary(res)
     cfg = res["cfg"]
@@ -485,6 +570,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(res["ms_per_step"], 4),
+        "event_ms_per_step": {"mean": round(res["event_ms_mean"], 4), "median": round(res["event_ms_median"], 4)},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -507,18 +593,22 @@ def main():
         line["secondary"] = {}
         for s in sec:
             torch.cuda.empty_cache()
+            progress(f"measuring {s}")
             r = measure(s, args.steps, args.warmup)
             line["secondary"][s] = summary(r)
             del r
         torch.cuda.empty_cache()
         if args.grouped:
+            progress("measuring the forward with group-limited sigmoid routing")
             line["grouped_routing"] = measure_grouped(args.grouped, args.steps, args.warmup)
             torch.cuda.empty_cache()
         if args.training:
+            progress("measuring the training step")
             line["training"] = measure_training(args.training, args.steps, args.warmup,
                                                 None if args.no_cpu_baseline else args.cpu_seconds)
             torch.cuda.empty_cache()
         if not args.no_cpu_baseline:
+            progress("timing the CPU oracle")
             line["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_seconds)
     if args.calibrate_copy_mib > 0:
         n = args.calibrate_copy_mib << 20

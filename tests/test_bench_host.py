@@ -17,22 +17,40 @@ def test_more_than_one_gpu_exits_with_a_message():
     assert r.stdout == ""
 
 
+def _copies(tmp_path, edit_index=None, edit=lambda s: s):
+    """Copies of the GEMM sources, the one at edit_index passed through edit."""
+    paths = []
+    for i, src in enumerate(bench.GEMM_SRCS):
+        p = tmp_path / os.path.basename(src)
+        text = open(src).read()
+        p.write_text(edit(text) if i == edit_index else text)
+        paths.append(str(p))
+    return paths
+
+
 def test_kernel_hash_ignores_comments_and_layout(tmp_path, monkeypatch):
-    src = open(bench.GEMM_SRC).read()
     h0 = bench.kernel_hash()
-    p = tmp_path / "experts.hip"
-    p.write_text("// a comment\n/* another\n one */\n" + src.replace("\n", "\n\n"))
-    monkeypatch.setattr(bench, "GEMM_SRC", str(p))
-    assert bench.kernel_hash() == h0
-    p.write_text(src + "\nint changed_code;\n")
-    assert bench.kernel_hash() != h0
+    for i in range(len(bench.GEMM_SRCS)):
+        monkeypatch.setattr(bench, "GEMM_SRCS",
+                            _copies(tmp_path, i, lambda s: "// a comment\n/* another\n one */\n" + s.replace("\n", "\n\n")))
+        assert bench.kernel_hash() == h0
+
+
+def test_kernel_hash_covers_every_gemm_source(tmp_path, monkeypatch):
+    """The kernel file and each header compiled into the GEMM kernels: a code
+    edit in any of them changes the hash."""
+    names = [os.path.basename(p) for p in bench.GEMM_SRCS]
+    assert {"experts.hip", "mfma.h", "tiles.h", "moe_internal.h"} <= set(names)
+    h0 = bench.kernel_hash()
+    for i in range(len(bench.GEMM_SRCS)):
+        monkeypatch.setattr(bench, "GEMM_SRCS", _copies(tmp_path, i, lambda s: s + "\nint changed_code;\n"))
+        assert bench.kernel_hash() != h0
 
 
 def test_traffic_only_for_the_counted_source(tmp_path, monkeypatch):
     got = bench.traffic_for("prefill_bf16")
     assert got is None or (isinstance(got, int) and got > 0)
-    p = tmp_path / "experts.hip"
-    p.write_text(open(bench.GEMM_SRC).read() + "\nint changed_code;\n")
-    monkeypatch.setattr(bench, "GEMM_SRC", str(p))
-    assert bench.traffic_for("prefill_bf16") is None
+    for i in range(len(bench.GEMM_SRCS)):
+        monkeypatch.setattr(bench, "GEMM_SRCS", _copies(tmp_path, i, lambda s: s + "\nint changed_code;\n"))
+        assert bench.traffic_for("prefill_bf16") is None
     assert bench.traffic_for("no_such_workload") is None
