@@ -287,6 +287,33 @@ moe_status moe_forward_sigmoid_grouped(const moe_tensor* gate, const moe_tensor*
                                        moe_group_routing_options options, moe_tensor* output,
                                        void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * moe_forward_no_alloc -- moe_forward for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid hipMalloc.  It takes no workspace: the library
+ * keeps a static device array of 64 MiB (67108864 bytes) per device, held
+ * from the library's load until the process ends, and runs moe_forward's
+ * kernels with that array as their workspace.  It calls no hipMalloc,
+ * hipFree or allocating library routine.
+ *   Arguments as for moe_forward, without workspace and workspace_bytes.
+ *   Limit: moe_forward_workspace_bytes(T, H, I, E, top_k, dtype) must not
+ *   exceed 67108864 (e.g. T*top_k rows of H = 4096, I = 1536 in BF16 up to
+ *   about 5900 rows); larger batches get MOE_ERR_WORKSPACE and nothing is
+ *   enqueued.
+ *   The first call on a device looks up that device's array (a host-side
+ *   symbol lookup, no allocation); make one call before capturing a graph
+ *   if that lookup must stay outside the capture.  A device error of the
+ *   stream is reported before shape errors.
+ *   Every call on one device uses the same array, so calls that overlap on
+ *   one device (two streams, or two host threads) race and give undefined
+ *   results: serialise them.  Every value the chain needs zeroed is cleared
+ *   by its own kernels, so the contents left by an earlier call do not
+ *   matter.
+ */
+moe_status moe_forward_no_alloc(const moe_tensor* gate, const moe_tensor* up, const moe_tensor* down,
+                                const moe_tensor* input, const moe_tensor* logits,
+                                moe_routing_options options, moe_tensor* output, void* stream);
+
 /* ------------------------------------------------------------------ */
 /* First-order training (RUDA ruDNN library guide, section 12).          */
 /* The forward keeps what the backward needs (the FP32 pre-activations   */

@@ -42,6 +42,7 @@ EXPORTS = (
     "moe_forward_workspace_bytes",
     "moe_forward",
     "moe_forward_sigmoid_grouped",
+    "moe_forward_no_alloc",
     "moe_router_weights",
     "moe_router_backward",
     "moe_combine_backward",
@@ -114,6 +115,7 @@ def load() -> ctypes.CDLL:
     L.moe_forward_workspace_bytes.restype = sz
     L.moe_forward.argtypes = [P, P, P, P, P, MoeRoutingOptions, P, vp, sz, vp]
     L.moe_forward_sigmoid_grouped.argtypes = [P, P, P, P, P, P, MoeGroupRoutingOptions, P, vp, sz, vp]
+    L.moe_forward_no_alloc.argtypes = [P, P, P, P, P, MoeRoutingOptions, P, vp]
     L.moe_router_weights.argtypes = [P, P, MoeRouterWeightOptions, P, vp]
     L.moe_router_backward.argtypes = [P, P, P, MoeRouterWeightOptions, P, vp]
     L.moe_combine_backward.argtypes = [P, P, P, P, P, P, vp]
@@ -126,7 +128,7 @@ def load() -> ctypes.CDLL:
     L.moe_status_string.restype = ctypes.c_char_p
     for f in ("moe_route", "moe_route_sigmoid_grouped", "moe_dispatch", "moe_experts_forward",
               "moe_experts_gate_up", "moe_experts_gate_up_gathered", "moe_experts_down", "moe_combine",
-              "moe_forward", "moe_forward_sigmoid_grouped", "moe_router_weights", "moe_router_backward",
+              "moe_forward", "moe_forward_sigmoid_grouped", "moe_forward_no_alloc", "moe_router_weights", "moe_router_backward",
               "moe_combine_backward", "moe_experts_forward_training", "moe_experts_backward",
               "moe_dispatch_backward"):
         getattr(L, f).restype = i32

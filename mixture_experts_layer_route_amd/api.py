@@ -376,6 +376,18 @@ class SwiGluExperts:
         _lib.check(st, "moe_forward")
         return out
 
+    def forward_no_alloc(self, input: torch.Tensor, logits: torch.Tensor, options: RoutingOptions,
+                         out: torch.Tensor) -> torch.Tensor:
+        """moe_forward without a workspace (moe_forward_no_alloc): the library
+        runs on its static per-device scratch array; the caller provides out."""
+        L = _lib.load()
+        dx, dl, do = _desc(input), _desc(logits), _desc(out)
+        g, u, d = self._dw
+        st = L.moe_forward_no_alloc(_ref(g), _ref(u), _ref(d), _ref(dx), _ref(dl), options._c(), _ref(do),
+                                    _stream(input.device))
+        _lib.check(st, "moe_forward_no_alloc")
+        return out
+
     def forward_sigmoid_grouped(self, input: torch.Tensor, logits: torch.Tensor, bias: torch.Tensor | None,
                                 options: GroupRoutingOptions, workspace: torch.Tensor | None = None,
                                 out: torch.Tensor | None = None) -> torch.Tensor:

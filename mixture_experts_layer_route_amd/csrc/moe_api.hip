@@ -8,6 +8,8 @@
 // are reported as errors rather than computed).
 #include <string.h>
 
+#include <mutex>
+
 #include "moe_internal.h"
 
 using namespace moe;
@@ -545,7 +547,7 @@ template <typename RouteFn>
 moe_status forward_chain(const moe_tensor* gate, const moe_tensor* up, const moe_tensor* down,
                          const moe_tensor* input, const moe_tensor* logits, const moe_tensor* bias, int64_t k,
                          moe_tensor* output, void* workspace, size_t workspace_bytes, void* stream,
-                         RouteFn route) {
+                         RouteFn route, bool check_workspace_device = true) {
     const int64_t E = gate->dims[0], I = gate->dims[1], H = gate->dims[2];
     const int64_t T = input->dims[0];
     if (input->dims[1] != H) return MOE_ERR_SHAPE;
@@ -559,7 +561,8 @@ moe_status forward_chain(const moe_tensor* gate, const moe_tensor* up, const moe
     if (T == 0) return MOE_OK;
     hipStream_t s = (hipStream_t)stream;
     MOE_TRY(check_devices(s, {gate->data, up->data, down->data, input->data, logits->data,
-                              bias ? bias->data : logits->data, output->data, workspace}));
+                              bias ? bias->data : logits->data, output->data,
+                              check_workspace_device ? workspace : nullptr}));
     char* ws = (char*)workspace;
     uint32_t* idx = (uint32_t*)(ws + l.idx);
     void* w = ws + l.w;
@@ -625,6 +628,71 @@ moe_status moe_forward_sigmoid_grouped(const moe_tensor* gate, const moe_tensor*
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------- forward without allocation
+// moe_forward for callers that cannot allocate: the forward's workspace is a
+// static device array of kNoAllocScratchBytes, of which every device the
+// library runs on holds its own copy until the process ends.  Host code never
+// passes the array's name to a kernel (on the host it only stands in for the
+// symbol): the device address comes from hipGetSymbolAddress, taken once per
+// device with that device current, and is kept per device.
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxScratchDevices = 256;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxScratchDevices];
+
+// The device address of device dev's scratch array (set up on the first call
+// on that device).
+moe_status scratch_of_device(int dev, void** ptr) {
+    if (dev < 0 || dev >= kMaxScratchDevices) return MOE_ERR_DEVICE;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        int cur = -1;
+        if (hipGetDevice(&cur) != hipSuccess) {
+            (void)hipGetLastError();
+            return MOE_ERR_DEVICE;
+        }
+        if (cur != dev && hipSetDevice(dev) != hipSuccess) {
+            (void)hipGetLastError();
+            return MOE_ERR_DEVICE;
+        }
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) (void)hipSetDevice(cur);
+        if (e != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return MOE_ERR_LAUNCH;
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return MOE_OK;
+}
+}  // namespace
+
+extern "C" moe_status moe_forward_no_alloc(const moe_tensor* gate, const moe_tensor* up, const moe_tensor* down,
+                                           const moe_tensor* input, const moe_tensor* logits,
+                                           moe_routing_options options, moe_tensor* output, void* stream) {
+    MOE_TRY(check_forward_tensors(gate, up, down, input, logits, output));
+    const int64_t E = gate->dims[0];
+    if (logits->dims[1] == E && (options.top_k < 1 || options.top_k > E)) return MOE_ERR_TOP_K;
+    if (options.renormalize != 0 && options.renormalize != 1) return MOE_ERR_INVALID_ARGUMENT;
+    // the stream's device, and that device's array (set up on the first call
+    // there); then the checks and launches of moe_forward, with the array as
+    // the workspace: a batch whose forward workspace exceeds it gets
+    // MOE_ERR_WORKSPACE
+    int dev = 0;
+    MOE_TRY(stream_device((hipStream_t)stream, &dev));
+    void* ws = nullptr;
+    MOE_TRY(scratch_of_device(dev, &ws));
+    return forward_chain(gate, up, down, input, logits, nullptr, options.top_k, output, ws, kNoAllocScratchBytes,
+                         stream, [&](uint32_t* idx, void* w, hipStream_t s) {
+                             return enqueue_route(logits, options, idx, w, s);
+                         }, false);
+}
 
 // ---------------------------------------------------------------- first-order training
 namespace {
