@@ -13,13 +13,21 @@ constexpr int kGroupM = MOE_GROUP_M;
 static_assert(kGroupM >= 1 && kGroupM < 64, "group size is packed in 6 bits");
 constexpr int64_t kMaxTiles = int64_t(1) << 26;  // tile index packed in 26 bits
 
-// Upper bound of the M-tiles of BM rows that N rows over E experts produce.
-int64_t max_mtiles(int64_t N, int64_t E, int BM);
-// Writes the (expert, row_begin, row_end, group) M-tile list of BM-row tiles
-// for expert_offsets into tiles (at most max_tiles entries) and its length
-// into *count, in one workgroup on stream s.
+// An expert with 1..stream_rows rows gets a single stream tile (its whole row
+// range), marked by this bit in the tile's expert field; the others get
+// BM-row tiles.  stream_rows = 0: BM-row tiles only.
+constexpr int kStreamTileFlag = 1 << 30;
+
+// Upper bound of the M-tiles that N rows over E experts produce: BM-row
+// tiles only (each expert adds at most one partial tile), or with stream
+// tiles (an expert of 1..stream_rows rows adds one, a larger one
+// ceil(c / BM) <= 1 + floor(c / BM)), so at most E + floor(N / BM).
+int64_t max_mtiles(int64_t N, int64_t E, int BM, int stream_rows = 0);
+// Writes the (expert, row_begin, row_end, group) M-tile list for
+// expert_offsets into tiles (at most max_tiles entries) and its length into
+// *count, in one workgroup on stream s.
 hipError_t launch_build_tiles(const uint32_t* offsets, int E, int64_t N, int BM, int64_t max_tiles, int4* tiles,
-                              uint32_t* count, hipStream_t s);
+                              uint32_t* count, hipStream_t s, int stream_rows = 0);
 
 // ------------------------------------------------------------------ tile order
 // Workgroup b -> (token tile, weight tile).  The grid is sized for the most

@@ -76,6 +76,19 @@ def deep_cases():
     ]
 
 
+def stream_cases():
+    """The 64-K kernel's per-expert tile choice: experts of at most 64 rows run
+    as stream tiles (64 token slots against 256 weight rows), the others on
+    256-row tiles, in the same launch.  All-stream batches (decode-sized), f16,
+    and a Zipf-skewed batch mixing both (1024 tokens, top-8 of 256 experts)."""
+    return [
+        S.small_config("stream_decode_bf16", T=32, H=256, I=192, E=16, top_k=4, dtype="bf16", seed=83),
+        S.small_config("stream_f16", T=60, H=128, I=128, E=8, top_k=2, dtype="f16", logits_dtype="f32", seed=84),
+        S.small_config("stream_mixed_zipf_bf16", T=1024, H=512, I=256, E=256, top_k=8, dtype="bf16", zipf_s=1.1,
+                       seed=85),
+    ]
+
+
 # ------------------------------------------------------------------ routing
 @pytest.mark.parametrize("cfg", [
     S.CONFIGS["tiny_f32"],
@@ -169,7 +182,8 @@ def test_invalid_indices_give_nan_rows_without_oob():
 
 
 # ------------------------------------------------------------------ experts
-@pytest.mark.parametrize("cfg", small_cases() + deep_cases() + [S.CONFIGS["edge_f32"]], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", small_cases() + deep_cases() + stream_cases() + [S.CONFIGS["edge_f32"]],
+                         ids=lambda c: c.name)
 def test_experts_parity(cfg):
     log(f"experts parity {cfg.name}")
     x, lg = S.make_tokens(cfg)
@@ -184,6 +198,25 @@ def test_experts_parity(cfg):
     gy = ex.forward_dispatched(g_rows, g_off)
     torch.cuda.synchronize()
     assert_close(values(gy, cfg.dtype), oracle.widen(Y, cfg.dtype), cfg.dtype, f"expert outputs {cfg.name}")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_experts_tile_choice_at_its_boundaries(dt):
+    """Experts of 1, 63, 64 (stream tiles), 65, 200, 256, 257 and 300 rows
+    (256-row tiles) and an empty one, in one launch, against the oracle."""
+    counts = [64, 65, 1, 0, 200, 257, 63, 256, 300, 1]
+    E, H, I = len(counts), 128, 192
+    cfg = S.small_config(f"boundary_{dt}", T=sum(counts), H=H, I=I, E=E, top_k=1, dtype=dt, seed=86)
+    x, _ = S.make_tokens(cfg)
+    W = S.make_weights(cfg)
+    rows = host_bits(x)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.uint32)
+    Y = oracle.experts(*[host_bits(w) for w in W], dt, rows, offsets, E, H, I, nthreads=NTHREADS)
+    ex = moe.SwiGluExperts(*[w.to(DEV) for w in W])
+    g_off = torch.from_numpy(offsets.view(np.int32)).view(torch.uint32).to(DEV)
+    gy = ex.forward_dispatched(x.to(DEV), g_off)
+    torch.cuda.synchronize()
+    assert_close(values(gy, dt), oracle.widen(Y, dt), dt, f"expert outputs, tile boundaries ({dt})")
 
 
 @pytest.mark.parametrize("cfg", [
@@ -270,7 +303,7 @@ def run_forward_case(cfg, repeat_check=True):
     return out
 
 
-@pytest.mark.parametrize("cfg", small_cases() + deep_cases() + [
+@pytest.mark.parametrize("cfg", small_cases() + deep_cases() + stream_cases() + [
     S.CONFIGS["edge_f32"],
     S.small_config("edge_norenorm", T=1024, H=256, I=512, E=16, top_k=4, renormalize=False, edge_rows=True,
                    seed=1001),
@@ -288,6 +321,7 @@ def test_forward_parity(cfg):
     S.small_config("split_small", T=20, H=96, I=64, E=16, top_k=2, dtype="f16", seed=43),
     S.small_config("split_f32", T=130, H=40, I=24, E=4, top_k=2, dtype="f32", seed=44),
     S.small_config("split_edge", T=300, H=64, I=96, E=16, top_k=4, dtype="bf16", edge_rows=True, seed=45),
+    S.small_config("split_stream_mixed", T=1024, H=512, I=256, E=256, top_k=8, dtype="bf16", zipf_s=1.1, seed=46),
 ], ids=lambda c: c.name)
 def test_split_stages_equal_fused_forward(cfg):
     log(f"split == fused {cfg.name}")

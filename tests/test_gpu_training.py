@@ -179,6 +179,9 @@ EXPERT_CASES = [
     # more weight-gradient tiles (16 experts x 8 x 8 of 128 x 256) than the
     # GPU runs at once
     S.small_config("ex_many_tiles_bf16", T=1100, H=2048, I=512, E=16, top_k=2, dtype="bf16", seed=409),
+    # experts of at most 64 rows: stream tiles of the 64-K kernel, which also
+    # save the FP32 pre-activations
+    S.small_config("ex_stream_bf16", T=40, H=128, I=192, E=16, top_k=4, dtype="bf16", seed=410),
 ]
 
 

@@ -3,36 +3,51 @@
 The expert products walk a list of (expert, row range) token tiles that one
 workgroup builds on the device from expert_offsets, and map each workgroup
 id to one (token tile, weight tile) pair, group by group, in runs per XCD
-(csrc/experts.hip build_tiles_kernel, csrc/tiles.h tile_of_block).  These
-tests restate both in Python, integer for integer, and check on random
+(csrc/experts.hip build_tiles_kernel, csrc/tiles.h tile_of_block).  With
+stream tiles enabled, an expert with at most SR rows gets one stream tile
+(flagged in bit 30 of its expert field) and the others tiles of BM rows.
+These tests restate both in Python, integer for integer, and check on random
 routings -- Zipf-skewed, uniform, empty experts, one hot expert -- that
-every row of every expert lies in exactly one token tile of at most BM rows
-and that the launched grid computes every (token tile, weight tile) pair
-exactly once.  Section 5 of the ruDNN user guide requires the dispatch to
-drop no token; a hole or a double count here would drop or double rows.
+every row of every expert lies in exactly one token tile of at most BM (or
+SR) rows, that the host's bound on the list length holds, and that the
+launched grid computes every (token tile, weight tile) pair exactly once.
+Section 5 of the ruDNN user guide requires the dispatch to drop no token; a
+hole or a double count here would drop or double rows.
 """
 import numpy as np
 import pytest
 
 MAX_TILE_BITS = 26
+STREAM_FLAG = 1 << 30
 
 
-def max_mtiles(N, E, BM):
+def max_mtiles(N, E, BM, SR=0):
+    """The host's bound on the list length.  Without stream tiles each expert
+    adds at most one partial tile; with them an expert of at most SR rows
+    adds one tile and a larger one ceil(c / BM) <= 1 + floor(c / BM)."""
     if N <= 0:
         return 0
+    if SR:
+        return min(N, E + N // BM)
     return min((N + E * (BM - 1)) // BM, N)
 
 
-def build_tiles(offsets, E, N, BM, max_tiles, G):
-    """build_tiles_kernel: per expert, ceil(rows / BM) tiles in ascending
-    expert order, split into ceil(n / G) groups of near-equal size (the first
-    n % ng groups one tile larger); each tile records its group's first tile
-    (26 bits) and size (6 bits)."""
+def build_tiles(offsets, E, N, BM, max_tiles, G, SR=0):
+    """build_tiles_kernel: per expert, in ascending expert order, one stream
+    tile if it holds 1..SR rows, else ceil(rows / BM) tiles split into
+    ceil(n / G) groups of near-equal size (the first n % ng groups one tile
+    larger); each tile records its group's first tile (26 bits) and size
+    (6 bits)."""
     tiles = []
     t = 0
     for e in range(E):
         b = min(int(offsets[e]), N)
         en = max(min(int(offsets[e + 1]), N), b)
+        if 0 < en - b <= SR:
+            if t < max_tiles:
+                tiles.append((e | STREAM_FLAG, b, en, t | (1 << MAX_TILE_BITS)))
+            t += 1
+            continue
         n = (en - b + BM - 1) // BM
         ng = (n + G - 1) // G
         sz = n // ng if ng else 0
@@ -81,24 +96,31 @@ def routing_counts(rng, kind, E, N):
     return c
 
 
-def check_cover(counts, BM, G, n_tiles):
+def check_cover(counts, BM, G, n_tiles, SR=0):
     E = len(counts)
     offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
     N = int(offsets[-1])
-    mt = max_mtiles(N, E, BM)
-    tiles, count = build_tiles(offsets, E, N, BM, mt, G)
+    mt = max_mtiles(N, E, BM, SR)
+    # the bound holds without truncation: build with room to spare
+    tiles, count = build_tiles(offsets, E, N, BM, mt + 10 ** 6, G, SR)
     assert count == len(tiles) <= mt
-    # token tiles: every row of every expert exactly once, in its own expert
+    # token tiles: every row of every expert exactly once, in its own expert;
+    # stream tiles hold a whole expert of 1..SR rows, the others <= BM rows
     seen = np.zeros(N, np.int64)
-    for e, r0, r1, _ in tiles:
-        assert offsets[e] <= r0 < r1 <= offsets[e + 1] and r1 - r0 <= BM
+    for x, r0, r1, _ in tiles:
+        e = x & ~STREAM_FLAG
+        assert offsets[e] <= r0 < r1 <= offsets[e + 1]
+        if x & STREAM_FLAG:
+            assert SR and (r0, r1) == (offsets[e], offsets[e + 1]) and r1 - r0 <= SR
+        else:
+            assert r1 - r0 <= BM and offsets[e + 1] - offsets[e] > SR
         seen[r0:r1] += 1
     assert (seen == 1).all()
     # groups: consecutive tiles of one expert, at most G of them
-    for m, (e, _, _, g) in enumerate(tiles):
+    for m, (x, _, _, g) in enumerate(tiles):
         first, gm = g & ((1 << MAX_TILE_BITS) - 1), g >> MAX_TILE_BITS
         assert 1 <= gm <= G and first <= m < first + gm
-        assert all(tiles[i][0] == e for i in range(first, min(first + gm, count)))
+        assert all(tiles[i][0] == x for i in range(first, min(first + gm, count)))
     # the launched grid: every (token tile, weight tile) pair exactly once
     nblocks = mt * n_tiles
     hits = np.zeros((max(count, 1), n_tiles), np.int64)
@@ -119,6 +141,29 @@ def test_tiles_cover_every_row_and_pair_once(G, kind):
         BM = int(rng.choice([16, 128, 256]))
         n_tiles = int(rng.integers(1, 20))
         check_cover(routing_counts(rng, kind, E, N), BM, G, n_tiles)
+
+
+@pytest.mark.parametrize("kind", ["zipf", "uniform", "holes", "hot"])
+def test_stream_and_block_tiles_cover_every_row_and_pair_once(kind):
+    """The 64-K kernel's list: stream tiles for experts of at most 64 rows,
+    256-row tiles for the others."""
+    rng = np.random.default_rng(300 + len(kind))
+    for _ in range(40):
+        E = int(rng.choice([1, 3, 8, 64, 128, 256]))
+        N = int(rng.integers(0, 9000))
+        check_cover(routing_counts(rng, kind, E, N), 256, 8, int(rng.integers(1, 20)), SR=64)
+
+
+def test_stream_bound_is_tight_and_holds_at_the_edges():
+    """Experts of exactly SR and SR+1 rows, and of 257 rows (two tiles each,
+    where the bound E + N / 256 is reached exactly)."""
+    for c in (1, 63, 64, 65, 255, 256, 257, 511, 512, 513):
+        for E in (1, 7, 100):
+            check_cover(np.full(E, c), 256, 8, 3, SR=64)
+    counts = np.full(100, 257)
+    offsets = np.concatenate([[0], np.cumsum(counts)])
+    tiles, count = build_tiles(offsets, 100, int(offsets[-1]), 256, 10 ** 6, 8, 64)
+    assert count == max_mtiles(int(offsets[-1]), 100, 256, 64) == 200
 
 
 def test_prefill_and_skewed_shapes():
