@@ -318,7 +318,7 @@ __global__ __launch_bounds__(WGM* WGN* kWave) void grouped_gemm_kernel(
 // tile, a ring of 4 LDS stages of 32 K-elements each, filled by direct
 // global->LDS loads (global_load_lds_dwordx4: each wave instruction writes
 // 1 KB of LDS, lane l at +16 l), issued three stages ahead.  Every LDS row is
-// 64 bytes; the 16-byte chunk c of row r sits at chunk c ^ ((r >> 1) & 3), so
+// 64 bytes; the 16-byte chunk c of row r sits at chunk c ^ swz64(r), so
 // the 16 rows a fragment read touches spread over all banks.  While the
 // matrix cores work on step k, the wave reads the fragments of step k+1 into
 // a second register set; one barrier per step publishes the next stage.
@@ -478,7 +478,7 @@ __global__ __launch_bounds__(WGM* WGN* kWave, MOE_P_MINB) void grouped_gemm_pipe
 #pragma unroll
     for (int j = 0; j < LPW; ++j) {
         const int row = (wid * LPW + j) * 16 + (lane >> 2);  // stage row 0..511
-        const int lc = (lane & 3) ^ ((row >> 1) & 3);        // logical chunk for this physical slot
+        const int lc = (lane & 3) ^ swz64(row);              // logical chunk for this physical slot
         const S* p;
         if (row < kPipeBM) {
             p = A + src_row(a_rows, a_nrows, min(r0 + row, r1 - 1)) * K;
@@ -495,8 +495,8 @@ __global__ __launch_bounds__(WGM* WGN* kWave, MOE_P_MINB) void grouped_gemm_pipe
     const uint32_t smem_base = lds_offset(smem) + wid * LPW * 1024;
     // fragment rows; the swizzle term depends only on the lane for every block
     const int frow = lane & 31;
-    const int sw0 = (((lane >> 5) + 0) ^ ((frow >> 1) & 3)) * 16;  // K half 0 of a stage
-    const int sw1 = (((lane >> 5) + 2) ^ ((frow >> 1) & 3)) * 16;  // K half 1
+    const int sw0 = (((lane >> 5) + 0) ^ swz64(frow)) * 16;  // K half 0 of a stage
+    const int sw1 = (((lane >> 5) + 2) ^ swz64(frow)) * 16;  // K half 1
     const int fa0 = (wm * WTM + frow) * ROWB;
     int fb[NB];
 #pragma unroll
@@ -619,7 +619,7 @@ __global__ __launch_bounds__(WGM* WGN* kWave, MOE_P_MINB) void grouped_gemm_pipe
 // of 8 waves and 160 KB of LDS.  Such a product is a stream of weight rows
 // (each is used by a few tokens only), so the tile is built for bytes in
 // flight: a ring of 4 stages of 40 KB (64 token rows and 256 weight rows of
-// 128 bytes, chunk c of row r at c ^ (r & 7)), filled by direct global->LDS
+// 128 bytes, chunk c of row r at c ^ swz128(r)), filled by direct global->LDS
 // loads issued 3 steps ahead, 120 KB in flight per CU.
 //   Each wave owns 32 weight rows -- it loads them and only it reads them --
 // and one 32x32 MFMA block of them: for gate/up, rows 0-15 are gate rows
@@ -664,13 +664,13 @@ __device__ __forceinline__ void stream_tile(const typename DT::storage* __restri
         const int mrow0 = min(wi0 + (GATEUP ? 8 * (j & 1) : 8 * j), NOUT - 1);  // base row of the piece
         const int mrow = min(mrow0 + row_l, NOUT - 1);
         wbase[j] = (const char*)(m + ((int64_t)e * NOUT + mrow0) * K);
-        woff[j] = (uint32_t)((int64_t)(mrow - mrow0) * K * (int64_t)sizeof(S)) + (((lane & 7) ^ (brow & 7)) << 4);
+        woff[j] = (uint32_t)((int64_t)(mrow - mrow0) * K * (int64_t)sizeof(S)) + (((lane & 7) ^ swz128(brow)) << 4);
     }
     // token piece: rows 8 wid + row_l of the 64 token slots, clamped to the
     // tile's last row (slots past it are computed but never stored)
     const int trow = 8 * wid + row_l;
     const uint32_t toff = (uint32_t)(src_row(a_rows, a_nrows, min(r0 + trow, r1 - 1)) * K * (int64_t)sizeof(S)) +
-                          (((lane & 7) ^ (trow & 7)) << 4);
+                          (((lane & 7) ^ swz128(trow)) << 4);
     const uint32_t lds0 = lds_offset(smem);
     auto issue = [&](int kt) {
         const int ks = min(kt, nk - 1);                           // past the end: re-load the last step
@@ -697,7 +697,7 @@ __device__ __forceinline__ void stream_tile(const typename DT::storage* __restri
         const unsigned char* st = smem + (kt % NS) * STAGE;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const int c = ((2 * q + kg) ^ (frow & 7)) << 4;
+            const int c = ((2 * q + kg) ^ swz128(frow)) << 4;
             const uint4 w = *(const uint4*)(st + TOK + wid * 4096 + frow * ROWB + c);
             const uint4 t0 = *(const uint4*)(st + frow * ROWB + c);
             const uint4 t1 = *(const uint4*)(st + (32 + frow) * ROWB + c);
@@ -744,7 +744,7 @@ __device__ __forceinline__ void stream_tile(const typename DT::storage* __restri
 // ------------------------------------------------------------------ pipelined grouped GEMM, 64-wide K stages
 // The same 256x256 tile and 8 waves of 128x64 as above, with 64-element K
 // stages: every LDS row holds 128 bytes (one whole cache line of each operand
-// row per stage, chunk c of row r at c ^ (r & 7)), so each DMA instruction
+// row per stage, chunk c of row r at c ^ swz128(r)), so each DMA instruction
 // moves 8 rows x 128 bytes, and one barrier covers 64 K instead of 32.
 // The token rows and the weight rows have rings of their own in the 160 KB
 // of LDS: 2 slots of 32 KB for the tokens, 3 for the weights, so the weight
@@ -805,7 +805,7 @@ __global__ __launch_bounds__(WGM* WGN* kWave, 1) void grouped_gemm_pipe64_kernel
     int e, r0, r1, n0;
     // DMA piece j of this wave, per operand: rows (wid * LPO + j) * 8 + lane / 8
     // of the operand tile, the lane's 16-byte physical slot (lane & 7) holding
-    // logical chunk slot ^ (row & 7).  Each piece is addressed as a
+    // logical chunk slot ^ swz128(row).  Each piece is addressed as a
     // wave-uniform base in scalar registers (the token buffer, or the weight
     // matrix's rows of this tile), advanced a step at a time, plus a 32-bit
     // per-lane offset; the host only picks this kernel when every offset fits
@@ -823,7 +823,7 @@ __global__ __launch_bounds__(WGM* WGN* kWave, 1) void grouped_gemm_pipe64_kernel
         for (int j = 0; j < LPO; ++j) {
             const int prow0 = (wid * LPO + j) * 8;  // first row of the piece (wave-uniform)
             const int row = prow0 + (lane >> 3);
-            const int lc = (lane & 7) ^ (row & 7);
+            const int lc = (lane & 7) ^ swz128(row);
             voffa[j] = (uint32_t)(src_row(a_rows, a_nrows, min(r0 + row, r1 - 1)) * K * (int64_t)sizeof(S)) + lc * 16;
             const S* m = (GATEUP && prow0 >= BN_OUT) ? B1 : B0;
             basb[j] = (const char*)(m + ((int64_t)e * NOUT + n0) * K);
@@ -834,7 +834,7 @@ __global__ __launch_bounds__(WGM* WGN* kWave, 1) void grouped_gemm_pipe64_kernel
     setup(m_idx, n_idx);
     const uint32_t lds_a = lds_offset(smem) + wid * LPO * 1024;
     const uint32_t lds_b = lds_a + NA * SLOT;
-    // fragment rows are 32-aligned blocks plus (lane & 31), so row & 7 == lane & 7
+    // fragment rows are 32-aligned blocks plus (lane & 31), whose chunk key is that of lane & 31
     const int frow = lane & 31, kg = lane >> 5;
     const int fa0 = (wm * WTM + frow) * ROWB;
     int fb[NB];
@@ -849,7 +849,7 @@ __global__ __launch_bounds__(WGM* WGN* kWave, 1) void grouped_gemm_pipe64_kernel
     }
     int csw[4];  // byte offset of sub-step q's chunk in this lane's rows
 #pragma unroll
-    for (int q = 0; q < 4; ++q) csw[q] = ((2 * q + kg) ^ (frow & 7)) * 16;
+    for (int q = 0; q < 4; ++q) csw[q] = ((2 * q + kg) ^ swz128(frow)) * 16;
 
     f32x16_t acc[MB][NB];
     uint4 av[2][MB], bv[2][NB];

@@ -86,6 +86,24 @@ __device__ __forceinline__ void save_preact(float* __restrict__ gu, int64_t row,
     *(float4*)(p + I) = make_float4(u[0], u[1], u[2], u[3]);
 }
 
+// ------------------------------------------------------------------ LDS row layout
+// Rows of 128 bytes (64 K-values of 16 bits) hold their 16-byte chunk c at
+// chunk slot c ^ swz128(r).  gfx950's LDS has 64 banks of 4 bytes and
+// serves a 16-byte-per-lane read 16 lanes per clock, so a read is
+// conflict-free when its 16 lanes reach 16 different 4-bank groups; row r
+// covers groups 8 (r % 2) + 0..7.  The fragment reads of the grouped GEMMs
+// take one logical chunk from 16 consecutive rows per 16 lanes: with the key
+// r & 7, rows r and r + 8 collide (2-way conflicts, measured at 127 B/clk
+// per CU); flipping bit 0 of the key for rows with bit 3 set separates them
+// (measured at 254 B/clk, the full 256).  The key of a row 32 i + f is that
+// of f.
+__device__ __forceinline__ int swz128(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+// Rows of 64 bytes (32 K-values) cover groups 4 (r % 4) + 0..3, so the 16
+// rows one read takes a chunk from are conflict-free with the key
+// (r >> 2) & 3 (with (r >> 1) & 3, rows r and r + 8 collide).  The key of a
+// row 32 i + f is that of f.
+__device__ __forceinline__ int swz64(int r) { return (r >> 2) & 3; }
+
 // ------------------------------------------------------------------ LDS pipelines
 // The stage ring is driven by hand: the DMA loads, the vmcnt waits and the
 // barriers below are the whole ordering protocol of the pipeline, so they

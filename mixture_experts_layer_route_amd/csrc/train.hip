@@ -357,7 +357,7 @@ __device__ __forceinline__ uint2 keep_first(uint2 v, int n) {
 // three column-operand slots of 16 KB), so two workgroups share a CU and one
 // computes while the other stores its tile.  Layouts per slot:
 //   K-contiguous row operand: 128 rows x 64 bytes, chunk c of row r at
-//     c ^ ((r >> 1) & 3);
+//     c ^ swz64(r);
 //   K-outer row operand (weight gradients): 32 K-rows x 256 bytes (128
 //     values), chunk c of K-row r at c ^ (4 (r & 3));
 //   K-outer column operand: 32 K-rows x 512 bytes, chunk c at c ^ ((r & 7) << 2).
@@ -440,7 +440,7 @@ __global__ __launch_bounds__(kT2Waves* kWave, 2) void train_pipe2_kernel(TrainGe
         } else {
             // 16 rows x 64 bytes per piece
             const int row = (wid * LPA + j) * 16 + (lane >> 2);
-            const int lc = (lane & 3) ^ ((row >> 1) & 3);
+            const int lc = (lane & 3) ^ swz64(row);
             base = A + (int64_t)m0 * lda;
             off = (uint32_t)(min(row, m1 - m0 - 1) * lda) * (uint32_t)sizeof(S) +
                   (uint32_t)min(64 * s + lc * 16, ke * (int)sizeof(S) - 16);
@@ -499,7 +499,7 @@ __global__ __launch_bounds__(kT2Waves* kWave, 2) void train_pipe2_kernel(TrainGe
     // K-contiguous row operand: row 32 i + frow, logical chunk 2 q + kg
     int kca[2];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) kca[q] = frow * 64 + (((2 * q + kg) ^ ((frow >> 1) & 3)) * 16);
+    for (int q = 0; q < 2; ++q) kca[q] = frow * 64 + (((2 * q + kg) ^ swz64(frow)) * 16);
 
     f32x16_t acc[MB][NB];
     uint4 av[2][MB], bv[2][NB];
@@ -522,7 +522,7 @@ __global__ __launch_bounds__(kT2Waves* kWave, 2) void train_pipe2_kernel(TrainGe
                     av[set][i].w = v.y;
                 }
             } else {
-                // rows 32 r + frow keep (row >> 1) & 3 of frow
+                // rows 32 r + frow keep the chunk key of frow
                 uint4 v = *(const uint4*)(base + kca[q] + r * 32 * 64);
                 if (MASK && kv < 32 && 16 * q + 8 * kg >= kv) v = make_uint4(0, 0, 0, 0);
                 av[set][r] = v;

@@ -23,6 +23,10 @@ LDS = 160 * 1024
 U32 = 1 << 32
 
 
+def swz128(r):
+    return (r & 7) ^ ((r >> 3) & 1)
+
+
 def weight_offsets(gateup, n0, NOUT, K, wid, lane, j):
     """(base row of the piece, per-lane byte offset before the 32-bit cast,
     the matrix row the lane loads) for weight piece j of wave wid."""
@@ -31,7 +35,7 @@ def weight_offsets(gateup, n0, NOUT, K, wid, lane, j):
     brow = 8 * j + row_l
     mrow0 = min(wi0 + (8 * (j & 1) if gateup else 8 * j), NOUT - 1)
     mrow = min(mrow0 + row_l, NOUT - 1)
-    off = (mrow - mrow0) * K * 2 + (((lane & 7) ^ (brow & 7)) << 4)
+    off = (mrow - mrow0) * K * 2 + (((lane & 7) ^ swz128(brow)) << 4)
     return mrow0, off, mrow
 
 
@@ -56,14 +60,14 @@ def check_tile(gateup, NOUT, K, n_idx, r0, r1, x_rows):
             trow = 8 * wid + (lane >> 3)
             row = min(r0 + trow, r1 - 1)
             assert 0 <= row < x_rows
-            off = row * K * 2 + (((lane & 7) ^ (trow & 7)) << 4)
+            off = row * K * 2 + (((lane & 7) ^ swz128(trow)) << 4)
             assert off + (nk - 1) * ROWB + 16 <= x_rows * K * 2 and off < U32
         assert (NS - 1) * STAGE + wid * 1024 + 1024 <= TOK + (NS - 1) * STAGE
         # fragment reads: own weight rows and both token blocks
         for lane in lanes:
             frow, kg = lane & 31, lane >> 5
             for q in range(4):
-                c = ((2 * q + kg) ^ (frow & 7)) << 4
+                c = ((2 * q + kg) ^ swz128(frow)) << 4
                 assert TOK + wid * 4096 + frow * ROWB + c + 16 <= STAGE
                 assert (32 + frow) * ROWB + c + 16 <= TOK
         # epilogue columns: a 4-wide store that starts inside the row ends inside it
