@@ -105,6 +105,9 @@ def traffic_for(workload: str):
     return None if w is None else w.get("bytes_per_launch")
 
 
+STAGE_WARMUP = 30
+
+
 def measure(name: str, steps: int, warmup: int, only_forward: bool = False) -> dict:
     import torch
 
@@ -121,7 +124,9 @@ def measure(name: str, steps: int, warmup: int, only_forward: bool = False) -> d
     out = torch.empty_like(x)
     res = {"workload": name, "cfg": cfg}
     if not only_forward:
-        res.update(stage_times(moe, ex, x, lg, opts, cfg, steps, warmup))
+        # at least 30 untimed split forwards first: the stage times the
+        # roofline uses must not fall into the clock's settling either
+        res.update(stage_times(moe, ex, x, lg, opts, cfg, steps, max(warmup, STAGE_WARMUP)))
 
     # The timed region: W untimed fused forwards, then exactly K, bracketed
     # by synchronisations; an event before each step gives per-step device
@@ -217,7 +222,7 @@ def roofline(res: dict) -> dict:
         ach = flops / t / 1e12
         r = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
              "frac": round(ach / PEAK_BF16_TFLOPS, 4)}
-    r["kernel"] = ("grouped_gemm_pipe64_kernel, stream tiles (gate/up, fused SiLU*mul)"
+    r["kernel"] = ("grouped_gemm_kernel, 16-row tiles (gate/up, fused SiLU*mul)"
                    if res["workload"] == "decode_bf16" else "grouped_gemm_pipe64_kernel (gate/up, fused SiLU*mul)")
     r["avg_launch_ms"] = round(res["stages_ms"]["experts_gate_up"], 4)
     r["traffic"] = traffic_for(res["workload"])
