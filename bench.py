@@ -222,7 +222,7 @@ def roofline(res: dict) -> dict:
         ach = flops / t / 1e12
         r = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
              "frac": round(ach / PEAK_BF16_TFLOPS, 4)}
-    r["kernel"] = ("grouped_gemm_kernel, 16-row tiles (gate/up, fused SiLU*mul)"
+    r["kernel"] = ("decode_stream_kernel (gate/up, fused SiLU*mul)"
                    if res["workload"] == "decode_bf16" else "grouped_gemm_pipe64_kernel (gate/up, fused SiLU*mul)")
     r["avg_launch_ms"] = round(res["stages_ms"]["experts_gate_up"], 4)
     r["traffic"] = traffic_for(res["workload"])

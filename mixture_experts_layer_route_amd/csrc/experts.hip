@@ -24,7 +24,12 @@
 // M-tiles any routing could produce; only the live ones get workgroup ids,
 // spread over the 8 XCDs, each XCD walking groups of one expert's tiles.
 //
-// Three kernels:
+// Four kernels:
+//   decode_stream_kernel (bf16/f16, H and I multiples of 64, experts of a
+//     few rows each): one persistent workgroup per CU streams units of 32
+//     weight rows against token tiles of at most 16 rows, each wave walking
+//     8 weight rows 128 bytes per load (the HBM read pattern measured
+//     fastest), through an LDS ring that runs on from unit to unit.
 //   grouped_gemm_pipe64_kernel (bf16/f16, H and I multiples of 64; the
 //     default for prefill-sized batches): 256x256 tiles on 8 waves of
 //     32x32x16 MFMAs; 64-element K steps filled by direct global->LDS loads
@@ -37,11 +42,12 @@
 //     8 waves of 32x32x16 MFMAs; 32-element K stages filled by direct
 //     global->LDS loads in a 4-stage ring, issued three stages ahead and
 //     interleaved with the MFMAs and the next fragment reads.
-//   grouped_gemm_kernel (f32, other K, and the 16-row tile for decode-sized
-//     batches): 128-byte K slices staged through registers into padded LDS,
+//   grouped_gemm_kernel (f32, other K, and a 16-row tile for few-row experts
+//     there): 128-byte K slices staged through registers into padded LDS,
 //     double buffered, 16x16 MFMAs.
 // FP32 accumulation throughout.
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "mfma.h"
@@ -741,6 +747,241 @@ __device__ __forceinline__ void stream_tile(const typename DT::storage* __restri
     }
 }
 
+// ------------------------------------------------------------------ decode stream kernel
+// For batches whose experts own a few rows each (decode), where the products
+// are a stream of weight rows that each serve a handful of tokens, so the
+// kernel is built around the HBM read pattern.  Measured on this chip with
+// direct global->LDS loads: a wave whose loads in flight spread over 32 rows
+// of an 8 KB-pitch matrix streams at 5.2 TB/s in all (8 rows x 128 B or
+// 1 row x 1 KB per load alike), over 16 rows at 5.5-5.8, and over 8 rows --
+// walking them 128 bytes per load -- at 6.2-6.4, above a contiguous stream
+// (6.1).  So each wave owns 8 weight rows, one 1 KB load (8 rows x 128 B)
+// per 64 K.
+//   One persistent workgroup of 4 waves per CU walks units of (a token tile
+// of at most 16 rows, 32 weight rows): workgroup b of G takes units b,
+// b + G, ...  A unit's K runs in steps of 256 (4 quarters of 64): per step
+// each wave loads its 8 rows' 4 quarters and 2 of the 8 token pieces (16
+// token rows x one quarter half), 6 loads of 1 KB; the ring of 6 stages of
+// 24 KB (LDS rows of 128 bytes, chunk c of row r at c ^ swz128(r)) runs on
+// from one unit into the next, so the stream never drains between units,
+// and the ~40 units per workgroup at decode size keep the launch's tail
+// short.  For gate/up a wave's rows are gate rows i0 .. i0 + 3 and the up
+// rows of the same i; for down, 8 output columns.
+//   16x16x32 MFMAs take the wave's 8 rows twice (rows 8-15 repeat 0-7) as
+// the first operand and the 16 token slots as the second; lanes 0-31 then
+// hold the 8 rows of one token each.  The waits on the vector-memory
+// counter are counted by hand (6 loads per wave and step), so every other
+// memory read here is a scalar load (the unit's tile, the token row
+// indices), which that counter does not see; the loads past a workgroup's
+// last step re-load that step into the stage the ring has just freed,
+// keeping the count of loads per step fixed.  A last step past K (K a
+// multiple of 64 but not of 256) loads its missing quarters from the last
+// valid one and skips their MFMAs.
+#ifndef MOE_DEC_ROWS
+#define MOE_DEC_ROWS 16
+#define MOE_DEC_STAGES 6
+#endif
+constexpr int kDecRows = MOE_DEC_ROWS, kDecWaveRows = 8, kDecStages = MOE_DEC_STAGES, kDecWaves = 4;
+// The host takes this kernel when no expert can own more than kStreamRows
+// rows, or when the experts own at most kDecMeanRows rows on average: then
+// even an expert that owns every row costs at most N / kDecRows extra
+// passes over its weights, E + N / kDecRows <= 1.25 E expert matrices read
+// in all, against E for kernels with taller tiles.
+constexpr int kDecMeanRows = 4;
+
+// Scalar loads of values the whole wave shares.
+__device__ __forceinline__ uint32_t sload_u32(const uint32_t* p) {
+    uint32_t v;
+    asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+    return v;
+}
+// Eight scalar loads with one wait: p[i0], ..., p[i7].
+__device__ __forceinline__ void sload8(const uint32_t* p, const int (&i)[8], uint32_t (&v)[8]) {
+    asm volatile(
+        "s_load_dword %0, %8, 0x0\n\ts_load_dword %1, %9, 0x0\n\t"
+        "s_load_dword %2, %10, 0x0\n\ts_load_dword %3, %11, 0x0\n\t"
+        "s_load_dword %4, %12, 0x0\n\ts_load_dword %5, %13, 0x0\n\t"
+        "s_load_dword %6, %14, 0x0\n\ts_load_dword %7, %15, 0x0\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&s"(v[0]), "=&s"(v[1]), "=&s"(v[2]), "=&s"(v[3]), "=&s"(v[4]), "=&s"(v[5]), "=&s"(v[6]), "=&s"(v[7])
+        : "s"(p + i[0]), "s"(p + i[1]), "s"(p + i[2]), "s"(p + i[3]), "s"(p + i[4]), "s"(p + i[5]), "s"(p + i[6]),
+          "s"(p + i[7])
+        : "memory");
+}
+__device__ __forceinline__ int4 sload_int4(const int4* p) {
+    typedef int v4i_t __attribute__((ext_vector_type(4)));
+    v4i_t v;
+    asm volatile("s_load_dwordx4 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+    return make_int4(v.x, v.y, v.z, v.w);
+}
+
+template <typename DT, bool GATEUP>
+__global__ __launch_bounds__(kDecWaves* kWave, 1) void decode_stream_kernel(
+    const typename DT::storage* __restrict__ A, const typename DT::storage* __restrict__ B0,
+    const typename DT::storage* __restrict__ B1, typename DT::storage* __restrict__ C, float* __restrict__ gu,
+    const uint32_t* __restrict__ a_rows, int a_nrows, const int4* __restrict__ tiles,
+    const uint32_t* __restrict__ tile_count, int K, int NOUT, int n_units) {
+    using S = typename DT::storage;
+    constexpr int ROWB = 128;                                  // bytes per row per quarter (64 K)
+    constexpr int TQ = kDecRows * ROWB;                        // 2 KB: the token rows of one quarter
+    constexpr int TOK = 4 * TQ;                                // 8 KB of token rows per stage
+    constexpr int WQ = kDecWaveRows * ROWB;                    // 1 KB: a wave's rows of one quarter
+    constexpr int STAGE = TOK + kDecWaves * 4 * WQ;            // 24 KB
+    constexpr int TPW = kDecRows / 8;                          // token loads per wave and step
+    constexpr int NS = kDecStages, PIECES = 4 + TPW;           // 1 KB loads per wave and step
+    constexpr int UN = GATEUP ? kDecWaves * kDecWaveRows / 2 : kDecWaves * kDecWaveRows;  // outputs per unit
+    constexpr int WN = UN / kDecWaves;                         // outputs per wave
+    static_assert(NS * STAGE <= 160 * 1024 && (NS - 2) * PIECES < 64, "ring fits the LDS and the counter");
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[NS * STAGE];
+
+    const int lane = lane_id(), wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int G = (int)gridDim.x, b = (int)blockIdx.x;
+    const int U = (int)sload_u32(tile_count) * n_units;
+    if (b >= U) return;
+    const int nu = (U - 1 - b) / G + 1;                        // this workgroup's units
+    const int nq = K / 64, nk = (nq + 3) / 4;                  // quarters, steps of 4 quarters
+    const int row_l = lane >> 3;                               // row of this lane within a 1 KB load
+
+    // the unit's tile: expert, token rows [r0, r1), first output
+    auto unit_tile = [&](int j, int& e, int& r0, int& r1, int& n0) __attribute__((always_inline)) {
+        const int u = b + j * G;
+        const int mi = u / n_units;
+        const int4 tl = sload_int4(tiles + mi);
+        e = tl.x;
+        r0 = tl.y;
+        r1 = tl.z;
+        n0 = (u - mi * n_units) * UN;
+    };
+
+    // ---- issue cursor: unit iu, step is; the addressing of unit iu
+    int iu = 0, is = 0;
+    const char* wptr = nullptr;                                // this lane's weight row, chunk included
+    uint32_t toff[TPW];                                        // token slots 8 h + row_l
+    auto set_unit = [&](int j) __attribute__((always_inline)) {
+        int e, r0, r1, n0;
+        unit_tile(j, e, r0, r1, n0);
+        // gate/up: lanes 0-31 read gate rows i0 + row_l, lanes 32-63 up rows
+        // i0 + row_l - 4; down: output rows n0 + 8 wid + row_l.  Rows past the
+        // matrix's last row read that row (their outputs are not stored).
+        const S* m = (GATEUP && row_l >= 4) ? B1 : B0;
+        const int mrow = min(n0 + WN * wid + (GATEUP ? (row_l & 3) : row_l), NOUT - 1);
+        wptr = (const char*)(m + ((int64_t)e * NOUT + mrow) * K) + (((lane & 7) ^ swz128(row_l)) << 4);
+        // token slots 8 h + row_l, clamped to the tile's last row (slots past
+        // it are computed but never stored); the wave reads the source rows
+        // of its 16 slots with scalar loads and each lane keeps its own
+        uint32_t src[TPW];
+#pragma unroll
+        for (int h = 0; h < TPW; ++h) {
+            src[h] = 0;
+            int rows[8];
+            uint32_t v[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) v[t] = rows[t] = __builtin_amdgcn_readfirstlane(min(r0 + 8 * h + t, r1 - 1));
+            if (a_rows) {
+                sload8(a_rows, rows, v);
+#pragma unroll
+                for (int t = 0; t < 8; ++t) v[t] = min(v[t], (uint32_t)(a_nrows - 1));
+            }
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+                if (row_l == t) src[h] = v[t];
+        }
+#pragma unroll
+        for (int h = 0; h < TPW; ++h)
+            toff[h] = (uint32_t)((int64_t)src[h] * K * (int64_t)sizeof(S)) + (((lane & 7) ^ swz128(8 * h + row_l)) << 4);
+    };
+    const uint32_t lds0 = lds_offset(smem);
+    int slot_issue = 0;                                        // stage of the next loads
+    auto issue = [&]() __attribute__((always_inline)) {
+        const uint32_t st = lds0 + slot_issue * STAGE;
+        // token quarter wid (both halves of the 16 slots), then the wave's
+        // rows, quarter by quarter; quarters past K repeat the last one
+        const int qt = min(4 * is + wid, nq - 1);
+#pragma unroll
+        for (int h = 0; h < TPW; ++h) lds_dma16_so((const char*)A + qt * ROWB, toff[h], st + wid * TQ + h * 1024);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            lds_dma16(wptr + min(4 * is + q, nq - 1) * ROWB, st + TOK + (4 * wid + q) * WQ);
+        slot_issue = slot_issue == NS - 1 ? 0 : slot_issue + 1;
+        // advance, except past the last step, which later loads repeat
+        if (is + 1 < nk) {
+            ++is;
+        } else if (iu + 1 < nu) {
+            is = 0;
+            set_unit(++iu);
+        }
+    };
+
+    set_unit(0);
+#pragma unroll 1
+    for (int p = 0; p < NS - 1; ++p) issue();
+
+    // fragments: weight row (lane & 7) of the wave's block, token slot
+    // (lane & 15); K group lane / 16 of each 32-K half of a quarter
+    const int kg = lane >> 4;
+    const int fw = TOK + 4 * wid * WQ + (lane & 7) * ROWB, ft = (lane & (kDecRows - 1)) * ROWB;
+    const int sw_w = swz128(lane & 7), sw_t = swz128(lane & (kDecRows - 1));
+    f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    int cj = 0, cs = 0, slot = 0;                              // compute cursor
+#pragma unroll 1
+    for (int g = 0, total = nu * nk; g < total; ++g) {
+        // step g landed (only the loads of the next NS - 2 steps may be in
+        // flight); after the barrier every wave's token rows of step g are
+        // in, and every wave is done with the stage of step g - 1, which the
+        // loads issued now reuse
+        wait_vm<(NS - 2) * PIECES>();
+        barrier_lds();
+        issue();
+        const unsigned char* st = smem + slot * STAGE;
+        const int qv = min(nq - 4 * cs, 4);                    // valid quarters of this step
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (q < qv) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int c = 4 * h + kg;
+                    const uint4 w = *(const uint4*)(st + fw + q * WQ + ((c ^ sw_w) << 4));
+                    const uint4 t = *(const uint4*)(st + q * TQ + ft + ((c ^ sw_t) << 4));
+                    acc = mma<DT>::run(w, t, acc);
+                }
+            }
+        }
+        slot = slot == NS - 1 ? 0 : slot + 1;
+        if (++cs < nk) continue;
+        // the unit's last step: lane l holds token slot l % 16 and block rows
+        // 4 (l / 16) + 0..3 (rows 8-15, lanes 32-63, repeat rows 0-7)
+        int e, r0, r1, n0;
+        unit_tile(cj, e, r0, r1, n0);
+        const int col0 = n0 + WN * wid;
+        const int grow = (lane & 15) < kDecRows ? r0 + (lane & 15) : r1;
+        if constexpr (GATEUP) {
+            // gate rows 0-3 in lanes 0-15, the up rows of the same i in 16-31
+            float u4[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) u4[r] = __shfl_down(acc[r], 16);
+            if (lane < 16 && grow < r1 && col0 < NOUT) {
+                const float g4[4] = {acc[0], acc[1], acc[2], acc[3]};
+                float v[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) v[r] = silu_mul(g4[r], u4[r]);
+                store4<DT>::run(C + (int64_t)grow * NOUT + col0, v);
+                if (gu) save_preact(gu, grow, NOUT, col0, g4, u4);
+            }
+        } else {
+            const int col = col0 + 4 * kg;
+            if (lane < 32 && grow < r1 && col < NOUT) {
+                const float v[4] = {acc[0], acc[1], acc[2], acc[3]};
+                store4<DT>::run(C + (int64_t)grow * NOUT + col, v);
+            }
+        }
+        acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        cs = 0;
+        ++cj;
+    }
+    // the repeated loads of the last steps land before the workgroup ends
+    wait_vm<0>();
+}
+
 // ------------------------------------------------------------------ pipelined grouped GEMM, 64-wide K stages
 // The same 256x256 tile and 8 waves of 128x64 as above, with 64-element K
 // stages: every LDS row holds 128 bytes (one whole cache line of each operand
@@ -1015,14 +1256,47 @@ hipError_t launch_pipe64(const void* A, const uint32_t* a_rows, int64_t a_nrows,
     return hipGetLastError();
 }
 
+// The compute units of the current device, looked up once per device.
+hipError_t device_cus(int* n) {
+    static std::atomic<int> cached[256];
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    if (dev >= 0 && dev < 256 && (*n = cached[dev].load(std::memory_order_relaxed)) > 0) return hipSuccess;
+    err = hipDeviceGetAttribute(n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (err != hipSuccess) return err;
+    if (*n <= 0) return hipErrorInvalidDevice;
+    if (dev >= 0 && dev < 256) cached[dev].store(*n, std::memory_order_relaxed);
+    return hipSuccess;
+}
+
+template <typename DT, bool GATEUP>
+hipError_t launch_decode(const void* A, const uint32_t* a_rows, int64_t a_nrows, const void* B0, const void* B1,
+                         void* C, float* gu, const int4* tiles, const uint32_t* count, int64_t mt, int K, int NOUT,
+                         hipStream_t s) {
+    using S = typename DT::storage;
+    constexpr int UN = GATEUP ? kDecWaves * kDecWaveRows / 2 : kDecWaves * kDecWaveRows;
+    const int n_units = (NOUT + UN - 1) / UN;
+    const int64_t units = mt * n_units;  // the most the tile list can give
+    if (units == 0) return hipSuccess;
+    if (units > 0x7fffffff) return hipErrorInvalidValue;
+    int cus = 0;
+    hipError_t err = device_cus(&cus);
+    if (err != hipSuccess) return err;
+    const unsigned grid = (unsigned)std::min<int64_t>(units, cus);
+    decode_stream_kernel<DT, GATEUP><<<grid, kDecWaves * kWave, 0, s>>>(
+        (const S*)A, (const S*)B0, (const S*)B1, (S*)C, gu, a_rows, (int)a_nrows, tiles, count, K, NOUT, n_units);
+    return hipGetLastError();
+}
+
 #ifndef MOE_P_WM
 #define MOE_P_WM 2   // waves along token rows of the pipelined tile
 #define MOE_P_WN 4   // waves along weight rows
 #endif
 
-// Two tile shapes: a large tile for experts that own many rows, and a
-// 16-row tile for decode-sized batches, where each expert owns a handful of
-// rows and the products are a stream of weight rows.
+// The register-staged kernel's two tile shapes (f32, and 16-bit types whose
+// K extents are not multiples of 64): a large tile for experts that own many
+// rows, and a 16-row tile for experts that own a handful of rows each.
 #ifndef MOE_L_BM
 #define MOE_L_BM 128   // rows of the large tile
 #define MOE_L_BN 128   // weight rows of the large tile
@@ -1041,20 +1315,41 @@ hipError_t launch_typed(const ExpertsArgs& a, hipStream_t s, ExpertsPart part) {
     int4* tiles = (int4*)((char*)a.tiles + 256);
     uint32_t* count = (uint32_t*)a.tiles;
     const int64_t cap = ((int64_t)experts_tile_bytes(a.N, a.E) - 256) / 16;  // entries the workspace holds
-    // The 64-K kernel (16-bit types, both K extents multiples of 64) picks
-    // each expert's tile on the device: a stream tile for an expert of at
-    // most kStreamRows rows, 256-row tiles for the others.  It addresses each
-    // operand row as a scalar base plus a 32-bit per-lane offset, so the row
-    // operands must span less than 4 GiB.  When no expert can hold more than
-    // kStreamRows rows -- a token picks an expert at most once, so an expert
-    // holds at most T rows when the rows are read through token_of_row --
-    // the 16-row register-staged kernel runs instead: on a pure weight stream
-    // (the decode workload) it measured 3.5% faster on gate/up than stream
-    // tiles, whose one workgroup per CU steps in lockstep.
+    // 16-bit types with both K extents multiples of 64, and row operands
+    // that span less than 4 GiB (the kernels address a row as a scalar base
+    // plus a 32-bit per-lane offset), take one of two kernels:
+    //   - the decode stream kernel, when no expert can hold more than
+    //     kStreamRows rows (a token picks an expert at most once, so an
+    //     expert holds at most T rows when the rows are read through
+    //     token_of_row) or the experts hold at most kDecMeanRows rows on
+    //     average: a weight stream in the HBM read pattern measured fastest
+    //     (decode gate/up 480 us against 495 for the 16-row register-staged
+    //     kernel and ~510 for stream tiles);
+    //   - otherwise the 64-K kernel, which picks each expert's tile on the
+    //     device: a stream tile for an expert of at most kStreamRows rows,
+    //     256-row tiles for the others.
     const int64_t x_rows = a.x_rows ? a.x_nrows : a.N, esz = (int64_t)sizeof(typename DT::storage);
     const bool fits32 = x_rows * a.H * esz < (int64_t(1) << 32) - 256 && a.N * a.I * esz < (int64_t(1) << 32) - 256;
     const int64_t max_expert_rows = a.x_rows ? std::min(a.N, a.x_nrows) : a.N;
-    if (esz == 2 && MOE_P_BK64 && a.H % 64 == 0 && a.I % 64 == 0 && fits32 && max_expert_rows > kStreamRows) {
+    const bool k64 = esz == 2 && MOE_P_BK64 && a.H % 64 == 0 && a.I % 64 == 0 && fits32;
+    if (k64 && (max_expert_rows <= kStreamRows || a.N <= kDecMeanRows * (int64_t)a.E)) {
+        // decode-sized: the persistent stream kernel on token tiles of at
+        // most kDecRows rows
+        const int64_t mt = max_mtiles(a.N, a.E, kDecRows);
+        if (mt > cap) return hipErrorInvalidValue;
+        hipError_t err = launch_build_tiles(a.offsets, a.E, a.N, kDecRows, mt, tiles, count, s);
+        if (err != hipSuccess) return err;
+        if constexpr (sizeof(typename DT::storage) == 2) {
+            if (part != kDown) {
+                err = launch_decode<DT, true>(a.x, a.x_rows, a.x_nrows, a.gate, a.up, a.h, a.gu, tiles, count, mt, H, I, s);
+                if (err != hipSuccess) return err;
+            }
+            if (part != kGateUp)
+                err = launch_decode<DT, false>(a.h, nullptr, 0, a.down, nullptr, a.y, nullptr, tiles, count, mt, I, H, s);
+        }
+        return err;
+    }
+    if (k64) {
         const int64_t mt = max_mtiles(a.N, a.E, kPipeBM, kStreamRows);
         if (mt > cap) return hipErrorInvalidValue;
         hipError_t err = launch_build_tiles(a.offsets, a.E, a.N, kPipeBM, mt, tiles, count, s, kStreamRows);
@@ -1069,8 +1364,9 @@ hipError_t launch_typed(const ExpertsArgs& a, hipStream_t s, ExpertsPart part) {
         }
         return err;
     }
-    // Otherwise one tile height for every expert: 16 rows when the experts
-    // own few rows on average (or none can own more than kStreamRows), else
+    // Otherwise (f32, K not a multiple of 64, or larger operands) one tile
+    // height for every expert: 16 rows when the experts own few rows on
+    // average (or none can own more than kStreamRows), else
     // the pipelined 32-K kernel (16-bit, K extents multiples of 32) or the
     // register-staged kernel.
     const bool small = a.N < 64 * (int64_t)a.E || max_expert_rows <= kStreamRows;
@@ -1121,7 +1417,8 @@ hipError_t launch_build_tiles(const uint32_t* offsets, int E, int64_t N, int BM,
 
 // the largest list of any tile policy the expert products use
 size_t experts_tile_bytes(int64_t N, int64_t E) {
-    const int64_t a = max_mtiles(N, E, kSmallBM), b = max_mtiles(N, E, kPipeBM, kStreamRows);
+    const int64_t a = std::max(max_mtiles(N, E, kSmallBM), max_mtiles(N, E, kDecRows)),
+                  b = max_mtiles(N, E, kPipeBM, kStreamRows);
     return 256 + 16 * (size_t)(a > b ? a : b);
 }
 

@@ -89,6 +89,17 @@ def stream_cases():
     ]
 
 
+def decode_cases():
+    """The decode stream kernel (experts of a few rows): H and I not
+    multiples of 256, so the last K step of each product holds 3 and 1 of
+    its 4 quarters; and a Zipf-hot expert that owns most of the 64 tokens,
+    i.e. several 16-row token tiles of one expert."""
+    return [
+        S.small_config("decode_partial_k_bf16", T=50, H=448, I=320, E=64, top_k=4, dtype="bf16", seed=87),
+        S.small_config("decode_hot_f16", T=64, H=256, I=192, E=32, top_k=2, dtype="f16", zipf_s=2.0, seed=88),
+    ]
+
+
 # ------------------------------------------------------------------ routing
 @pytest.mark.parametrize("cfg", [
     S.CONFIGS["tiny_f32"],
@@ -182,8 +193,8 @@ def test_invalid_indices_give_nan_rows_without_oob():
 
 
 # ------------------------------------------------------------------ experts
-@pytest.mark.parametrize("cfg", small_cases() + deep_cases() + stream_cases() + [S.CONFIGS["edge_f32"]],
-                         ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", small_cases() + deep_cases() + stream_cases() + decode_cases() +
+                         [S.CONFIGS["edge_f32"]], ids=lambda c: c.name)
 def test_experts_parity(cfg):
     log(f"experts parity {cfg.name}")
     x, lg = S.make_tokens(cfg)
@@ -217,6 +228,27 @@ def test_experts_tile_choice_at_its_boundaries(dt):
     gy = ex.forward_dispatched(x.to(DEV), g_off)
     torch.cuda.synchronize()
     assert_close(values(gy, dt), oracle.widen(Y, dt), dt, f"expert outputs, tile boundaries ({dt})")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_decode_kernel_token_tiles_at_their_boundaries(dt):
+    """Experts of 15, 16 (one 16-row token tile), 17, 33 and 48 rows (two to
+    three tiles), 1, 2 and none, among 40 experts (132 rows, at most 4 per
+    expert on average, so the decode stream kernel runs), against the
+    oracle."""
+    counts = [15, 16, 17, 0, 1, 33, 48, 2] + [0] * 32
+    E, H, I = len(counts), 128, 192
+    cfg = S.small_config(f"decode_boundary_{dt}", T=sum(counts), H=H, I=I, E=E, top_k=1, dtype=dt, seed=89)
+    x, _ = S.make_tokens(cfg)
+    W = S.make_weights(cfg)
+    rows = host_bits(x)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.uint32)
+    Y = oracle.experts(*[host_bits(w) for w in W], dt, rows, offsets, E, H, I, nthreads=NTHREADS)
+    ex = moe.SwiGluExperts(*[w.to(DEV) for w in W])
+    g_off = torch.from_numpy(offsets.view(np.int32)).view(torch.uint32).to(DEV)
+    gy = ex.forward_dispatched(x.to(DEV), g_off)
+    torch.cuda.synchronize()
+    assert_close(values(gy, dt), oracle.widen(Y, dt), dt, f"expert outputs, decode token tiles ({dt})")
 
 
 @pytest.mark.parametrize("cfg", [
@@ -303,7 +335,7 @@ def run_forward_case(cfg, repeat_check=True):
     return out
 
 
-@pytest.mark.parametrize("cfg", small_cases() + deep_cases() + stream_cases() + [
+@pytest.mark.parametrize("cfg", small_cases() + deep_cases() + stream_cases() + decode_cases() + [
     S.CONFIGS["edge_f32"],
     S.small_config("edge_norenorm", T=1024, H=256, I=512, E=16, top_k=4, renormalize=False, edge_rows=True,
                    seed=1001),
@@ -322,6 +354,7 @@ def test_forward_parity(cfg):
     S.small_config("split_f32", T=130, H=40, I=24, E=4, top_k=2, dtype="f32", seed=44),
     S.small_config("split_edge", T=300, H=64, I=96, E=16, top_k=4, dtype="bf16", edge_rows=True, seed=45),
     S.small_config("split_stream_mixed", T=1024, H=512, I=256, E=256, top_k=8, dtype="bf16", zipf_s=1.1, seed=46),
+    S.small_config("split_decode", T=40, H=448, I=320, E=64, top_k=4, dtype="bf16", seed=47),
 ], ids=lambda c: c.name)
 def test_split_stages_equal_fused_forward(cfg):
     log(f"split == fused {cfg.name}")
