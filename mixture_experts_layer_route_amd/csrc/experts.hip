@@ -765,8 +765,9 @@ __device__ __forceinline__ void stream_tile(const typename DT::storage* __restri
 // 24 KB (LDS rows of 128 bytes, chunk c of row r at c ^ swz128(r)) runs on
 // from one unit into the next, so the stream never drains between units,
 // and the ~40 units per workgroup at decode size keep the launch's tail
-// short.  For gate/up a wave's rows are gate rows i0 .. i0 + 3 and the up
-// rows of the same i; for down, 8 output columns.
+// short.  Each XCD's workgroups take adjacent units.  For gate/up a wave's
+// rows are gate rows i0 .. i0 + 3 and the up rows of the same i; for down,
+// 8 output columns.
 //   16x16x32 MFMAs take the wave's 8 rows twice (rows 8-15 repeat 0-7) as
 // the first operand and the 16 token slots as the second; lanes 0-31 then
 // hold the 8 rows of one token each.  The waits on the vector-memory
@@ -835,7 +836,11 @@ __global__ __launch_bounds__(kDecWaves* kWave, 1) void decode_stream_kernel(
     __shared__ __attribute__((aligned(1024))) unsigned char smem[NS * STAGE];
 
     const int lane = lane_id(), wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int G = (int)gridDim.x, b = (int)blockIdx.x;
+    // units b, b + G, ... of workgroup b, numbered so that the ~32
+    // workgroups of each XCD stream adjacent units (adjacent weight rows):
+    // measured 4.6% faster on decode gate/up than consecutive workgroups on
+    // adjacent units, which spreads every XCD's rows over the whole window
+    const int G = (int)gridDim.x, b = xcd_contiguous((int)blockIdx.x, (int)gridDim.x);
     const int U = (int)sload_u32(tile_count) * n_units;
     if (b >= U) return;
     const int nu = (U - 1 - b) / G + 1;                        // this workgroup's units

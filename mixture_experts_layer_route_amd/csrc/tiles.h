@@ -30,6 +30,15 @@ hipError_t launch_build_tiles(const uint32_t* offsets, int E, int64_t N, int BM,
                               uint32_t* count, hipStream_t s, int stream_rows = 0);
 
 // ------------------------------------------------------------------ tile order
+// Workgroup id -> logical id: the hardware hands workgroup b of a launch to
+// XCD b % 8, and this gives each XCD a contiguous run of the ids [0, n)
+// (the first n % 8 XCDs one more), a permutation of [0, n).
+__device__ __forceinline__ int xcd_contiguous(int bid, int n) {
+    const int q = n / 8, rem = n % 8;
+    const int xcd = bid % 8, loc = bid / 8;
+    return (xcd < rem ? xcd * (q + 1) : rem * (q + 1) + (xcd - rem) * q) + loc;
+}
+
 // Workgroup b -> (token tile, weight tile).  The grid is sized for the most
 // token tiles the routing could produce; only the first m_tiles (the count the
 // tile-list kernel wrote) exist.  The hardware hands workgroup b to XCD b % 8,
@@ -46,9 +55,7 @@ __device__ __forceinline__ bool tile_of_block(int bid, int nblocks, int n_tiles,
                                               const int4* __restrict__ tiles, int* m_idx, int* n_idx) {
     const int live = min(nblocks, m_tiles * n_tiles);
     if (bid >= live) return false;
-    const int q = live / 8, rem = live % 8;
-    const int xcd = bid % 8, loc = bid / 8;
-    const int pid = (xcd < rem ? xcd * (q + 1) : rem * (q + 1) + (xcd - rem) * q) + loc;
+    const int pid = xcd_contiguous(bid, live);
     const uint32_t g = (uint32_t)tiles[pid / n_tiles].w;
     const int first_m = (int)(g & 0x3ffffffu);  // 26 bits of first tile, 6 of group size
     const int gm = max(1, min((int)(g >> 26), m_tiles - first_m));

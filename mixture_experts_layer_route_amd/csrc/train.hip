@@ -74,13 +74,6 @@ constexpr int kTBM = 128, kTBN = 128, kTThreads = 256;
 constexpr int kTStride = 144;  // LDS bytes per operand row: 128 of K + 16 of padding
 constexpr int kTStage = (kTBM + kTBN) * kTStride;
 
-// Workgroup -> logical tile id: each XCD (workgroup b runs on XCD b % 8)
-// gets a contiguous run of ids, so neighbouring tiles share its L2.
-__device__ __forceinline__ int xcd_contiguous(int bid, int nblocks) {
-    const int q = nblocks / 8, rem = nblocks % 8;
-    const int xcd = bid % 8, loc = bid / 8;
-    return (xcd < rem ? xcd * (q + 1) : rem * (q + 1) + (xcd - rem) * q) + loc;
-}
 
 // 4 K-rows of V values each (w[j] = 16 bytes of K-row j) -> V K-runs of 4
 // values (out[i] = values (i, K-rows 0..3), the lower K-row in the lower bits).

@@ -1,7 +1,8 @@
 """The persistent decode kernel's work walk and addresses, modelled on the CPU.
 
 decode_stream_kernel (csrc/experts.hip) has each of G workgroups walk units
-b, b + G, ... of (token tile of at most 16 rows, 32 weight rows: 8 per wave),
+b', b' + G, ... (b' = xcd_contiguous(b, G), so each XCD's workgroups start on
+adjacent units) of (token tile of at most 16 rows, 32 weight rows: 8 per wave),
 in steps of 4 K-quarters of 64, with a ring of 6 LDS stages that its direct
 global->LDS loads fill 5 steps ahead and that runs on from one unit into the
 next.  These tests restate its cursors and its address arithmetic integer
@@ -174,6 +175,23 @@ def test_decode_units_stay_in_their_buffers(gateup, NOUT, K):
     a_rows = [int(v) for v in rng.integers(0, x_rows, N)]
     check_units(gateup, counts, NOUT, K, a_rows, x_rows)
     check_units(gateup, counts, NOUT, K, None, N)
+
+
+def xcd_contiguous(bid, n):
+    q, rem = n // 8, n % 8
+    xcd, loc = bid % 8, bid // 8
+    return (xcd * (q + 1) if xcd < rem else rem * (q + 1) + (xcd - rem) * q) + loc
+
+
+@pytest.mark.parametrize("G", [1, 7, 8, 9, 80, 255, 256, 304])
+def test_workgroup_numbering_is_a_permutation_contiguous_per_xcd(G):
+    """Workgroup b runs on XCD b % 8 and walks units from xcd_contiguous(b, G):
+    every unit start is taken once, and each XCD's starts are one run."""
+    ids = [xcd_contiguous(b, G) for b in range(G)]
+    assert sorted(ids) == list(range(G))
+    for x in range(8):
+        mine = sorted(ids[b] for b in range(x, G, 8))
+        assert mine == list(range(mine[0], mine[0] + len(mine))) if mine else True
 
 
 def test_decode_shape():
