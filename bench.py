@@ -105,7 +105,7 @@ def traffic_for(workload: str):
     return None if w is None else w.get("bytes_per_launch")
 
 
-STAGE_WARMUP = 30
+STAGE_WARMUP = 40
 
 
 def measure(name: str, steps: int, warmup: int, only_forward: bool = False) -> dict:
@@ -123,18 +123,19 @@ def measure(name: str, steps: int, warmup: int, only_forward: bool = False) -> d
     ws = torch.empty(ex.forward_workspace_bytes(cfg.T, cfg.top_k, x.dtype), dtype=torch.uint8, device=dev)
     out = torch.empty_like(x)
     res = {"workload": name, "cfg": cfg}
+    # The split-stage loop (at least 40 untimed iterations, then K timed) is
+    # only enqueued here, and the fused forwards follow it with no idle gap:
+    # the GPU's power control answers any idle gap of 10 ms or more with ~30
+    # forwards that run up to 30% slower before settling (prefill, per-step
+    # events: 0.89, 0.92, 1.01, 1.09, 1.11, ... back to 0.89 ms by the 30th),
+    # which a warmup of a few steps would otherwise leave in the timed region.
+    stage = None
     if not only_forward:
-        # at least 30 untimed split forwards first: the stage times the
-        # roofline uses must not fall into the clock's settling either
-        res.update(stage_times(moe, ex, x, lg, opts, cfg, steps, max(warmup, STAGE_WARMUP)))
+        stage = stage_loop(moe, ex, x, lg, opts, cfg, steps, max(warmup, STAGE_WARMUP))
 
     # The timed region: W untimed fused forwards, then exactly K, bracketed
     # by synchronisations; an event before each step gives per-step device
-    # times (their median sits next to the wall-clock mean).  The stage loop
-    # above runs first, so the timed steps do not fall into the first ~30
-    # forwards after the GPU starts working, whose clock is still settling
-    # (a kernel trace of 30 fused, 30 split and 30 fused forwards: gate/up
-    # 606, 554 and 550 us on average).
+    # times (their median sits next to the wall-clock mean).
     for _ in range(warmup):
         ex.forward(x, lg, opts, ws, out)
     torch.cuda.synchronize()
@@ -152,23 +153,22 @@ def measure(name: str, steps: int, warmup: int, only_forward: bool = False) -> d
                 "event_ms_median": (per[(steps - 1) // 2] + per[steps // 2]) / 2,
                 "tokens_per_s": cfg.T * steps / wall})
     res["tflops"] = cfg.flops() / (ms_step * 1e-3) / 1e12
+    if stage is not None:
+        res.update(stage_results(stage, x, steps, warmup))
     return res
 
 
-def stage_times(moe, ex, x, lg, opts, cfg, steps: int, warmup: int) -> dict:
-    """Per-stage times: the split calls run the kernels of the fused forward
-    (mapping-only dispatch, gate/up reading the tokens in place), back to
-    back like the forward steps, with events on the stream every call is
-    launched on (torch's current stream) and one synchronisation at the end;
-    then the split API's copying dispatch alone."""
+def stage_loop(moe, ex, x, lg, opts, cfg, steps: int, warmup: int) -> dict:
+    """Enqueues the per-stage timing loop: the split calls run the kernels of
+    the fused forward (mapping-only dispatch, gate/up reading the tokens in
+    place), back to back like the forward steps, with events on the stream
+    every call is launched on (torch's current stream).  Nothing here waits
+    for the GPU; stage_results reads the events."""
     import torch
 
-    dev = x.device
-    names = ["route", "dispatch", "experts_gate_up", "experts_down", "combine"]
-    acc = {n: 0.0 for n in names}
     ews = torch.empty(moe.load().moe_experts_workspace_bytes(cfg.N, cfg.H, cfg.I, cfg.E, 2 if cfg.dtype == "bf16"
                                                               else (1 if cfg.dtype == "f16" else 0)),
-                      dtype=torch.uint8, device=dev)
+                      dtype=torch.uint8, device=x.device)
     plan = None
     marks = []
     for it in range(warmup + steps):
@@ -186,11 +186,22 @@ def stage_times(moe, ex, x, lg, opts, cfg, steps: int, warmup: int) -> dict:
         evs[5].record()
         if it >= warmup:
             marks.append(evs)
-    torch.cuda.synchronize()
-    for evs in marks:
+    return {"marks": marks, "plan": plan}
+
+
+def stage_results(stage: dict, x, steps: int, warmup: int) -> dict:
+    """Per-stage times from the loop stage_loop enqueued (the GPU has
+    finished it), then the split API's copying dispatch alone, timed after
+    everything else."""
+    import torch
+
+    names = ["route", "dispatch", "experts_gate_up", "experts_down", "combine"]
+    acc = {n: 0.0 for n in names}
+    for evs in stage["marks"]:
         for i, n in enumerate(names):
             acc[n] += evs[i].elapsed_time(evs[i + 1])
     res = {"stages_ms": {n: acc[n] / steps for n in names}}
+    plan = stage["plan"]
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     for _ in range(warmup):
         plan.dispatch(x)
