@@ -92,11 +92,16 @@ def stream_cases():
 def decode_cases():
     """The decode stream kernel (experts of a few rows): H and I not
     multiples of 256, so the last K step of each product holds 3 and 1 of
-    its 4 quarters; and a Zipf-hot expert that owns most of the 64 tokens,
-    i.e. several 16-row token tiles of one expert."""
+    its 4 quarters; a Zipf-hot expert that owns most of the 64 tokens, i.e.
+    several 16-row token tiles of one expert; 1024 experts for 16 tokens;
+    and K = 64, a single quarter per step."""
     return [
         S.small_config("decode_partial_k_bf16", T=50, H=448, I=320, E=64, top_k=4, dtype="bf16", seed=87),
         S.small_config("decode_hot_f16", T=64, H=256, I=192, E=32, top_k=2, dtype="f16", zipf_s=2.0, seed=88),
+        # 1024 experts for 16 tokens: most units belong to experts of one row
+        S.small_config("decode_many_experts_bf16", T=16, H=128, I=64, E=1024, top_k=8, dtype="bf16", seed=90),
+        # K = 64 on both products: every step holds a single quarter
+        S.small_config("decode_k64_bf16", T=24, H=64, I=64, E=16, top_k=4, dtype="bf16", seed=91),
     ]
 
 
