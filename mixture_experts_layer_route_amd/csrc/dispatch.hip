@@ -15,6 +15,11 @@
 //              expert id, into offsets[E+1].
 //   gather  -- one thread per (token, 16-byte unit): the unit is read once
 //              and written to each of the token's k dispatched rows.
+// When only the mapping is asked for and the batch has at most
+// kSmallDispatchSlots slots, one workgroup does all of it instead (LDS
+// histogram, scan, mapping): one launch instead of four, which at decode
+// sizes, where each launch is a few microseconds of latency, is most of the
+// dispatch's time.
 #include "moe_internal.h"
 
 namespace moe {
@@ -130,6 +135,62 @@ __global__ __launch_bounds__(256) void gather_kernel(const V* __restrict__ x, in
     }
 }
 
+// The mapping-only dispatch of a small batch in one workgroup of 1024
+// threads.  Slot s = i * 1024 + thread takes its rank inside its expert from
+// the LDS atomic that counts it (order inside an expert comes from atomics,
+// as in hist_kernel); the counts are scanned in ascending expert id into
+// offsets[E+1]; then row = offsets[e] + rank.  A slot whose index is >= E
+// gets kInvalidRow and no row.
+constexpr int kSmallDispatchSlots = 16384;
+constexpr int kSmallDispatchPer = kSmallDispatchSlots / 1024;
+constexpr int kMaxDispatchExperts = 4096;
+
+__global__ __launch_bounds__(1024) void dispatch_small_kernel(const uint32_t* __restrict__ idx, int N, int k,
+                                                              int E, uint32_t* __restrict__ offsets,
+                                                              uint32_t* __restrict__ row_of_slot,
+                                                              uint32_t* __restrict__ token_of_row) {
+    __shared__ uint32_t cnt[kMaxDispatchExperts];
+    for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
+    __syncthreads();
+    uint32_t ex[kSmallDispatchPer], loc[kSmallDispatchPer];
+#pragma unroll
+    for (int i = 0; i < kSmallDispatchPer; ++i) {
+        const int sl = i * 1024 + (int)threadIdx.x;
+        ex[i] = sl < N ? idx[sl] : kInvalidRow;
+        loc[i] = ex[i] < (uint32_t)E ? atomicAdd(&cnt[ex[i]], 1u) : 0u;
+    }
+    __syncthreads();
+    // exclusive scan, each thread over a contiguous run of experts
+    const int per = (E + 1023) / 1024, e0 = (int)threadIdx.x * per;
+    uint32_t local = 0;
+    for (int j = 0; j < per; ++j)
+        if (e0 + j < E) local += cnt[e0 + j];
+    uint32_t total;
+    uint32_t run = block_exclusive_scan(local, &total);
+    for (int j = 0; j < per; ++j) {
+        if (e0 + j < E) {
+            const uint32_t c = cnt[e0 + j];
+            cnt[e0 + j] = run;
+            offsets[e0 + j] = run;
+            run += c;
+        }
+    }
+    if (threadIdx.x == 0) offsets[E] = total;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kSmallDispatchPer; ++i) {
+        const int sl = i * 1024 + (int)threadIdx.x;
+        if (sl < N) {
+            uint32_t row = kInvalidRow;
+            if (ex[i] < (uint32_t)E) {
+                row = cnt[ex[i]] + loc[i];
+                token_of_row[row] = (uint32_t)(sl / k);
+            }
+            row_of_slot[sl] = row;
+        }
+    }
+}
+
 template <typename V>
 hipError_t launch_gather(const DispatchArgs& a, hipStream_t s) {
     const int64_t units = a.dispatched ? a.row_bytes / (int64_t)sizeof(V) : 0;
@@ -145,6 +206,12 @@ hipError_t launch_gather(const DispatchArgs& a, hipStream_t s) {
 
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
     hipError_t err;
+    const int64_t slots = a.T * (int64_t)a.k;
+    if (!a.dispatched && slots <= kSmallDispatchSlots && a.E <= kMaxDispatchExperts) {
+        dispatch_small_kernel<<<1, 1024, 0, s>>>(a.idx, (int)slots, a.k, a.E, a.offsets, a.row_of_slot,
+                                                 a.token_of_row);
+        return hipGetLastError();
+    }
     fill_u32_kernel<<<(a.E + 255) / 256, 256, 0, s>>>(a.counts, a.E, 0u);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     const int64_t N = a.T * (int64_t)a.k;
