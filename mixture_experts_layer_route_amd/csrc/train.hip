@@ -654,7 +654,9 @@ __global__ __launch_bounds__(kT2Waves* kWave, 2) void train_pipe2_kernel(TrainGe
                                       : (float*)p.c1 + ((int64_t)e * p.I + (m - p.I)) * p.H + col;
                     else
                         out = (float*)p.c0 + ((int64_t)e * p.H + m) * p.I + col;
-                    *(float4*)out = v;
+                    // written once and never read back here: non-temporal
+                    // (measured ~1% faster on the experts backward)
+                    store_nt16(out, __builtin_bit_cast(uint4, v));
                 }
             }
             wait_lgkm0();
