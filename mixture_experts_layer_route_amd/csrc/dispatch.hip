@@ -135,15 +135,21 @@ __global__ __launch_bounds__(256) void gather_kernel(const V* __restrict__ x, in
     }
 }
 
-// The mapping-only dispatch of a small batch in one workgroup of 1024
-// threads.  Slot s = i * 1024 + thread takes its rank inside its expert from
-// the LDS atomic that counts it (order inside an expert comes from atomics,
-// as in hist_kernel); the counts are scanned in ascending expert id into
-// offsets[E+1]; then row = offsets[e] + rank.  A slot whose index is >= E
-// gets kInvalidRow and no row.
+// The mapping-only dispatch of a batch of at most kSmallDispatchSlots slots
+// in one workgroup of 1024 threads.  Thread t owns slots i * 1024 + t; it
+// loads all of their expert ids first (one round of memory latency), then
+// takes each slot's rank inside its expert from the LDS atomic that counts it
+// (order inside an expert comes from atomics, as in hist_kernel) and keeps
+// expert and rank packed in one register: expert in the low kSmallExpertBits
+// bits, rank above them (rank < 16384, expert < 4096).  The counts are scanned
+// in ascending expert id into offsets[E+1]; then row = offsets[e] + rank.  A
+// slot whose index is >= E gets kInvalidRow and no row.  Past 16384 slots
+// the one CU's LDS atomics take longer than the four launches of the general
+// path (49152 slots: 31 us against 19 us).
 constexpr int kSmallDispatchSlots = 16384;
-constexpr int kSmallDispatchPer = kSmallDispatchSlots / 1024;
-constexpr int kMaxDispatchExperts = 4096;
+constexpr int kSmallPer = kSmallDispatchSlots / 1024;
+constexpr int kSmallExpertBits = 12;
+constexpr int kMaxDispatchExperts = 1 << kSmallExpertBits;
 
 __global__ __launch_bounds__(1024) void dispatch_small_kernel(const uint32_t* __restrict__ idx, int N, int k,
                                                               int E, uint32_t* __restrict__ offsets,
@@ -151,14 +157,17 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(const uint32_t* __
                                                               uint32_t* __restrict__ token_of_row) {
     __shared__ uint32_t cnt[kMaxDispatchExperts];
     for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
-    __syncthreads();
-    uint32_t ex[kSmallDispatchPer], loc[kSmallDispatchPer];
+    uint32_t st[kSmallPer];
 #pragma unroll
-    for (int i = 0; i < kSmallDispatchPer; ++i) {
+    for (int i = 0; i < kSmallPer; ++i) {
         const int sl = i * 1024 + (int)threadIdx.x;
-        ex[i] = sl < N ? idx[sl] : kInvalidRow;
-        loc[i] = ex[i] < (uint32_t)E ? atomicAdd(&cnt[ex[i]], 1u) : 0u;
+        st[i] = sl < N ? idx[sl] : kInvalidRow;
     }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kSmallPer; ++i)
+        if (i * 1024 < N)  // uniform
+            st[i] = st[i] < (uint32_t)E ? st[i] | (atomicAdd(&cnt[st[i]], 1u) << kSmallExpertBits) : kInvalidRow;
     __syncthreads();
     // exclusive scan, each thread over a contiguous run of experts
     const int per = (E + 1023) / 1024, e0 = (int)threadIdx.x * per;
@@ -177,16 +186,30 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(const uint32_t* __
     }
     if (threadIdx.x == 0) offsets[E] = total;
     __syncthreads();
+    // token of slot i * 1024 + t, stepped by 1024 = qs * k + rs
+    const uint32_t qs = 1024u / (uint32_t)k, rs = 1024u % (uint32_t)k;
+    uint32_t tok = threadIdx.x / (uint32_t)k, rem = threadIdx.x % (uint32_t)k;
+    constexpr uint32_t kExpertMask = (1u << kSmallExpertBits) - 1;
+    // the slot offsets are recomputed here rather than kept live from the
+    // loads, which would take one register per slot
+    int t3 = (int)threadIdx.x;
+    asm volatile("" : "+v"(t3));
 #pragma unroll
-    for (int i = 0; i < kSmallDispatchPer; ++i) {
-        const int sl = i * 1024 + (int)threadIdx.x;
+    for (int i = 0; i < kSmallPer; ++i) {
+        const int sl = i * 1024 + t3;
         if (sl < N) {
             uint32_t row = kInvalidRow;
-            if (ex[i] < (uint32_t)E) {
-                row = cnt[ex[i]] + loc[i];
-                token_of_row[row] = (uint32_t)(sl / k);
+            if (st[i] != kInvalidRow) {
+                row = cnt[st[i] & kExpertMask] + (st[i] >> kSmallExpertBits);
+                token_of_row[row] = tok;
             }
             row_of_slot[sl] = row;
+        }
+        tok += qs;
+        rem += rs;
+        if (rem >= (uint32_t)k) {
+            rem -= (uint32_t)k;
+            ++tok;
         }
     }
 }

@@ -197,6 +197,42 @@ def test_invalid_indices_give_nan_rows_without_oob():
     assert nan_rows[3] and nan_rows[10] and int(nan_rows.sum()) == 2
 
 
+@pytest.mark.parametrize("T,k,E,skew", [
+    (8192, 6, 64, 0.0),      # 49152 slots, the prefill routing's shape
+    (16384, 4, 128, 1.5),    # 65536 slots, skewed
+    (4096, 4, 128, 1.5),     # 16384 slots, the most one workgroup maps; skewed
+    (4097, 4, 128, 0.0),     # one token more: the multi-kernel path
+    (2001, 7, 4096, 0.0),    # ragged, the most experts one workgroup counts
+    (3000, 2, 4096, 1.2),    # the same, skewed
+    (16000, 1, 3, 0.0),      # k = 1, few experts
+    (10, 1500, 2048, 0.0),   # k > 1024
+], ids=lambda v: str(v))
+def test_mapping_only_dispatch_at_batch_sizes(T, k, E, skew):
+    """The mapping-only dispatch across the sizes its one-workgroup kernel
+    takes (at most 16384 slots and 4096 experts) and past them, with invalid
+    ids sprinkled in: offsets bit-exact, mapping valid and equal per expert to
+    the oracle's."""
+    log(f"mapping-only dispatch T={T} k={k} E={E}")
+    rng = np.random.default_rng(T + k + E)
+    if skew:
+        p = 1.0 / np.arange(1, E + 1) ** skew
+        idx = rng.choice(E, size=(T, k), p=p / p.sum()).astype(np.uint32)
+    else:
+        idx = rng.integers(0, E, size=(T, k), dtype=np.uint32)
+    bad = rng.random((T, k)) < 0.001
+    idx[bad] = np.where(rng.random(int(bad.sum())) < 0.5, E, 0xFFFFFFFF).astype(np.uint32)
+    x = torch.from_numpy(rng.integers(-2**15, 2**15, size=(T, 8), dtype=np.int16)).view(torch.bfloat16)
+    xb = host_bits(x)
+    o = oracle.dispatch(idx, E, xb, "bf16")
+    m = moe.dispatch(x.to(DEV), torch.from_numpy(idx.view(np.int32)).view(torch.uint32).to(DEV), E,
+                     copy_rows=False)
+    torch.cuda.synchronize()
+    tor = host_bits(m.token_of_row)
+    gpu = {"rows": xb[np.minimum(tor, T - 1)], "offsets": host_bits(m.expert_offsets),
+           "row_of_slot": host_bits(m.row_of_slot), "token_of_row": tor}
+    compare_dispatch(gpu, *o, xb, idx, E)
+
+
 # ------------------------------------------------------------------ experts
 @pytest.mark.parametrize("cfg", small_cases() + deep_cases() + stream_cases() + decode_cases() +
                          [S.CONFIGS["edge_f32"]], ids=lambda c: c.name)
