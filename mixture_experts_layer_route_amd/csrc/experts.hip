@@ -81,7 +81,9 @@ __device__ uint32_t block_exclusive_scan_1024(uint32_t v, uint32_t* total) {
 __global__ __launch_bounds__(1024) void build_tiles_kernel(const uint32_t* __restrict__ offsets, int E,
                                                            uint32_t N, int BM, uint32_t stream_rows,
                                                            uint32_t max_tiles, int4* __restrict__ tiles,
-                                                           uint32_t* __restrict__ count) {
+                                                           uint32_t* __restrict__ count,
+                                                           unsigned long long* __restrict__ queues, int n_queues) {
+    if ((int)threadIdx.x < n_queues) queues[threadIdx.x] = 0;
     const int per = (E + 1023) / 1024;
     const int e0 = threadIdx.x * per;
     uint32_t local = 0;
@@ -1003,13 +1005,20 @@ __global__ __launch_bounds__(kDecWaves* kWave, 1) void decode_stream_kernel(
 // kt+3 into the slots step kt leaves; the other weight rows of kt+3 follow,
 // a quarter per sub-step, over sub-steps 0-2 of step kt+1.  Requires
 // K % 64 == 0.
+//   The launch is persistent: one workgroup per CU claims tiles (tiles.h,
+// claimed tiles) until every XCD's run is used up, so an XCD whose run holds
+// cheap tiles (stream tiles, an expert's few last rows) takes tiles off the
+// back of the others' runs instead of idling.  Thread 0 makes the claim for
+// the next tile while the epilogue stores the current one, and hands it to
+// the other waves through LDS word 0 between two barriers.
 constexpr int kP64SlotsA = 2, kP64SlotsB = 3;
 template <typename DT, bool GATEUP, int WGM, int WGN>
 __global__ __launch_bounds__(WGM* WGN* kWave, 1) void grouped_gemm_pipe64_kernel(
     const typename DT::storage* __restrict__ A, const typename DT::storage* __restrict__ B0,
     const typename DT::storage* __restrict__ B1, typename DT::storage* __restrict__ C, float* __restrict__ gu,
     const uint32_t* __restrict__ a_rows, int a_nrows, const int4* __restrict__ tiles,
-    const uint32_t* __restrict__ tile_count, int K, int NOUT, int n_tiles, int nblocks) {
+    const uint32_t* __restrict__ tile_count, int K, int NOUT, int n_tiles, int nblocks,
+    unsigned long long* __restrict__ queues) {
     using S = typename DT::storage;
     constexpr int NW = WGM * WGN;
     constexpr int ROWB = 128;                                   // bytes per row per step
@@ -1037,17 +1046,26 @@ __global__ __launch_bounds__(WGM* WGN* kWave, 1) void grouped_gemm_pipe64_kernel
     const int live_m = (int)*tile_count;
     const int nk = K / 64;
 
-    int m_idx, n_idx;
-    if (!tile_of_block(blockIdx.x, nblocks, n_tiles, live_m, tiles, &m_idx, &n_idx)) return;
-    {
-        const int4 tl = tiles[m_idx];
-        if (tl.x & kStreamTileFlag) {
-            static_assert(NW == 8, "a stream tile runs on 8 waves of 32 weight rows");
-            stream_tile<DT, GATEUP>(A, B0, B1, C, gu, a_rows, a_nrows, tl.x & ~kStreamTileFlag, tl.y, tl.z,
-                                    n_idx * BN_OUT, K, NOUT, wid, lane, smem);
-            return;
+    const int xcd = blockIdx.x % kXcds, live = min(nblocks, live_m * n_tiles);
+    volatile int* const claim_word = (volatile int*)smem;
+    // thread 0 finishes a claim (the front word `old` returned, else the
+    // other runs' backs) and hands it to every wave through LDS word 0,
+    // which no wave touches between the first and the last barrier here
+    auto publish_claim = [&](unsigned long long old) {
+        wait_lgkm0();
+        barrier_lds();
+        if (threadIdx.x == 0) {
+            int p = front_claim(old, xcd, live);
+            if (p < 0) p = steal_claim(queues, xcd, live);
+            *claim_word = p;
         }
-    }
+        wait_lgkm0();
+        barrier_lds();
+        const int p = __builtin_amdgcn_readfirstlane(*claim_word);
+        wait_lgkm0();
+        barrier_lds();
+        return p;
+    };
     int e, r0, r1, n0;
     // DMA piece j of this wave, per operand: rows (wid * LPO + j) * 8 + lane / 8
     // of the operand tile, the lane's 16-byte physical slot (lane & 7) holding
@@ -1077,7 +1095,6 @@ __global__ __launch_bounds__(WGM* WGN* kWave, 1) void grouped_gemm_pipe64_kernel
             voffb[j] = (uint32_t)((int64_t)(min(n0 + brow, NOUT - 1) - n0) * K * (int64_t)sizeof(S)) + lc * 16;
         }
     };
-    setup(m_idx, n_idx);
     const uint32_t lds_a = lds_offset(smem) + wid * LPO * 1024;
     const uint32_t lds_b = lds_a + NA * SLOT;
     // fragment rows are 32-aligned blocks plus (lane & 31), whose chunk key is that of lane & 31
@@ -1178,38 +1195,57 @@ __global__ __launch_bounds__(WGM* WGN* kWave, 1) void grouped_gemm_pipe64_kernel
         }
     };
 
-    prologue_dma();
-    rows_live = __builtin_amdgcn_readfirstlane(r1 - r0) - __builtin_amdgcn_readfirstlane(wm) * WTM;
+    int pid = publish_claim(threadIdx.x == 0 ? atomicAdd(queues + xcd, 1ull) : 0ull);
+    while (pid >= 0) {
+        int m_idx, n_idx;
+        tile_of_id(pid, n_tiles, live_m, tiles, &m_idx, &n_idx);
+        unsigned long long next = 0;
+        const int4 tl = tiles[m_idx];
+        if (tl.x & kStreamTileFlag) {
+            static_assert(NW == 8, "a stream tile runs on 8 waves of 32 weight rows");
+            stream_tile<DT, GATEUP>(A, B0, B1, C, gu, a_rows, a_nrows, tl.x & ~kStreamTileFlag, tl.y, tl.z,
+                                    n_idx * BN_OUT, K, NOUT, wid, lane, smem);
+            if (threadIdx.x == 0) next = atomicAdd(queues + xcd, 1ull);
+        } else {
+            setup(m_idx, n_idx);
+            prologue_dma();
+            rows_live = __builtin_amdgcn_readfirstlane(r1 - r0) - __builtin_amdgcn_readfirstlane(wm) * WTM;
 #pragma unroll
-    for (int i = 0; i < MB; ++i)
+            for (int i = 0; i < MB; ++i)
 #pragma unroll
-        for (int f = 0; f < NB; ++f)
+                for (int f = 0; f < NB; ++f)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][f][r] = 0.0f;
-    wait_vm<kPrologueAfter0>();
-    barrier_lds();
+                    for (int r = 0; r < 16; ++r) acc[i][f][r] = 0.0f;
+            wait_vm<kPrologueAfter0>();
+            barrier_lds();
 #pragma unroll
-    for (int r = 0; r < NR; ++r) read_one(0, 0, 0, r);
-    if (rows_live >= MB * 32)
-        main_loop(std::true_type{});
-    else
-        main_loop(std::false_type{});
-    // every DMA of this tile landed and every wave finished its reads: the
-    // LDS is free to stage the outputs
-    wait_vm<0>();
-    wait_lgkm0();
-    barrier_lds();
-    if constexpr (GATEUP) {
-        constexpr bool staged_gu = WCN == 32 && NB == 2;
-        store_tile32<DT, GATEUP, MB, NB, WTM, WTN, WCN>(acc, C, staged_gu ? nullptr : gu, r0, r1, n0, wm, wn, NOUT,
-                                                        lane);
-        if constexpr (staged_gu)
-            if (gu) save_preact_staged<MB, NB, WTM, WCN>(acc, gu, r0, r1, n0, wm, wn, NOUT, lane, smem + wid * 16384);
-    } else if constexpr (WTN == 64) {
-        store_tile32_staged<DT, MB, NB, WTM, WTN>(acc, C, r0, r1, n0, wm, wn, NOUT, lane,
-                                                  smem + wid * (WTM * WTN * (int)sizeof(S)));
-    } else {
-        store_tile32<DT, GATEUP, MB, NB, WTM, WTN, WCN>(acc, C, nullptr, r0, r1, n0, wm, wn, NOUT, lane);
+            for (int r = 0; r < NR; ++r) read_one(0, 0, 0, r);
+            if (rows_live >= MB * 32)
+                main_loop(std::true_type{});
+            else
+                main_loop(std::false_type{});
+            // every DMA of this tile landed and every wave finished its reads:
+            // the LDS is free to stage the outputs
+            wait_vm<0>();
+            wait_lgkm0();
+            barrier_lds();
+            if (threadIdx.x == 0) next = atomicAdd(queues + xcd, 1ull);
+            if constexpr (GATEUP) {
+                constexpr bool staged_gu = WCN == 32 && NB == 2;
+                store_tile32<DT, GATEUP, MB, NB, WTM, WTN, WCN>(acc, C, staged_gu ? nullptr : gu, r0, r1, n0, wm, wn,
+                                                                NOUT, lane);
+                if constexpr (staged_gu)
+                    if (gu)
+                        save_preact_staged<MB, NB, WTM, WCN>(acc, gu, r0, r1, n0, wm, wn, NOUT, lane,
+                                                             smem + wid * 16384);
+            } else if constexpr (WTN == 64) {
+                store_tile32_staged<DT, MB, NB, WTM, WTN>(acc, C, r0, r1, n0, wm, wn, NOUT, lane,
+                                                          smem + wid * (WTM * WTN * (int)sizeof(S)));
+            } else {
+                store_tile32<DT, GATEUP, MB, NB, WTM, WTN, WCN>(acc, C, nullptr, r0, r1, n0, wm, wn, NOUT, lane);
+            }
+        }
+        pid = publish_claim(next);
     }
 }
 
@@ -1245,22 +1281,6 @@ hipError_t launch_pipe(const void* A, const uint32_t* a_rows, int64_t a_nrows, c
     return hipGetLastError();
 }
 
-template <typename DT, bool GATEUP>
-hipError_t launch_pipe64(const void* A, const uint32_t* a_rows, int64_t a_nrows, const void* B0, const void* B1,
-                         void* C, float* gu, const int4* tiles, const uint32_t* count, int64_t mt, int K,
-                         int NOUT, hipStream_t s) {
-    using S = typename DT::storage;
-    constexpr int BN_OUT = GATEUP ? kPipeBN / 2 : kPipeBN;
-    const int n_tiles = (NOUT + BN_OUT - 1) / BN_OUT;
-    const int64_t nb = mt * n_tiles;
-    if (nb == 0) return hipSuccess;
-    if (nb > 0x7fffffff) return hipErrorInvalidValue;
-    grouped_gemm_pipe64_kernel<DT, GATEUP, MOE_P64_WM, MOE_P64_WN><<<(unsigned)nb, MOE_P64_WM * MOE_P64_WN * kWave, 0, s>>>(
-        (const S*)A, (const S*)B0, (const S*)B1, (S*)C, gu, a_rows, (int)a_nrows, tiles, count, K, NOUT, n_tiles,
-        (int)nb);
-    return hipGetLastError();
-}
-
 // The compute units of the current device, looked up once per device.
 hipError_t device_cus(int* n) {
     static std::atomic<int> cached[256];
@@ -1274,6 +1294,29 @@ hipError_t device_cus(int* n) {
     if (dev >= 0 && dev < 256) cached[dev].store(*n, std::memory_order_relaxed);
     return hipSuccess;
 }
+
+// One workgroup per CU (the kernel's LDS allows no more), claiming tiles from
+// the eight claim words at `queues`, which the tile-list kernel cleared.
+template <typename DT, bool GATEUP>
+hipError_t launch_pipe64(const void* A, const uint32_t* a_rows, int64_t a_nrows, const void* B0, const void* B1,
+                         void* C, float* gu, const int4* tiles, const uint32_t* count, int64_t mt, int K,
+                         int NOUT, unsigned long long* queues, hipStream_t s) {
+    using S = typename DT::storage;
+    constexpr int BN_OUT = GATEUP ? kPipeBN / 2 : kPipeBN;
+    const int n_tiles = (NOUT + BN_OUT - 1) / BN_OUT;
+    const int64_t nb = mt * n_tiles;
+    if (nb == 0) return hipSuccess;
+    if (nb > 0x7fffffff) return hipErrorInvalidValue;
+    int cus = 0;
+    hipError_t err = device_cus(&cus);
+    if (err != hipSuccess) return err;
+    const unsigned grid = (unsigned)std::min<int64_t>(nb, cus);
+    grouped_gemm_pipe64_kernel<DT, GATEUP, MOE_P64_WM, MOE_P64_WN><<<grid, MOE_P64_WM * MOE_P64_WN * kWave, 0, s>>>(
+        (const S*)A, (const S*)B0, (const S*)B1, (S*)C, gu, a_rows, (int)a_nrows, tiles, count, K, NOUT, n_tiles,
+        (int)nb, queues);
+    return hipGetLastError();
+}
+
 
 template <typename DT, bool GATEUP>
 hipError_t launch_decode(const void* A, const uint32_t* a_rows, int64_t a_nrows, const void* B0, const void* B1,
@@ -1313,6 +1356,11 @@ hipError_t launch_decode(const void* A, const uint32_t* a_rows, int64_t a_nrows,
 #define MOE_S_WN 4
 #endif
 constexpr int kSmallBM = 16;
+
+// The tile list's 256-byte header: the count at byte 0, the 64-K kernels'
+// claim words (8 per product) from byte 64.
+constexpr int kTileQueueOffset = 64;
+static_assert(kTileQueueOffset + 2 * kXcds * 8 <= 256, "the claim words fit the header");
 
 template <typename DT>
 hipError_t launch_typed(const ExpertsArgs& a, hipStream_t s, ExpertsPart part) {
@@ -1355,17 +1403,22 @@ hipError_t launch_typed(const ExpertsArgs& a, hipStream_t s, ExpertsPart part) {
         return err;
     }
     if (k64) {
+        // the claim words of the two products, in the list's header
+        unsigned long long* queues = (unsigned long long*)((char*)a.tiles + kTileQueueOffset);
         const int64_t mt = max_mtiles(a.N, a.E, kPipeBM, kStreamRows);
         if (mt > cap) return hipErrorInvalidValue;
-        hipError_t err = launch_build_tiles(a.offsets, a.E, a.N, kPipeBM, mt, tiles, count, s, kStreamRows);
+        hipError_t err =
+            launch_build_tiles(a.offsets, a.E, a.N, kPipeBM, mt, tiles, count, s, kStreamRows, queues, 2 * kXcds);
         if (err != hipSuccess) return err;
         if constexpr (sizeof(typename DT::storage) == 2) {
             if (part != kDown) {
-                err = launch_pipe64<DT, true>(a.x, a.x_rows, a.x_nrows, a.gate, a.up, a.h, a.gu, tiles, count, mt, H, I, s);
+                err = launch_pipe64<DT, true>(a.x, a.x_rows, a.x_nrows, a.gate, a.up, a.h, a.gu, tiles, count, mt, H, I,
+                                              queues, s);
                 if (err != hipSuccess) return err;
             }
             if (part != kGateUp)
-                err = launch_pipe64<DT, false>(a.h, nullptr, 0, a.down, nullptr, a.y, nullptr, tiles, count, mt, I, H, s);
+                err = launch_pipe64<DT, false>(a.h, nullptr, 0, a.down, nullptr, a.y, nullptr, tiles, count, mt, I, H,
+                                               queues + kXcds, s);
         }
         return err;
     }
@@ -1413,10 +1466,12 @@ int64_t max_mtiles(int64_t N, int64_t E, int BM, int stream_rows) {
 }
 
 hipError_t launch_build_tiles(const uint32_t* offsets, int E, int64_t N, int BM, int64_t max_tiles, int4* tiles,
-                              uint32_t* count, hipStream_t s, int stream_rows) {
+                              uint32_t* count, hipStream_t s, int stream_rows, unsigned long long* queues,
+                              int n_queues) {
     if (max_tiles >= kMaxTiles || N >= (int64_t)0xFFFFFFFF || stream_rows < 0) return hipErrorInvalidValue;
+    if (n_queues < 0 || n_queues > 1024 || (n_queues > 0 && !queues)) return hipErrorInvalidValue;
     build_tiles_kernel<<<1, 1024, 0, s>>>(offsets, E, (uint32_t)N, BM, (uint32_t)stream_rows, (uint32_t)max_tiles,
-                                          tiles, count);
+                                          tiles, count, queues, n_queues);
     return hipGetLastError();
 }
 

@@ -10,7 +10,10 @@ These tests restate both in Python, integer for integer, and check on random
 routings -- Zipf-skewed, uniform, empty experts, one hot expert -- that
 every row of every expert lies in exactly one token tile of at most BM (or
 SR) rows, that the host's bound on the list length holds, and that the
-launched grid computes every (token tile, weight tile) pair exactly once.
+launched grid computes every (token tile, weight tile) pair exactly once --
+both the grid of one workgroup per pair and the persistent grid of the
+64-K kernel, whose workgroups claim tiles with atomic adds on one word per
+XCD (csrc/tiles.h, claimed tiles), under random interleavings of the claims.
 Section 5 of the ruDNN user guide requires the dispatch to drop no token; a
 hole or a double count here would drop or double rows.
 """
@@ -66,13 +69,20 @@ def build_tiles(offsets, E, N, BM, max_tiles, G, SR=0):
     return tiles, min(t, max_tiles)
 
 
+def xcd_run(x, live):
+    q, rem = live // 8, live % 8
+    return (x * (q + 1) if x < rem else rem * (q + 1) + (x - rem) * q), q + (1 if x < rem else 0)
+
+
 def tile_of_block(bid, nblocks, n_tiles, m_tiles, tiles):
     live = min(nblocks, m_tiles * n_tiles)
     if bid >= live:
         return None
-    q, rem = live // 8, live % 8
     xcd, loc = bid % 8, bid // 8
-    pid = (xcd * (q + 1) if xcd < rem else rem * (q + 1) + (xcd - rem) * q) + loc
+    return tile_of_id(xcd_run(xcd, live)[0] + loc, n_tiles, m_tiles, tiles)
+
+
+def tile_of_id(pid, n_tiles, m_tiles, tiles):
     g = tiles[pid // n_tiles][3]
     first_m = g & ((1 << MAX_TILE_BITS) - 1)
     gm = max(1, min(g >> MAX_TILE_BITS, m_tiles - first_m))
@@ -129,6 +139,71 @@ def check_cover(counts, BM, G, n_tiles, SR=0):
         if r is not None:
             hits[r] += 1
     assert (hits[:count] == 1).all()
+    for seed in range(2):
+        claimed = claim_walk(count, n_tiles, nblocks, int(np.random.default_rng(seed).choice([1, 5, 8, 37, 256])),
+                             np.random.default_rng(seed + N))
+        hits = np.zeros((max(count, 1), n_tiles), np.int64)
+        for pid in claimed:
+            hits[tile_of_id(pid, n_tiles, count, tiles)] += 1
+        assert (hits[:count] == 1).all()
+
+
+def claim_walk(m_tiles, n_tiles, nblocks, cus, rng):
+    """The persistent launch: min(nblocks, cus) workgroups, workgroup b on XCD
+    b % 8, each claiming from the front of its XCD's run (one 64-bit word per
+    XCD: front claims add 1, back claims 2^32) until that run is used up,
+    then from the backs of the other runs, nearest XCD first, and ending when
+    all are used up.  Every atomic add is one step, and the steps of all
+    workgroups interleave at random.  Returns the logical ids claimed."""
+    live = min(nblocks, m_tiles * n_tiles)
+    grid = min(nblocks, cus)
+    words = [0] * 8
+    claimed = []
+
+    def workgroup(b):
+        x = b % 8
+        while True:
+            old = words[x]
+            words[x] += 1
+            yield
+            start, ln = xcd_run(x, live)
+            f, bk = old & 0xFFFFFFFF, old >> 32
+            if f + bk < ln:
+                claimed.append(start + f)
+                continue
+            for d in range(1, 8):
+                v = (x + d) % 8
+                start, ln = xcd_run(v, live)
+                if ln == 0:
+                    continue
+                old = words[v]
+                words[v] += 1 << 32
+                yield
+                f, bk = old & 0xFFFFFFFF, old >> 32
+                if f + bk < ln:
+                    claimed.append(start + ln - 1 - bk)
+                    break
+            else:
+                return
+
+    active = [workgroup(b) for b in range(grid)]
+    while active:
+        i = int(rng.integers(len(active)))
+        try:
+            next(active[i])
+        except StopIteration:
+            active.pop(i)
+    assert sorted(claimed) == list(range(live)), "each logical id claimed exactly once"
+    return claimed
+
+
+@pytest.mark.parametrize("live,cus", [(0, 256), (1, 256), (7, 3), (9, 256), (300, 8), (2409, 256), (5000, 256),
+                                      (64, 1), (100, 13)])
+def test_claims_take_every_id_once(live, cus):
+    """Claim words alone, on id ranges of every size against grids of 1 to
+    256 workgroups, including XCDs with no workgroup and runs of length 0."""
+    for seed in range(6):
+        claim_walk(live, 1, live, cus, np.random.default_rng(seed))
 
 
 @pytest.mark.parametrize("G", range(1, 9))
