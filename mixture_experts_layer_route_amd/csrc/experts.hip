@@ -1232,12 +1232,15 @@ __global__ __launch_bounds__(WGM* WGN* kWave, 1) void grouped_gemm_pipe64_kernel
             if (threadIdx.x == 0) next = atomicAdd(queues + xcd, 1ull);
             if constexpr (GATEUP) {
                 constexpr bool staged_gu = WCN == 32 && NB == 2;
-                store_tile32<DT, GATEUP, MB, NB, WTM, WTN, WCN>(acc, C, staged_gu ? nullptr : gu, r0, r1, n0, wm, wn,
-                                                                NOUT, lane);
-                if constexpr (staged_gu)
-                    if (gu)
-                        save_preact_staged<MB, NB, WTM, WCN>(acc, gu, r0, r1, n0, wm, wn, NOUT, lane,
-                                                             smem + wid * 16384);
+                static_assert(staged_gu && NW == 8, "h is staged tile-wide: 8 waves of 32 h columns");
+                store_gateup_staged<DT, MB, WTM>(acc, C, r0, r1, n0, wm, wn, wid, NOUT, lane, smem);
+                if (gu) {
+                    // every wave has read its h rows back before the region is reused
+                    wait_lgkm0();
+                    barrier_lds();
+                    save_preact_staged<MB, NB, WTM, WCN>(acc, gu, r0, r1, n0, wm, wn, NOUT, lane,
+                                                         smem + wid * 16384);
+                }
             } else if constexpr (WTN == 64) {
                 store_tile32_staged<DT, MB, NB, WTM, WTN>(acc, C, r0, r1, n0, wm, wn, NOUT, lane,
                                                           smem + wid * (WTM * WTN * (int)sizeof(S)));

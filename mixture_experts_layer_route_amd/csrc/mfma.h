@@ -195,4 +195,48 @@ __device__ __forceinline__ void store_tile32_staged(const f32x16_t (&acc)[MB][NB
     }
 }
 
+// The gate/up epilogue staged through LDS across the whole tile: the tile's
+// 256 token rows of h (its 128 columns, 256 bytes a row; 16-byte chunk c of
+// row t at c ^ (t % 16)) are written by the 8 waves, each its 128 x 32 part
+// after the SiLU*mul, then read back a row chunk per lane after a barrier, so
+// each store instruction writes 4 whole 256-byte row segments instead of 16
+// bytes of 32 rows.  Needs 64 KB of LDS that no wave reads until the next
+// barrier; MB x 32 = WTM token rows and 32 h columns per wave (gate block
+// f = 0, up block f = 1).
+template <typename DT, int MB, int WTM>
+__device__ __forceinline__ void store_gateup_staged(const f32x16_t (&acc)[MB][2], typename DT::storage* __restrict__ C,
+                                                    int r0, int r1, int n0, int wm, int wn, int wid, int NOUT,
+                                                    int lane, unsigned char* stage) {
+    using S = typename DT::storage;
+    static_assert(sizeof(S) == 2 && WTM == MB * 32, "2-byte outputs");
+    constexpr int RB = 256;  // 128 columns of h per staged row
+    asm volatile("" : "+v"(lane));
+    const int frow = lane & 31, half = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+        const int t = wm * WTM + i * 32 + frow;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int c = wn * 4 + g;  // 8 columns wn * 32 + 8 g .. of the tile's 128
+            uint2 w;
+            w.x = fmt<DT>::store2(silu_mul(acc[i][0][g * 4], acc[i][1][g * 4]),
+                                  silu_mul(acc[i][0][g * 4 + 1], acc[i][1][g * 4 + 1]));
+            w.y = fmt<DT>::store2(silu_mul(acc[i][0][g * 4 + 2], acc[i][1][g * 4 + 2]),
+                                  silu_mul(acc[i][0][g * 4 + 3], acc[i][1][g * 4 + 3]));
+            *(uint2*)(stage + t * RB + ((c ^ (t & 15)) << 4) + half * 8) = w;
+        }
+    }
+    wait_lgkm0();
+    barrier_lds();
+    const int c = lane & 15, rr = lane >> 4;
+    const int col = n0 + c * 8;
+#pragma unroll
+    for (int t0 = 0; t0 < 32; t0 += 4) {
+        const int t = wid * 32 + t0 + rr;
+        const uint4 v = *(const uint4*)(stage + t * RB + ((c ^ (t & 15)) << 4));
+        const int grow = r0 + t;
+        if (grow < r1 && col < NOUT) *(uint4*)(C + (int64_t)grow * NOUT + col) = v;
+    }
+}
+
 }  // namespace moe
