@@ -20,9 +20,12 @@
 //
 // Work list: a one-workgroup kernel turns expert_offsets into a list of
 // (expert, row_begin, row_end) M-tiles in ascending expert order, on the
-// device, so no host sync is needed.  The GEMM grid is sized for the most
-// M-tiles any routing could produce; only the live ones get workgroup ids,
-// spread over the 8 XCDs, each XCD walking groups of one expert's tiles.
+// device, so no host sync is needed.  Each XCD walks a contiguous run of the
+// live (M-tile, weight tile) pairs, group by group of one expert's tiles:
+// the 64-K kernel's persistent workgroups claim them at run time (and take
+// tiles off other XCDs' runs once their own is used up), the other kernels
+// get one workgroup per pair from a grid sized for the most M-tiles any
+// routing could produce.
 //
 // Four kernels:
 //   decode_stream_kernel (bf16/f16, H and I multiples of 64, experts of a
@@ -31,11 +34,12 @@
 //     8 weight rows 128 bytes per load (the HBM read pattern measured
 //     fastest), through an LDS ring that runs on from unit to unit.
 //   grouped_gemm_pipe64_kernel (bf16/f16, H and I multiples of 64; the
-//     default for prefill-sized batches): 256x256 tiles on 8 waves of
-//     32x32x16 MFMAs; 64-element K steps filled by direct global->LDS loads
-//     into two token-row slots and three weight-row slots of 32 KB, the
-//     weight rows issued about two steps ahead, a quarter per 16-K sub-step,
-//     and the token rows one step ahead, in the last sub-step of a step.
+//     default for prefill-sized batches): one persistent workgroup per CU
+//     claiming 256x256 tiles, 8 waves of 32x32x16 MFMAs; 64-element K steps
+//     filled by direct global->LDS loads into two token-row slots and three
+//     weight-row slots of 32 KB, the weight rows issued about two steps
+//     ahead, a quarter per 16-K sub-step, and the token rows one step ahead,
+//     in the last sub-step of a step; epilogues staged through LDS.
 //   grouped_gemm_pipe_kernel (bf16/f16, K a multiple of 32 but not of 64, or
 //     a row-operand buffer of 4 GiB or more, which the 64-K kernel's 32-bit
 //     offsets cannot span): 256x256 tiles on
