@@ -414,6 +414,48 @@ def test_split_stages_equal_fused_forward(cfg):
     assert torch.equal(fused.view(bits), split.view(bits))
 
 
+@pytest.mark.parametrize("cfg", [
+    # the 64-K kernel's persistent launch (its claim words cleared by the
+    # tile-list kernel of each call), and the decode stream kernel
+    S.small_config("graph_pipe64", T=2048, H=512, I=384, E=16, top_k=2, dtype="bf16", seed=61),
+    S.small_config("graph_decode", T=24, H=256, I=192, E=32, top_k=4, dtype="bf16", seed=62),
+], ids=lambda c: c.name)
+def test_fused_forward_replays_in_a_hip_graph(cfg):
+    """The fused forward captured in a HIP graph: no memset, copy or
+    allocation of its own inside, so every replay must give the eager bits.
+    Replays are separated by eager forwards on other inputs, which leave the
+    workspace (tile list, claim words) in another state each time."""
+    log(f"graph replay {cfg.name}")
+    x, lg = S.make_tokens(cfg)
+    W = [w.to(DEV) for w in S.make_weights(cfg)]
+    ex = moe.SwiGluExperts(*W)
+    opts = moe.RoutingOptions(cfg.top_k, True)
+    gx, glg = x.to(DEV), lg.to(DEV)
+    need = moe.load().moe_forward_workspace_bytes(cfg.T, cfg.H, cfg.I, cfg.E, cfg.top_k, 2)
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    out = torch.empty_like(gx)
+    eager = ex.forward(gx, glg, opts, workspace=ws).clone()
+    other_x, other_lg = torch.randn_like(gx), torch.randn_like(glg)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        ex.forward(gx, glg, opts, workspace=ws, out=out)  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ex.forward(gx, glg, opts, workspace=ws, out=out)
+    bits = torch.int16
+    for rep in range(3):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(bits), eager.view(bits)), f"replay {rep}"
+        ex.forward(other_x, other_lg, opts, workspace=ws)
+        torch.cuda.synchronize()
+
+
 def test_forward_empty_batch():
     cfg = S.small_config("empty", T=0, H=64, I=64, E=4, top_k=2, dtype="bf16")
     W = [w.to(DEV) for w in S.make_weights(cfg)]
