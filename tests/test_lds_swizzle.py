@@ -77,3 +77,45 @@ def test_key_of_a_fragment_row_is_that_of_its_lane():
     for i in range(16):
         for f in range(32):
             assert swz128(32 * i + f) == swz128(f) and swz64(32 * i + f) == swz64(f)
+
+
+def test_staged_gate_up_rows_cover_the_tile_once_and_read_back_conflict_free():
+    """The gate/up epilogue's tile-wide staging (csrc/mfma.h,
+    store_gateup_staged): 256 rows of 256 bytes, chunk c of row t at
+    c ^ (t % 16).  Wave (wm, wn) writes 8 bytes per lane of rows
+    wm * 128 + 32 i + (lane & 31), chunk 4 wn + g, half lane >> 5; wave w
+    reads back rows 32 w + 4 j + (lane >> 4), chunk lane & 15.  Every byte of
+    the tile is written exactly once, and read back exactly once, from where
+    it was written; each 16-lane quarter of a read-back hits 16 different
+    4-bank groups."""
+    RB = 256
+    owner = {}
+    for wm in range(2):
+        for wn in range(4):
+            for i in range(4):
+                for g in range(4):
+                    for lane in range(64):
+                        t = wm * 128 + i * 32 + (lane & 31)
+                        c = wn * 4 + g
+                        addr = t * RB + ((c ^ (t & 15)) << 4) + (lane >> 5) * 8
+                        for b in range(8):
+                            assert addr + b not in owner
+                            owner[addr + b] = (t, c, lane >> 5, b)
+    assert len(owner) == 256 * RB
+    read = set()
+    for w in range(8):
+        for j in range(8):
+            quarters = {}
+            for lane in range(64):
+                t = w * 32 + 4 * j + (lane >> 4)
+                c = lane & 15
+                addr = t * RB + ((c ^ (t & 15)) << 4)
+                for b in range(16):
+                    tt, cc, half, bb = owner[addr + b]
+                    assert (tt, cc, 8 * half + bb) == (t, c, b)   # the bytes of chunk c of row t
+                    assert addr + b not in read
+                    read.add(addr + b)
+                quarters.setdefault(lane // 16, []).append((addr // 16) % 16)
+            for q in quarters.values():
+                assert len(set(q)) == 16
+    assert len(read) == 256 * RB
