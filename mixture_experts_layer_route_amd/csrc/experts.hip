@@ -1013,8 +1013,11 @@ __global__ __launch_bounds__(kDecWaves* kWave, 1) void decode_stream_kernel(
 // claimed tiles) until every XCD's run is used up, so an XCD whose run holds
 // cheap tiles (stream tiles, an expert's few last rows) takes tiles off the
 // back of the others' runs instead of idling.  Thread 0 makes the claim for
-// the next tile while the epilogue stores the current one, and hands it to
-// the other waves through LDS word 0 between two barriers.
+// the next tile as the K loop ends, and hands it to the other waves through
+// LDS word 0 between two barriers.  The next tile's token rows of steps 0
+// and 1 and weight rows of step 0 then go out before the current tile's
+// epilogue, which stages its outputs in the other two slots, so the new
+// tile's first step does not wait on memory.
 constexpr int kP64SlotsA = 2, kP64SlotsB = 3;
 template <typename DT, bool GATEUP, int WGM, int WGN>
 __global__ __launch_bounds__(WGM* WGN* kWave, 1) void grouped_gemm_pipe64_kernel(
@@ -1051,7 +1054,16 @@ __global__ __launch_bounds__(WGM* WGN* kWave, 1) void grouped_gemm_pipe64_kernel
     const int nk = K / 64;
 
     const int xcd = blockIdx.x % kXcds, live = min(nblocks, live_m * n_tiles);
-    volatile int* const claim_word = (volatile int*)smem;
+    // The epilogue stages its outputs in weight slots 1 and 2 (64 KB), so the
+    // next tile's token rows of steps 0 and 1 and weight rows of step 0 can
+    // land in the other three slots meanwhile (the training forward's FP32
+    // pre-activations need more of the LDS: it loads them afterwards).
+    const bool prefetch = !GATEUP || gu == nullptr;
+    unsigned char* const stage = smem + (NA + 1) * SLOT;
+    // (an LDS pointer: through a generic one the word's accesses would be
+    // flat instructions, whose waits also drain every load and store)
+    volatile __attribute__((address_space(3))) int* const claim_word =
+        (volatile __attribute__((address_space(3))) int*)smem;
     // thread 0 finishes a claim (the front word `old` returned, else the
     // other runs' backs) and hands it to every wave through LDS word 0,
     // which no wave touches between the first and the last barrier here
@@ -1081,18 +1093,30 @@ __global__ __launch_bounds__(WGM* WGN* kWave, 1) void grouped_gemm_pipe64_kernel
     // step: 2-3% of the product's time.)
     const char* basb[LPO];
     uint32_t voffa[LPO], voffb[LPO];
-    auto setup = [&](int mi, int ni) {
-        const int4 tl = tiles[mi];
+    auto setup = [&](int4 tl, int ni) {
         e = tl.x;
         r0 = tl.y;
         r1 = tl.z;
         n0 = ni * BN_OUT;
+        // the token rows of the pieces, looked up together
+        static_assert(LPO == 4, "four token-row lookups per lane");
+        int srow[LPO];
+#pragma unroll
+        for (int j = 0; j < LPO; ++j) srow[j] = min(r0 + (wid * LPO + j) * 8 + (lane >> 3), r1 - 1);
+        if (a_rows) {
+            uint32_t v[4];
+#pragma unroll
+            for (int j = 0; j < LPO; ++j) v[j] = (uint32_t)srow[j] * 4u;
+            load4_u32(a_rows, v);
+#pragma unroll
+            for (int j = 0; j < LPO; ++j) srow[j] = (int)min(v[j], (uint32_t)(a_nrows - 1));
+        }
 #pragma unroll
         for (int j = 0; j < LPO; ++j) {
             const int prow0 = (wid * LPO + j) * 8;  // first row of the piece (wave-uniform)
             const int row = prow0 + (lane >> 3);
             const int lc = (lane & 7) ^ swz128(row);
-            voffa[j] = (uint32_t)(src_row(a_rows, a_nrows, min(r0 + row, r1 - 1)) * K * (int64_t)sizeof(S)) + lc * 16;
+            voffa[j] = (uint32_t)((int64_t)srow[j] * K * (int64_t)sizeof(S)) + lc * 16;
             const S* m = (GATEUP && prow0 >= BN_OUT) ? B1 : B0;
             basb[j] = (const char*)(m + ((int64_t)e * NOUT + n0) * K);
             const int brow = GATEUP ? row % BN_OUT : row;
@@ -1200,19 +1224,25 @@ __global__ __launch_bounds__(WGM* WGN* kWave, 1) void grouped_gemm_pipe64_kernel
     };
 
     int pid = publish_claim(threadIdx.x == 0 ? atomicAdd(queues + xcd, 1ull) : 0ull);
+    bool pre = false;  // pid's token rows of steps 0-1 and weight rows of step 0 are in flight
     while (pid >= 0) {
-        int m_idx, n_idx;
-        tile_of_id(pid, n_tiles, live_m, tiles, &m_idx, &n_idx);
-        unsigned long long next = 0;
-        const int4 tl = tiles[m_idx];
-        if (tl.x & kStreamTileFlag) {
-            static_assert(NW == 8, "a stream tile runs on 8 waves of 32 weight rows");
-            stream_tile<DT, GATEUP>(A, B0, B1, C, gu, a_rows, a_nrows, tl.x & ~kStreamTileFlag, tl.y, tl.z,
-                                    n_idx * BN_OUT, K, NOUT, wid, lane, smem);
-            if (threadIdx.x == 0) next = atomicAdd(queues + xcd, 1ull);
-        } else {
-            setup(m_idx, n_idx);
-            prologue_dma();
+        bool streamed = false;
+        if (!pre) {
+            int m_idx, n_idx;
+            tile_of_id(pid, n_tiles, live_m, tiles, &m_idx, &n_idx);
+            const int4 tl = tiles[m_idx];
+            if (tl.x & kStreamTileFlag) {
+                static_assert(NW == 8, "a stream tile runs on 8 waves of 32 weight rows");
+                stream_tile<DT, GATEUP>(A, B0, B1, C, gu, a_rows, a_nrows, tl.x & ~kStreamTileFlag, tl.y, tl.z,
+                                        n_idx * BN_OUT, K, NOUT, wid, lane, smem);
+                pid = publish_claim(threadIdx.x == 0 ? atomicAdd(queues + xcd, 1ull) : 0ull);
+                streamed = true;
+            } else {
+                setup(tl, n_idx);
+                prologue_dma();
+            }
+        }
+        if (!streamed) {
             rows_live = __builtin_amdgcn_readfirstlane(r1 - r0) - __builtin_amdgcn_readfirstlane(wm) * WTM;
 #pragma unroll
             for (int i = 0; i < MB; ++i)
@@ -1220,6 +1250,11 @@ __global__ __launch_bounds__(WGM* WGN* kWave, 1) void grouped_gemm_pipe64_kernel
                 for (int f = 0; f < NB; ++f)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) acc[i][f][r] = 0.0f;
+            // the loads complete in order, so at most 2 LPO + BQ pieces still
+            // in flight means A0 and B0 landed: after B0 went out either
+            // B1 A1 B2[0, BQ), or (a prefetched tile) A1, the previous
+            // epilogue's stores, B1 B2[0, BQ); the stores only make the wait
+            // stricter
             wait_vm<kPrologueAfter0>();
             barrier_lds();
 #pragma unroll
@@ -1229,30 +1264,68 @@ __global__ __launch_bounds__(WGM* WGN* kWave, 1) void grouped_gemm_pipe64_kernel
             else
                 main_loop(std::false_type{});
             // every DMA of this tile landed and every wave finished its reads:
-            // the LDS is free to stage the outputs
-            wait_vm<0>();
+            // the LDS is free to stage the outputs.  The claim goes out before
+            // that wait, which thus also covers it: a wait the compiler placed
+            // at its use would count only the stores it issued after it, and
+            // so would also wait for the next tile's loads below.
+            unsigned long long next = 0;
+            if (threadIdx.x == 0) next = atomicAdd(queues + xcd, 1ull);
+            wait_vm0_known();
             wait_lgkm0();
             barrier_lds();
-            if (threadIdx.x == 0) next = atomicAdd(queues + xcd, 1ull);
+            const int nxt = publish_claim(next);
+            const int t_r0 = r0, t_r1 = r1, t_n0 = n0;
+            // the next tile's first loads, into token slots 0 and 1 and weight
+            // slot 0; its weight rows of step 1 and first ones of step 2 go
+            // into the staging slots once every wave has read them back
+            pre = false;
+            if (prefetch && nxt >= 0) {
+                int m_idx, n_idx;
+                tile_of_id(nxt, n_tiles, live_m, tiles, &m_idx, &n_idx);
+                const int4 tl = tiles[m_idx];
+                if (!(tl.x & kStreamTileFlag)) {
+                    setup(tl, n_idx);
+#pragma unroll
+                    for (int j = 0; j < LPO; ++j) dma_a(0, j);
+#pragma unroll
+                    for (int j = 0; j < LPO; ++j) dma_b(0, j);
+#pragma unroll
+                    for (int j = 0; j < LPO; ++j) dma_a(1, j);
+                    pre = true;
+                }
+            }
             if constexpr (GATEUP) {
                 constexpr bool staged_gu = WCN == 32 && NB == 2;
                 static_assert(staged_gu && NW == 8, "h is staged tile-wide: 8 waves of 32 h columns");
-                store_gateup_staged<DT, MB, WTM>(acc, C, r0, r1, n0, wm, wn, wid, NOUT, lane, smem);
+                store_gateup_staged<DT, MB, WTM>(acc, C, t_r0, t_r1, t_n0, wm, wn, wid, NOUT, lane, stage);
                 if (gu) {
                     // every wave has read its h rows back before the region is reused
                     wait_lgkm0();
                     barrier_lds();
-                    save_preact_staged<MB, NB, WTM, WCN>(acc, gu, r0, r1, n0, wm, wn, NOUT, lane,
+                    save_preact_staged<MB, NB, WTM, WCN>(acc, gu, t_r0, t_r1, t_n0, wm, wn, NOUT, lane,
                                                          smem + wid * 16384);
                 }
             } else if constexpr (WTN == 64) {
-                store_tile32_staged<DT, MB, NB, WTM, WTN>(acc, C, r0, r1, n0, wm, wn, NOUT, lane,
-                                                          smem + wid * (WTM * WTN * (int)sizeof(S)));
+                // two rounds of 8 KB per wave
+                static_assert(NW * WTM * WTN * (int)sizeof(S) / 2 == 2 * SLOT, "two rounds in two slots");
+                store_tile32_staged<DT, MB, NB, WTM, WTN, 2>(acc, C, t_r0, t_r1, t_n0, wm, wn, NOUT, lane,
+                                                             stage + wid * (WTM * WTN * (int)sizeof(S) / 2));
             } else {
-                store_tile32<DT, GATEUP, MB, NB, WTM, WTN, WCN>(acc, C, nullptr, r0, r1, n0, wm, wn, NOUT, lane);
+                store_tile32<DT, GATEUP, MB, NB, WTM, WTN, WCN>(acc, C, nullptr, t_r0, t_r1, t_n0, wm, wn, NOUT,
+                                                                lane);
             }
+            // every wave has read its staged outputs back before the slots are
+            // refilled
+            wait_lgkm0();
+            barrier_lds();
+            if (pre) {
+#pragma unroll
+                for (int j = 0; j < LPO; ++j) dma_b(1, j);
+#pragma unroll
+                for (int j = 0; j < BQ; ++j) dma_b(2, j);
+            }
+            pid = nxt;
         }
-        pid = publish_claim(next);
     }
 }
 

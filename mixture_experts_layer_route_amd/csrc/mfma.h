@@ -132,6 +132,26 @@ __device__ __forceinline__ void lds_dma16_so(const void* base, uint32_t voff, ui
                  "s"(__builtin_amdgcn_readfirstlane(lds_base))
                  : "memory", "m0");
 }
+// Four 32-bit loads from a wave-uniform base at per-lane byte offsets
+// (replaced in place by the values), issued together and waited for once.
+// Short of registers, the compiler gives such loads one destination and so
+// issues and waits for them one at a time.  The wait drains every vector
+// memory operation of the wave, so this goes where none of the hand-counted
+// DMA loads can be in flight.
+__device__ __forceinline__ void load4_u32(const void* base, uint32_t (&v)[4]) {
+    const uint64_t b = (uint64_t)(uintptr_t)base;
+    const uint64_t sb = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                        (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+    asm volatile(
+        "global_load_dword %0, %0, %4\n\t"
+        "global_load_dword %1, %1, %4\n\t"
+        "global_load_dword %2, %2, %4\n\t"
+        "global_load_dword %3, %3, %4\n\t"
+        "s_waitcnt vmcnt(0)"
+        : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3])
+        : "s"(sb)
+        : "memory");
+}
 #pragma clang diagnostic pop
 __device__ __forceinline__ void barrier_lds() { asm volatile("s_barrier" ::: "memory"); }
 // Keeps the instruction scheduler from moving anything across this point.
@@ -143,17 +163,25 @@ template <int N> __device__ __forceinline__ void wait_vm() { asm volatile("s_wai
 // lgkmcnt(0) through the builtin, so the compiler's own LDS-read tracking
 // knows the fragment registers are complete
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+// vmcnt(0) through the builtin: every vector memory operation issued so far
+// has completed, which the compiler then knows too, so it adds no wait of its
+// own (counted without the hand-issued DMA loads) before using a result that
+// was pending here
+__device__ __forceinline__ void wait_vm0_known() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // An epilogue of 2-byte outputs staged through LDS: each wave
 // writes its WTM-token x WTN-column block into its own LDS region (`stage`,
-// WTM * WTN * 2 bytes that no other wave touches before the next barrier),
-// row by row, then reads it back a 16-byte chunk per lane, so a store
-// instruction writes whole 128-byte row segments of 8 rows instead of 8 bytes
-// of 32 rows.  Staged row t holds its 16-byte chunk c at c ^ ((t / 2) % 8),
-// which spreads both the 8-byte writes and the 16-byte reads over all 64
-// banks.  The lane layout is the 32x32 MFMA result's: row (lane % 32) of each
-// 32-row block, columns 8 g + 4 (lane / 32) + 0..3 of each 32-column block.
-template <typename DT, int MB, int NB, int WTM, int WTN>
+// WTM / ROUNDS * WTN * 2 bytes that no other wave touches before the next
+// barrier), row by row, then reads it back a 16-byte chunk per lane, so a
+// store instruction writes whole 128-byte row segments of 8 rows instead of
+// 8 bytes of 32 rows.  With ROUNDS > 1 the block goes through the region in
+// that many rounds of WTM / ROUNDS rows (a wave's LDS operations complete in
+// order, so a round's writes never overtake the reads of the one before).
+// Staged row t holds its 16-byte chunk c at c ^ ((t / 2) % 8), which spreads
+// both the 8-byte writes and the 16-byte reads over all 64 banks.  The lane
+// layout is the 32x32 MFMA result's: row (lane % 32) of each 32-row block,
+// columns 8 g + 4 (lane / 32) + 0..3 of each 32-column block.
+template <typename DT, int MB, int NB, int WTM, int WTN, int ROUNDS = 1>
 __device__ __forceinline__ void store_tile32_staged(const f32x16_t (&acc)[MB][NB],
                                                     typename DT::storage* __restrict__ C, int r0, int r1, int n0,
                                                     int wm, int wn, int NOUT, int lane, unsigned char* stage) {
@@ -161,37 +189,43 @@ __device__ __forceinline__ void store_tile32_staged(const f32x16_t (&acc)[MB][NB
     constexpr int RB = WTN * 2;     // bytes per staged row
     constexpr int CPR = RB / 16;    // 16-byte chunks per row
     constexpr int RPS = 256 / RB;   // rows per sweep of the 64 banks
+    constexpr int MBR = MB / ROUNDS, WTR = WTM / ROUNDS;  // 32-row blocks and rows per round
     static_assert(sizeof(S) == 2 && RB == 128, "2-byte outputs, 64 per wave row");
+    static_assert(MB % ROUNDS == 0, "whole 32-row blocks per round");
     // an opaque copy of the lane id keeps the compiler from computing the
     // staging addresses before the K loop and holding them through it
     asm volatile("" : "+v"(lane));
     const int frow = lane & 31, half = lane >> 5;
-#pragma unroll
-    for (int i = 0; i < MB; ++i) {
-        const int t = i * 32 + frow;
-        const int sw = (t / RPS) % CPR;
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-#pragma unroll
-            for (int f = 0; f < NB; ++f) {
-                const int col = f * 32 + g * 8 + half * 4;
-                uint2 w;
-                w.x = fmt<DT>::store2(acc[i][f][g * 4], acc[i][f][g * 4 + 1]);
-                w.y = fmt<DT>::store2(acc[i][f][g * 4 + 2], acc[i][f][g * 4 + 3]);
-                *(uint2*)(stage + t * RB + (((col >> 3) ^ sw) << 4) + half * 8) = w;
-            }
-        }
-    }
-    wait_lgkm0();
     constexpr int RPI = 64 / CPR;  // staged rows per store instruction
     const int c = lane % CPR, rr = lane / CPR;
     const int col = n0 + wn * WTN + c * 8;
 #pragma unroll
-    for (int t0 = 0; t0 < WTM; t0 += RPI) {
-        const int t = t0 + rr;
-        const uint4 v = *(const uint4*)(stage + t * RB + ((c ^ ((t / RPS) % CPR)) << 4));
-        const int grow = r0 + wm * WTM + t;
-        if (grow < r1 && col < NOUT) *(uint4*)(C + (int64_t)grow * NOUT + col) = v;
+    for (int rd = 0; rd < ROUNDS; ++rd) {
+#pragma unroll
+        for (int ib = 0; ib < MBR; ++ib) {
+            const int i = rd * MBR + ib;
+            const int t = ib * 32 + frow;
+            const int sw = (t / RPS) % CPR;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+#pragma unroll
+                for (int f = 0; f < NB; ++f) {
+                    const int col = f * 32 + g * 8 + half * 4;
+                    uint2 w;
+                    w.x = fmt<DT>::store2(acc[i][f][g * 4], acc[i][f][g * 4 + 1]);
+                    w.y = fmt<DT>::store2(acc[i][f][g * 4 + 2], acc[i][f][g * 4 + 3]);
+                    *(uint2*)(stage + t * RB + (((col >> 3) ^ sw) << 4) + half * 8) = w;
+                }
+            }
+        }
+        wait_lgkm0();
+#pragma unroll
+        for (int t0 = 0; t0 < WTR; t0 += RPI) {
+            const int t = t0 + rr;
+            const uint4 v = *(const uint4*)(stage + t * RB + ((c ^ ((t / RPS) % CPR)) << 4));
+            const int grow = r0 + wm * WTM + rd * WTR + t;
+            if (grow < r1 && col < NOUT) *(uint4*)(C + (int64_t)grow * NOUT + col) = v;
+        }
     }
 }
 
