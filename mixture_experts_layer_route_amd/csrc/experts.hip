@@ -1150,7 +1150,9 @@ __global__ __launch_bounds__(WGM* WGN* kWave, 1) void grouped_gemm_pipe64_kernel
         else
             bv[set][r - MB] = *(const uint4*)(smem + (kt % NB_) * SLOT + csw[q] + fb[r - MB]);
     };
-    // steps past the end re-load the last step into a slot nobody reads again
+    // a step past the end (the first weight rows of one, from the loop's
+    // third-last step, or a K of at most 128's in the prologue) re-loads the
+    // last step into a slot nobody reads again
     auto dma_a = [&](int kt, int j) {
         lds_dma16_so((const char*)A + min(kt, nk - 1) * ROWB, voffa[j], lds_a + (kt % NA) * SLOT + j * 1024);
     };
@@ -1202,8 +1204,10 @@ __global__ __launch_bounds__(WGM* WGN* kWave, 1) void grouped_gemm_pipe64_kernel
     };
     using q_dma = std::integral_constant<int, BQ>;
     using q3_dma = std::integral_constant<int, LPO + BQ>;
+    using no_dma = std::integral_constant<int, 0>;
     auto main_loop = [&](auto full) {
-        for (int kt = 0; kt < nk; ++kt) {
+        int kt = 0;
+        for (; kt < nk - 2; ++kt) {
             wait_lgkm0();
             substep(full, q_dma{}, 0, kt, 1, [&](int d) { dma_b(kt + 2, BQ + d); });
             wait_lgkm0();
@@ -1220,6 +1224,21 @@ __global__ __launch_bounds__(WGM* WGN* kWave, 1) void grouped_gemm_pipe64_kernel
             // token rows of kt+2, then the first weight rows of kt+3
             substep(full, q3_dma{}, 1, kt + 1, 0,
                     [&](int d) { if (d < LPO) dma_a(kt + 2, d); else dma_b(kt + 3, d - LPO); });
+        }
+        // The last two steps load nothing: after the token rows of the last
+        // step only BQ pieces went out (the first weight rows of the step
+        // past the end, from the loop above, or of step 2, from the prologue).
+        for (; kt < nk; ++kt) {
+            wait_lgkm0();
+            substep(full, no_dma{}, 0, kt, 1, [](int) {});
+            wait_lgkm0();
+            substep(full, no_dma{}, 1, kt, 2, [](int) {});
+            wait_lgkm0();
+            substep(full, no_dma{}, 0, kt, 3, [](int) {});
+            wait_vm<BQ>();
+            wait_lgkm0();
+            barrier_lds();
+            substep(full, no_dma{}, 1, kt + 1, 0, [](int) {});
         }
     };
 
