@@ -96,7 +96,7 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const uint32_t* __res
         if (e < E) {
             const uint32_t b = min(offsets[e], N);
             const uint32_t en = max(min(offsets[e + 1], N), b);
-            local += (en - b <= stream_rows && en > b) ? 1u : (en - b + BM - 1) / BM;
+            local += (en - b + BM - 1) / BM;
         }
     }
     uint32_t total;
@@ -106,14 +106,12 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const uint32_t* __res
         if (e < E) {
             const uint32_t b = min(offsets[e], N);
             const uint32_t en = max(min(offsets[e + 1], N), b);
-            if (en > b && en - b <= stream_rows) {
-                // one stream tile holding the whole expert, a group of its own
-                if (t < max_tiles) tiles[t] = make_int4(e | kStreamTileFlag, (int)b, (int)en, (int)(t | (1u << 26)));
-                ++t;
-                continue;
-            }
             // the expert's M-tiles are split into ceil(n / kGroupM) groups of
-            // near-equal size; each tile records its group (first tile, size)
+            // near-equal size; each tile records its group (first tile, size).
+            // Its last tile, when it holds at most stream_rows rows (a whole
+            // small expert, or the rows past its full tiles), is a stream
+            // tile; in the expert's group it reads the weight tiles while the
+            // others have them in L2.
             const uint32_t n = (en - b + BM - 1) / BM;
             const uint32_t ng = (n + kGroupM - 1) / kGroupM;
             const uint32_t sz = ng ? n / ng : 0, big = ng ? n % ng : 0;  // `big` groups of sz+1
@@ -126,9 +124,9 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const uint32_t* __res
                     first = big * (sz + 1) + (j - big * (sz + 1)) / sz * sz;
                     gm = sz;
                 }
-                const uint32_t r = b + j * BM;
-                if (t < max_tiles)
-                    tiles[t] = make_int4(e, (int)r, (int)min(r + BM, en), (int)((t - j + first) | (gm << 26)));
+                const uint32_t r = b + j * BM, re = min(r + BM, en);
+                const int flag = re - r <= stream_rows ? kStreamTileFlag : 0;  // only the last can be short
+                if (t < max_tiles) tiles[t] = make_int4(e | flag, (int)r, (int)re, (int)((t - j + first) | (gm << 26)));
             }
         }
     }
@@ -626,9 +624,11 @@ __global__ __launch_bounds__(WGM* WGN* kWave, MOE_P_MINB) void grouped_gemm_pipe
 }
 
 // ------------------------------------------------------------------ stream tiles
-// An expert with at most kStreamRows rows runs as one stream tile: its rows
-// (64 token slots) against 256 weight rows, on the 64-K kernel's workgroup
-// of 8 waves and 160 KB of LDS.  Such a product is a stream of weight rows
+// An expert's last token tile, when it holds at most kStreamRows rows (a
+// whole small expert, or the rows past its full tiles), runs as a stream
+// tile: its rows (64 token slots) against 256 weight rows, on the 64-K
+// kernel's workgroup of 8 waves and 160 KB of LDS.  Such a product is a
+// stream of weight rows
 // (each is used by a few tokens only), so the tile is built for bytes in
 // flight: a ring of 4 stages of 40 KB (64 token rows and 256 weight rows of
 // 128 bytes, chunk c of row r at c ^ swz128(r)), filled by direct global->LDS
@@ -1567,7 +1567,8 @@ int64_t max_mtiles(int64_t N, int64_t E, int BM, int stream_rows) {
 hipError_t launch_build_tiles(const uint32_t* offsets, int E, int64_t N, int BM, int64_t max_tiles, int4* tiles,
                               uint32_t* count, hipStream_t s, int stream_rows, unsigned long long* queues,
                               int n_queues) {
-    if (max_tiles >= kMaxTiles || N >= (int64_t)0xFFFFFFFF || stream_rows < 0) return hipErrorInvalidValue;
+    if (max_tiles >= kMaxTiles || N >= (int64_t)0xFFFFFFFF || stream_rows < 0 || (stream_rows && stream_rows >= BM))
+        return hipErrorInvalidValue;
     if (n_queues < 0 || n_queues > 1024 || (n_queues > 0 && !queues)) return hipErrorInvalidValue;
     build_tiles_kernel<<<1, 1024, 0, s>>>(offsets, E, (uint32_t)N, BM, (uint32_t)stream_rows, (uint32_t)max_tiles,
                                           tiles, count, queues, n_queues);

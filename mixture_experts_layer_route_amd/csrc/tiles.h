@@ -13,9 +13,10 @@ constexpr int kGroupM = MOE_GROUP_M;
 static_assert(kGroupM >= 1 && kGroupM < 64, "group size is packed in 6 bits");
 constexpr int64_t kMaxTiles = int64_t(1) << 26;  // tile index packed in 26 bits
 
-// An expert with 1..stream_rows rows gets a single stream tile (its whole row
-// range), marked by this bit in the tile's expert field; the others get
-// BM-row tiles.  stream_rows = 0: BM-row tiles only.
+// An expert's rows are cut into BM-row tiles; its last tile, when it holds
+// 1..stream_rows rows (a whole small expert, or the rows past its full
+// tiles), is a stream tile, marked by this bit in the tile's expert field.
+// stream_rows = 0: BM-row tiles only.  (stream_rows < BM.)
 constexpr int kStreamTileFlag = 1 << 30;
 
 // Upper bound of the M-tiles that N rows over E experts produce: BM-row

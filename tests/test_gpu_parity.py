@@ -254,9 +254,11 @@ def test_experts_parity(cfg):
 
 @pytest.mark.parametrize("dt", ["bf16", "f16"])
 def test_experts_tile_choice_at_its_boundaries(dt):
-    """Experts of 1, 63, 64 (stream tiles), 65, 200, 256, 257 and 300 rows
-    (256-row tiles) and an empty one, in one launch, against the oracle."""
-    counts = [64, 65, 1, 0, 200, 257, 63, 256, 300, 1]
+    """Experts of 1, 63 and 64 rows (one stream tile), 65, 200 and 256 (one
+    256-row tile), 257, 300 and 576 (256-row tiles and a stream tile of the
+    last 1, 44 and 64 rows), 577 (three 256-row tiles, the last of 65 rows)
+    and an empty one, in one launch, against the oracle."""
+    counts = [64, 65, 1, 0, 200, 257, 63, 256, 300, 1, 576, 577]
     E, H, I = len(counts), 128, 192
     cfg = S.small_config(f"boundary_{dt}", T=sum(counts), H=H, I=I, E=E, top_k=1, dtype=dt, seed=86)
     x, _ = S.make_tokens(cfg)

@@ -4,8 +4,9 @@ The expert products walk a list of (expert, row range) token tiles that one
 workgroup builds on the device from expert_offsets, and map each workgroup
 id to one (token tile, weight tile) pair, group by group, in runs per XCD
 (csrc/experts.hip build_tiles_kernel, csrc/tiles.h tile_of_block).  With
-stream tiles enabled, an expert with at most SR rows gets one stream tile
-(flagged in bit 30 of its expert field) and the others tiles of BM rows.
+stream tiles enabled, an expert's last tile, when it holds at most SR rows
+(a whole small expert, or the rows past its full tiles), is a stream tile
+(flagged in bit 30 of its expert field); the others hold BM rows.
 These tests restate both in Python, integer for integer, and check on random
 routings -- Zipf-skewed, uniform, empty experts, one hot expert -- that
 every row of every expert lies in exactly one token tile of at most BM (or
@@ -36,21 +37,17 @@ def max_mtiles(N, E, BM, SR=0):
 
 
 def build_tiles(offsets, E, N, BM, max_tiles, G, SR=0):
-    """build_tiles_kernel: per expert, in ascending expert order, one stream
-    tile if it holds 1..SR rows, else ceil(rows / BM) tiles split into
-    ceil(n / G) groups of near-equal size (the first n % ng groups one tile
-    larger); each tile records its group's first tile (26 bits) and size
-    (6 bits)."""
+    """build_tiles_kernel: per expert, in ascending expert order,
+    ceil(rows / BM) tiles split into ceil(n / G) groups of near-equal size
+    (the first n % ng groups one tile larger); each tile records its group's
+    first tile (26 bits) and size (6 bits).  The last tile is a stream tile
+    when it holds 1..SR rows (SR < BM)."""
+    assert SR < BM
     tiles = []
     t = 0
     for e in range(E):
         b = min(int(offsets[e]), N)
         en = max(min(int(offsets[e + 1]), N), b)
-        if 0 < en - b <= SR:
-            if t < max_tiles:
-                tiles.append((e | STREAM_FLAG, b, en, t | (1 << MAX_TILE_BITS)))
-            t += 1
-            continue
         n = (en - b + BM - 1) // BM
         ng = (n + G - 1) // G
         sz = n // ng if ng else 0
@@ -63,8 +60,10 @@ def build_tiles(offsets, E, N, BM, max_tiles, G, SR=0):
                 first = big * (sz + 1) + (j - big * (sz + 1)) // sz * sz
                 gm = sz
             r = b + j * BM
+            re = min(r + BM, en)
+            flag = STREAM_FLAG if re - r <= SR else 0
             if t < max_tiles:
-                tiles.append((e, r, min(r + BM, en), (t - j + first) | (gm << MAX_TILE_BITS)))
+                tiles.append((e | flag, r, re, (t - j + first) | (gm << MAX_TILE_BITS)))
             t += 1
     return tiles, min(t, max_tiles)
 
@@ -115,22 +114,24 @@ def check_cover(counts, BM, G, n_tiles, SR=0):
     tiles, count = build_tiles(offsets, E, N, BM, mt + 10 ** 6, G, SR)
     assert count == len(tiles) <= mt
     # token tiles: every row of every expert exactly once, in its own expert;
-    # stream tiles hold a whole expert of 1..SR rows, the others <= BM rows
+    # a stream tile is an expert's last and holds 1..SR rows, the others
+    # hold BM rows, or fewer in an expert's last tile when that is over SR
     seen = np.zeros(N, np.int64)
     for x, r0, r1, _ in tiles:
         e = x & ~STREAM_FLAG
         assert offsets[e] <= r0 < r1 <= offsets[e + 1]
+        assert (r0 - offsets[e]) % BM == 0
         if x & STREAM_FLAG:
-            assert SR and (r0, r1) == (offsets[e], offsets[e + 1]) and r1 - r0 <= SR
+            assert SR and r1 == offsets[e + 1] and r1 - r0 <= SR
         else:
-            assert r1 - r0 <= BM and offsets[e + 1] - offsets[e] > SR
+            assert r1 - r0 == BM or (r1 == offsets[e + 1] and r1 - r0 > SR)
         seen[r0:r1] += 1
     assert (seen == 1).all()
-    # groups: consecutive tiles of one expert, at most G of them
+    # groups: consecutive tiles of one expert (its stream tile among them), at most G of them
     for m, (x, _, _, g) in enumerate(tiles):
         first, gm = g & ((1 << MAX_TILE_BITS) - 1), g >> MAX_TILE_BITS
         assert 1 <= gm <= G and first <= m < first + gm
-        assert all(tiles[i][0] == x for i in range(first, min(first + gm, count)))
+        assert all(tiles[i][0] & ~STREAM_FLAG == x & ~STREAM_FLAG for i in range(first, min(first + gm, count)))
     # the launched grid: every (token tile, weight tile) pair exactly once
     nblocks = mt * n_tiles
     hits = np.zeros((max(count, 1), n_tiles), np.int64)
@@ -220,8 +221,8 @@ def test_tiles_cover_every_row_and_pair_once(G, kind):
 
 @pytest.mark.parametrize("kind", ["zipf", "uniform", "holes", "hot"])
 def test_stream_and_block_tiles_cover_every_row_and_pair_once(kind):
-    """The 64-K kernel's list: stream tiles for experts of at most 64 rows,
-    256-row tiles for the others."""
+    """The 64-K kernel's list: 256-row tiles, and a stream tile for an
+    expert's last tile of at most 64 rows."""
     rng = np.random.default_rng(300 + len(kind))
     for _ in range(40):
         E = int(rng.choice([1, 3, 8, 64, 128, 256]))
@@ -243,14 +244,30 @@ def test_stream_bound_is_tight_and_holds_at_the_edges():
 
 def test_prefill_and_skewed_shapes():
     """The benchmark's shapes: 49152 rows over 64 experts (11 and 8 weight
-    tiles), 65536 rows over 256 Zipf-skewed experts (16 and 28)."""
+    tiles), 65536 rows over 256 Zipf-skewed experts (16 and 28), with and
+    without stream tiles."""
     rng = np.random.default_rng(7)
-    check_cover(routing_counts(rng, "uniform", 64, 49152), 256, 8, 11)
-    check_cover(routing_counts(rng, "uniform", 64, 49152), 256, 8, 8)
-    w = np.arange(1, 257, dtype=np.float64) ** -2.2
-    c = rng.multinomial(65536, w / w.sum())
-    check_cover(c, 256, 8, 16)
-    check_cover(c, 256, 8, 28)
+    for SR in (0, 64):
+        check_cover(routing_counts(rng, "uniform", 64, 49152), 256, 8, 11, SR=SR)
+        check_cover(routing_counts(rng, "uniform", 64, 49152), 256, 8, 8, SR=SR)
+        w = np.arange(1, 257, dtype=np.float64) ** -2.2
+        c = rng.multinomial(65536, w / w.sum())
+        check_cover(c, 256, 8, 16, SR=SR)
+        check_cover(c, 256, 8, 28, SR=SR)
+
+
+def test_short_last_tiles_become_stream_tiles():
+    """769 rows: three 256-row tiles and a stream tile of one row, in the
+    expert's group; 64 rows: one stream tile; 321 rows: 256 + a stream tile
+    of 65 rows is not allowed, so a 65-row block tile."""
+    offsets = np.array([0, 769, 833, 1154])
+    tiles, count = build_tiles(offsets, 3, 1154, 256, 100, 8, 64)
+    assert [(x & ~STREAM_FLAG, bool(x & STREAM_FLAG), r0, r1) for x, r0, r1, _ in tiles] == [
+        (0, False, 0, 256), (0, False, 256, 512), (0, False, 512, 768), (0, True, 768, 769),
+        (1, True, 769, 833),
+        (2, False, 833, 1089), (2, False, 1089, 1154)]
+    assert [(g & ((1 << MAX_TILE_BITS) - 1), g >> MAX_TILE_BITS) for *_, g in tiles] == [
+        (0, 4), (0, 4), (0, 4), (0, 4), (4, 1), (5, 2), (5, 2)]
 
 
 def test_group_bits_hold_the_largest_list():
