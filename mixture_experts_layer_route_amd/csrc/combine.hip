@@ -18,9 +18,9 @@ namespace moe {
 namespace {
 
 // grid (tokens, column chunks): thread -> VEC consecutive columns of one
-// token.  The token's k rows and weights are wave-uniform; the k loads are
-// issued in batches of 8 before their multiply-adds, so the loads of one
-// thread overlap instead of forming a chain of round trips.
+// token.  The token's k rows and weights are wave-uniform; they and the k row
+// loads are issued in batches of 8 before their multiply-adds, so the loads
+// of one thread overlap instead of forming a chain of round trips.
 template <typename DT, typename WT, int VEC>
 __global__ __launch_bounds__(256) void combine_kernel(const typename DT::storage* __restrict__ Y, int64_t N,
                                                       const uint32_t* __restrict__ row_of_slot,
@@ -33,36 +33,49 @@ __global__ __launch_bounds__(256) void combine_kernel(const typename DT::storage
     if (c0 >= H) return;
     const uint32_t* rs = row_of_slot + t * k;
     const typename WT::storage* ws = w + t * k;
-    bool nan_row = false;
-    for (int j = 0; j < k; ++j) nan_row |= (int64_t)rs[j] >= N;
     float acc[VEC];
 #pragma unroll
-    for (int v = 0; v < VEC; ++v) acc[v] = nan_row ? __uint_as_float(0x7fc00000u) : 0.0f;
-    if (!nan_row) {
-        constexpr int B = 8;
-        for (int j0 = 0; j0 < k; j0 += B) {
-            S vals[B][VEC];
+    for (int v = 0; v < VEC; ++v) acc[v] = 0.0f;
+    bool nan_row = false;
+    constexpr int B = 8;
+    for (int j0 = 0; j0 < k; j0 += B) {
+        // the batch's rows and weights, loaded unconditionally (slots past
+        // k re-read the last one) so that the loads go out together
+        uint32_t r[B];
+        float wj[B];
 #pragma unroll
-            for (int b = 0; b < B; ++b) {
-                if (j0 + b < k) {
-                    const S* yr = Y + (int64_t)rs[j0 + b] * H + c0;
-                    if constexpr (VEC * sizeof(S) == 16) {
-                        *(uint4*)vals[b] = load_nt16(yr);
-                    } else {
+        for (int b = 0; b < B; ++b) {
+            const int j = min(j0 + b, k - 1);
+            r[b] = rs[j];
+            wj[b] = fmt<WT>::load(ws[j]);
+        }
 #pragma unroll
-                        for (int v = 0; v < VEC; ++v) vals[b][v] = yr[v];
-                    }
-                }
-            }
+        for (int b = 0; b < B; ++b) nan_row |= j0 + b < k && (int64_t)r[b] >= N;
+        if (nan_row) break;
+        S vals[B][VEC];
 #pragma unroll
-            for (int b = 0; b < B; ++b) {
-                if (j0 + b < k) {  // slots in fixed order j = 0..k-1
-                    const float wj = fmt<WT>::load(ws[j0 + b]);
+        for (int b = 0; b < B; ++b) {
+            if (j0 + b < k) {
+                const S* yr = Y + (int64_t)r[b] * H + c0;
+                if constexpr (VEC * sizeof(S) == 16) {
+                    *(uint4*)vals[b] = load_nt16(yr);
+                } else {
 #pragma unroll
-                    for (int v = 0; v < VEC; ++v) acc[v] = fmaf(wj, fmt<DT>::load(vals[b][v]), acc[v]);
+                    for (int v = 0; v < VEC; ++v) vals[b][v] = yr[v];
                 }
             }
         }
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            if (j0 + b < k) {  // slots in fixed order j = 0..k-1
+#pragma unroll
+                for (int v = 0; v < VEC; ++v) acc[v] = fmaf(wj[b], fmt<DT>::load(vals[b][v]), acc[v]);
+            }
+        }
+    }
+    if (nan_row) {
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) acc[v] = __uint_as_float(0x7fc00000u);
     }
     S res[VEC];
 #pragma unroll

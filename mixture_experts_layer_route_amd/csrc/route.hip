@@ -35,7 +35,10 @@ __global__ __launch_bounds__(256) void route_kernel(const typename LT::storage* 
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
         const int e = lane + kWave * i;
-        v[i] = (e < E) ? fmt<LT>::load(row[e]) : -INFINITY;
+        // loaded unconditionally (lanes past E re-read the last logit), so
+        // that the lane's loads go out together
+        const float x = fmt<LT>::load(row[min(e, E - 1)]);
+        v[i] = (e < E) ? x : -INFINITY;
         if (e < E) {
             nan_or_pinf |= (v[i] != v[i]) || (v[i] == INFINITY);
             finite_or_pinf |= (v[i] != -INFINITY);

@@ -49,14 +49,23 @@ __global__ __launch_bounds__(kGroupedWaves* kWave) void route_grouped_kernel(
 
     float c[EPL];
     bool nan_seen = false;
+    // the lane's logits and biases, loaded unconditionally (lanes past E
+    // re-read the last expert's) so that the loads go out together
+    float xs[EPL], bs[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        const int ec = min(lane + kWave * i, E - 1);
+        xs[i] = fmt<LT>::load(row[ec]);
+        bs[i] = bias ? bias[ec] : 0.0f;
+    }
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
         const int e = lane + kWave * i;
         c[i] = 0.0f;
         if (e < E) {
-            const float x = fmt<LT>::load(row[e]);
+            const float x = xs[i];
             const float s = 1.0f / (1.0f + expf(-x));
-            c[i] = (s + (bias ? bias[e] : 0.0f)) + 0.0f;  // + 0 turns -0 into +0
+            c[i] = (s + bs[i]) + 0.0f;  // + 0 turns -0 into +0
             nan_seen |= (c[i] != c[i]);
             cs[e] = c[i];
             ss[e] = s;

@@ -49,7 +49,8 @@ __device__ __forceinline__ void row_scores(const typename LT::storage* row, int 
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
         const int e = lane + kWave * i;
-        v[i] = e < E ? fmt<LT>::load(row[e]) : -INFINITY;
+        const float x = fmt<LT>::load(row[min(e, E - 1)]);  // unconditional: the loads go out together
+        v[i] = e < E ? x : -INFINITY;
     }
     if (scoring == 0) {
         float m = -INFINITY;

@@ -945,8 +945,16 @@ __global__ __launch_bounds__(256) void combine_backward_kernel(
     const int64_t t = blockIdx.x;
     const int tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
     const uint32_t* rs = row_of_slot + t * k;
+    // slot rows and weights are loaded unconditionally, clamped to the last
+    // slot, so that each batch's loads go out together
     bool invalid = false;
-    for (int j = 0; j < k; ++j) invalid |= (int64_t)rs[j] >= N;
+    for (int j0 = 0; j0 < k; j0 += B) {
+        uint32_t r[B];
+#pragma unroll
+        for (int b = 0; b < B; ++b) r[b] = rs[min(j0 + b, k - 1)];
+#pragma unroll
+        for (int b = 0; b < B; ++b) invalid |= j0 + b < k && (int64_t)r[b] >= N;
+    }
     const S* gt = g + t * H;
     const int64_t chunks = H / VEC;
     for (int j0 = 0; j0 < k; j0 += B) {
@@ -954,9 +962,12 @@ __global__ __launch_bounds__(256) void combine_backward_kernel(
         int64_t row[B];
 #pragma unroll
         for (int b = 0; b < B; ++b) {
+            const int j = min(j0 + b, k - 1);
+            const uint32_t rr = rs[j];
+            const float wv = fmt<WT>::load(w[t * k + j]);
             dot[b] = 0.0f;
-            row[b] = j0 + b < k ? (int64_t)rs[j0 + b] : N;  // N: no slot, or a slot past the rows
-            wj[b] = row[b] < N ? fmt<WT>::load(w[t * k + j0 + b]) : 0.0f;
+            row[b] = j0 + b < k ? (int64_t)rr : N;  // N: no slot, or a slot past the rows
+            wj[b] = row[b] < N ? wv : 0.0f;
         }
         for (int64_t c = tid; c < chunks; c += 256) {
             S gv[VEC], yv[B][VEC];
@@ -1023,33 +1034,42 @@ __global__ __launch_bounds__(256) void dispatch_backward_kernel(const typename D
     const int64_t c0 = ((int64_t)blockIdx.y * blockDim.x + threadIdx.x) * VEC;
     if (c0 >= H) return;
     const uint32_t* rs = row_of_slot + t * k;
-    bool invalid = false;
-    for (int j = 0; j < k; ++j) invalid |= (int64_t)rs[j] >= N;
     float acc[VEC];
 #pragma unroll
-    for (int v = 0; v < VEC; ++v) acc[v] = invalid ? __uint_as_float(0x7fc00000u) : 0.0f;
-    if (!invalid) {
-        constexpr int B = 8;
-        for (int j0 = 0; j0 < k; j0 += B) {
-            S vals[B][VEC];
+    for (int v = 0; v < VEC; ++v) acc[v] = 0.0f;
+    bool invalid = false;
+    constexpr int B = 8;
+    for (int j0 = 0; j0 < k; j0 += B) {
+        // the batch's rows, loaded unconditionally (slots past k re-read the
+        // last one) so that the loads go out together
+        uint32_t r[B];
 #pragma unroll
-            for (int b = 0; b < B; ++b) {
-                if (j0 + b < k) {
-                    const S* src = drows + (int64_t)rs[j0 + b] * H + c0;
-                    if constexpr (VEC * sizeof(S) == 16)
-                        *(uint4*)vals[b] = load_nt16(src);
-                    else
-                        vals[b][0] = *src;
-                }
-            }
+        for (int b = 0; b < B; ++b) r[b] = rs[min(j0 + b, k - 1)];
 #pragma unroll
-            for (int b = 0; b < B; ++b) {
-                if (j0 + b < k) {
+        for (int b = 0; b < B; ++b) invalid |= j0 + b < k && (int64_t)r[b] >= N;
+        if (invalid) break;
+        S vals[B][VEC];
 #pragma unroll
-                    for (int v = 0; v < VEC; ++v) acc[v] += fmt<DT>::load(vals[b][v]);
-                }
+        for (int b = 0; b < B; ++b) {
+            if (j0 + b < k) {
+                const S* src = drows + (int64_t)r[b] * H + c0;
+                if constexpr (VEC * sizeof(S) == 16)
+                    *(uint4*)vals[b] = load_nt16(src);
+                else
+                    vals[b][0] = *src;
             }
         }
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            if (j0 + b < k) {
+#pragma unroll
+                for (int v = 0; v < VEC; ++v) acc[v] += fmt<DT>::load(vals[b][v]);
+            }
+        }
+    }
+    if (invalid) {
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) acc[v] = __uint_as_float(0x7fc00000u);
     }
     S ov[VEC];
 #pragma unroll
