@@ -274,6 +274,29 @@ def test_experts_tile_choice_at_its_boundaries(dt):
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_leftover_rows_with_deep_k_and_several_weight_tiles(dt):
+    """Experts whose last token tile holds 1, 10, 33 and 64 rows after full
+    256-row tiles (a stream tile in the gate/up product, a 256-row tile in
+    the down product), whole experts of 64 and 65 rows, an empty expert and
+    one of exactly three tiles, with K of 8 (gate/up) and 7 (down) 64-wide
+    steps and 4 and 2 weight tiles: the persistent launch moves between
+    prefetched 256-row tiles and stream tiles in both products."""
+    counts = [3 * 256 + 10, 2 * 256 + 64, 256 + 1, 64, 4 * 256 + 33, 65, 0, 3 * 256]
+    E, H, I = len(counts), 512, 448
+    cfg = S.small_config(f"leftover_{dt}", T=sum(counts), H=H, I=I, E=E, top_k=1, dtype=dt, seed=90)
+    x, _ = S.make_tokens(cfg)
+    W = S.make_weights(cfg)
+    rows = host_bits(x)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.uint32)
+    Y = oracle.experts(*[host_bits(w) for w in W], dt, rows, offsets, E, H, I, nthreads=NTHREADS)
+    ex = moe.SwiGluExperts(*[w.to(DEV) for w in W])
+    g_off = torch.from_numpy(offsets.view(np.int32)).view(torch.uint32).to(DEV)
+    gy = ex.forward_dispatched(x.to(DEV), g_off)
+    torch.cuda.synchronize()
+    assert_close(values(gy, dt), oracle.widen(Y, dt), dt, f"expert outputs, leftover rows ({dt})")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
 def test_decode_kernel_token_tiles_at_their_boundaries(dt):
     """Experts of 15, 16 (one 16-row token tile), 17, 33 and 48 rows (two to
     three tiles), 1, 2 and none, among 40 experts (132 rows, at most 4 per
