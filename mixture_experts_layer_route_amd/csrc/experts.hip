@@ -39,7 +39,10 @@
 //     filled by direct global->LDS loads into two token-row slots and three
 //     weight-row slots of 32 KB, the weight rows issued about two steps
 //     ahead, a quarter per 16-K sub-step, and the token rows one step ahead,
-//     in the last sub-step of a step; epilogues staged through LDS.
+//     in the last sub-step of a step; epilogues staged through LDS while the
+//     next tile's first steps load.  An expert of at most 64 rows, and in
+//     the gate/up product an expert's last rows past its full tiles when at
+//     most 64, run as a stream tile of 64 token slots.
 //   grouped_gemm_pipe_kernel (bf16/f16, K a multiple of 32 but not of 64, or
 //     a row-operand buffer of 4 GiB or more, which the 64-K kernel's 32-bit
 //     offsets cannot span): 256x256 tiles on
