@@ -409,41 +409,44 @@ __device__ __forceinline__ void store_tile32(const f32x16_t (&acc)[MB][NB], type
 
 // The training forward's FP32 pre-activations of the gate/up product (g at
 // columns [0, I) of a row of gu, u at [I, 2I)), staged through LDS: per
-// round of 64 token rows each wave writes its 64 x 32 g and u values into its
-// own 16 KB (128-byte rows, 16-byte chunk c of row t at c ^ ((t / 2) % 8)),
-// then reads them back a chunk per lane, so a store instruction writes 8
-// whole 128-byte row segments instead of 16 bytes of 32 rows.
-template <int MB, int NB, int WTM, int WCN>
+// round of RR token rows (32 or 64) each wave writes its RR x 32 g and u
+// values into its own RR * 256 bytes (128-byte rows, g rows then u rows,
+// 16-byte chunk c of row t at c ^ ((t / 2) % 8)), then reads them back a
+// chunk per lane, so a store instruction writes 8 whole 128-byte row
+// segments instead of 16 bytes of 32 rows.
+template <int MB, int NB, int WTM, int WCN, int RR = 64>
 __device__ __forceinline__ void save_preact_staged(const f32x16_t (&acc)[MB][NB], float* __restrict__ gu, int r0,
                                                    int r1, int n0, int wm, int wn, int I, int lane,
                                                    unsigned char* stage) {
-    static_assert(WCN == 32 && NB == 2 && MB % 2 == 0, "one gate and one up block of 32 columns per wave");
+    static_assert(WCN == 32 && NB == 2, "one gate and one up block of 32 columns per wave");
+    static_assert((RR == 32 || RR == 64) && (MB * 32) % RR == 0, "rounds of whole 32-row blocks");
+    constexpr int BPR = RR / 32, UOFF = RR * 128;  // blocks per round; offset of the u rows
     asm volatile("" : "+v"(lane));  // keeps the addresses out of the K loop
     const int frow = lane & 31, kg = lane >> 5;
     const int c = lane & 7, rr = lane >> 3;
     const int col = n0 + wn * WCN + 4 * c;
 #pragma unroll
-    for (int h = 0; h < MB / 2; ++h) {
+    for (int h = 0; h < MB / BPR; ++h) {
 #pragma unroll
-        for (int ii = 0; ii < 2; ++ii) {
+        for (int ii = 0; ii < BPR; ++ii) {
             const int t = 32 * ii + frow, sw = (t >> 1) & 7;
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const f32x16_t& ga = acc[2 * h + ii][0];
-                const f32x16_t& ua = acc[2 * h + ii][1];
+                const f32x16_t& ga = acc[BPR * h + ii][0];
+                const f32x16_t& ua = acc[BPR * h + ii][1];
                 const int a = t * 128 + (((2 * g + kg) ^ sw) << 4);
                 *(float4*)(stage + a) = make_float4(ga[4 * g], ga[4 * g + 1], ga[4 * g + 2], ga[4 * g + 3]);
-                *(float4*)(stage + 8192 + a) = make_float4(ua[4 * g], ua[4 * g + 1], ua[4 * g + 2], ua[4 * g + 3]);
+                *(float4*)(stage + UOFF + a) = make_float4(ua[4 * g], ua[4 * g + 1], ua[4 * g + 2], ua[4 * g + 3]);
             }
         }
         wait_lgkm0();
 #pragma unroll
-        for (int t0 = 0; t0 < 64; t0 += 8) {
+        for (int t0 = 0; t0 < RR; t0 += 8) {
             const int t = t0 + rr;
             const int a = t * 128 + ((c ^ ((t >> 1) & 7)) << 4);
             const float4 g4 = *(const float4*)(stage + a);
-            const float4 u4 = *(const float4*)(stage + 8192 + a);
-            const int grow = r0 + wm * WTM + 64 * h + t;
+            const float4 u4 = *(const float4*)(stage + UOFF + a);
+            const int grow = r0 + wm * WTM + RR * h + t;
             if (grow < r1 && col < I) {
                 float* p = gu + (int64_t)grow * 2 * I + col;
                 *(float4*)p = g4;
@@ -1045,7 +1048,7 @@ __global__ __launch_bounds__(WGM* WGN* kWave, 1) void grouped_gemm_pipe64_kernel
     static_assert(LPO + LPO / 4 <= 2 * NM, "at most two DMA pieces per MFMA of a sub-step");
     static_assert(NA == 2 && NB_ == 3, "the vmcnt waits below are counted for 2 token and 3 weight slots");
     static_assert(GATEUP || NW * WTM * WTN * 2 <= (NA + NB_) * SLOT, "the staged outputs fit the LDS");
-    static_assert(!GATEUP || NW * 16384 <= (NA + NB_) * SLOT, "the staged pre-activations fit the LDS");
+    static_assert(!GATEUP || NW * 8192 <= 2 * SLOT, "the staged pre-activations fit the staging slots");
     static_assert(NW * kWave <= 512, "one workgroup of at most 8 waves");
     __shared__ __attribute__((aligned(1024))) unsigned char smem[(NA + NB_) * SLOT];
 
@@ -1059,9 +1062,7 @@ __global__ __launch_bounds__(WGM* WGN* kWave, 1) void grouped_gemm_pipe64_kernel
     const int xcd = blockIdx.x % kXcds, live = min(nblocks, live_m * n_tiles);
     // The epilogue stages its outputs in weight slots 1 and 2 (64 KB), so the
     // next tile's token rows of steps 0 and 1 and weight rows of step 0 can
-    // land in the other three slots meanwhile (the training forward's FP32
-    // pre-activations need more of the LDS: it loads them afterwards).
-    const bool prefetch = !GATEUP || gu == nullptr;
+    // land in the other three slots meanwhile.
     unsigned char* const stage = smem + (NA + 1) * SLOT;
     // (an LDS pointer: through a generic one the word's accesses would be
     // flat instructions, whose waits also drain every load and store)
@@ -1309,7 +1310,7 @@ __global__ __launch_bounds__(WGM* WGN* kWave, 1) void grouped_gemm_pipe64_kernel
             // slot 0; its weight rows of step 1 and first ones of step 2 go
             // into the staging slots once every wave has read them back
             pre = false;
-            if (prefetch && nxt >= 0) {
+            if (nxt >= 0) {
                 int m_idx, n_idx;
                 tile_of_id(nxt, n_tiles, live_m, tiles, &m_idx, &n_idx);
                 const int4 tl = tiles[m_idx];
@@ -1329,11 +1330,13 @@ __global__ __launch_bounds__(WGM* WGN* kWave, 1) void grouped_gemm_pipe64_kernel
                 static_assert(staged_gu && NW == 8, "h is staged tile-wide: 8 waves of 32 h columns");
                 store_gateup_staged<DT, MB, WTM>(acc, C, t_r0, t_r1, t_n0, wm, wn, wid, NOUT, lane, stage);
                 if (gu) {
-                    // every wave has read its h rows back before the region is reused
+                    // every wave has read its h rows back before the region is
+                    // reused: 8 KB per wave, in rounds of 32 rows
                     wait_lgkm0();
                     barrier_lds();
-                    save_preact_staged<MB, NB, WTM, WCN>(acc, gu, t_r0, t_r1, t_n0, wm, wn, NOUT, lane,
-                                                         smem + wid * 16384);
+                    static_assert(NW * 32 * 256 == 2 * SLOT, "rounds of 32 rows in the two staging slots");
+                    save_preact_staged<MB, NB, WTM, WCN, 32>(acc, gu, t_r0, t_r1, t_n0, wm, wn, NOUT, lane,
+                                                             stage + wid * (32 * 256));
                 }
             } else if constexpr (WTN == 64) {
                 // two rounds of 8 KB per wave
