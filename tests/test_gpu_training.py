@@ -341,21 +341,16 @@ def run_step_on_device(cfg):
                 ddown=ddown, dx=dx, dlg=dlg)
 
 
-def check_sampled(cfg, r, tokens, experts, n_cols, rng):
-    """Sampled checks the oracle computes one by one: dx and dlogits of some
-    tokens (each token's rows through the oracle with the full expert
-    weights), and dgate / dup / ddown on some intermediate columns of some
-    experts (column i of those gradients depends only on column i of g, u, h
-    and dh, so a sliced expert gives them exactly)."""
-    E, H, I, k = cfg.E, cfg.H, cfg.I, cfg.top_k
+def check_tokens(cfg, r, tokens):
+    """dx and dlogits of some tokens, each token's k rows through the oracle
+    with the full expert weights (dx sums the token's k row gradients, and
+    dlogits needs the combine backward's weight gradients of all k slots)."""
+    H, I, k = cfg.H, cfg.I, cfg.top_k
     W = r["W"]
     idx = host_bits(r["plan"].expert_indices())
-    offsets = host_bits(r["d"].expert_offsets)
-    tor = host_bits(r["d"].token_of_row)
     ros = host_bits(r["d"].row_of_slot)
     xb, lb, gb = host_bits(r["x"]), host_bits(r["lg"]), host_bits(r["gout"])
     ldt = cfg.logits_dtype
-    assert int(offsets[E]) == cfg.T * k
     for t in tokens:
         rows_t = ros[t * k:(t + 1) * k]
         w32 = oracle.router_weights(lb[t:t + 1], ldt, idx[t:t + 1], "softmax", cfg.renormalize, 1.0)
@@ -378,9 +373,63 @@ def check_sampled(cfg, r, tokens, experts, n_cols, rng):
         assert_close(values(r["dx"][t], cfg.dtype), oracle.widen(oracle.narrow(gdx_t, cfg.dtype), cfg.dtype),
                      cfg.dtype, f"{cfg.name} dx token {t}")
         assert_close(values(r["dlg"][t], ldt), oracle.widen(odl, ldt)[0], cfg.dtype, f"{cfg.name} dlogits token {t}")
+
+
+def check_rows_of_every_tile(cfg, r, tile_rows=128):
+    """The combine backward's dY and the experts backward's grad_rows on the
+    first and last row of every tile_rows-row tile of every expert (the row
+    products' tiles are 128 rows, the forward's 256), each row through the
+    oracle with its expert's full weights.  A row's results depend on that
+    row alone, so these rows are exact references at any batch size."""
+    E, H, I, k = cfg.E, cfg.H, cfg.I, cfg.top_k
+    W = r["W"]
+    idx = host_bits(r["plan"].expert_indices())
+    offsets = host_bits(r["d"].expert_offsets).astype(np.int64)
+    tor = host_bits(r["d"].token_of_row).astype(np.int64)
+    ros = host_bits(r["d"].row_of_slot).astype(np.int64).reshape(cfg.T, k)
+    xb, lb, gb = host_bits(r["x"]), host_bits(r["lg"]), host_bits(r["gout"])
+    n_checked = 0
+    for e in range(E):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if b == a:
+            continue
+        starts = list(range(a, b, tile_rows))
+        rows = np.array(sorted(set(starts) | {min(s + tile_rows, b) - 1 for s in starts}), np.int64)
+        toks = tor[rows]
+        slot = np.argmax(ros[toks] == rows[:, None], axis=1)
+        assert np.all(ros[toks, slot] == rows)
+        w32 = oracle.router_weights(lb[toks], cfg.logits_dtype, idx[toks], "softmax", cfg.renormalize, 1.0)
+        wsel = np.ascontiguousarray(w32[np.arange(rows.size), slot][:, None])
+        We = [host_bits(w[e:e + 1]) for w in W]
+        n = rows.size
+        off1 = np.array([0, n], np.uint32)
+        fw = oracle.experts_train_forward(*We, cfg.dtype, xb[toks], off1, 1, H, I, NTHREADS)
+        ody, _ = oracle.combine_backward(fw["output"], cfg.dtype, np.arange(n, dtype=np.uint32), wsel, "f32",
+                                         gb[toks], n, 1, H)
+        odx, _, _, _ = oracle.experts_backward(*We, cfg.dtype, xb[toks], off1, 1, H, I, fw["g"], fw["u"], fw["h"],
+                                               ody, NTHREADS)
+        ti = torch.as_tensor(rows, device=DEV)
+        tag = f"{cfg.name} expert {e} ({b - a} rows, {n} rows checked)"
+        assert_close(values(r["dy"][ti], cfg.dtype), oracle.widen(ody, cfg.dtype), cfg.dtype, f"dY {tag}")
+        assert_close(values(r["drows"][ti], cfg.dtype), oracle.widen(odx, cfg.dtype), cfg.dtype, f"grad_rows {tag}")
+        n_checked += n
+    log(f"  dY and grad_rows checked on {n_checked} rows (first and last of every {tile_rows}-row tile)")
+
+
+def check_expert_columns(cfg, r, experts, cols_of):
+    """dgate, dup and ddown of the given experts on columns cols_of(e) of the
+    intermediate dimension: column i of these gradients depends only on
+    column i of g, u, h and dh, so the oracle on the expert's weights sliced
+    to those columns gives them exactly (rows [i, :] of dgate and dup,
+    column [:, i] of ddown)."""
+    H = cfg.H
+    W = r["W"]
+    offsets = host_bits(r["d"].expert_offsets)
+    tor = host_bits(r["d"].token_of_row)
+    xb = host_bits(r["x"])
     for e in experts:
         a, b = int(offsets[e]), int(offsets[e + 1])
-        cols = np.sort(rng.choice(I, size=n_cols, replace=False))
+        cols = np.asarray(cols_of(e), np.int64)
         gate_s = host_bits(W[0][e, cols])[None]
         up_s = host_bits(W[1][e, cols])[None]
         down_s = np.ascontiguousarray(host_bits(W[2][e][:, cols]))[None]
@@ -398,22 +447,38 @@ def check_sampled(cfg, r, tokens, experts, n_cols, rng):
         assert_close_sum(r["ddown"][e][:, cols].cpu().double().numpy(), odd[0], ld[0], cfg.dtype, f"ddown {tag}")
 
 
+def one_column_per_block(I, rng, block=128):
+    """A random column in every block of 128 intermediate columns (the
+    weight-gradient tiles' extent along I), plus one more anywhere."""
+    cols = {int(rng.integers(s, min(s + block, I))) for s in range(0, I, block)}
+    cols.add(int(rng.integers(0, I)))
+    return sorted(cols)
+
+
 def test_training_step_full_size_sampled():
     """Prefill BF16 (T=8192, H=2048, I=1408, E=64, top_k=6) through the same
-    calls the benchmark times, checked on sampled tokens and gradient columns."""
+    calls the benchmark times: dY and grad_rows on the first and last row of
+    every row tile of every expert, the weight gradients of every expert on
+    a column in every 128-column block, and dx and dlogits of 16 tokens."""
     cfg = S.CONFIGS["prefill_bf16"]
     log("training full size: prefill_bf16")
     r = run_step_on_device(cfg)
-    log("  device step done; sampling")
+    log("  device step done; checking")
     rng = np.random.default_rng(9)
-    check_sampled(cfg, r, rng.choice(cfg.T, size=6, replace=False), rng.choice(cfg.E, size=2, replace=False), 8, rng)
+    check_rows_of_every_tile(cfg, r)
+    check_expert_columns(cfg, r, range(cfg.E), lambda e: one_column_per_block(cfg.I, rng))
+    log(f"  weight gradients checked on all {cfg.E} experts")
+    check_tokens(cfg, r, rng.choice(cfg.T, size=16, replace=False))
 
 
 def test_training_step_skewed_routing_sampled():
     """Zipf(1.1)-skewed routing over 256 experts (the skewed workload's
     routing at H=1024, I=512): the hottest expert owns thousands of rows, so
     the weight-gradient products run long K loops and the row products many
-    tiles of one expert, while cold experts own a few rows or none."""
+    tiles of one expert, while cold experts own a few rows or none.  dY and
+    grad_rows on the first and last row of every row tile, the weight
+    gradients of every expert with rows on a column per 128-column block,
+    zero gradients for experts without rows, and dx and dlogits of 4 tokens."""
     cfg = S.small_config("skewed_train_bf16", T=8192, H=1024, I=512, E=256, top_k=8, dtype="bf16", zipf_s=1.1,
                          seed=1104)
     log("training skewed routing: T=8192 H=1024 I=512 E=256 k=8")
@@ -423,8 +488,9 @@ def test_training_step_skewed_routing_sampled():
     log(f"  rows per expert: max {counts.max()}, median {int(np.median(counts))}, empty {int((counts == 0).sum())}")
     assert counts[0] > 2000
     rng = np.random.default_rng(10)
-    experts = [0, int(np.argmin(np.where(counts > 0, counts, 1 << 30))), int(rng.integers(1, cfg.E))]
-    check_sampled(cfg, r, rng.choice(cfg.T, size=4, replace=False), experts, 6, rng)
+    check_rows_of_every_tile(cfg, r)
+    check_expert_columns(cfg, r, np.nonzero(counts > 0)[0], lambda e: one_column_per_block(cfg.I, rng))
+    check_tokens(cfg, r, rng.choice(cfg.T, size=4, replace=False))
     empty = np.nonzero(counts == 0)[0]
     for e in empty[:3]:
         assert float(r["dgate"][e].abs().max()) == 0.0 and float(r["ddown"][e].abs().max()) == 0.0
