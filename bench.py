@@ -9,7 +9,7 @@ inputs and weights already resident in HBM.  Prints one JSON line:
   value        whole-job tokens/s of the timed fused forwards;
   event_ms_per_step  their per-step device times (mean, median), and the
                median of K more forwards each run after a 512 MiB scratch
-               write that flushes the last-level cache (cold_median);
+               read that flushes the last-level cache (cold_median);
   roofline     the dominant kernel (the gate/up grouped GEMM), its
                algorithmic FLOPs (or bytes, at decode) per launch over its
                average launch time, measured with HIP events recorded on the
@@ -167,15 +167,17 @@ COLD_SCRATCH_MIB = 512
 
 def cold_forwards(ex, x, lg, opts, ws, out, steps: int) -> float:
     """Median device time of K fused forwards, each after a 512 MiB scratch
-    write that evicts the 256 MB last-level cache, so no input of the
-    forward is cached when it starts (timed after the K steps of record,
-    back to back, with events around each forward only)."""
+    read that evicts the 256 MB last-level cache, so no input of the forward
+    is cached when it starts (timed after the K steps of record, back to
+    back, with events around each forward only).  The scratch is written once
+    beforehand: flushing with writes would leave the forward ~256 MB of dirty
+    lines to write back, which added ~50 us to the decode forward."""
     import torch
 
-    scratch = torch.empty(COLD_SCRATCH_MIB << 20, dtype=torch.uint8, device=x.device)
+    scratch = torch.ones(COLD_SCRATCH_MIB << 17, dtype=torch.int32, device=x.device)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for i, (a, b) in enumerate(evs):
-        scratch.fill_(i & 0xFF)
+    for a, b in evs:
+        scratch.sum()
         a.record()
         ex.forward(x, lg, opts, ws, out)
         b.record()
